@@ -1,0 +1,250 @@
+"""Acceptance, residual/bonus sampling and longest-path selection (oracle; test infrastructure only).
+
+Rules, in the pages' order:
+
+* Token-level test: accept draft x with probability min(1, p(x)/q(x)); with a
+  supplied uniform u in [0,1) this is  u < p(x)/q(x)  ([P2] section 2.1; [P4]
+  section "数学保证：无损输出质量" compares a uniform with the ratio; [P5]
+  section on exact verification).  For tree node i, p is the target row of its
+  parent (the row that predicts node i) and q is node i's own draft row.
+* On rejection, sample from norm([p - q]_+) ([P2] section 2.1; [P4] same
+  section; [P5]).  If every candidate on the path passed, draw a bonus token
+  from the target's next-position distribution ([P2] section 2.2; [P5]).
+* Chains are checked left to right and stop at the first rejection ([P2]
+  section 2.2); in a tree only the prefix accepted consecutively from the root
+  counts and the longest such path is kept ([P1] section 2.3; [P5] figure 3).
+* Greedy mode accepts a candidate iff it equals the target's best token at
+  that position ([P1] section 3.1 item 3; [P5]).
+
+Readings where the pages are silent (also listed with the design notes):
+  - v* = deepest node whose whole root path is accepted; ties -> smallest index.
+  - the residual at v* uses q of v*'s smallest-index child; if [p - q]_+ sums
+    to 0, sample from p.
+  - q_i(x_i) = 0 for a supplied draft: reject and flag status bit 4.
+  - in a tree with several drafted children per node each child is tested
+    independently against its parent's p; this is lossless for chains and
+    single-child trees only (parity unpinned for the multi-child sampling law).
+
+Status bits: 1 invalid parent[], 2 token id out of range, 4 some q_i(x_i) = 0,
+8 kv_len out of range.  Bits 1 or 2 void the sequence: accept_len 0,
+final_node -1, path and out_tokens all -1.
+
+Near-ties: a decision whose uniform lies within NEAR_TIE of its threshold
+(accept test, inverse-CDF boundary), or a top-p cut whose cumulative mass lies
+within TOPP_NEAR_TIE of top_p, is reported, and every output of that sequence
+that depends on it is excluded from bit-exact comparison.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+from .attention import tree_attention_sequence
+from .sampling import argmax_first, effective_distribution, inverse_cdf_rows, nucleus_margin
+from .tree import check_parent
+
+NEAR_TIE = 1e-5        # band for decisions taken against a supplied uniform
+TOPP_NEAR_TIE = 1e-6   # band for the top-p cut (no uniform: fp32 mass error bound, ~2e-7, x5)
+
+
+def _widen(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored activations -> float64 (bf16 arrives as uint16 bit patterns)."""
+    if dtype == "bf16":
+        return (np.asarray(arr).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return np.asarray(arr, dtype=np.float64)
+
+
+def row_distributions(logits: np.ndarray, temperature: float, top_p: float):
+    """Effective distribution and top-p margin of every row of logits [R, V]."""
+    p = np.empty(logits.shape, dtype=np.float64)
+    margin = np.empty(logits.shape[0], dtype=np.float64)
+    for r in range(logits.shape[0]):
+        p[r] = effective_distribution(logits[r], temperature, top_p)
+        margin[r] = nucleus_margin(logits[r], temperature, top_p)
+    return p, margin
+
+
+def accept_and_select(parent: np.ndarray, tokens: np.ndarray, u_accept: np.ndarray,
+                      u_final: np.ndarray, mode: str, vocab: int,
+                      p_rows: Optional[np.ndarray] = None, q_rows: Optional[np.ndarray] = None,
+                      greedy_rows: Optional[np.ndarray] = None,
+                      all_rows: bool = True) -> Dict[str, np.ndarray]:
+    """Steps 3 and 4 for a batch of sequences.
+
+    parent, tokens, u_accept: [B,T]; u_final: [B].
+    sampling: p_rows, q_rows [B,T,V] effective target / draft distributions
+              (q row 0 unused).
+    greedy:   greedy_rows [B,T] = best target token of each row.
+    all_rows: compute the candidate final token of every row (else only v*).
+    """
+    parent = np.asarray(parent, dtype=np.int64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    B, T = parent.shape
+    # parent[] must be a topologically ordered tree (see check_parent), tokens in [0, V)
+    steps = np.arange(T)[None, :]
+    bad_parent = (parent[:, 0] != -1) | ((parent[:, 1:] < 0) | (parent[:, 1:] >= steps[:, 1:])).any(axis=1)
+    bad_token = ((tokens[:, 1:] < 0) | (tokens[:, 1:] >= vocab)).any(axis=1)
+    status = (bad_parent * 1 + bad_token * 2).astype(np.int32)
+    ok = status == 0
+    par = np.where(ok[:, None], parent, 0)
+    par[:, 0] = 0
+    tok = np.where(ok[:, None], tokens, 0)
+    bidx = np.arange(B)
+
+    node_p = np.zeros((B, T), dtype=np.float64)
+    node_q = np.zeros((B, T), dtype=np.float64)
+    accept_margin = np.full((B, T), np.inf)
+    a = np.zeros((B, T), dtype=bool)
+    a[:, 0] = True
+    for i in range(1, T):
+        if mode == "sampling":
+            pi = p_rows[bidx, par[:, i], tok[:, i]]
+            qi = q_rows[bidx, i, tok[:, i]]
+            node_p[:, i] = pi
+            node_q[:, i] = qi
+            zero_q = qi <= 0.0
+            ratio = np.where(zero_q, 0.0, pi / np.where(zero_q, 1.0, qi))
+            a[:, i] = (~zero_q) & (u_accept[:, i].astype(np.float64) < ratio)
+            accept_margin[:, i] = np.where(zero_q, np.inf, np.abs(u_accept[:, i] - ratio))
+            status |= np.where(ok & zero_q, 4, 0).astype(np.int32)
+        else:
+            a[:, i] = tok[:, i] == greedy_rows[bidx, par[:, i]]
+
+    # acc*(i) = a_i and acc*(parent(i)); depth(i) = depth(parent(i)) + 1
+    acc = np.zeros((B, T), dtype=bool)
+    acc[:, 0] = True
+    depth = np.zeros((B, T), dtype=np.int64)
+    for i in range(1, T):
+        acc[:, i] = a[:, i] & acc[bidx, par[:, i]]
+        depth[:, i] = depth[bidx, par[:, i]] + 1
+    key = np.where(acc, depth, -1)
+    vstar = np.argmax(key, axis=1)            # deepest; first index wins ties
+    accept_len = depth[bidx, vstar]
+
+    # first (smallest-index) child of every node, -1 for leaves
+    first_child = np.full((B, T), -1, dtype=np.int64)
+    for i in range(T - 1, 0, -1):
+        first_child[bidx, par[:, i]] = i
+
+    # candidate final token of each row v (the one emitted if v turns out to be v*):
+    #   greedy -> best target token of row v
+    #   v has children -> residual norm([p_v - q_c]_+), c = first child (p_v if that is all zero)
+    #   leaf -> bonus token from p_v
+    rows = np.arange(T)[None, :].repeat(B, axis=0) if all_rows else vstar[:, None]
+    nb = np.arange(B)[:, None]
+    cdf_margin = np.full((B, T), np.inf)
+    row_token = np.full((B, T), -1, dtype=np.int64)
+    row_residual = np.zeros((B, T), dtype=np.uint8)
+    if mode == "greedy":
+        row_token[nb, rows] = greedy_rows[nb, rows]
+    else:
+        fc = first_child[nb, rows]
+        pv = p_rows[nb, rows]
+        qc = q_rows[nb, np.maximum(fc, 0)]
+        resid = np.maximum(pv - qc, 0.0)
+        use_resid = (fc >= 0) & (resid.sum(axis=-1) > 0.0)
+        w = np.where(use_resid[..., None], resid, pv)
+        uf = np.broadcast_to(np.asarray(u_final, dtype=np.float64)[:, None], rows.shape)
+        y, m = inverse_cdf_rows(w, uf)
+        row_token[nb, rows] = y
+        cdf_margin[nb, rows] = m
+        row_residual[nb, rows] = (fc >= 0).astype(np.uint8)
+
+    # root-to-v* path and the emitted tokens
+    path = np.full((B, T), -1, dtype=np.int64)
+    j = vstar.copy()
+    for _ in range(T):
+        live = j >= 0
+        path[bidx[live], depth[bidx[live], j[live]]] = j[live]
+        j = np.where(live & (j > 0), par[bidx, np.maximum(j, 0)], -1)
+    out_tokens = np.full((B, T), -1, dtype=np.int64)
+    for k in range(T - 1):
+        take = k < accept_len
+        out_tokens[take, k] = tok[take, path[take, k + 1]]
+    out_tokens[bidx, accept_len] = row_token[bidx, vstar]
+    path[~ok] = -1
+    out_tokens[~ok] = -1
+
+    final_node = np.where(ok, vstar, -1)
+    accept_len = np.where(ok, accept_len, 0)
+    final_from_residual = np.where(ok, row_residual[bidx, vstar], 0).astype(np.uint8)
+    return dict(status=status, accept_len=accept_len.astype(np.int32),
+                final_node=final_node.astype(np.int32), path=path.astype(np.int32),
+                out_tokens=out_tokens.astype(np.int32), node_accept=a.astype(np.uint8),
+                node_p=node_p, node_q=node_q, row_token=row_token.astype(np.int32),
+                final_from_residual=final_from_residual,
+                accept_margin=accept_margin, cdf_margin=cdf_margin, first_child=first_child)
+
+
+def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final, *,
+                 mode: str, temperature: float = 1.0, top_p: float = 1.0,
+                 all_rows: bool = True) -> Dict[str, np.ndarray]:
+    """Steps 2-4 for a batch: distributions, acceptance, final token and path."""
+    target_logits = np.asarray(target_logits)
+    B, T, V = target_logits.shape
+    p_rows = q_rows = greedy_rows = None
+    tmargin = np.full((B, T), np.inf)
+    dmargin = np.full((B, T), np.inf)
+    if mode == "sampling":
+        p_rows = np.empty((B, T, V), dtype=np.float64)
+        q_rows = np.zeros((B, T, V), dtype=np.float64)
+        for b in range(B):
+            p_rows[b], tmargin[b] = row_distributions(target_logits[b], temperature, top_p)
+            if T > 1:
+                q_rows[b, 1:], dmargin[b, 1:] = row_distributions(
+                    np.asarray(draft_logits)[b, 1:], temperature, top_p)
+    else:
+        greedy_rows = argmax_first(target_logits)
+    out = accept_and_select(parent, tokens, u_accept, u_final, mode, V, p_rows=p_rows,
+                            q_rows=q_rows, greedy_rows=greedy_rows, all_rows=all_rows)
+
+    # near-tie bookkeeping
+    par = np.clip(np.asarray(parent, dtype=np.int64), 0, T - 1)
+    bidx = np.arange(B)[:, None]
+    node_near = ((out["accept_margin"] < NEAR_TIE) | (tmargin[bidx, par] < TOPP_NEAR_TIE)
+                 | (dmargin < TOPP_NEAR_TIE))
+    node_near[:, 0] = False
+    fc = out["first_child"]
+    child_margin = np.where(fc >= 0, dmargin[bidx, np.maximum(fc, 0)], np.inf)
+    row_near = ((out["cdf_margin"] < NEAR_TIE) | (tmargin < TOPP_NEAR_TIE)
+                | (child_margin < TOPP_NEAR_TIE))
+    vstar = np.maximum(out["final_node"], 0)
+    seq_near = node_near.any(axis=1) | row_near[np.arange(B), vstar]
+    out.update(node_near=node_near, row_near=row_near, seq_near=seq_near,
+               target_topp_margin=tmargin, draft_topp_margin=dmargin)
+    if mode == "sampling":
+        out["p_rows"], out["q_rows"] = p_rows, q_rows
+    return out
+
+
+def verify(case, *, attention: bool = True, seqs=None) -> Dict[str, np.ndarray]:
+    """The whole verify step on a case (any object with the synthetic-case fields).
+
+    seqs: restrict to some sequence indices (outputs are for those, in order).
+    """
+    spec = case.spec
+    seqs = list(range(case.parent.shape[0])) if seqs is None else list(seqs)
+    draft = None if case.draft_logits is None else case.draft_logits[seqs]
+    out = verify_vocab(case.parent[seqs], case.tokens[seqs], case.target_logits[seqs], draft,
+                       case.u_accept[seqs], case.u_final[seqs], mode=spec.mode,
+                       temperature=spec.temperature, top_p=spec.top_p)
+    if attention:
+        T = case.parent.shape[1]
+        lcap = case.k_cache.shape[2]
+        attn = np.full((len(seqs),) + case.q.shape[1:], np.nan)
+        kv_status = np.zeros(len(seqs), dtype=np.int32)
+        for n, b in enumerate(seqs):
+            L = int(case.kv_len[b])
+            if L < 0 or L + T > lcap:
+                kv_status[n] = 8
+                continue
+            if not check_parent(case.parent[b]):
+                continue
+            attn[n] = tree_attention_sequence(_widen(case.q[b], spec.dtype),
+                                              _widen(case.k_cache[b], spec.dtype),
+                                              _widen(case.v_cache[b], spec.dtype),
+                                              L, case.parent[b])
+        out["attn_out"] = attn
+        out["status"] = out["status"] | kv_status
+    return out
