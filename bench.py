@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Verify-step benchmark on one MI355X.
+
+One step = one spec_verify_run over a batch of synthetic inputs already resident
+in HBM: tree attention + split merge + vocab pass + selection.  The default
+workload is the 70B-shaped GQA Medusa-tree verify (batch 8, 64 query / 8 KV
+heads x 128, prefix 8192, 64-node tree, vocab 32000) in sampling mode.
+
+Prints one JSON line: verified candidate tokens/s (B*T per step), the roofline
+of the dominant kernel (HIP events on the run's stream), HBM GB/s of the whole
+step, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+VALU_FP32_PEAK_TFLOPS = 157.3
+RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop/byte
+KERNEL_SOURCES = {"attention": "tree_attn.hip", "combine": "tree_attn.hip", "vocab": "vocab_pass.hip",
+                  "select": "select_path.hip"}
+KERNEL_NAMES = {"attention": "attn_mfma_kernel", "combine": "attn_combine_kernel", "vocab": "vocab_kernel",
+                "select": "select_kernel"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--mode", default=None, help="sampling or greedy (default: the workload's own)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="instead of the verify step, run a plain device copy of this many bytes "
+                         "(--steps times): the reference kernel for scaling HBM counters")
+    return ap.parse_args()
+
+
+def algorithmic_work(case):
+    """Bytes and flops the method itself must move / do, per step (see the design notes)."""
+    spec = case.spec
+    e = 2 if spec.dtype == "bf16" else 4
+    B, T = case.parent.shape
+    attn_bytes = 0
+    attn_flops = 0
+    for b in range(B):
+        L = int(case.kv_len[b])
+        attn_bytes += 2 * spec.hkv * spec.head_dim * e * (L + T) + 2 * T * spec.hq * spec.head_dim * e
+        depth = [0] * T          # node i sees the prefix and its depth(i) + 1 root-path nodes
+        for i in range(1, T):
+            depth[i] = depth[int(case.parent[b, i])] + 1
+        visible = sum(L + d + 1 for d in depth)
+        attn_flops += 4 * spec.hq * spec.head_dim * visible
+    rows = T + (T - 1 if spec.mode == "sampling" else 0)
+    vocab_bytes = 4 * spec.vocab * rows * B
+    return dict(attention_bytes=int(attn_bytes), attention_flops=int(attn_flops), vocab_bytes=int(vocab_bytes))
+
+
+def source_hash(stage):
+    path = os.path.join(ROOT, "tree_attention_verification_verify_amd", "csrc", KERNEL_SOURCES[stage])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (KERNEL_NAMES[stage], workload))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256_16") != source_hash(stage):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, got, nseq=2):
+    """The oracle, as it stands, on the first `nseq` sequences of the same workload.
+
+    Also a parity spot check of those sequences against the GPU run.
+    """
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    seqs = list(range(min(nseq, case.parent.shape[0])))
+    t0 = time.perf_counter()
+    ref = oracle.verify(case, attention=True, seqs=seqs)
+    dt = time.perf_counter() - t0
+    T = case.parent.shape[1]
+    ok = True
+    err = 0.0
+    for n, b in enumerate(seqs):
+        if not ref["seq_near"][n] and int(ref["status"][n]) == 0:
+            ok &= int(got["accept_len"][b]) == int(ref["accept_len"][n])
+            ok &= bool((got["out_tokens"][b] == ref["out_tokens"][n]).all())
+        err = max(err, float(np.abs(got["attn_out"][b].astype(np.float64) - ref["attn_out"][n]).max()))
+    ok &= err <= (2e-2 if case.spec.dtype == "bf16" else 1e-4)
+    return dict(value=len(seqs) * T / dt, unit="candidate tokens/s", cores=int(threads), kind="oracle",
+                sample="sequences 0..%d of %d (%d nodes, prefix %d, vocab %d each): attention + vocab + "
+                       "acceptance + selection, %.1f s" % (len(seqs) - 1, case.parent.shape[0], T,
+                                                           int(case.kv_len[0]), case.spec.vocab, dt),
+                seconds=dt), ok, err
+
+
+def copy_probe(nbytes, steps):
+    import torch
+
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_probe_bytes": nbytes, "ms_per_copy": dt * 1e3,
+                      "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs the verify step on one GPU only; --gpus %d is not supported "
+              "(sequences shard across GPUs with no exchange; see the design notes)" % args.gpus)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
+
+    import numpy as np
+    import torch
+
+    import synth
+    from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs, load_library
+
+    load_library()   # fail loudly if the HIP library is missing
+    overrides = {}
+    if args.mode:
+        overrides["mode"] = args.mode
+    spec = synth.config(args.config, **overrides)
+    t_gen = time.perf_counter()
+    case = synth.make_case(spec)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda")
+
+    def up(a, dtype=None):
+        a = np.ascontiguousarray(a)
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    ins = dict(q=up(case.q, spec.dtype), k_cache=up(case.k_cache, spec.dtype), v_cache=up(case.v_cache, spec.dtype),
+               kv_len=up(case.kv_len), parent=up(case.parent), tokens=up(case.tokens),
+               target_logits=up(case.target_logits),
+               draft_logits=None if case.draft_logits is None else up(case.draft_logits),
+               u_accept=up(case.u_accept), u_final=up(case.u_final))
+    B, T = case.parent.shape
+    outs = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
+    cfg = dict(max_batch=B, max_nodes=T, num_q_heads=spec.hq, num_kv_heads=spec.hkv, head_dim=spec.head_dim,
+               kv_capacity=spec.kv_capacity, vocab=spec.vocab, dtype=spec.dtype, mode=spec.mode,
+               temperature=spec.temperature, top_p=spec.top_p)
+    stream = torch.cuda.current_stream()
+    work = algorithmic_work(case)
+
+    with SpecVerify(timing=True, **cfg) as sv:
+        for _ in range(args.warmup):
+            sv.run(ins, outs, stream)
+        torch.cuda.synchronize()
+        sv.timing_read()                     # discard warm-up records
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            sv.run(ins, outs, stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stage_ms, nruns = sv.timing_read()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_launch = {k: v / max(nruns, 1) for k, v in stage_ms.items()}
+
+    # same loop without event records, to show they cost nothing measurable
+    with SpecVerify(timing=False, **cfg) as sv:
+        for _ in range(args.warmup):
+            sv.run(ins, outs, stream)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            sv.run(ins, outs, stream)
+        torch.cuda.synchronize()
+        ms_untimed = (time.perf_counter() - t2) * 1e3 / args.steps
+    torch.cuda.synchronize()
+    got = {k: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy() for k, v in outs.items()}
+
+    workload = "cfg%d-%s" % (args.config, spec.mode)
+    # dominant kernel by measured time
+    dominant = max(("attention", "vocab"), key=lambda k: per_launch[k])
+    if dominant == "attention":
+        ai = work["attention_flops"] / work["attention_bytes"]
+        t = per_launch["attention"] * 1e-3
+        if ai > RIDGE and spec.dtype == "bf16":
+            achieved = work["attention_flops"] / t / 1e12
+            roof = dict(bound="mfma", achieved=achieved, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=achieved / MFMA_BF16_PEAK_TFLOPS)
+        else:
+            achieved = work["attention_bytes"] / t / 1e9
+            roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=achieved / HBM_PEAK_GBPS)
+    else:
+        achieved = work["vocab_bytes"] / (per_launch["vocab"] * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS)
+    roof["kernel"] = KERNEL_NAMES[dominant]
+    roof["ms_per_launch"] = per_launch[dominant]
+    roof["traffic"] = measured_traffic(dominant, workload)
+
+    step_bytes = work["attention_bytes"] + work["vocab_bytes"]
+    attn_t = (per_launch["attention"] + per_launch["combine"]) * 1e-3
+    hbm = dict(step_GBps=step_bytes / (ms_per_step * 1e-3) / 1e9,
+               step_frac=step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               attention_GBps=work["attention_bytes"] / attn_t / 1e9,
+               attention_TFLOPs=work["attention_flops"] / attn_t / 1e12,
+               vocab_GBps=work["vocab_bytes"] / (per_launch["vocab"] * 1e-3) / 1e9,
+               vocab_frac=work["vocab_bytes"] / (per_launch["vocab"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               algorithmic_bytes_per_step=step_bytes, attention_flops_per_step=work["attention_flops"])
+
+    result = {
+        "metric": "verified candidate tokens/sec + achieved HBM GB/s vs peak (verify step)",
+        "value": B * T / (ms_per_step * 1e-3),
+        "unit": "candidate tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": "70b-gqa-medusa-tree verify" if args.config == 3 else spec.name,
+                   "config_index": args.config, "mode": spec.mode, "batch": B, "nodes": T,
+                   "q_heads": spec.hq, "kv_heads": spec.hkv, "head_dim": spec.head_dim,
+                   "prefix": int(case.kv_len.max()), "vocab": spec.vocab, "temperature": spec.temperature,
+                   "top_p": spec.top_p},
+        "roofline": roof,
+        "hbm": hbm,
+        "stage_ms_per_launch": per_launch,
+        "ms_per_step_without_event_records": ms_untimed,
+        "accepted_tokens_per_step": int(got["accept_len"].sum() + B),
+    }
+    if not args.no_cpu_baseline:
+        base, ok, err = cpu_baseline(case, got)
+        result["cpu_baseline"] = base
+        result["parity_sample"] = {"ok": bool(ok), "attn_max_abs_err": err}
+    result["input_generation_s"] = t_gen
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * spec_verify.h - C ABI of the MI355X verify-step library (libspecverify.so).
+ *
+ * The library runs the target-model verify step of speculative decoding and
+ * Medusa tree decoding for a batch of sequences, on one HIP stream, in four
+ * parts:
+ *
+ *   1. Tree-masked attention of the T candidate nodes over the shared KV
+ *      prefix plus each node's own root path.  Flattening the tree into one
+ *      sequence with a mask: "大模型推理加速：推测解码与MTP核心原理与工程实践"
+ *      section 3.2; the mask itself: "推测解码技术详解：加速LLM推理的关键" section
+ *      "Tree Attention验证"; siblings never see each other: "投机解码的五条路线"
+ *      section 4.  Prefix KV reuse: the first page, section 3.1 item 2.
+ *   2. Per-node temperature (+ top-p) softmax over the vocabulary: target p,
+ *      and draft q where a draft exists ("投机解码的五条路线", section on exact
+ *      verification: the effective sampling distributions must be used).
+ *   3. Token-level acceptance u < p(x)/q(x), resampling from norm([p-q]_+) on
+ *      rejection and a bonus token when a whole path passed (featured article
+ *      on the founding speculative-decoding paper, sections 2.1-2.2); greedy
+ *      mode accepts a candidate iff it is the target's best token.
+ *   4. Selection of the longest root path accepted consecutively from the
+ *      root (first page, section 2.3; "投机解码的五条路线", figure 3).
+ *
+ * All pointers in the input/output structs are DEVICE pointers unless noted;
+ * the caller owns them and keeps them alive until the stream work is done.
+ * Shapes use B = inputs.batch, T = inputs.nodes, Hq/Hkv/D/Lcap/V from the
+ * config; arrays are dense, row-major, in the order of their dimensions.
+ *
+ * Errors: every entry point returns SPEC_VERIFY_OK (0) or a negative code and
+ * sets a thread-local message (spec_verify_last_error).  Host-checkable faults
+ * are caught before any HIP call.  Data-dependent faults (bad parent[], token
+ * ids, kv_len) are reported per sequence in outputs.status, asynchronously.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_VERIFY_OK 0
+#define SPEC_VERIFY_ERR_INVALID_ARG (-1)
+#define SPEC_VERIFY_ERR_UNSUPPORTED (-2)
+#define SPEC_VERIFY_ERR_HIP (-3)
+#define SPEC_VERIFY_ERR_OOM (-4)
+
+#define SPEC_VERIFY_F32 0
+#define SPEC_VERIFY_BF16 1
+
+#define SPEC_VERIFY_GREEDY 0
+#define SPEC_VERIFY_SAMPLING 1
+
+/* config.flags: record HIP events around each kernel of every run (see
+ * spec_verify_timing_read).  Costs a few event records per run. */
+#define SPEC_VERIFY_FLAG_TIMING 1u
+
+/* Status bits written to outputs.status[b]. */
+#define SPEC_VERIFY_STATUS_BAD_PARENT 1   /* parent[0] != -1 or not 0 <= parent[i] < i   */
+#define SPEC_VERIFY_STATUS_BAD_TOKEN 2    /* tokens[b,i] outside [0,V) for some i >= 1    */
+#define SPEC_VERIFY_STATUS_ZERO_DRAFT 4   /* q_i(x_i) = 0 for a supplied draft (rejected) */
+#define SPEC_VERIFY_STATUS_BAD_KVLEN 8    /* kv_len[b] < 0 or kv_len[b] + T > Lcap        */
+
+/* Kernel stages reported by spec_verify_timing_read. */
+#define SPEC_VERIFY_STAGE_ATTENTION 0     /* tree attention main kernel              */
+#define SPEC_VERIFY_STAGE_COMBINE 1       /* merge of split-prefix partials          */
+#define SPEC_VERIFY_STAGE_VOCAB 2         /* per-row softmax stats, ratios, sampling */
+#define SPEC_VERIFY_STAGE_SELECT 3        /* decisions and longest accepted path     */
+#define SPEC_VERIFY_NUM_STAGES 4
+
+typedef struct spec_verify_config {
+    int32_t max_batch;      /* >= 1: largest B a run may pass                        */
+    int32_t max_nodes;      /* 1..64: largest T (tree nodes incl. the root)          */
+    int32_t num_q_heads;    /* Hq >= 1                                               */
+    int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0; query head h uses KV head
+                               h / (Hq/Hkv) (contiguous groups)                      */
+    int32_t head_dim;       /* D: 64 or 128                                          */
+    int32_t kv_capacity;    /* Lcap >= max_nodes: slots per (sequence, KV head)      */
+    int32_t vocab;          /* V >= 1                                                */
+    int32_t dtype;          /* SPEC_VERIFY_F32 or SPEC_VERIFY_BF16: Q, K, V, attn_out */
+    int32_t mode;           /* SPEC_VERIFY_GREEDY or SPEC_VERIFY_SAMPLING            */
+    float temperature;      /* > 0 (sampling mode); applied to target and draft      */
+    float top_p;            /* (0,1]; 1 = off.  top_p < 1 needs V <= 32768           */
+    float softmax_scale;    /* attention scale; 0 => 1/sqrt(D)                       */
+    uint32_t flags;         /* SPEC_VERIFY_FLAG_*                                    */
+} spec_verify_config;
+
+typedef struct spec_verify_inputs {
+    const void* q;              /* [B,T,Hq,D] dtype: node i's queries (RoPE applied)     */
+    const void* k_cache;        /* [B,Hkv,Lcap,D] dtype: slots 0..L_b-1 = prefix,
+                                   slot L_b+i = tree node i's own key                     */
+    const void* v_cache;        /* [B,Hkv,Lcap,D] dtype: same slots for values            */
+    const int32_t* kv_len;      /* [B]: L_b, prefix length of sequence b                  */
+    const int32_t* parent;      /* [B,T]: parent[b,0] = -1, 0 <= parent[b,i] < i           */
+    const int32_t* tokens;      /* [B,T]: token of node i (node 0 = current token, unused) */
+    const float* target_logits; /* [B,T,V] fp32: row i = target logits after node i       */
+    const float* draft_logits;  /* [B,T,V] fp32: row i = logits node i was drafted from
+                                   (row 0 unused); sampling mode only, NULL in greedy     */
+    const float* u_accept;      /* [B,T] fp32 in [0,1): uniform of node i's accept test   */
+    const float* u_final;       /* [B] fp32 in [0,1): uniform of the final token draw     */
+    int32_t batch;              /* B: 1..max_batch                                        */
+    int32_t nodes;              /* T: 1..max_nodes                                        */
+} spec_verify_inputs;
+
+typedef struct spec_verify_outputs {
+    void* attn_out;                /* [B,T,Hq,D] dtype: attention output of every node      */
+    int32_t* accept_len;           /* [B]: depth of the selected node v* (accepted drafts)  */
+    int32_t* final_node;           /* [B]: v* (-1 if the sequence is void)                  */
+    int32_t* path;                 /* [B,T]: root..v* node ids, then -1                      */
+    int32_t* out_tokens;           /* [B,T]: accepted tokens, then the final token, then -1  */
+    int32_t* status;               /* [B]: SPEC_VERIFY_STATUS_* bits                         */
+    float* node_p;                 /* [B,T]: p_parent(i)(x_i) (sampling; 0 otherwise)        */
+    float* node_q;                 /* [B,T]: q_i(x_i) (sampling; 0 otherwise)                */
+    uint8_t* node_accept;          /* [B,T]: per-node test result (node 0 = 1)               */
+    uint8_t* final_from_residual;  /* [B]: 1 if the final token came from norm([p-q]_+)      */
+    int32_t* row_token;            /* [B,T]: final token node v would emit if it were v*     */
+} spec_verify_outputs;
+
+typedef struct spec_verify_handle spec_verify_handle;
+
+/* Validate cfg, size and allocate the workspace on the current HIP device.
+ * *out receives the handle.  No kernel is launched.  Errors: INVALID_ARG
+ * (bad field), UNSUPPORTED (top_p < 1 with V > 32768), OOM, HIP. */
+int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out);
+
+/* Enqueue one verify step on `stream` (a hipStream_t; NULL = default stream).
+ * Asynchronous: allocates nothing, never synchronises.  All output arrays are
+ * written (entries past T or past a sequence's path are -1).  One run per
+ * handle may be in flight at a time unless runs share the same stream.
+ * Errors: INVALID_ARG (NULL pointer, B or T out of range, draft_logits NULL in
+ * sampling mode), HIP (launch failure). */
+int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in,
+                    const spec_verify_outputs* out, void* stream);
+
+/* Free the workspace and the handle.  The caller's streams must be idle. */
+int spec_verify_destroy(spec_verify_handle* h);
+
+/* Message of the last error on this thread ("" if none).  Valid until the
+ * next call into the library on this thread. */
+const char* spec_verify_last_error(void);
+
+/* With SPEC_VERIFY_FLAG_TIMING: wait for the runs recorded since the last
+ * read, then write into stage_ms[SPEC_VERIFY_NUM_STAGES] the summed kernel
+ * time of each stage over those runs (HIP events on the run's stream) and the
+ * run count into *runs (host pointers).  At most 1024 runs are kept between
+ * reads (older ones are dropped).  Errors: INVALID_ARG (no timing flag). */
+int spec_verify_timing_read(spec_verify_handle* h, float* stage_ms, int32_t* runs);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -48,7 +48,7 @@ NEAR_TIE = 1e-5        # band for decisions taken against a supplied uniform
 TOPP_NEAR_TIE = 1e-6   # band for the top-p cut (no uniform: fp32 mass error bound, ~2e-7, x5)
 
 
-def _widen(arr: np.ndarray, dtype: str) -> np.ndarray:
+def widen(arr: np.ndarray, dtype: str) -> np.ndarray:
     """Stored activations -> float64 (bf16 arrives as uint16 bit patterns)."""
     if dtype == "bf16":
         return (np.asarray(arr).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
@@ -179,8 +179,13 @@ def accept_and_select(parent: np.ndarray, tokens: np.ndarray, u_accept: np.ndarr
 
 def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final, *,
                  mode: str, temperature: float = 1.0, top_p: float = 1.0,
-                 all_rows: bool = True) -> Dict[str, np.ndarray]:
-    """Steps 2-4 for a batch: distributions, acceptance, final token and path."""
+                 all_rows: bool = True, accept_band: float = NEAR_TIE, cdf_band: float = NEAR_TIE,
+                 topp_band: float = TOPP_NEAR_TIE) -> Dict[str, np.ndarray]:
+    """Steps 2-4 for a batch: distributions, acceptance, final token and path.
+
+    The *_band arguments set how close to its threshold a decision must be to
+    be flagged as a near-tie (defaults: the bands stated above).
+    """
     target_logits = np.asarray(target_logits)
     B, T, V = target_logits.shape
     p_rows = q_rows = greedy_rows = None
@@ -202,13 +207,13 @@ def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final,
     # near-tie bookkeeping
     par = np.clip(np.asarray(parent, dtype=np.int64), 0, T - 1)
     bidx = np.arange(B)[:, None]
-    node_near = ((out["accept_margin"] < NEAR_TIE) | (tmargin[bidx, par] < TOPP_NEAR_TIE)
-                 | (dmargin < TOPP_NEAR_TIE))
+    node_near = ((out["accept_margin"] < accept_band) | (tmargin[bidx, par] < topp_band)
+                 | (dmargin < topp_band))
     node_near[:, 0] = False
     fc = out["first_child"]
     child_margin = np.where(fc >= 0, dmargin[bidx, np.maximum(fc, 0)], np.inf)
-    row_near = ((out["cdf_margin"] < NEAR_TIE) | (tmargin < TOPP_NEAR_TIE)
-                | (child_margin < TOPP_NEAR_TIE))
+    row_near = ((out["cdf_margin"] < cdf_band) | (tmargin < topp_band)
+                | (child_margin < topp_band))
     vstar = np.maximum(out["final_node"], 0)
     seq_near = node_near.any(axis=1) | row_near[np.arange(B), vstar]
     out.update(node_near=node_near, row_near=row_near, seq_near=seq_near,
@@ -218,17 +223,18 @@ def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final,
     return out
 
 
-def verify(case, *, attention: bool = True, seqs=None) -> Dict[str, np.ndarray]:
+def verify(case, *, attention: bool = True, seqs=None, **bands) -> Dict[str, np.ndarray]:
     """The whole verify step on a case (any object with the synthetic-case fields).
 
     seqs: restrict to some sequence indices (outputs are for those, in order).
+    bands: accept_band / cdf_band / topp_band overrides for the near-tie flags.
     """
     spec = case.spec
     seqs = list(range(case.parent.shape[0])) if seqs is None else list(seqs)
     draft = None if case.draft_logits is None else case.draft_logits[seqs]
     out = verify_vocab(case.parent[seqs], case.tokens[seqs], case.target_logits[seqs], draft,
                        case.u_accept[seqs], case.u_final[seqs], mode=spec.mode,
-                       temperature=spec.temperature, top_p=spec.top_p)
+                       temperature=spec.temperature, top_p=spec.top_p, **bands)
     if attention:
         T = case.parent.shape[1]
         lcap = case.k_cache.shape[2]
@@ -241,9 +247,9 @@ def verify(case, *, attention: bool = True, seqs=None) -> Dict[str, np.ndarray]:
                 continue
             if not check_parent(case.parent[b]):
                 continue
-            attn[n] = tree_attention_sequence(_widen(case.q[b], spec.dtype),
-                                              _widen(case.k_cache[b], spec.dtype),
-                                              _widen(case.v_cache[b], spec.dtype),
+            attn[n] = tree_attention_sequence(widen(case.q[b], spec.dtype),
+                                              widen(case.k_cache[b], spec.dtype),
+                                              widen(case.v_cache[b], spec.dtype),
                                               L, case.parent[b])
         out["attn_out"] = attn
         out["status"] = out["status"] | kv_status

@@ -1,0 +1,192 @@
+"""ctypes binding of libspecverify.so: argument marshalling only.
+
+The functions mirror the C ABI in include/spec_verify.h one to one
+(spec_verify_create / spec_verify_run / spec_verify_destroy /
+spec_verify_last_error / spec_verify_timing_read).  Tensors are PyTorch device
+tensors; only their data pointers cross the boundary.  Every step of the
+verify step runs in the library's HIP kernels: there is no fallback, and a
+missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SPEC_VERIFY_OK = 0
+SPEC_VERIFY_ERR_INVALID_ARG = -1
+SPEC_VERIFY_ERR_UNSUPPORTED = -2
+SPEC_VERIFY_ERR_HIP = -3
+SPEC_VERIFY_ERR_OOM = -4
+SPEC_VERIFY_F32 = 0
+SPEC_VERIFY_BF16 = 1
+SPEC_VERIFY_GREEDY = 0
+SPEC_VERIFY_SAMPLING = 1
+SPEC_VERIFY_FLAG_TIMING = 1
+SPEC_VERIFY_NUM_STAGES = 4
+STAGES = ("attention", "combine", "vocab", "select")
+
+EXPORTED = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
+            "spec_verify_timing_read")
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("spec_verify error %d: %s" % (code, msg))
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("max_batch", ctypes.c_int32), ("max_nodes", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kv_capacity", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32), ("temperature", ctypes.c_float),
+                ("top_p", ctypes.c_float), ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+class Inputs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("kv_len", ctypes.c_void_p), ("parent", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
+                ("target_logits", ctypes.c_void_p), ("draft_logits", ctypes.c_void_p),
+                ("u_accept", ctypes.c_void_p), ("u_final", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("nodes", ctypes.c_int32)]
+
+
+class Outputs(ctypes.Structure):
+    _fields_ = [("attn_out", ctypes.c_void_p), ("accept_len", ctypes.c_void_p), ("final_node", ctypes.c_void_p),
+                ("path", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("node_p", ctypes.c_void_p), ("node_q", ctypes.c_void_p), ("node_accept", ctypes.c_void_p),
+                ("final_from_residual", ctypes.c_void_p), ("row_token", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError("%s is missing: build it with __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    lib.spec_verify_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_void_p)]
+    lib.spec_verify_create.restype = ctypes.c_int
+    lib.spec_verify_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(Inputs), ctypes.POINTER(Outputs),
+                                    ctypes.c_void_p]
+    lib.spec_verify_run.restype = ctypes.c_int
+    lib.spec_verify_destroy.argtypes = [ctypes.c_void_p]
+    lib.spec_verify_destroy.restype = ctypes.c_int
+    lib.spec_verify_last_error.argtypes = []
+    lib.spec_verify_last_error.restype = ctypes.c_char_p
+    lib.spec_verify_timing_read.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
+                                            ctypes.POINTER(ctypes.c_int32)]
+    lib.spec_verify_timing_read.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def spec_verify_last_error() -> str:
+    return load_library().spec_verify_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != SPEC_VERIFY_OK:
+        raise SpecVerifyError(rc, spec_verify_last_error())
+
+
+def make_config(*, max_batch, max_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, vocab,
+                dtype="bf16", mode="sampling", temperature=1.0, top_p=1.0, softmax_scale=0.0,
+                timing=False) -> Config:
+    return Config(max_batch, max_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, vocab,
+                  SPEC_VERIFY_BF16 if dtype == "bf16" else SPEC_VERIFY_F32,
+                  SPEC_VERIFY_SAMPLING if mode == "sampling" else SPEC_VERIFY_GREEDY,
+                  temperature, top_p, softmax_scale, SPEC_VERIFY_FLAG_TIMING if timing else 0)
+
+
+def spec_verify_create(cfg: Config) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load_library().spec_verify_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return h
+
+
+def spec_verify_destroy(handle: ctypes.c_void_p) -> None:
+    _check(load_library().spec_verify_destroy(handle))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def spec_verify_run(handle, inputs: Dict, outputs: Dict, stream=None) -> None:
+    """inputs/outputs: dicts of device tensors named as the C struct fields."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    B, T = inputs["parent"].shape
+    i = Inputs(_ptr(inputs["q"]), _ptr(inputs["k_cache"]), _ptr(inputs["v_cache"]), _ptr(inputs["kv_len"]),
+               _ptr(inputs["parent"]), _ptr(inputs["tokens"]), _ptr(inputs["target_logits"]),
+               _ptr(inputs.get("draft_logits")), _ptr(inputs["u_accept"]), _ptr(inputs["u_final"]), B, T)
+    o = Outputs(*[_ptr(outputs[f]) for f, _ in Outputs._fields_])
+    _check(load_library().spec_verify_run(handle, ctypes.byref(i), ctypes.byref(o), ctypes.c_void_p(stream)))
+
+
+def spec_verify_timing_read(handle):
+    """Summed per-stage kernel milliseconds over the runs since the last read, and the run count."""
+    ms = (ctypes.c_float * SPEC_VERIFY_NUM_STAGES)()
+    n = ctypes.c_int32()
+    _check(load_library().spec_verify_timing_read(handle, ms, ctypes.byref(n)))
+    return dict(zip(STAGES, list(ms))), int(n.value)
+
+
+def allocate_outputs(batch: int, nodes: int, num_q_heads: int, head_dim: int, dtype: str, device="cuda"):
+    """Device output tensors for one run (PyTorch is only the allocator here)."""
+    import torch
+
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, T = batch, nodes
+    return dict(
+        attn_out=torch.empty((B, T, num_q_heads, head_dim), dtype=dt, device=device),
+        accept_len=torch.empty(B, dtype=torch.int32, device=device),
+        final_node=torch.empty(B, dtype=torch.int32, device=device),
+        path=torch.empty((B, T), dtype=torch.int32, device=device),
+        out_tokens=torch.empty((B, T), dtype=torch.int32, device=device),
+        status=torch.empty(B, dtype=torch.int32, device=device),
+        node_p=torch.empty((B, T), dtype=torch.float32, device=device),
+        node_q=torch.empty((B, T), dtype=torch.float32, device=device),
+        node_accept=torch.empty((B, T), dtype=torch.uint8, device=device),
+        final_from_residual=torch.empty(B, dtype=torch.uint8, device=device),
+        row_token=torch.empty((B, T), dtype=torch.int32, device=device),
+    )
+
+
+class SpecVerify:
+    """Handle owner: create on construction, destroy on close()."""
+
+    def __init__(self, **config):
+        self.config = dict(config)
+        self.cfg = make_config(**config)
+        self.handle = spec_verify_create(self.cfg)
+
+    def run(self, inputs: Dict, outputs: Dict, stream=None) -> None:
+        spec_verify_run(self.handle, inputs, outputs, stream)
+
+    def timing_read(self):
+        return spec_verify_timing_read(self.handle)
+
+    def close(self) -> None:
+        if self.handle is not None:
+            spec_verify_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -1,0 +1,88 @@
+// Device helpers shared by the verify-step kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Per-node ancestor bitmasks anc*(i) (bit j set iff node j is on node i's
+// root path, i itself included), by pointer jumping over parent[] in one
+// wave: after k rounds each node has collected 2^k nodes of its chain, so 6
+// rounds cover any depth below 64.  Lane i handles node i (T <= 64).  Nodes
+// whose parent entry is invalid (root not -1, or not 0 <= parent[i] < i) get
+// only their own bit; *bad is set for the whole wave in that case.
+__device__ __forceinline__ unsigned long long ancestor_mask(const int32_t* parent_row, int T,
+                                                            bool* bad) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int p = -1;
+    bool invalid = false;
+    if (lane < T) {
+        p = parent_row[lane];
+        if (lane == 0) invalid = (p != -1);
+        else invalid = (p < 0 || p >= lane);
+        if (invalid) p = -1;
+    }
+    unsigned long long a = (lane < T) ? (1ull << lane) : 0ull;
+#pragma unroll
+    for (int round = 0; round < 6; ++round) {
+        const int src = p < 0 ? lane : p;
+        unsigned long long pa = __shfl(a, src, kWave);
+        int pp = __shfl(p, src, kWave);
+        if (p >= 0) {
+            a |= pa;
+            p = pp;
+        }
+    }
+    *bad = __any(invalid);
+    return a;
+}
+
+}  // namespace sv

@@ -1,0 +1,76 @@
+// Internal kernel launch interface of libspecverify (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+// Tree attention over the prefix split into `nsplit` key ranges of `chunk`
+// keys.  Rows of one (sequence, KV head) pair are r = node * g + (h % g).
+struct AttnParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* kv_len;
+    const int32_t* parent;
+    void* out;          // [B,T,Hq,D] dtype (written directly when nsplit == 1)
+    float* part_o;      // [pairs][nsplit][Rpad][D] un-normalised partial outputs
+    float2* part_ml;    // [pairs][nsplit][Rpad] (running max in log2 units, row sum)
+    int B, T, Hq, Hkv, g, D, Lcap;
+    int R;              // g * T rows per pair
+    int Rpad;           // rowblocks * rows_per_block
+    int rowblocks;
+    int nsplit;
+    int chunk;          // keys per split (multiple of 64)
+    int groups_per_xcd; // XCD-aware block mapping (mfma path with rowblocks > 1)
+    float c;            // softmax_scale * log2(e)
+};
+
+struct VocabParams {
+    const float* target;
+    const float* draft;
+    const int32_t* parent;
+    const int32_t* tokens;
+    const float* u_final;
+    float* node_p;
+    float* node_q;
+    int32_t* row_token;
+    int B, T, V;
+    int sampling;
+    float ilog;         // log2(e) / temperature
+    float top_p;
+    int nchunks;
+};
+
+struct SelectParams {
+    const int32_t* parent;
+    const int32_t* tokens;
+    const int32_t* kv_len;
+    const float* u_accept;
+    const int32_t* row_token;
+    float* node_p;
+    float* node_q;
+    int32_t* accept_len;
+    int32_t* final_node;
+    int32_t* path;
+    int32_t* out_tokens;
+    int32_t* status;
+    uint8_t* node_accept;
+    uint8_t* final_from_residual;
+    int B, T, V, Lcap;
+    int sampling;
+};
+
+// Returns hipSuccess or the launch error.
+hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s);
+hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
+hipError_t launch_attention_combine(const AttnParams& p, bool bf16, hipStream_t s);
+hipError_t launch_vocab(const VocabParams& p, hipStream_t s);
+hipError_t launch_select(const SelectParams& p, hipStream_t s);
+
+constexpr int kValuRows = 16;      // rows per block of the VALU attention kernel
+constexpr int kVocabThreads = 1024;
+constexpr int kVocabChunk = kVocabThreads * 32;   // logits held on chip per pass
+
+}  // namespace sv

@@ -1,0 +1,333 @@
+// Host side of libspecverify: C ABI, validation, workspace and launch order.
+//
+// A run enqueues, on the caller's stream and without synchronising:
+//   tree attention (MFMA or VALU kernel) -> split merge (when split)
+//   vocab pass (row statistics, ratios, candidate final tokens)
+//   selection (decisions, longest accepted path, emitted tokens)
+// The attention and the vocabulary work read disjoint inputs.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "spec_verify.h"
+
+namespace sv {
+int valu_rows_for(int R);
+}
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    g_err = std::string(what) + ": " + hipGetErrorString(e);
+    return SPEC_VERIFY_ERR_HIP;
+}
+
+constexpr int kTimingRing = 1024;
+constexpr int kEventsPerRun = SPEC_VERIFY_NUM_STAGES + 1;
+constexpr int kTargetWaves = 2048;   // two waves per SIMD on 256 CUs
+constexpr int kMinSplitKeys = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnPlan {
+    bool mfma = false;
+    int waves = 1;          // waves per block
+    int rows_per_block = 0;
+    int rowblocks = 1;
+    int Rpad = 0;
+    int nsplit = 1;
+    int chunk = 0;
+    size_t part_rows = 0;   // pairs * nsplit * Rpad
+};
+
+AttnPlan plan_attention(const spec_verify_config& c, int B, int T) {
+    AttnPlan p;
+    const int g = c.num_q_heads / c.num_kv_heads;
+    const int R = g * T;
+    p.mfma = (c.dtype == SPEC_VERIFY_BF16) && R >= 16;
+    if (p.mfma) {
+        p.waves = std::min(4, (R + 31) / 32);
+        p.rows_per_block = 32 * p.waves;
+    } else {
+        p.waves = 1;
+        p.rows_per_block = sv::valu_rows_for(R);
+    }
+    p.rowblocks = (R + p.rows_per_block - 1) / p.rows_per_block;
+    p.Rpad = p.rowblocks * p.rows_per_block;
+    const long pairs = (long)B * c.num_kv_heads;
+    const long base_waves = pairs * p.rowblocks * p.waves;
+    long want = (kTargetWaves + base_waves - 1) / base_waves;
+    const long keys = c.kv_capacity;
+    const long max_split = std::max(1L, keys / kMinSplitKeys);
+    long ns = std::max(1L, std::min(want, max_split));
+    long chunk = (keys + ns - 1) / ns;
+    chunk = ((chunk + 63) / 64) * 64;
+    ns = (keys + chunk - 1) / chunk;
+    p.nsplit = (int)ns;
+    p.chunk = (int)chunk;
+    p.part_rows = p.nsplit > 1 ? (size_t)pairs * p.nsplit * p.Rpad : 0;
+    return p;
+}
+
+}  // namespace
+
+struct spec_verify_handle {
+    spec_verify_config cfg;
+    int device = 0;
+    size_t part_rows_cap = 0;
+    float* part_o = nullptr;
+    float2* part_ml = nullptr;
+    bool timing = false;
+    std::vector<hipEvent_t> events;   // kTimingRing * kEventsPerRun
+    long runs_recorded = 0;           // since the last read
+    long ring_head = 0;               // total runs recorded
+};
+
+extern "C" {
+
+const char* spec_verify_last_error(void) { return g_err.c_str(); }
+
+int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) {
+    g_err.clear();
+    if (!cfg || !out) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "cfg and out must be non-NULL");
+    *out = nullptr;
+    const spec_verify_config& c = *cfg;
+    if (c.max_batch < 1) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "max_batch must be >= 1");
+    if (c.max_nodes < 1 || c.max_nodes > 64) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "max_nodes must be in [1, 64]");
+    if (c.num_q_heads < 1 || c.num_kv_heads < 1) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "head counts must be >= 1");
+    if (c.num_q_heads % c.num_kv_heads != 0)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+    if ((long)(c.num_q_heads / c.num_kv_heads) * c.max_nodes > 65536)
+        return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "too many query rows per KV head");
+    if (c.head_dim != 64 && c.head_dim != 128) return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (c.kv_capacity < c.max_nodes) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "kv_capacity must be >= max_nodes");
+    if (c.vocab < 1 || c.vocab > sv::kVocabChunk * 128)
+        return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "vocab must be in [1, 4194304]");
+    if (c.dtype != SPEC_VERIFY_F32 && c.dtype != SPEC_VERIFY_BF16)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "dtype must be SPEC_VERIFY_F32 or SPEC_VERIFY_BF16");
+    if (c.mode != SPEC_VERIFY_GREEDY && c.mode != SPEC_VERIFY_SAMPLING)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "mode must be SPEC_VERIFY_GREEDY or SPEC_VERIFY_SAMPLING");
+    if (c.mode == SPEC_VERIFY_SAMPLING) {
+        if (!(c.temperature > 0.f) || !std::isfinite(c.temperature))
+            return fail(SPEC_VERIFY_ERR_INVALID_ARG, "temperature must be a finite value > 0");
+        if (!(c.top_p > 0.f && c.top_p <= 1.f)) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+        if (c.top_p < 1.f && c.vocab > sv::kVocabChunk)
+            return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "top_p < 1 needs vocab <= 32768");
+    }
+    if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    if ((c.flags & ~SPEC_VERIFY_FLAG_TIMING) != 0u) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "unknown flag bits");
+    const long long lcap_elems = (long long)c.kv_capacity * c.head_dim;
+    if (lcap_elems > (1LL << 40)) return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "kv_capacity too large");
+
+    // workspace: the largest split-prefix partial buffer over every (B, T) a run may use
+    size_t cap = 0;
+    for (int B = 1; B <= c.max_batch; ++B)
+        for (int T = 1; T <= c.max_nodes; ++T) cap = std::max(cap, plan_attention(c, B, T).part_rows);
+
+    spec_verify_handle* h = new (std::nothrow) spec_verify_handle();
+    if (!h) return fail(SPEC_VERIFY_ERR_OOM, "host allocation failed");
+    h->cfg = c;
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e, "hipGetDevice");
+    }
+    h->part_rows_cap = cap;
+    if (cap > 0) {
+        e = hipMalloc((void**)&h->part_o, cap * c.head_dim * sizeof(float));
+        if (e == hipSuccess) e = hipMalloc((void**)&h->part_ml, cap * sizeof(float2));
+        if (e != hipSuccess) {
+            (void)hipFree(h->part_o);
+            delete h;
+            (void)hipGetLastError();
+            return fail(SPEC_VERIFY_ERR_OOM, "workspace allocation failed");
+        }
+    }
+    h->timing = (c.flags & SPEC_VERIFY_FLAG_TIMING) != 0u;
+    if (h->timing) {
+        h->events.resize((size_t)kTimingRing * kEventsPerRun, nullptr);
+        for (auto& ev : h->events) {
+            e = hipEventCreate(&ev);
+            if (e != hipSuccess) {
+                spec_verify_destroy(h);
+                return hip_fail(e, "hipEventCreate");
+            }
+        }
+    }
+    *out = h;
+    return SPEC_VERIFY_OK;
+}
+
+int spec_verify_destroy(spec_verify_handle* h) {
+    g_err.clear();
+    if (!h) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle is NULL");
+    int dev = -1;
+    (void)hipGetDevice(&dev);
+    if (dev != h->device) (void)hipSetDevice(h->device);
+    for (auto& ev : h->events)
+        if (ev) (void)hipEventDestroy(ev);
+    if (h->part_o) (void)hipFree(h->part_o);
+    if (h->part_ml) (void)hipFree(h->part_ml);
+    if (dev >= 0 && dev != h->device) (void)hipSetDevice(dev);
+    delete h;
+    return SPEC_VERIFY_OK;
+}
+
+int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_outputs* out,
+                    void* stream) {
+    g_err.clear();
+    if (!h || !in || !out) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle, inputs and outputs must be non-NULL");
+    const spec_verify_config& c = h->cfg;
+    const int B = in->batch, T = in->nodes;
+    if (B < 1 || B > c.max_batch) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "batch out of range");
+    if (T < 1 || T > c.max_nodes) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes out of range");
+    const bool sampling = c.mode == SPEC_VERIFY_SAMPLING;
+    if (!in->q || !in->k_cache || !in->v_cache || !in->kv_len || !in->parent || !in->tokens ||
+        !in->target_logits || !in->u_accept || !in->u_final)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an input pointer is NULL");
+    if (sampling && !in->draft_logits) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "draft_logits is NULL in sampling mode");
+    if (!out->attn_out || !out->accept_len || !out->final_node || !out->path || !out->out_tokens || !out->status ||
+        !out->node_p || !out->node_q || !out->node_accept || !out->final_from_residual || !out->row_token)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an output pointer is NULL");
+    hipStream_t s = (hipStream_t)stream;
+
+    const int D = c.head_dim;
+    const bool bf16 = c.dtype == SPEC_VERIFY_BF16;
+    AttnPlan plan = plan_attention(c, B, T);
+    if (plan.part_rows > h->part_rows_cap) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "workspace too small (internal)");
+
+    hipEvent_t* ev = nullptr;
+    if (h->timing) {
+        ev = &h->events[(size_t)(h->ring_head % kTimingRing) * kEventsPerRun];
+        hipError_t e = hipEventRecord(ev[0], s);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    auto mark = [&](int stage) -> int {
+        if (!ev) return SPEC_VERIFY_OK;
+        hipError_t e = hipEventRecord(ev[stage + 1], s);
+        return e == hipSuccess ? SPEC_VERIFY_OK : hip_fail(e, "hipEventRecord");
+    };
+
+    sv::AttnParams ap{};
+    ap.q = in->q;
+    ap.k = in->k_cache;
+    ap.v = in->v_cache;
+    ap.kv_len = in->kv_len;
+    ap.parent = in->parent;
+    ap.out = out->attn_out;
+    ap.part_o = h->part_o;
+    ap.part_ml = h->part_ml;
+    ap.B = B;
+    ap.T = T;
+    ap.Hq = c.num_q_heads;
+    ap.Hkv = c.num_kv_heads;
+    ap.g = c.num_q_heads / c.num_kv_heads;
+    ap.D = D;
+    ap.Lcap = c.kv_capacity;
+    ap.R = ap.g * T;
+    ap.Rpad = plan.Rpad;
+    ap.rowblocks = plan.rowblocks;
+    ap.nsplit = plan.nsplit;
+    ap.chunk = plan.chunk;
+    const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt((float)D);
+    ap.c = scale * kLog2e;
+
+    hipError_t e = plan.mfma ? sv::launch_attention_mfma(ap, plan.waves, s) : sv::launch_attention_valu(ap, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if (int rc = mark(SPEC_VERIFY_STAGE_ATTENTION)) return rc;
+    if (plan.nsplit > 1) {
+        e = sv::launch_attention_combine(ap, bf16, s);
+        if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
+    if (int rc = mark(SPEC_VERIFY_STAGE_COMBINE)) return rc;
+
+    sv::VocabParams vp{};
+    vp.target = in->target_logits;
+    vp.draft = in->draft_logits;
+    vp.parent = in->parent;
+    vp.tokens = in->tokens;
+    vp.u_final = in->u_final;
+    vp.node_p = out->node_p;
+    vp.node_q = out->node_q;
+    vp.row_token = out->row_token;
+    vp.B = B;
+    vp.T = T;
+    vp.V = c.vocab;
+    vp.sampling = sampling ? 1 : 0;
+    vp.ilog = sampling ? kLog2e / c.temperature : kLog2e;
+    vp.top_p = sampling ? c.top_p : 1.f;
+    vp.nchunks = (c.vocab + sv::kVocabChunk - 1) / sv::kVocabChunk;
+    e = sv::launch_vocab(vp, s);
+    if (e != hipSuccess) return hip_fail(e, "vocab launch");
+    if (int rc = mark(SPEC_VERIFY_STAGE_VOCAB)) return rc;
+
+    sv::SelectParams sp{};
+    sp.parent = in->parent;
+    sp.tokens = in->tokens;
+    sp.kv_len = in->kv_len;
+    sp.u_accept = in->u_accept;
+    sp.row_token = out->row_token;
+    sp.node_p = out->node_p;
+    sp.node_q = out->node_q;
+    sp.accept_len = out->accept_len;
+    sp.final_node = out->final_node;
+    sp.path = out->path;
+    sp.out_tokens = out->out_tokens;
+    sp.status = out->status;
+    sp.node_accept = out->node_accept;
+    sp.final_from_residual = out->final_from_residual;
+    sp.B = B;
+    sp.T = T;
+    sp.V = c.vocab;
+    sp.Lcap = c.kv_capacity;
+    sp.sampling = sampling ? 1 : 0;
+    e = sv::launch_select(sp, s);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    if (int rc = mark(SPEC_VERIFY_STAGE_SELECT)) return rc;
+
+    if (h->timing) {
+        ++h->ring_head;
+        h->runs_recorded = std::min<long>(h->runs_recorded + 1, kTimingRing);
+    }
+    return SPEC_VERIFY_OK;
+}
+
+int spec_verify_timing_read(spec_verify_handle* h, float* stage_ms, int32_t* runs) {
+    g_err.clear();
+    if (!h || !stage_ms || !runs) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "NULL argument");
+    if (!h->timing) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle was created without SPEC_VERIFY_FLAG_TIMING");
+    for (int k = 0; k < SPEC_VERIFY_NUM_STAGES; ++k) stage_ms[k] = 0.f;
+    const long n = h->runs_recorded;
+    for (long r = 0; r < n; ++r) {
+        const long slot = (h->ring_head - n + r) % kTimingRing;
+        hipEvent_t* ev = &h->events[(size_t)slot * kEventsPerRun];
+        hipError_t e = hipEventSynchronize(ev[kEventsPerRun - 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        for (int k = 0; k < SPEC_VERIFY_NUM_STAGES; ++k) {
+            float ms = 0.f;
+            e = hipEventElapsedTime(&ms, ev[k], ev[k + 1]);
+            if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+            stage_ms[k] += ms;
+        }
+    }
+    *runs = (int32_t)n;
+    h->runs_recorded = 0;
+    return SPEC_VERIFY_OK;
+}
+
+}  // extern "C"
