@@ -24,9 +24,9 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 VALU_FP32_PEAK_TFLOPS = 157.3
 RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop/byte
-KERNEL_SOURCES = {"attention": "tree_attn.hip", "combine": "tree_attn.hip", "vocab": "vocab_pass.hip",
-                  "select": "select_path.hip"}
-KERNEL_NAMES = {"attention": "attn_mfma_kernel", "combine": "attn_combine_kernel", "vocab": "vocab_kernel",
+KERNEL_SOURCES = {"attention": "tree_attn.hip", "combine": "tree_attn.hip", "vocab": "vocab_stats.hip",
+                  "select": "select_final.hip"}
+KERNEL_NAMES = {"attention": "attn_mfma_kernel", "combine": "attn_combine_kernel", "vocab": "row_stats_stream_kernel",
                 "select": "select_kernel"}
 
 

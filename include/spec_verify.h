@@ -65,8 +65,8 @@ extern "C" {
 /* Kernel stages reported by spec_verify_timing_read. */
 #define SPEC_VERIFY_STAGE_ATTENTION 0     /* tree attention main kernel              */
 #define SPEC_VERIFY_STAGE_COMBINE 1       /* merge of split-prefix partials          */
-#define SPEC_VERIFY_STAGE_VOCAB 2         /* per-row softmax stats, ratios, sampling */
-#define SPEC_VERIFY_STAGE_SELECT 3        /* decisions and longest accepted path     */
+#define SPEC_VERIFY_STAGE_VOCAB 2         /* per-row softmax statistics (one read)   */
+#define SPEC_VERIFY_STAGE_SELECT 3        /* ratios, decisions, path, final draw     */
 #define SPEC_VERIFY_NUM_STAGES 4
 
 typedef struct spec_verify_config {
@@ -114,7 +114,7 @@ typedef struct spec_verify_outputs {
     float* node_q;                 /* [B,T]: q_i(x_i) (sampling; 0 otherwise)                */
     uint8_t* node_accept;          /* [B,T]: per-node test result (node 0 = 1)               */
     uint8_t* final_from_residual;  /* [B]: 1 if the final token came from norm([p-q]_+)      */
-    int32_t* row_token;            /* [B,T]: final token node v would emit if it were v*     */
+    int32_t* row_token;            /* [B,T]: best token of target row v (smallest id on ties) */
 } spec_verify_outputs;
 
 typedef struct spec_verify_handle spec_verify_handle;

@@ -68,15 +68,14 @@ def row_distributions(logits: np.ndarray, temperature: float, top_p: float):
 def accept_and_select(parent: np.ndarray, tokens: np.ndarray, u_accept: np.ndarray,
                       u_final: np.ndarray, mode: str, vocab: int,
                       p_rows: Optional[np.ndarray] = None, q_rows: Optional[np.ndarray] = None,
-                      greedy_rows: Optional[np.ndarray] = None,
-                      all_rows: bool = True) -> Dict[str, np.ndarray]:
+                      greedy_rows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Steps 3 and 4 for a batch of sequences.
 
     parent, tokens, u_accept: [B,T]; u_final: [B].
     sampling: p_rows, q_rows [B,T,V] effective target / draft distributions
               (q row 0 unused).
-    greedy:   greedy_rows [B,T] = best target token of each row.
-    all_rows: compute the candidate final token of every row (else only v*).
+    greedy_rows [B,T]: best target token of each row (needed in greedy mode,
+              reported as row_token when given).
     """
     parent = np.asarray(parent, dtype=np.int64)
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -127,29 +126,22 @@ def accept_and_select(parent: np.ndarray, tokens: np.ndarray, u_accept: np.ndarr
     for i in range(T - 1, 0, -1):
         first_child[bidx, par[:, i]] = i
 
-    # candidate final token of each row v (the one emitted if v turns out to be v*):
-    #   greedy -> best target token of row v
-    #   v has children -> residual norm([p_v - q_c]_+), c = first child (p_v if that is all zero)
-    #   leaf -> bonus token from p_v
-    rows = np.arange(T)[None, :].repeat(B, axis=0) if all_rows else vstar[:, None]
-    nb = np.arange(B)[:, None]
-    cdf_margin = np.full((B, T), np.inf)
-    row_token = np.full((B, T), -1, dtype=np.int64)
-    row_residual = np.zeros((B, T), dtype=np.uint8)
+    # the token drawn at v*:
+    #   greedy -> best target token of row v*
+    #   v* has children -> residual norm([p_v* - q_c]_+), c = first child (p_v* if that is all zero)
+    #   v* is a leaf -> bonus token from p_v*
+    cdf_margin = np.full(B, np.inf)
+    fc = first_child[bidx, vstar]
     if mode == "greedy":
-        row_token[nb, rows] = greedy_rows[nb, rows]
+        final_tok = greedy_rows[bidx, vstar].astype(np.int64)
     else:
-        fc = first_child[nb, rows]
-        pv = p_rows[nb, rows]
-        qc = q_rows[nb, np.maximum(fc, 0)]
+        pv = p_rows[bidx, vstar]
+        qc = q_rows[bidx, np.maximum(fc, 0)]
         resid = np.maximum(pv - qc, 0.0)
         use_resid = (fc >= 0) & (resid.sum(axis=-1) > 0.0)
-        w = np.where(use_resid[..., None], resid, pv)
-        uf = np.broadcast_to(np.asarray(u_final, dtype=np.float64)[:, None], rows.shape)
-        y, m = inverse_cdf_rows(w, uf)
-        row_token[nb, rows] = y
-        cdf_margin[nb, rows] = m
-        row_residual[nb, rows] = (fc >= 0).astype(np.uint8)
+        w = np.where(use_resid[:, None], resid, pv)
+        final_tok, cdf_margin = inverse_cdf_rows(w, np.asarray(u_final, dtype=np.float64))
+    from_residual = ((fc >= 0) & (mode == "sampling")).astype(np.uint8)
 
     # root-to-v* path and the emitted tokens
     path = np.full((B, T), -1, dtype=np.int64)
@@ -162,13 +154,15 @@ def accept_and_select(parent: np.ndarray, tokens: np.ndarray, u_accept: np.ndarr
     for k in range(T - 1):
         take = k < accept_len
         out_tokens[take, k] = tok[take, path[take, k + 1]]
-    out_tokens[bidx, accept_len] = row_token[bidx, vstar]
+    out_tokens[bidx, accept_len] = final_tok
     path[~ok] = -1
     out_tokens[~ok] = -1
 
     final_node = np.where(ok, vstar, -1)
     accept_len = np.where(ok, accept_len, 0)
-    final_from_residual = np.where(ok, row_residual[bidx, vstar], 0).astype(np.uint8)
+    final_from_residual = np.where(ok, from_residual, 0).astype(np.uint8)
+    row_token = (np.asarray(greedy_rows, dtype=np.int64) if greedy_rows is not None
+                 else np.full((B, T), -1, dtype=np.int64))
     return dict(status=status, accept_len=accept_len.astype(np.int32),
                 final_node=final_node.astype(np.int32), path=path.astype(np.int32),
                 out_tokens=out_tokens.astype(np.int32), node_accept=a.astype(np.uint8),
@@ -179,7 +173,7 @@ def accept_and_select(parent: np.ndarray, tokens: np.ndarray, u_accept: np.ndarr
 
 def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final, *,
                  mode: str, temperature: float = 1.0, top_p: float = 1.0,
-                 all_rows: bool = True, accept_band: float = NEAR_TIE, cdf_band: float = NEAR_TIE,
+                 accept_band: float = NEAR_TIE, cdf_band: float = NEAR_TIE,
                  topp_band: float = TOPP_NEAR_TIE) -> Dict[str, np.ndarray]:
     """Steps 2-4 for a batch: distributions, acceptance, final token and path.
 
@@ -199,10 +193,9 @@ def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final,
             if T > 1:
                 q_rows[b, 1:], dmargin[b, 1:] = row_distributions(
                     np.asarray(draft_logits)[b, 1:], temperature, top_p)
-    else:
-        greedy_rows = argmax_first(target_logits)
+    greedy_rows = argmax_first(target_logits)
     out = accept_and_select(parent, tokens, u_accept, u_final, mode, V, p_rows=p_rows,
-                            q_rows=q_rows, greedy_rows=greedy_rows, all_rows=all_rows)
+                            q_rows=q_rows, greedy_rows=greedy_rows)
 
     # near-tie bookkeeping
     par = np.clip(np.asarray(parent, dtype=np.int64), 0, T - 1)
@@ -210,13 +203,14 @@ def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final,
     node_near = ((out["accept_margin"] < accept_band) | (tmargin[bidx, par] < topp_band)
                  | (dmargin < topp_band))
     node_near[:, 0] = False
-    fc = out["first_child"]
-    child_margin = np.where(fc >= 0, dmargin[bidx, np.maximum(fc, 0)], np.inf)
-    row_near = ((out["cdf_margin"] < cdf_band) | (tmargin < topp_band)
-                | (child_margin < topp_band))
+    # the final draw at v*: its CDF boundary and the top-p cuts of the rows it reads
     vstar = np.maximum(out["final_node"], 0)
-    seq_near = node_near.any(axis=1) | row_near[np.arange(B), vstar]
-    out.update(node_near=node_near, row_near=row_near, seq_near=seq_near,
+    b1 = np.arange(B)
+    fc = out["first_child"][b1, vstar]
+    final_near = ((out["cdf_margin"] < cdf_band) | (tmargin[b1, vstar] < topp_band)
+                  | ((fc >= 0) & (dmargin[b1, np.maximum(fc, 0)] < topp_band)))
+    seq_near = node_near.any(axis=1) | final_near
+    out.update(node_near=node_near, final_near=final_near, seq_near=seq_near,
                target_topp_margin=tmargin, draft_topp_margin=dmargin)
     if mode == "sampling":
         out["p_rows"], out["q_rows"] = p_rows, q_rows

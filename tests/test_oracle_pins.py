@@ -195,7 +195,7 @@ def _chain_inputs(p_rows, q_rows, drafts, u_acc, u_fin):
     P = np.broadcast_to(p_rows, (B,) + p_rows.shape)
     Q = np.broadcast_to(q_rows, (B,) + q_rows.shape)
     return oracle.accept_and_select(parent, tokens, u_acc, u_fin, "sampling", p_rows.shape[1],
-                                    p_rows=P, q_rows=Q, all_rows=False)
+                                    p_rows=P, q_rows=Q)
 
 
 def _draw(rng, probs, n):
@@ -453,7 +453,7 @@ def test_joint_law_of_two_tokens_table_lm():
         tokens = np.concatenate([np.zeros((n, 1), dtype=np.int64), drafts], axis=1)
         parent = np.tile(np.arange(-1, T - 1), (n, 1))
         return oracle.accept_and_select(parent, tokens, rng.random((n, T)), rng.random(n),
-                                        "sampling", V, p_rows=prows, q_rows=qrows, all_rows=False)
+                                        "sampling", V, p_rows=prows, q_rows=qrows)
 
     trials = 400_000
     r1 = one_round(np.zeros((trials, 0), dtype=np.int64), trials)

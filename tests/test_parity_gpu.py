@@ -27,7 +27,7 @@ def check(case, label, seqs=None, attn_rows=None):
     stats = compare(case, got, ref, seqs=seqs, attn=True, attn_rows=attn_rows)
     loose = oracle.verify(case, attention=False, seqs=seqs)
     stats.update(seq_near_1e5=int(loose["seq_near"].sum()), node_near_1e5=int(loose["node_near"].sum()),
-                 row_near_1e5=int(loose["row_near"].sum()))
+                 final_near_1e5=int(loose["final_near"].sum()))
     print(label, stats, flush=True)
     return got, ref, stats
 

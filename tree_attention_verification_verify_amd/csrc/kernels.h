@@ -27,30 +27,38 @@ struct AttnParams {
     float c;            // softmax_scale * log2(e)
 };
 
-struct VocabParams {
+// Statistics of one logits row under temperature (and top-p).
+struct RowStat {
+    float zmax;      // largest logit
+    int argmax;      // smallest token id holding it
+    uint32_t thr;    // top-p cut: bit pattern of the smallest kept unnormalised probability
+    int cutoff;      // tokens whose value equals the cut are kept when id < cutoff
+    double Z;        // sum over the kept tokens of exp((z - zmax) / temperature)
+};
+
+// stats[b * 2T + r]: r < T -> target row r; r = T + i -> draft row of node i (i >= 1).
+struct StatsParams {
     const float* target;
     const float* draft;
-    const int32_t* parent;
-    const int32_t* tokens;
-    const float* u_final;
-    float* node_p;
-    float* node_q;
-    int32_t* row_token;
+    RowStat* stats;
     int B, T, V;
     int sampling;
     float ilog;         // log2(e) / temperature
     float top_p;
-    int nchunks;
 };
 
 struct SelectParams {
+    const float* target;
+    const float* draft;
+    const RowStat* stats;
     const int32_t* parent;
     const int32_t* tokens;
     const int32_t* kv_len;
     const float* u_accept;
-    const int32_t* row_token;
+    const float* u_final;
     float* node_p;
     float* node_q;
+    int32_t* row_token;
     int32_t* accept_len;
     int32_t* final_node;
     int32_t* path;
@@ -60,17 +68,19 @@ struct SelectParams {
     uint8_t* final_from_residual;
     int B, T, V, Lcap;
     int sampling;
+    float ilog;
 };
 
 // Returns hipSuccess or the launch error.
 hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s);
 hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
 hipError_t launch_attention_combine(const AttnParams& p, bool bf16, hipStream_t s);
-hipError_t launch_vocab(const VocabParams& p, hipStream_t s);
+hipError_t launch_row_stats(const StatsParams& p, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
 
 constexpr int kValuRows = 16;      // rows per block of the VALU attention kernel
-constexpr int kVocabThreads = 1024;
+constexpr int kVocabThreads = 1024;               // register-resident row kernels
 constexpr int kVocabChunk = kVocabThreads * 32;   // logits held on chip per pass
+constexpr int kStatsThreads = 256;                // streaming row-statistics kernel
 
 }  // namespace sv

@@ -1,0 +1,380 @@
+// Block-wide helpers for the 1024-thread row kernels (wave64, gfx950):
+// deterministic reductions and scans, register-resident logits chunks, the
+// top-p radix select and the inverse-CDF search.  Internal to the library.
+//
+// Element layout of a chunk: thread t holds float4 slots j = 0..VPT4-1 at
+// token ids cb + 4*(t + NT*j) + e, so (j, t, e) order is token-id order and
+// every slot is one coalesced 16 KB read by the workgroup.
+#pragma once
+
+#include <limits.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace sv {
+namespace rows {
+
+constexpr int NT = kVocabThreads;
+constexpr int NW = NT / kWave;
+constexpr int VPT4 = 8;                     // float4 per thread per chunk
+constexpr int CHUNK = NT * VPT4 * 4;
+static_assert(CHUNK == kVocabChunk, "chunk size");
+constexpr int MAX_CHUNKS = 128;
+constexpr float kFix = 1099511627776.0f;    // 2^40: fixed-point scale of top-p masses
+
+struct Smem {
+    float f[NW];
+    double d[NW];
+    unsigned long long u[NW];
+    int i[NW];
+    double dpre[NW + 1];
+    unsigned long long upre[NW + 1];
+    float fr;
+    double dr;
+    unsigned long long ur;
+    int ir;
+    unsigned long long hist[1024];
+    double chunk_sum[MAX_CHUNKS];
+    int winner;
+    int found;
+};
+
+__device__ __forceinline__ int tid_() { return threadIdx.x; }
+__device__ __forceinline__ int lane_() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_() { return threadIdx.x >> 6; }
+
+// element index of (slot j, component e) for this thread in chunk cb
+__device__ __forceinline__ int elem_index(int cb, int j, int e) { return cb + 4 * (tid_() + NT * j) + e; }
+
+__device__ __forceinline__ float f4get(const float4& v, int e) {
+    return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ void f4set(float4& v, int e, float x) {
+    if (e == 0) v.x = x; else if (e == 1) v.y = x; else if (e == 2) v.z = x; else v.w = x;
+}
+
+// Block reductions: each wave reduces, wave 0 reduces the wave results in a
+// fixed order and broadcasts one value (deterministic, two barriers).
+__device__ float block_max(float v, Smem& sm) {
+    v = wave_max(v);
+    if (lane_() == 0) sm.f[wave_()] = v;
+    __syncthreads();
+    if (wave_() == 0) {
+        float x = wave_max(lane_() < NW ? sm.f[lane_()] : -INFINITY);
+        if (lane_() == 0) sm.fr = x;
+    }
+    __syncthreads();
+    return sm.fr;
+}
+
+__device__ double block_sum_d(double v, Smem& sm) {
+    v = wave_sum_d(v);
+    if (lane_() == 0) sm.d[wave_()] = v;
+    __syncthreads();
+    if (wave_() == 0) {
+        double x = wave_sum_d(lane_() < NW ? sm.d[lane_()] : 0.0);
+        if (lane_() == 0) sm.dr = x;
+    }
+    __syncthreads();
+    return sm.dr;
+}
+
+__device__ unsigned long long block_sum_u64(unsigned long long v, Smem& sm) {
+    v = wave_sum_u64(v);
+    if (lane_() == 0) sm.u[wave_()] = v;
+    __syncthreads();
+    if (wave_() == 0) {
+        unsigned long long x = wave_sum_u64(lane_() < NW ? sm.u[lane_()] : 0ull);
+        if (lane_() == 0) sm.ur = x;
+    }
+    __syncthreads();
+    return sm.ur;
+}
+
+__device__ int block_max_int(int v, Smem& sm) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+    if (lane_() == 0) sm.i[wave_()] = v;
+    __syncthreads();
+    if (wave_() == 0) {
+        int x = lane_() < NW ? sm.i[lane_()] : INT_MIN;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, kWave));
+        if (lane_() == 0) sm.ir = x;
+    }
+    __syncthreads();
+    return sm.ir;
+}
+
+__device__ __forceinline__ void argmax_step(float& v, int& idx, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < idx)) { v = v2; idx = i2; }
+}
+
+// (value, index) max with the smallest index among equal values.
+__device__ int block_argmax(float v, int idx, Smem& sm) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) argmax_step(v, idx, __shfl_xor(v, o, kWave), __shfl_xor(idx, o, kWave));
+    if (lane_() == 0) { sm.f[wave_()] = v; sm.i[wave_()] = idx; }
+    __syncthreads();
+    if (wave_() == 0) {
+        float x = lane_() < NW ? sm.f[lane_()] : -INFINITY;
+        int xi = lane_() < NW ? sm.i[lane_()] : INT_MAX;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) argmax_step(x, xi, __shfl_xor(x, o, kWave), __shfl_xor(xi, o, kWave));
+        if (lane_() == 0) sm.ir = xi;
+    }
+    __syncthreads();
+    return sm.ir;
+}
+
+// Inclusive scan of v over thread order; *excl receives the exclusive prefix.
+// Adjacent threads' bounds are bitwise equal (incl_t == excl_{t+1}): wave
+// offsets are accumulated sequentially from the waves' last inclusive values.
+__device__ unsigned long long block_scan_u64(unsigned long long v, unsigned long long* excl, Smem& sm) {
+    unsigned long long x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned long long y = __shfl_up(x, o, kWave);
+        if (lane_() >= o) x += y;
+    }
+    if (lane_() == kWave - 1) sm.u[wave_()] = x;
+    unsigned long long prev = __shfl_up(x, 1, kWave);
+    if (lane_() == 0) prev = 0;
+    __syncthreads();
+    if (tid_() == 0) {
+        unsigned long long acc = 0;
+        for (int w = 0; w < NW; ++w) { sm.upre[w] = acc; acc += sm.u[w]; }
+    }
+    __syncthreads();
+    const unsigned long long base = sm.upre[wave_()];
+    *excl = base + prev;
+    return base + x;
+}
+
+__device__ double block_scan_d(double v, double* excl, Smem& sm) {
+    double x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double y = __shfl_up(x, o, kWave);
+        if (lane_() >= o) x += y;
+    }
+    if (lane_() == kWave - 1) sm.d[wave_()] = x;
+    double prev = __shfl_up(x, 1, kWave);
+    if (lane_() == 0) prev = 0.0;
+    __syncthreads();
+    if (tid_() == 0) {
+        double acc = 0.0;
+        for (int w = 0; w < NW; ++w) { sm.dpre[w] = acc; acc += sm.d[w]; }
+    }
+    __syncthreads();
+    const double base = sm.dpre[wave_()];
+    *excl = base + prev;
+    return base + x;
+}
+
+// Load chunk cb of a row: out-of-range entries become -inf.
+__device__ void load_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[VPT4]) {
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j) {
+        const int idx = elem_index(cb, j, 0);
+        if (aligned && idx + 3 < V) {
+            x[j] = *(const float4*)(row + idx);
+        } else {
+            float4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f4set(v, e, (idx + e < V) ? row[idx + e] : -INFINITY);
+            x[j] = v;
+        }
+    }
+}
+
+__device__ float thread_max(const float4 (&x)[VPT4]) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j) m = fmaxf(fmaxf(fmaxf(m, x[j].x), fmaxf(x[j].y, x[j].z)), x[j].w);
+    return m;
+}
+
+// Unnormalised probability of a logit: exp((z - zmax) / temperature).
+__device__ __forceinline__ float unnorm(float z, float zmax, float ilog) { return exp2f((z - zmax) * ilog); }
+
+// max(0, p - q) from unnormalised values and inverse normalisers.  Both
+// products are rounded before the subtraction (contraction into a fused
+// multiply-add is switched off here), so identical distributions give
+// exactly zero.
+__device__ __forceinline__ float resid_weight(float ep, float ip, float eq, float iq) {
+#pragma clang fp contract(off)
+    const float p = ep * ip;
+    const float q = eq * iq;
+    return fmaxf(p - q, 0.f);
+}
+
+// Top-p cut of a register-resident row of unnormalised probabilities e.
+struct Nucleus {
+    uint32_t thr;   // bit pattern of the cut value
+    int cutoff;     // ties at thr are kept for token ids < cutoff
+};
+
+__device__ __forceinline__ bool in_nucleus(float e, int idx, const Nucleus& nu) {
+    const uint32_t bits = __float_as_uint(e);
+    return bits > nu.thr || (bits == nu.thr && idx < nu.cutoff);
+}
+
+__device__ __forceinline__ unsigned long long fixmass(float e) { return (unsigned long long)__float2ull_rn(e * kFix); }
+
+// One radix level: histogram (by `shift`/`width` bits) of the mass of the
+// elements whose bits above the level equal `prefix`, then the bucket where
+// the mass counted from the top first reaches `need`.  Returns the bucket;
+// *above receives the mass of the larger buckets.
+__device__ int radix_level(const float4 (&e)[VPT4], int cb, int V, int shift, uint32_t prefix, int prefix_shift,
+                           double need, unsigned long long* above, Smem& sm) {
+    const int tid = tid_();
+    sm.hist[tid] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int idx = elem_index(cb, j, c);
+            if (idx < V) {
+                const float v = f4get(e[j], c);
+                const uint32_t bits = __float_as_uint(v);
+                if ((bits >> prefix_shift) == prefix) {
+                    const int bucket = (bits >> shift) & 1023;
+                    atomicAdd(&sm.hist[bucket], fixmass(v));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // thread t holds bucket 1023 - t: scanning thread order = descending value
+    unsigned long long excl;
+    const unsigned long long incl = block_scan_u64(sm.hist[1023 - tid], &excl, sm);
+    if (tid == 0) sm.found = -1;
+    __syncthreads();
+    if ((double)excl < need && need <= (double)incl) atomicMax(&sm.found, tid);
+    __syncthreads();
+    int t = sm.found;
+    if (t < 0) t = NT - 1;   // need above every bucket: cannot happen for need <= total
+    if (tid == t) sm.u[0] = excl;
+    __syncthreads();
+    *above = sm.u[0];
+    __syncthreads();
+    return 1023 - t;
+}
+
+__device__ Nucleus find_nucleus(const float4 (&e)[VPT4], int cb, int V, float top_p, Smem& sm) {
+    unsigned long long mine = 0;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (elem_index(cb, j, c) < V) mine += fixmass(f4get(e[j], c));
+    const unsigned long long total = block_sum_u64(mine, sm);
+    const double need = (double)top_p * (double)total;
+    unsigned long long a1, a2, a3;
+    const int b1 = radix_level(e, cb, V, 20, 0u, 31, need, &a1, sm);
+    const int b2 = radix_level(e, cb, V, 10, (uint32_t)b1, 20, need - (double)a1, &a2, sm);
+    const int b3 = radix_level(e, cb, V, 0, ((uint32_t)b1 << 10) | (uint32_t)b2, 10, need - (double)a1 - (double)a2,
+                               &a3, sm);
+    Nucleus nu;
+    nu.thr = ((uint32_t)b1 << 20) | ((uint32_t)b2 << 10) | (uint32_t)b3;
+    nu.cutoff = INT_MAX;
+    const unsigned long long above = a1 + a2 + a3;
+    const unsigned long long tie_mass = fixmass(__uint_as_float(nu.thr));
+    int ties = 0;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (elem_index(cb, j, c) < V && __float_as_uint(f4get(e[j], c)) == nu.thr) ++ties;
+    ties = (int)block_sum_u64((unsigned long long)ties, sm);
+    if (ties > 1 && tie_mass > 0) {
+        const double rest = need - (double)above;
+        long long k = (long long)ceil(rest / (double)tie_mass);
+        if (k < 1) k = 1;
+        if (k < ties) {
+            // smallest cutoff c with #ties(idx < c) >= k, by bisection on the token id
+            int lo = 0, hi = V;
+            while (lo < hi) {
+                const int mid = lo + (hi - lo) / 2;
+                int cnt = 0;
+#pragma unroll
+                for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int idx = elem_index(cb, j, c);
+                        if (idx < V && idx <= mid && __float_as_uint(f4get(e[j], c)) == nu.thr) ++cnt;
+                    }
+                cnt = (int)block_sum_u64((unsigned long long)cnt, sm);
+                if (cnt >= k) hi = mid; else lo = mid + 1;
+            }
+            nu.cutoff = lo + 1;
+        }
+    }
+    return nu;
+}
+
+// Sum of w over a chunk (fp64, fixed order).
+__device__ double chunk_total(const float4 (&w)[VPT4], Smem& sm) {
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j)
+        s += ((double)w[j].x + (double)w[j].y) + ((double)w[j].z + (double)w[j].w);
+    return block_sum_d(s, sm);
+}
+
+// Smallest token id k of this chunk with base + C_k > target (C = prefix sums
+// of w in id order within the chunk), or -1 if the chunk does not reach it.
+__device__ int locate_in_chunk(const float4 (&w)[VPT4], int cb, int V, double base, double target, Smem& sm) {
+    double cum = base;
+    int jstar = -1;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j) {
+        const double sj = ((double)w[j].x + (double)w[j].y) + ((double)w[j].z + (double)w[j].w);
+        const double S = block_sum_d(sj, sm);
+        if (jstar < 0) {
+            if (cum + S > target) jstar = j;
+            else cum += S;
+        }
+    }
+    if (jstar < 0) return -1;
+    float4 wv = w[0];
+#pragma unroll
+    for (int j = 1; j < VPT4; ++j)
+        if (j == jstar) wv = w[j];
+    const double mysum = ((double)wv.x + (double)wv.y) + ((double)wv.z + (double)wv.w);
+    double excl;
+    double incl = block_scan_d(mysum, &excl, sm);
+    excl += cum;
+    incl += cum;
+    if (tid_() == 0) { sm.winner = INT_MAX; sm.found = -1; }
+    __syncthreads();
+    if (excl <= target && target < incl) atomicMin(&sm.winner, tid_());
+    __syncthreads();
+    int last_pos = -1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (f4get(wv, c) > 0.f) last_pos = elem_index(cb, jstar, c);
+    if (tid_() == sm.winner) {
+        double run = excl;
+        int y = -1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            run += (double)f4get(wv, c);
+            if (y < 0 && run > target) y = elem_index(cb, jstar, c);
+        }
+        sm.found = (y >= 0) ? y : last_pos;
+    }
+    __syncthreads();
+    int y = sm.found;
+    __syncthreads();
+    if (y < 0) {  // rounding left no winner: last positive weight of the slot
+        y = block_max_int(last_pos, sm);
+    }
+    return y;
+}
+
+}  // namespace rows
+}  // namespace sv

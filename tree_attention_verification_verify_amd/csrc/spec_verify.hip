@@ -2,8 +2,8 @@
 //
 // A run enqueues, on the caller's stream and without synchronising:
 //   tree attention (MFMA or VALU kernel) -> split merge (when split)
-//   vocab pass (row statistics, ratios, candidate final tokens)
-//   selection (decisions, longest accepted path, emitted tokens)
+//   row statistics of every target / draft logits row (one read)
+//   selection (ratios, decisions, longest accepted path, final draw at v*)
 // The attention and the vocabulary work read disjoint inputs.
 
 #include <hip/hip_runtime.h>
@@ -91,6 +91,7 @@ struct spec_verify_handle {
     size_t part_rows_cap = 0;
     float* part_o = nullptr;
     float2* part_ml = nullptr;
+    sv::RowStat* stats = nullptr;     // max_batch * 2 * max_nodes row statistics
     bool timing = false;
     std::vector<hipEvent_t> events;   // kTimingRing * kEventsPerRun
     long runs_recorded = 0;           // since the last read
@@ -158,6 +159,14 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
             return fail(SPEC_VERIFY_ERR_OOM, "workspace allocation failed");
         }
     }
+    e = hipMalloc((void**)&h->stats, (size_t)c.max_batch * 2 * c.max_nodes * sizeof(sv::RowStat));
+    if (e != hipSuccess) {
+        (void)hipFree(h->part_o);
+        (void)hipFree(h->part_ml);
+        delete h;
+        (void)hipGetLastError();
+        return fail(SPEC_VERIFY_ERR_OOM, "workspace allocation failed");
+    }
     h->timing = (c.flags & SPEC_VERIFY_FLAG_TIMING) != 0u;
     if (h->timing) {
         h->events.resize((size_t)kTimingRing * kEventsPerRun, nullptr);
@@ -183,6 +192,7 @@ int spec_verify_destroy(spec_verify_handle* h) {
         if (ev) (void)hipEventDestroy(ev);
     if (h->part_o) (void)hipFree(h->part_o);
     if (h->part_ml) (void)hipFree(h->part_ml);
+    if (h->stats) (void)hipFree(h->stats);
     if (dev >= 0 && dev != h->device) (void)hipSetDevice(dev);
     delete h;
     return SPEC_VERIFY_OK;
@@ -256,34 +266,32 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     }
     if (int rc = mark(SPEC_VERIFY_STAGE_COMBINE)) return rc;
 
-    sv::VocabParams vp{};
-    vp.target = in->target_logits;
-    vp.draft = in->draft_logits;
-    vp.parent = in->parent;
-    vp.tokens = in->tokens;
-    vp.u_final = in->u_final;
-    vp.node_p = out->node_p;
-    vp.node_q = out->node_q;
-    vp.row_token = out->row_token;
-    vp.B = B;
-    vp.T = T;
-    vp.V = c.vocab;
-    vp.sampling = sampling ? 1 : 0;
-    vp.ilog = sampling ? kLog2e / c.temperature : kLog2e;
-    vp.top_p = sampling ? c.top_p : 1.f;
-    vp.nchunks = (c.vocab + sv::kVocabChunk - 1) / sv::kVocabChunk;
-    e = sv::launch_vocab(vp, s);
-    if (e != hipSuccess) return hip_fail(e, "vocab launch");
+    sv::StatsParams tp{};
+    tp.target = in->target_logits;
+    tp.draft = in->draft_logits;
+    tp.stats = h->stats;
+    tp.B = B;
+    tp.T = T;
+    tp.V = c.vocab;
+    tp.sampling = sampling ? 1 : 0;
+    tp.ilog = sampling ? kLog2e / c.temperature : kLog2e;
+    tp.top_p = sampling ? c.top_p : 1.f;
+    e = sv::launch_row_stats(tp, s);
+    if (e != hipSuccess) return hip_fail(e, "row statistics launch");
     if (int rc = mark(SPEC_VERIFY_STAGE_VOCAB)) return rc;
 
     sv::SelectParams sp{};
+    sp.target = in->target_logits;
+    sp.draft = in->draft_logits;
+    sp.stats = h->stats;
     sp.parent = in->parent;
     sp.tokens = in->tokens;
     sp.kv_len = in->kv_len;
     sp.u_accept = in->u_accept;
-    sp.row_token = out->row_token;
+    sp.u_final = in->u_final;
     sp.node_p = out->node_p;
     sp.node_q = out->node_q;
+    sp.row_token = out->row_token;
     sp.accept_len = out->accept_len;
     sp.final_node = out->final_node;
     sp.path = out->path;
@@ -296,6 +304,7 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     sp.V = c.vocab;
     sp.Lcap = c.kv_capacity;
     sp.sampling = sampling ? 1 : 0;
+    sp.ilog = tp.ilog;
     e = sv::launch_select(sp, s);
     if (e != hipSuccess) return hip_fail(e, "select launch");
     if (int rc = mark(SPEC_VERIFY_STAGE_SELECT)) return rc;

@@ -41,6 +41,14 @@ __device__ __forceinline__ int swap_bits_2_3(int x) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+
+// Byte offset of the 16-byte chunk c (8 keys) of V^T row d in a 64-key tile:
+// chunk positions are XOR-swizzled with bits 1..3 and 4..6 of d, so that 16
+// consecutive rows read at one chunk, and 16 lanes storing 8-byte halves of 8
+// row-spaced chunks, both touch distinct banks.
+__device__ __forceinline__ int vt_offset(int d, int c) { return d * 128 + ((c ^ (((d >> 1) ^ (d >> 4)) & 7)) << 4); }
+
 // ---------------------------------------------------------------- MFMA path
 
 template <int D, int WAVES>
@@ -54,10 +62,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     constexpr int KLOADS = (KCHUNKS + NTHR - 1) / NTHR;
     constexpr int VBLOCKS = (KT / 4) * CH;  // blocks of 4 keys x 8 columns
     constexpr int VLOADS = (VBLOCKS + NTHR - 1) / NTHR;
-    constexpr int VT_ROW = KT * 2;          // bytes per V^T row in LDS
 
-    __shared__ __align__(16) uint8_t k_lds[KT * D * 2];
-    __shared__ __align__(16) uint8_t vt_lds[D * KT * 2];
+    __shared__ __align__(16) uint8_t k_lds[2 * KT * D * 2];     // two buffers
+    __shared__ __align__(16) uint8_t vt_lds[2 * D * KT * 2];
     __shared__ unsigned long long anc_lds[64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -129,49 +136,56 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     float m_run = -INFINITY, l_run = 0.f;
     const int krow = swap_bits_2_3(qcol);   // key (within a 32-key sub-tile) fed to MFMA row qcol
 
-    // register prefetch of the next tile
+    // Tile staging, software-pipelined: the global loads of tile t+1 are in
+    // flight (in registers) while tile t is computed from the other LDS buffer.
+    // K rows go to LDS as-is (16-byte chunks XOR-swizzled by the key).  V is
+    // transposed on the way: each thread takes a block of 4 keys x 8 columns;
+    // the thread -> block map puts 8 consecutive column blocks and two key
+    // parities in every 16 lanes, so the 8-byte V^T stores of 16 lanes fill one
+    // 128-byte row segment without bank conflicts.
     u32x4 kreg[KLOADS];
     u32x4 vreg[VLOADS][4];
     auto load_tile = [&](int t) {
 #pragma unroll
         for (int j = 0; j < KLOADS; ++j) {
             const int cid = tid + j * NTHR;
-            u32x4 v = {0u, 0u, 0u, 0u};
+            kreg[j] = u32x4{0u, 0u, 0u, 0u};
             if (cid < KCHUNKS) {
                 const int key = cid / CH, c = cid - key * CH;
-                if (t + key < k1) v = *(const u32x4*)(kbase + (size_t)(t + key) * D + c * 8);
+                if (t + key < k1) kreg[j] = *(const u32x4*)(kbase + (size_t)(t + key) * D + c * 8);
             }
-            kreg[j] = v;
         }
 #pragma unroll
         for (int j = 0; j < VLOADS; ++j) {
             const int bid = tid + j * NTHR;
+            // bid bits: [2:0] column block low, [3] key-group parity, then the rest
+            const int dc = (bid & 7) | (((bid >> 4) & (CH / 8 - 1)) << 3);
+            const int kg = ((bid >> 3) & 1) | ((bid >> (4 + CH / 8 / 2)) << 1);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (bid < VBLOCKS) {
-                    const int kg = bid / CH, dc = bid - kg * CH;
-                    const int key = t + kg * 4 + jj;
-                    if (key < k1) v = *(const u32x4*)(vbase + (size_t)key * D + dc * 8);
-                }
-                vreg[j][jj] = v;
+                const int key = t + kg * 4 + jj;
+                vreg[j][jj] = u32x4{0u, 0u, 0u, 0u};
+                if (bid < VBLOCKS && key < k1) vreg[j][jj] = *(const u32x4*)(vbase + (size_t)key * D + dc * 8);
             }
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
+        uint8_t* kl = k_lds + buf * (KT * D * 2);
+        uint8_t* vl = vt_lds + buf * (D * KT * 2);
 #pragma unroll
         for (int j = 0; j < KLOADS; ++j) {
             const int cid = tid + j * NTHR;
             if (cid < KCHUNKS) {
                 const int key = cid / CH, c = cid - key * CH;
-                *(u32x4*)(k_lds + key * (D * 2) + ((c ^ (key & (CH - 1))) << 4)) = kreg[j];
+                *(u32x4*)(kl + key * (D * 2) + ((c ^ (key & (CH - 1))) << 4)) = kreg[j];
             }
         }
 #pragma unroll
         for (int j = 0; j < VLOADS; ++j) {
             const int bid = tid + j * NTHR;
             if (bid < VBLOCKS) {
-                const int kg = bid / CH, dc = bid - kg * CH;
+                const int dc = (bid & 7) | (((bid >> 4) & (CH / 8 - 1)) << 3);
+                const int kg = ((bid >> 3) & 1) | ((bid >> (4 + CH / 8 / 2)) << 1);
                 const int kc = kg >> 1, koff = (kg & 1) * 8;
 #pragma unroll
                 for (int m2 = 0; m2 < 4; ++m2) {
@@ -180,19 +194,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
                     const int d = dc * 8 + 2 * m2;
                     u32x2 lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
                     u32x2 hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-                    *(u32x2*)(vt_lds + d * VT_ROW + ((kc ^ ((d >> 1) & 7)) << 4) + koff) = lo;
-                    *(u32x2*)(vt_lds + (d + 1) * VT_ROW + ((kc ^ (((d + 1) >> 1) & 7)) << 4) + koff) = hi;
+                    *(u32x2*)(vl + vt_offset(d, kc) + koff) = lo;
+                    *(u32x2*)(vl + vt_offset(d + 1, kc) + koff) = hi;
                 }
             }
         }
     };
 
-    for (int t = k0; t < k1; t += KT) {
-        load_tile(t);
-        store_tile();
-        __syncthreads();
-
-        // S^T[32 keys x 32 queries] for the two sub-tiles
+    // One 64-key tile: S^T, online softmax (log2 domain), O^T += V^T P^T.
+    // need_mask (wave-uniform): the tile reaches the tree slots or the end of the split.
+    auto tile = [&](int t, int buf, bool need_mask) {
+        const uint8_t* kl = k_lds + buf * (KT * D * 2);
+        const uint8_t* vl = vt_lds + buf * (D * KT * 2);
         floatx16_t s[2];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
@@ -202,56 +215,60 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 const int c = 2 * ks + half;
-                const u32x4 a = *(const u32x4*)(k_lds + kk * (D * 2) + ((c ^ (kk & (CH - 1))) << 4));
+                const u32x4 a = *(const u32x4*)(kl + kk * (D * 2) + ((c ^ (kk & (CH - 1))) << 4));
                 s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[ks], s[sub], 0, 0, 0);
             }
         }
-
-        // scale, mask, running max.  Accumulator element e of lane (qcol, half)
-        // holds key 16*(e>>3) + 8*half + (e&7) of its sub-tile.
-        const bool need_mask = (t + KT > L);
+        // accumulator element e of lane (qcol, half) holds key 16*(e>>3) + 8*half + (e&7) of its sub-tile
+        if (need_mask) {
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = t + sub * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
+                    const unsigned rel = (unsigned)(key - L);
+                    const bool tree_vis = (key < k1) && ((anc_row >> (rel & 63u)) & 1ull);
+                    const bool vis = (key < L) | (key >= L && tree_vis);
+                    s[sub][e] = vis ? s[sub][e] : -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float val = s[sub][e] * P.c;
-                if (need_mask) {
-                    const int key = t + sub * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
-                    const bool vis = key < L || (key < k1 && ((anc_row >> (key - L)) & 1ull));
-                    if (!vis) val = -INFINITY;
-                }
-                s[sub][e] = val;
-                mx = fmaxf(mx, val);
-            }
-        }
+            for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[sub][e], s[sub][e + 1]));
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-        m_run = m_new;
+        const float m_new = fmaxf(m_run, mx * P.c);
+        if (__any(m_new > m_run)) {       // rescale only when some running max grows
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+            m_run = m_new;
+        }
+        const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
         float psum = 0.f;
         bf16x8_t pb[2][2];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                u32x4 pk;
+                float p[8];
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float p0 = exp2f(s[sub][8 * h2 + 2 * w] - m_use);
-                    const float p1 = exp2f(s[sub][8 * h2 + 2 * w + 1] - m_use);
-                    psum += p0 + p1;
-                    pk[w] = pack_bf16x2(p0, p1);
+                for (int w = 0; w < 8; ++w) {
+                    p[w] = __builtin_amdgcn_exp2f(fmaf(s[sub][8 * h2 + w], P.c, neg_m));
+                    psum += p[w];
                 }
-                pb[sub][h2] = as_bf16x8(pk);
+                bf16x2_t q0 = __builtin_convertvector((floatx2_t){p[0], p[1]}, bf16x2_t);
+                bf16x2_t q1 = __builtin_convertvector((floatx2_t){p[2], p[3]}, bf16x2_t);
+                bf16x2_t q2 = __builtin_convertvector((floatx2_t){p[4], p[5]}, bf16x2_t);
+                bf16x2_t q3 = __builtin_convertvector((floatx2_t){p[6], p[7]}, bf16x2_t);
+                pb[sub][h2] = bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
             }
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+        l_run += psum;
 
         // O^T[d x q] += V^T[d x keys] P^T[keys x q]
 #pragma unroll
@@ -262,12 +279,24 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
                     const int c = 4 * sub + 2 * h2 + half;
-                    const u32x4 a = *(const u32x4*)(vt_lds + d * VT_ROW + ((c ^ ((d >> 1) & 7)) << 4));
+                    const u32x4 a = *(const u32x4*)(vl + vt_offset(d, c));
                     o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[sub][h2], o[dt], 0, 0, 0);
                 }
             }
         }
+    };
+
+    load_tile(k0);
+    store_tile(0);
+    __syncthreads();
+    int buf = 0;
+    for (int t = k0; t < k1; t += KT) {
+        const bool more = t + KT < k1;
+        if (more) load_tile(t + KT);
+        tile(t, buf, t + KT > L || t + KT > k1);
+        if (more) store_tile(buf ^ 1);
         __syncthreads();
+        buf ^= 1;
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
