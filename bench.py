@@ -35,7 +35,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--workload", default="70b-gqa-medusa",
+                    help="one of: tiny-chain-f32, llama7b-medusa-greedy, chain-batch32-topp, "
+                         "70b-gqa-medusa, longctx-bigvocab")
     ap.add_argument("--mode", default=None, help="sampling or greedy (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -149,7 +151,7 @@ def main():
     overrides = {}
     if args.mode:
         overrides["mode"] = args.mode
-    spec = synth.config(args.config, **overrides)
+    spec = synth.workload(args.workload, **overrides)
     t_gen = time.perf_counter()
     case = synth.make_case(spec)
     t_gen = time.perf_counter() - t_gen
@@ -201,7 +203,7 @@ def main():
     torch.cuda.synchronize()
     got = {k: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy() for k, v in outs.items()}
 
-    workload = "cfg%d-%s" % (args.config, spec.mode)
+    workload = "%s-%s" % (args.workload, spec.mode)
     # dominant kernel by measured time
     dominant = max(("attention", "vocab"), key=lambda k: per_launch[k])
     if dominant == "attention":
@@ -240,8 +242,7 @@ def main():
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": spec.dtype, "data": "synthetic",
-        "config": {"workload": "70b-gqa-medusa-tree verify" if args.config == 3 else spec.name,
-                   "config_index": args.config, "mode": spec.mode, "batch": B, "nodes": T,
+        "config": {"workload": "%s tree verify" % args.workload, "mode": spec.mode, "batch": B, "nodes": T,
                    "q_heads": spec.hq, "kv_heads": spec.hkv, "head_dim": spec.head_dim,
                    "prefix": int(case.kv_len.max()), "vocab": spec.vocab, "temperature": spec.temperature,
                    "top_p": spec.top_p},

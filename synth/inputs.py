@@ -77,24 +77,24 @@ class CaseSpec:
 MEDUSA_64 = ("medusa", (10, 4, 2, 1, 1), 64)
 MEDUSA_26 = ("medusa", (10, 4, 2, 1), 26)
 
-# The five workloads (shapes and value distributions as named in the workload list).
-CONFIGS = {
-    0: CaseSpec("tiny-chain-f32", 1, "f32", 4, 4, 64, 128, 1000, "sampling", ("chain", 4),
+# The five workloads (shapes and value distributions as stated for each), by name.
+WORKLOADS = {
+    "tiny-chain-f32": CaseSpec("tiny-chain-f32", 1, "f32", 4, 4, 64, 128, 1000, "sampling", ("chain", 4),
                 temperature=1.0, top_p=1.0, target_sigma=2.0, draft_sigma=1.0, seed=(0, 0)),
-    1: CaseSpec("llama7b-medusa-greedy", 1, "bf16", 32, 32, 128, 2048, 32000, "greedy", MEDUSA_64,
+    "llama7b-medusa-greedy": CaseSpec("llama7b-medusa-greedy", 1, "bf16", 32, 32, 128, 2048, 32000, "greedy", MEDUSA_64,
                 target_sigma=3.0, seed=(0, 1)),
-    2: CaseSpec("chain-batch32-topp", 32, "bf16", 32, 32, 128, 4096, 32000, "sampling", ("chain", 5),
+    "chain-batch32-topp": CaseSpec("chain-batch32-topp", 32, "bf16", 32, 32, 128, 4096, 32000, "sampling", ("chain", 5),
                 temperature=0.8, top_p=0.9, target_sigma=3.0, draft_sigma=1.5, ragged=(1024, 4096),
                 seed=(0, 2)),
-    3: CaseSpec("70b-gqa-medusa", 8, "bf16", 64, 8, 128, 8192, 32000, "sampling", MEDUSA_64,
+    "70b-gqa-medusa": CaseSpec("70b-gqa-medusa", 8, "bf16", 64, 8, 128, 8192, 32000, "sampling", MEDUSA_64,
                 temperature=1.0, top_p=1.0, target_sigma=3.0, draft_sigma=1.0, seed=(0, 3)),
-    4: CaseSpec("longctx-bigvocab", 16, "bf16", 32, 8, 128, 32768, 128256, "sampling", MEDUSA_26,
+    "longctx-bigvocab": CaseSpec("longctx-bigvocab", 16, "bf16", 32, 8, 128, 32768, 128256, "sampling", MEDUSA_26,
                 temperature=0.7, top_p=1.0, target_sigma=3.0, draft_sigma=1.0, seed=(0, 4)),
 }
 
 
-def config(idx: int, **overrides) -> CaseSpec:
-    spec = CONFIGS[idx]
+def workload(name: str, **overrides) -> CaseSpec:
+    spec = WORKLOADS[name]
     return spec.replace(**overrides) if overrides else spec
 
 

@@ -32,66 +32,66 @@ def check(case, label, seqs=None, attn_rows=None):
     return got, ref, stats
 
 
-# ------------------------------------------------------------------ the five workloads, reduced
+# ------------------------------------------------------------------ the five workloads, short prefixes
 
-def test_config0_tiny_chain_fp32():
-    check(synth.make_case(synth.config(0)), "cfg0")
+def test_tiny_chain_fp32():
+    check(synth.make_case(synth.workload("tiny-chain-f32")), "tiny-chain")
 
 
-def test_config0_many_seeds():
+def test_tiny_chain_fp32_many_seeds():
     for s in range(6):
-        spec = synth.config(0, batch=8, seed=(7, s))
-        check(synth.make_case(spec), "cfg0-seed%d" % s)
+        spec = synth.workload("tiny-chain-f32", batch=8, seed=(7, s))
+        check(synth.make_case(spec), "tiny-chain-seed%d" % s)
 
 
-def test_config1_medusa_greedy_reduced():
-    spec = synth.config(1, prefix_len=300, seed=(1, 300))
-    check(synth.make_case(spec), "cfg1-L300")
+def test_llama7b_medusa_greedy_short_prefix():
+    spec = synth.workload("llama7b-medusa-greedy", prefix_len=300, seed=(1, 300))
+    check(synth.make_case(spec), "medusa-greedy-L300")
 
 
-def test_config2_chain_topp_ragged_reduced():
-    spec = synth.config(2, batch=6, prefix_len=700, ragged=(70, 700), seed=(2, 700))
-    check(synth.make_case(spec), "cfg2-L700")
+def test_chain_topp_ragged_short_prefix():
+    spec = synth.workload("chain-batch32-topp", batch=6, prefix_len=700, ragged=(70, 700), seed=(2, 700))
+    check(synth.make_case(spec), "chain-topp-L700")
 
 
 @pytest.mark.parametrize("mode", ["sampling", "greedy"])
-def test_config3_gqa_tree_reduced(mode):
-    spec = synth.config(3, batch=2, prefix_len=333, mode=mode, seed=(3, 333))
-    check(synth.make_case(spec), "cfg3-%s-L333" % mode)
+def test_gqa_medusa_tree_short_prefix(mode):
+    spec = synth.workload("70b-gqa-medusa", batch=2, prefix_len=333, mode=mode, seed=(3, 333))
+    check(synth.make_case(spec), "gqa-medusa-%s-L333" % mode)
 
 
-def test_config4_large_vocab_reduced():
-    spec = synth.config(4, batch=2, prefix_len=400, seed=(4, 400))
-    check(synth.make_case(spec), "cfg4-L400")
+def test_large_vocab_tree_short_prefix():
+    spec = synth.workload("longctx-bigvocab", batch=2, prefix_len=400, seed=(4, 400))
+    check(synth.make_case(spec), "bigvocab-L400")
 
 
 # ------------------------------------------------------------------ full sizes, sampled attention rows
 
-def _full(idx, picks, **kw):
-    spec = synth.config(idx, **kw)
+def _full(name, picks, **kw):
+    spec = synth.workload(name, **kw)
     case = synth.make_case(spec)
     rows = sampled_attention(case, picks)
-    return check(case, "cfg%d-full-%s" % (idx, spec.mode), attn_rows=rows)
+    return check(case, "%s-full-%s" % (name, spec.mode), attn_rows=rows)
 
 
-def test_config1_full():
-    _full(1, [(0, 0, 0), (0, 63, 31), (0, 17, 5), (0, 52, 20)])
+def test_llama7b_medusa_greedy_full():
+    _full("llama7b-medusa-greedy", [(0, 0, 0), (0, 63, 31), (0, 17, 5), (0, 52, 20)])
 
 
-def test_config2_full():
-    _full(2, [(0, 0, 0), (31, 5, 31), (7, 3, 12), (19, 2, 7)])
+def test_chain_batch32_topp_full():
+    _full("chain-batch32-topp", [(0, 0, 0), (31, 5, 31), (7, 3, 12), (19, 2, 7)])
 
 
-def test_config3_full_sampling():
-    _full(3, [(0, 0, 0), (7, 63, 63), (3, 40, 17), (5, 11, 36)])
+def test_70b_gqa_medusa_full_sampling():
+    _full("70b-gqa-medusa", [(0, 0, 0), (7, 63, 63), (3, 40, 17), (5, 11, 36)])
 
 
-def test_config3_full_greedy():
-    _full(3, [(1, 1, 8), (6, 50, 55)], mode="greedy")
+def test_70b_gqa_medusa_full_greedy():
+    _full("70b-gqa-medusa", [(1, 1, 8), (6, 50, 55)], mode="greedy")
 
 
-def test_config4_full():
-    _full(4, [(0, 0, 0), (15, 25, 31), (8, 12, 9)])
+def test_longctx_bigvocab_full():
+    _full("longctx-bigvocab", [(0, 0, 0), (15, 25, 31), (8, 12, 9)])
 
 
 # ------------------------------------------------------------------ edge cases
@@ -123,7 +123,7 @@ def test_valu_gqa_rows():
 
 
 def test_forced_accept_and_reject():
-    spec = synth.config(3, batch=3, prefix_len=64, vocab=4000, seed=(9, 7))
+    spec = synth.workload("70b-gqa-medusa", batch=3, prefix_len=64, vocab=4000, seed=(9, 7))
     case = synth.make_case(spec)
     case.draft_logits[0] = np.where(np.arange(case.nodes)[:, None] > 0,
                                     case.target_logits[0][case.parent[0].clip(0)], 0.0)
@@ -133,7 +133,7 @@ def test_forced_accept_and_reject():
 
 
 def test_invalid_inputs_are_flagged():
-    spec = synth.config(0, batch=5, seed=(9, 8))
+    spec = synth.workload("tiny-chain-f32", batch=5, seed=(9, 8))
     case = synth.make_case(spec)
     case.parent[1, 3] = 3          # not < i
     case.parent[2, 0] = 0          # root must be -1
@@ -147,7 +147,7 @@ def test_invalid_inputs_are_flagged():
 
 
 def test_zero_draft_probability_is_flagged():
-    spec = synth.config(2, batch=2, prefix_len=128, ragged=None, vocab=3000, seed=(9, 9))
+    spec = synth.workload("chain-batch32-topp", batch=2, prefix_len=128, ragged=None, vocab=3000, seed=(9, 9))
     case = synth.make_case(spec)
     # draft row of node 2 puts no top-p mass on its own token
     case.draft_logits[1, 2, case.tokens[1, 2]] = -1e4
@@ -156,7 +156,7 @@ def test_zero_draft_probability_is_flagged():
 
 
 def test_deterministic_across_runs():
-    spec = synth.config(3, batch=2, prefix_len=500, seed=(9, 10))
+    spec = synth.workload("70b-gqa-medusa", batch=2, prefix_len=500, seed=(9, 10))
     case = synth.make_case(spec)
     a, b = run_gpu(case, "determinism", repeat=2)
     for k in a:

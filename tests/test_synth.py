@@ -30,7 +30,7 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_cases_are_deterministic_and_well_formed():
-    spec = synth.config(2, batch=3, prefix_len=64, ragged=(8, 64))
+    spec = synth.workload("chain-batch32-topp", batch=3, prefix_len=64, ragged=(8, 64))
     a, b = synth.make_case(spec), synth.make_case(spec)
     for f in ("q", "k_cache", "v_cache", "kv_len", "tokens", "target_logits", "draft_logits",
               "u_accept", "u_final"):
@@ -42,7 +42,7 @@ def test_cases_are_deterministic_and_well_formed():
 
 
 def test_drafted_tokens_lie_in_the_draft_nucleus():
-    spec = synth.config(2, batch=2, prefix_len=16, ragged=None, vocab=2000)
+    spec = synth.workload("chain-batch32-topp", batch=2, prefix_len=16, ragged=None, vocab=2000)
     c = synth.make_case(spec, with_kv=False)
     for b in range(2):
         for i in range(1, c.nodes):
@@ -51,7 +51,7 @@ def test_drafted_tokens_lie_in_the_draft_nucleus():
 
 
 def test_greedy_children_are_distinct_ranked_candidates():
-    spec = synth.config(1, prefix_len=16, vocab=500)
+    spec = synth.workload("llama7b-medusa-greedy", prefix_len=16, vocab=500)
     c = synth.make_case(spec, with_kv=False)
     par = c.parent[0]
     for v in range(c.nodes):
