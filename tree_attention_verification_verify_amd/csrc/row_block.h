@@ -36,6 +36,8 @@ struct Smem {
     int ir;
     unsigned long long hist[1024];
     double chunk_sum[MAX_CHUNKS];
+    double slot_part[NW][VPT4];
+    double slot_tot[VPT4];
     int winner;
     int found;
 };
@@ -316,24 +318,40 @@ __device__ Nucleus find_nucleus(const float4 (&e)[VPT4], int cb, int V, float to
     return nu;
 }
 
-// Sum of w over a chunk (fp64, fixed order).
-__device__ double chunk_total(const float4 (&w)[VPT4], Smem& sm) {
-    double s = 0.0;
+// Totals of the weights of every slot j (token ids cb + 4*(t + NT*j) + e over
+// all threads t), all slots in one reduction: stored in sm.slot_tot[j]; the
+// chunk total (fp64, fixed order) is returned.
+__device__ double slot_totals(const float4 (&w)[VPT4], Smem& sm) {
+    double sj[VPT4];
 #pragma unroll
     for (int j = 0; j < VPT4; ++j)
-        s += ((double)w[j].x + (double)w[j].y) + ((double)w[j].z + (double)w[j].w);
-    return block_sum_d(s, sm);
+        sj[j] = wave_sum_d(((double)w[j].x + (double)w[j].y) + ((double)w[j].z + (double)w[j].w));
+    if (lane_() == 0)
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j) sm.slot_part[wave_()][j] = sj[j];
+    __syncthreads();
+    if (tid_() < VPT4) {
+        double t = 0.0;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) t += sm.slot_part[w2][tid_()];
+        sm.slot_tot[tid_()] = t;
+    }
+    __syncthreads();
+    double total = 0.0;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j) total += sm.slot_tot[j];
+    return total;
 }
 
 // Smallest token id k of this chunk with base + C_k > target (C = prefix sums
 // of w in id order within the chunk), or -1 if the chunk does not reach it.
+// Needs sm.slot_tot from slot_totals(w) on the same weights.
 __device__ int locate_in_chunk(const float4 (&w)[VPT4], int cb, int V, double base, double target, Smem& sm) {
     double cum = base;
     int jstar = -1;
 #pragma unroll
     for (int j = 0; j < VPT4; ++j) {
-        const double sj = ((double)w[j].x + (double)w[j].y) + ((double)w[j].z + (double)w[j].w);
-        const double S = block_sum_d(sj, sm);
+        const double S = sm.slot_tot[j];
         if (jstar < 0) {
             if (cum + S > target) jstar = j;
             else cum += S;

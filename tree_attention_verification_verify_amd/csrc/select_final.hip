@@ -88,12 +88,12 @@ __device__ int final_draw(const SelectParams& P, int b, int v, int c0, bool resi
             if (resid) {
                 load_chunk(zq, V, 0, aq, xq);
                 final_weights(xp, xq, 0, V, sp, sq, true, ilog);
-                W = chunk_total(xq, sm);
+                W = slot_totals(xq, sm);
                 with_resid = W > 0.0;
             }
             if (!with_resid) {
                 final_weights(xp, xq, 0, V, sp, sq, false, ilog);
-                W = chunk_total(xq, sm);
+                W = slot_totals(xq, sm);
             }
             int y = locate_in_chunk(xq, 0, V, 0.0, u * W, sm);
             if (y < 0) {
@@ -114,7 +114,7 @@ __device__ int final_draw(const SelectParams& P, int b, int v, int c0, bool resi
             load_chunk(zp, V, cb, ap, xp);
             if (use_resid) load_chunk(zq, V, cb, aq, xq);
             final_weights(xp, xq, cb, V, sp, sq, use_resid, ilog);
-            const double S = chunk_total(xq, sm);
+            const double S = slot_totals(xq, sm);
             if (threadIdx.x == 0) sm.chunk_sum[ci] = S;
             W += S;
         }
@@ -137,6 +137,7 @@ __device__ int final_draw(const SelectParams& P, int b, int v, int c0, bool resi
         load_chunk(zp, V, cb, ap, xp);
         if (use_resid) load_chunk(zq, V, cb, aq, xq);
         final_weights(xp, xq, cb, V, sp, sq, use_resid, ilog);
+        (void)slot_totals(xq, sm);
         int y = locate_in_chunk(xq, cb, V, cum, target, sm);
         if (y < 0) {
             int last = -1;

@@ -42,12 +42,14 @@ __device__ __forceinline__ int swap_bits_2_3(int x) {
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 typedef float floatx2_t __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-// Byte offset of the 16-byte chunk c (8 keys) of V^T row d in a 64-key tile:
-// chunk positions are XOR-swizzled with bits 1..3 and 4..6 of d, so that 16
-// consecutive rows read at one chunk, and 16 lanes storing 8-byte halves of 8
-// row-spaced chunks, both touch distinct banks.
-__device__ __forceinline__ int vt_offset(int d, int c) { return d * 128 + ((c ^ (((d >> 1) ^ (d >> 4)) & 7)) << 4); }
+// Chunk swizzle of V rows: the 4 consecutive keys one transposed read touches
+// land in 4 disjoint quarters of the row's chunk range.
+template <int CH>
+__device__ __forceinline__ int v_swizzle(int key) { return (key & 3) * (CH / 4); }
 
 // ---------------------------------------------------------------- MFMA path
 
@@ -60,11 +62,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     constexpr int DT = D / 32;              // 32-row tiles of O^T
     constexpr int KCHUNKS = KT * CH;
     constexpr int KLOADS = (KCHUNKS + NTHR - 1) / NTHR;
-    constexpr int VBLOCKS = (KT / 4) * CH;  // blocks of 4 keys x 8 columns
-    constexpr int VLOADS = (VBLOCKS + NTHR - 1) / NTHR;
 
     __shared__ __align__(16) uint8_t k_lds[2 * KT * D * 2];     // two buffers
-    __shared__ __align__(16) uint8_t vt_lds[2 * D * KT * 2];
+    __shared__ __align__(16) uint8_t v_lds[2 * KT * D * 2];
     __shared__ unsigned long long anc_lds[64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -134,89 +134,70 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
+    const floatx16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const int krow = swap_bits_2_3(qcol);   // key (within a 32-key sub-tile) fed to MFMA row qcol
 
     // Tile staging, software-pipelined: the global loads of tile t+1 are in
     // flight (in registers) while tile t is computed from the other LDS buffer.
-    // K rows go to LDS as-is (16-byte chunks XOR-swizzled by the key).  V is
-    // transposed on the way: each thread takes a block of 4 keys x 8 columns;
-    // the thread -> block map puts 8 consecutive column blocks and two key
-    // parities in every 16 lanes, so the 8-byte V^T stores of 16 lanes fill one
-    // 128-byte row segment without bank conflicts.
+    // K and V rows both go to LDS row-major in 16-byte chunks; K chunks are
+    // XOR-swizzled by the key (conflict-free MFMA operand reads), V chunks by
+    // the key's low two bits (conflict-free transposed reads, see below).
     u32x4 kreg[KLOADS];
-    u32x4 vreg[VLOADS][4];
+    u32x4 vreg[KLOADS];
     auto load_tile = [&](int t) {
 #pragma unroll
         for (int j = 0; j < KLOADS; ++j) {
             const int cid = tid + j * NTHR;
             kreg[j] = u32x4{0u, 0u, 0u, 0u};
+            vreg[j] = u32x4{0u, 0u, 0u, 0u};
             if (cid < KCHUNKS) {
                 const int key = cid / CH, c = cid - key * CH;
-                if (t + key < k1) kreg[j] = *(const u32x4*)(kbase + (size_t)(t + key) * D + c * 8);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < VLOADS; ++j) {
-            const int bid = tid + j * NTHR;
-            // bid bits: [2:0] column block low, [3] key-group parity, then the rest
-            const int dc = (bid & 7) | (((bid >> 4) & (CH / 8 - 1)) << 3);
-            const int kg = ((bid >> 3) & 1) | ((bid >> (4 + CH / 8 / 2)) << 1);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int key = t + kg * 4 + jj;
-                vreg[j][jj] = u32x4{0u, 0u, 0u, 0u};
-                if (bid < VBLOCKS && key < k1) vreg[j][jj] = *(const u32x4*)(vbase + (size_t)key * D + dc * 8);
+                if (t + key < k1) {
+                    kreg[j] = *(const u32x4*)(kbase + (size_t)(t + key) * D + c * 8);
+                    vreg[j] = *(const u32x4*)(vbase + (size_t)(t + key) * D + c * 8);
+                }
             }
         }
     };
     auto store_tile = [&](int buf) {
         uint8_t* kl = k_lds + buf * (KT * D * 2);
-        uint8_t* vl = vt_lds + buf * (D * KT * 2);
+        uint8_t* vl = v_lds + buf * (KT * D * 2);
 #pragma unroll
         for (int j = 0; j < KLOADS; ++j) {
             const int cid = tid + j * NTHR;
             if (cid < KCHUNKS) {
                 const int key = cid / CH, c = cid - key * CH;
                 *(u32x4*)(kl + key * (D * 2) + ((c ^ (key & (CH - 1))) << 4)) = kreg[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < VLOADS; ++j) {
-            const int bid = tid + j * NTHR;
-            if (bid < VBLOCKS) {
-                const int dc = (bid & 7) | (((bid >> 4) & (CH / 8 - 1)) << 3);
-                const int kg = ((bid >> 3) & 1) | ((bid >> (4 + CH / 8 / 2)) << 1);
-                const int kc = kg >> 1, koff = (kg & 1) * 8;
-#pragma unroll
-                for (int m2 = 0; m2 < 4; ++m2) {
-                    const uint32_t w0 = vreg[j][0][m2], w1 = vreg[j][1][m2];
-                    const uint32_t w2 = vreg[j][2][m2], w3 = vreg[j][3][m2];
-                    const int d = dc * 8 + 2 * m2;
-                    u32x2 lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-                    u32x2 hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-                    *(u32x2*)(vl + vt_offset(d, kc) + koff) = lo;
-                    *(u32x2*)(vl + vt_offset(d + 1, kc) + koff) = hi;
-                }
+                *(u32x4*)(vl + key * (D * 2) + ((c ^ v_swizzle<CH>(key)) << 4)) = vreg[j];
             }
         }
     };
+
+    // PV operand by transposed LDS reads (ds_read_b64_tr_b16): within each
+    // 16-lane group, source lane s addresses 4 columns (4*(s&3)..+3) of key row
+    // s>>2 of a 4-key block, and output lane j receives column j of all 4 keys.
+    // Lane l = (G = l>>4, s = l&15) therefore reads key 8*(G>>1) + 4*h + (s>>2)
+    // of the 16-key step and columns 32*dt + 16*(G&1) + 4*(s&3); it gets the
+    // column 32*dt + (l&31) for keys 8*(l>>5) + 4*h + 0..3: with h = 0, 1 these
+    // are the 8 k-slots the P^T operand of the lane holds.
+    const int tr_key = 8 * (lane >> 5) + (((lane & 15) >> 2));
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     // One 64-key tile: S^T, online softmax (log2 domain), O^T += V^T P^T.
     // need_mask (wave-uniform): the tile reaches the tree slots or the end of the split.
     auto tile = [&](int t, int buf, bool need_mask) {
         const uint8_t* kl = k_lds + buf * (KT * D * 2);
-        const uint8_t* vl = vt_lds + buf * (D * KT * 2);
+        const uint8_t* vl = v_lds + buf * (KT * D * 2);
         floatx16_t s[2];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[sub][e] = 0.f;
             const int kk = sub * 32 + krow;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 const int c = 2 * ks + half;
                 const u32x4 a = *(const u32x4*)(kl + kk * (D * 2) + ((c ^ (kk & (CH - 1))) << 4));
-                s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[ks], s[sub], 0, 0, 0);
+                s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[ks], ks == 0 ? zero16 : s[sub],
+                                                                 0, 0, 0);
             }
         }
         // accumulator element e of lane (qcol, half) holds key 16*(e>>3) + 8*half + (e&7) of its sub-tile
@@ -232,12 +213,14 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
                     s[sub][e] = vis ? s[sub][e] : -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+        float m16[16];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+        for (int e = 0; e < 16; ++e) m16[e] = fmaxf(s[0][e], s[1][e]);
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[sub][e], s[sub][e + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int e = 0; e < w; ++e) m16[e] = fmaxf(m16[e], m16[e + w]);
+        float mx = fmaxf(m16[0], __shfl_xor(m16[0], 32, kWave));
         const float m_new = fmaxf(m_run, mx * P.c);
         if (__any(m_new > m_run)) {       // rescale only when some running max grows
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -257,10 +240,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
             for (int h2 = 0; h2 < 2; ++h2) {
                 float p[8];
 #pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    p[w] = __builtin_amdgcn_exp2f(fmaf(s[sub][8 * h2 + w], P.c, neg_m));
-                    psum += p[w];
-                }
+                for (int w = 0; w < 8; ++w) p[w] = __builtin_amdgcn_exp2f(fmaf(s[sub][8 * h2 + w], P.c, neg_m));
+                psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
                 bf16x2_t q0 = __builtin_convertvector((floatx2_t){p[0], p[1]}, bf16x2_t);
                 bf16x2_t q1 = __builtin_convertvector((floatx2_t){p[2], p[3]}, bf16x2_t);
                 bf16x2_t q2 = __builtin_convertvector((floatx2_t){p[4], p[5]}, bf16x2_t);
@@ -273,14 +254,21 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
         // O^T[d x q] += V^T[d x keys] P^T[keys x q]
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const int d = 32 * dt + qcol;
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
-                    const int c = 4 * sub + 2 * h2 + half;
-                    const u32x4 a = *(const u32x4*)(vl + vt_offset(d, c));
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[sub][h2], o[dt], 0, 0, 0);
+                    const int col = 32 * dt + tr_col;
+                    const int key0 = sub * 32 + 16 * h2 + tr_key;
+                    const int key1 = key0 + 4;
+                    const int c = col >> 3;
+                    const uint8_t* p0 = vl + key0 * (D * 2) + ((c ^ v_swizzle<CH>(key0)) << 4) + (col & 7) * 2;
+                    const uint8_t* p1 = vl + key1 * (D * 2) + ((c ^ v_swizzle<CH>(key1)) << 4) + (col & 7) * 2;
+                    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
+                    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
+                    const v8s a = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[sub][h2],
+                                                                    o[dt], 0, 0, 0);
                 }
             }
         }

@@ -72,8 +72,8 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
         s += (double)part;
     };
 
-    // 4 float4 per step per thread: 16 logits
-    constexpr int U = 4;
+    // 8 float4 per step per thread: 32 logits in flight
+    constexpr int U = 8;
     int i4 = tid;
     for (; i4 + (U - 1) * ST < nv4; i4 += U * ST) {
         float x[4 * U];
