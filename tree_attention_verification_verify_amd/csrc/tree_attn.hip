@@ -53,15 +53,13 @@ __device__ __forceinline__ int v_swizzle(int key) { return (key & 3) * (CH / 4);
 
 // ---------------------------------------------------------------- MFMA path
 
-template <int D, int WAVES>
-__global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) {
-    constexpr int NTHR = WAVES * 64;
-    constexpr int KT = 64;                  // keys per tile
+template <int D, int WAVES, int NSUB>
+__global__ __launch_bounds__(WAVES * 64, NSUB == 1 ? 3 : 2) void attn_mfma_kernel(AttnParams P) {
+    constexpr int KT = 32 * NSUB;           // keys per tile (NSUB sub-tiles of 32)
     constexpr int CH = D / 8;               // 16-byte chunks per K/V row
     constexpr int KSTEPS = D / 16;          // k-steps of the QK^T product
     constexpr int DT = D / 32;              // 32-row tiles of O^T
-    constexpr int KCHUNKS = KT * CH;
-    constexpr int KLOADS = (KCHUNKS + NTHR - 1) / NTHR;
+    static_assert((KT * D * 2 / 1024) % WAVES == 0, "whole 1 KB blocks per wave");
 
     __shared__ __align__(16) uint8_t k_lds[2 * KT * D * 2];     // two buffers
     __shared__ __align__(16) uint8_t v_lds[2 * KT * D * 2];
@@ -137,39 +135,40 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     const floatx16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const int krow = swap_bits_2_3(qcol);   // key (within a 32-key sub-tile) fed to MFMA row qcol
 
-    // Tile staging, software-pipelined: the global loads of tile t+1 are in
-    // flight (in registers) while tile t is computed from the other LDS buffer.
-    // K and V rows both go to LDS row-major in 16-byte chunks; K chunks are
-    // XOR-swizzled by the key (conflict-free MFMA operand reads), V chunks by
-    // the key's low two bits (conflict-free transposed reads, see below).
-    u32x4 kreg[KLOADS];
-    u32x4 vreg[KLOADS];
-    auto load_tile = [&](int t) {
+    // Tile staging, software-pipelined, straight from HBM into LDS: buffer
+    // loads with the LDS as destination (each lane's 16 bytes land at the LDS
+    // base + 16 * lane) fill the other LDS buffer with tile t+1 while tile t is
+    // computed.  The chunk swizzles of the LDS layout (K: chunk ^ key%CH for
+    // the MFMA operand reads, V: chunk ^ v_swizzle(key) for the transposed
+    // reads) are applied on the global side: lane i of a 1 KB block loads the
+    // logical chunk that belongs at its slot.  The buffer resources end at key
+    // k1, so loads past the split read zeros (and those keys are masked).
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, k1 * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, k1 * D * 2, 0x00020000);
+    constexpr int BLOCKS = KT * D * 2 / 1024;          // 1 KB blocks per tile
+    constexpr int ROWS_PER_BLOCK = 1024 / (D * 2);
+    auto issue_k = [&](int t, int buf) {
 #pragma unroll
-        for (int j = 0; j < KLOADS; ++j) {
-            const int cid = tid + j * NTHR;
-            kreg[j] = u32x4{0u, 0u, 0u, 0u};
-            vreg[j] = u32x4{0u, 0u, 0u, 0u};
-            if (cid < KCHUNKS) {
-                const int key = cid / CH, c = cid - key * CH;
-                if (t + key < k1) {
-                    kreg[j] = *(const u32x4*)(kbase + (size_t)(t + key) * D + c * 8);
-                    vreg[j] = *(const u32x4*)(vbase + (size_t)(t + key) * D + c * 8);
-                }
-            }
+        for (int j = 0; j < BLOCKS / WAVES; ++j) {
+            const int blk = j * WAVES + wave;
+            const int row = blk * ROWS_PER_BLOCK + lane / CH;
+            const int kc = (lane % CH) ^ (row & (CH - 1));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                krs, (__attribute__((address_space(3))) void*)(k_lds + buf * (KT * D * 2) + blk * 1024), 16,
+                (t + row) * (D * 2) + kc * 16, 0, 0, 0);
         }
     };
-    auto store_tile = [&](int buf) {
-        uint8_t* kl = k_lds + buf * (KT * D * 2);
-        uint8_t* vl = v_lds + buf * (KT * D * 2);
+    auto issue_v = [&](int t, int buf) {
 #pragma unroll
-        for (int j = 0; j < KLOADS; ++j) {
-            const int cid = tid + j * NTHR;
-            if (cid < KCHUNKS) {
-                const int key = cid / CH, c = cid - key * CH;
-                *(u32x4*)(kl + key * (D * 2) + ((c ^ (key & (CH - 1))) << 4)) = kreg[j];
-                *(u32x4*)(vl + key * (D * 2) + ((c ^ v_swizzle<CH>(key)) << 4)) = vreg[j];
-            }
+        for (int j = 0; j < BLOCKS / WAVES; ++j) {
+            const int blk = j * WAVES + wave;
+            const int row = blk * ROWS_PER_BLOCK + lane / CH;
+            const int vc = (lane % CH) ^ v_swizzle<CH>(row);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vrs, (__attribute__((address_space(3))) void*)(v_lds + buf * (KT * D * 2) + blk * 1024), 16,
+                (t + row) * (D * 2) + vc * 16, 0, 0, 0);
         }
     };
 
@@ -183,14 +182,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     const int tr_key = 8 * (lane >> 5) + (((lane & 15) >> 2));
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // One 64-key tile: S^T, online softmax (log2 domain), O^T += V^T P^T.
-    // need_mask (wave-uniform): the tile reaches the tree slots or the end of the split.
-    auto tile = [&](int t, int buf, bool need_mask) {
-        const uint8_t* kl = k_lds + buf * (KT * D * 2);
-        const uint8_t* vl = v_lds + buf * (KT * D * 2);
-        floatx16_t s[2];
+    // S^T[KT keys x 32 queries] of one tile (NSUB 32-key sub-tiles).
+    auto qk = [&](int kbuf, floatx16_t (&s)[NSUB]) {
+        const uint8_t* kl = k_lds + kbuf * (KT * D * 2);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
+        for (int sub = 0; sub < NSUB; ++sub) {
             const int kk = sub * 32 + krow;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -200,10 +196,16 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
                                                                  0, 0, 0);
             }
         }
+    };
+
+    // Online softmax (log2 domain) of one tile's scores and O^T += V^T P^T.
+    // need_mask (wave-uniform): the tile reaches the tree slots or the end of the split.
+    auto softmax_pv = [&](int t, int vbuf, floatx16_t (&s)[NSUB], bool need_mask) {
+        const uint8_t* vl = v_lds + vbuf * (KT * D * 2);
         // accumulator element e of lane (qcol, half) holds key 16*(e>>3) + 8*half + (e&7) of its sub-tile
         if (need_mask) {
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
+            for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int key = t + sub * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
         }
         float m16[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) m16[e] = fmaxf(s[0][e], s[1][e]);
+        for (int e = 0; e < 16; ++e) m16[e] = NSUB == 1 ? s[0][e] : fmaxf(s[0][e], s[NSUB - 1][e]);
 #pragma unroll
         for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
@@ -233,9 +235,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
         }
         const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
         float psum = 0.f;
-        bf16x8_t pb[2][2];
+        bf16x8_t pb[NSUB][2];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
+        for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 float p[8];
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
+            for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
                     const int col = 32 * dt + tr_col;
@@ -274,17 +276,24 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
         }
     };
 
-    load_tile(k0);
-    store_tile(0);
+    // Double-buffered: tile t+1 streams into the other LDS buffers while tile t
+    // is computed; one barrier per tile.
+    floatx16_t s_cur[NSUB];
+    issue_k(k0, 0);
+    issue_v(k0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int buf = 0;
-    for (int t = k0; t < k1; t += KT) {
-        const bool more = t + KT < k1;
-        if (more) load_tile(t + KT);
-        tile(t, buf, t + KT > L || t + KT > k1);
-        if (more) store_tile(buf ^ 1);
+    int it = 0;
+    for (int t = k0; t < k1; t += KT, ++it) {
+        const int cur = it & 1;
+        if (t + KT < k1) {
+            issue_k(t + KT, cur ^ 1);
+            issue_v(t + KT, cur ^ 1);
+        }
+        qk(cur, s_cur);
+        softmax_pv(t, cur, s_cur, t + KT > L || t + KT > k1);
+        __builtin_amdgcn_s_waitcnt(0);    // tile t+1 has landed
         __syncthreads();
-        buf ^= 1;
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
@@ -573,14 +582,15 @@ hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s) 
     if (p.rowblocks == 1) blocks = groups;
     else blocks = ((groups + 7) / 8) * 8 * p.rowblocks;
     dim3 grid(blocks);
+    constexpr int S = kAttnSubTiles;
     if (p.D == 128) {
-        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<128, 4>), grid, dim3(256), 0, s, p);
-        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, dim3(128), 0, s, p);
-        else hipLaunchKernelGGL((attn_mfma_kernel<128, 1>), grid, dim3(64), 0, s, p);
+        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<128, 4, S>), grid, dim3(256), 0, s, p);
+        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<128, 2, S>), grid, dim3(128), 0, s, p);
+        else hipLaunchKernelGGL((attn_mfma_kernel<128, 1, S>), grid, dim3(64), 0, s, p);
     } else {
-        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<64, 4>), grid, dim3(256), 0, s, p);
-        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, dim3(128), 0, s, p);
-        else hipLaunchKernelGGL((attn_mfma_kernel<64, 1>), grid, dim3(64), 0, s, p);
+        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<64, 4, S>), grid, dim3(256), 0, s, p);
+        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<64, 2, S>), grid, dim3(128), 0, s, p);
+        else hipLaunchKernelGGL((attn_mfma_kernel<64, 1, S>), grid, dim3(64), 0, s, p);
     }
     return hipGetLastError();
 }
