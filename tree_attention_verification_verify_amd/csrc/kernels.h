@@ -79,10 +79,6 @@ hipError_t launch_row_stats(const StatsParams& p, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
 
 constexpr int kValuRows = 16;      // rows per block of the VALU attention kernel
-#ifndef SV_ATTN_SUBTILES
-#define SV_ATTN_SUBTILES 2
-#endif
-constexpr int kAttnSubTiles = SV_ATTN_SUBTILES;  // 32-key sub-tiles per MFMA attention tile
 constexpr int kVocabThreads = 1024;               // register-resident row kernels
 constexpr int kVocabChunk = kVocabThreads * 32;   // logits held on chip per pass
 constexpr int kStatsThreads = 256;                // streaming row-statistics kernel

@@ -51,18 +51,32 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 template <int CH>
 __device__ __forceinline__ int v_swizzle(int key) { return (key & 3) * (CH / 4); }
 
+// Maximum of three scores (v_maximum3_f32: NaN-propagating, so the inputs need
+// no quieting first; scores are finite or -inf).
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+    return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
+
 // ---------------------------------------------------------------- MFMA path
 
-template <int D, int WAVES, int NSUB>
-__global__ __launch_bounds__(WAVES * 64, NSUB == 1 ? 3 : 2) void attn_mfma_kernel(AttnParams P) {
-    constexpr int KT = 32 * NSUB;           // keys per tile (NSUB sub-tiles of 32)
+constexpr float kLazyMax = 8.f;   // log2 headroom of the lazily raised softmax reference
+
+template <int D, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) {
+    constexpr int NSUB = 2;                 // 32-key sub-tiles per tile
+    constexpr int KT = 32 * NSUB;           // keys per tile
     constexpr int CH = D / 8;               // 16-byte chunks per K/V row
     constexpr int KSTEPS = D / 16;          // k-steps of the QK^T product
     constexpr int DT = D / 32;              // 32-row tiles of O^T
     static_assert((KT * D * 2 / 1024) % WAVES == 0, "whole 1 KB blocks per wave");
 
-    __shared__ __align__(16) uint8_t k_lds[2 * KT * D * 2];     // two buffers
-    __shared__ __align__(16) uint8_t v_lds[2 * KT * D * 2];
+    // Two buffers each for K and V, as four separate LDS objects: the compiler
+    // then knows that the loads filling one buffer never alias the reads of
+    // another and does not wait for the prefetch before reading the current tile.
+    __shared__ __align__(16) uint8_t k_lds0[KT * D * 2];
+    __shared__ __align__(16) uint8_t k_lds1[KT * D * 2];
+    __shared__ __align__(16) uint8_t v_lds0[KT * D * 2];
+    __shared__ __align__(16) uint8_t v_lds1[KT * D * 2];
     __shared__ unsigned long long anc_lds[64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -132,46 +146,45 @@ __global__ __launch_bounds__(WAVES * 64, NSUB == 1 ? 3 : 2) void attn_mfma_kerne
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
+    float neg_m = 0.f;   // -m_run, or 0 while no key has been seen
     const floatx16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const int krow = swap_bits_2_3(qcol);   // key (within a 32-key sub-tile) fed to MFMA row qcol
 
-    // Tile staging, software-pipelined, straight from HBM into LDS: buffer
-    // loads with the LDS as destination (each lane's 16 bytes land at the LDS
-    // base + 16 * lane) fill the other LDS buffer with tile t+1 while tile t is
-    // computed.  The chunk swizzles of the LDS layout (K: chunk ^ key%CH for
-    // the MFMA operand reads, V: chunk ^ v_swizzle(key) for the transposed
-    // reads) are applied on the global side: lane i of a 1 KB block loads the
-    // logical chunk that belongs at its slot.  The buffer resources end at key
-    // k1, so loads past the split read zeros (and those keys are masked).
+    // Tile staging straight from HBM into LDS: buffer loads with the LDS as
+    // destination (each lane's 16 bytes land at the LDS base + 16 * lane).
+    // The chunk swizzles of the LDS layout (K: chunk ^ key%CH for the MFMA
+    // operand reads, V: chunk ^ v_swizzle(key) for the transposed reads) are
+    // applied on the global side: lane i of a 1 KB block loads the logical
+    // chunk that belongs at its slot.  The buffer resources end at key k1, so
+    // loads past the split read zeros (and those keys are masked or unused).
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, k1 * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, k1 * D * 2, 0x00020000);
-    constexpr int BLOCKS = KT * D * 2 / 1024;          // 1 KB blocks per tile
+    constexpr int BLOCKS = KT * D * 2 / 1024;          // 1 KB blocks per tile and operand
     constexpr int ROWS_PER_BLOCK = 1024 / (D * 2);
-    auto issue_k = [&](int t, int buf) {
-#pragma unroll
-        for (int j = 0; j < BLOCKS / WAVES; ++j) {
-            const int blk = j * WAVES + wave;
-            const int row = blk * ROWS_PER_BLOCK + lane / CH;
-            const int kc = (lane % CH) ^ (row & (CH - 1));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                krs, (__attribute__((address_space(3))) void*)(k_lds + buf * (KT * D * 2) + blk * 1024), 16,
-                (t + row) * (D * 2) + kc * 16, 0, 0, 0);
-        }
-    };
-    auto issue_v = [&](int t, int buf) {
-#pragma unroll
-        for (int j = 0; j < BLOCKS / WAVES; ++j) {
-            const int blk = j * WAVES + wave;
-            const int row = blk * ROWS_PER_BLOCK + lane / CH;
-            const int vc = (lane % CH) ^ v_swizzle<CH>(row);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                vrs, (__attribute__((address_space(3))) void*)(v_lds + buf * (KT * D * 2) + blk * 1024), 16,
-                (t + row) * (D * 2) + vc * 16, 0, 0, 0);
-        }
+    constexpr int LOADS = 2 * BLOCKS / WAVES;           // K and V blocks one wave loads per tile
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // block load l of a tile: l < LOADS/2 -> K of the tile at key tk, else V at key tv
+    auto issue_load = [&](int l, int tk, uint8_t* kdst, int tv, uint8_t* vdst) {
+        const bool isk = l < LOADS / 2;
+        const int blk = (isk ? l : l - LOADS / 2) * WAVES + wave_u;
+        const int row = blk * ROWS_PER_BLOCK + lane / CH;
+        const int c = (lane % CH) ^ (isk ? (row & (CH - 1)) : v_swizzle<CH>(row));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            isk ? krs : vrs, (__attribute__((address_space(3))) void*)((isk ? kdst : vdst) + blk * 1024), 16,
+            ((isk ? tk : tv) + row) * (D * 2) + c * 16, 0, 0, 0);
     };
 
+    // MFMA operands.  QK^T product i (i < NQK) is sub-tile i % NSUB, k-step
+    // i / NSUB; PV product i (i < NPV) is O^T tile i % DT, 16-key step i / DT.
+    constexpr int NQK = NSUB * KSTEPS;
+    constexpr int NPV = DT * NSUB * 2;
+    auto read_k = [&](const uint8_t* kl, int i) -> bf16x8_t {
+        const int kk = (i % NSUB) * 32 + krow;
+        const int c = 2 * (i / NSUB) + half;
+        return as_bf16x8(*(const u32x4*)(kl + kk * (D * 2) + ((c ^ (kk & (CH - 1))) << 4)));
+    };
     // PV operand by transposed LDS reads (ds_read_b64_tr_b16): within each
     // 16-lane group, source lane s addresses 4 columns (4*(s&3)..+3) of key row
     // s>>2 of a 4-key block, and output lane j receives column j of all 4 keys.
@@ -181,119 +194,153 @@ __global__ __launch_bounds__(WAVES * 64, NSUB == 1 ? 3 : 2) void attn_mfma_kerne
     // are the 8 k-slots the P^T operand of the lane holds.
     const int tr_key = 8 * (lane >> 5) + (((lane & 15) >> 2));
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-    // S^T[KT keys x 32 queries] of one tile (NSUB 32-key sub-tiles).
-    auto qk = [&](int kbuf, floatx16_t (&s)[NSUB]) {
-        const uint8_t* kl = k_lds + kbuf * (KT * D * 2);
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
-            const int kk = sub * 32 + krow;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const int c = 2 * ks + half;
-                const u32x4 a = *(const u32x4*)(kl + kk * (D * 2) + ((c ^ (kk & (CH - 1))) << 4));
-                s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[ks], ks == 0 ? zero16 : s[sub],
-                                                                 0, 0, 0);
-            }
-        }
+    auto read_v = [&](const uint8_t* vl, int i) -> bf16x8_t {
+        const int dt = i % DT, step16 = i / DT;
+        const int col = 32 * dt + tr_col;
+        const int key0 = 16 * step16 + tr_key;
+        const int key1 = key0 + 4;
+        const int c = col >> 3;
+        const uint8_t* p0 = vl + key0 * (D * 2) + ((c ^ v_swizzle<CH>(key0)) << 4) + (col & 7) * 2;
+        const uint8_t* p1 = vl + key1 * (D * 2) + ((c ^ v_swizzle<CH>(key1)) << 4) + (col & 7) * 2;
+        const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
+        const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    // Online softmax (log2 domain) of one tile's scores and O^T += V^T P^T.
-    // need_mask (wave-uniform): the tile reaches the tree slots or the end of the split.
-    auto softmax_pv = [&](int t, int vbuf, floatx16_t (&s)[NSUB], bool need_mask) {
-        const uint8_t* vl = v_lds + vbuf * (KT * D * 2);
-        // accumulator element e of lane (qcol, half) holds key 16*(e>>3) + 8*half + (e&7) of its sub-tile
-        if (need_mask) {
+    // Scores: accumulator element e of lane (qcol, half) in sub-tile sub holds
+    // key sub*32 + 16*(e>>3) + 8*half + (e&7).  Masking is needed only for
+    // tiles that reach the tree slots or the end of the split.
+    auto mask_tile = [&](int t, floatx16_t (&s)[NSUB]) {
 #pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub)
+        for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = t + sub * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
-                    const unsigned rel = (unsigned)(key - L);
-                    const bool tree_vis = (key < k1) && ((anc_row >> (rel & 63u)) & 1ull);
-                    const bool vis = (key < L) | (key >= L && tree_vis);
-                    s[sub][e] = vis ? s[sub][e] : -INFINITY;
-                }
-        }
-        float m16[16];
+            for (int e = 0; e < 16; ++e) {
+                const int key = t + sub * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
+                const unsigned rel = (unsigned)(key - L);
+                const bool tree_vis = (key < k1) && ((anc_row >> (rel & 63u)) & 1ull);
+                const bool vis = (key < L) | (key >= L && tree_vis);
+                s[sub][e] = vis ? s[sub][e] : -INFINITY;
+            }
+    };
+    auto tile_max = [&](const floatx16_t (&s)[NSUB]) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) m16[e] = NSUB == 1 ? s[0][e] : fmaxf(s[0][e], s[NSUB - 1][e]);
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-            for (int e = 0; e < w; ++e) m16[e] = fmaxf(m16[e], m16[e + w]);
-        float mx = fmaxf(m16[0], __shfl_xor(m16[0], 32, kWave));
-        const float m_new = fmaxf(m_run, mx * P.c);
-        if (__any(m_new > m_run)) {       // rescale only when some running max grows
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        for (int f = 0; f < 16 * NSUB; f += 2) mx = fmax3(mx, s[f / 16][f % 16], s[f / 16][f % 16 + 1]);
+        return fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    };
+    // Online softmax in the log2 domain.  The exponent reference m_run is
+    // raised lazily, only when a score of the tile exceeds it by more than
+    // 2^kLazyMax, so most tiles need no rescale of O and weights stay below
+    // 2^kLazyMax.
+    auto raise_reference = [&](float mx) {
+        const float mt = mx * P.c;
+        if (__any(mt > m_run + kLazyMax)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
             m_run = m_new;
-        }
-        const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-        float psum = 0.f;
-        bf16x8_t pb[NSUB][2];
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                float p[8];
-#pragma unroll
-                for (int w = 0; w < 8; ++w) p[w] = __builtin_amdgcn_exp2f(fmaf(s[sub][8 * h2 + w], P.c, neg_m));
-                psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-                bf16x2_t q0 = __builtin_convertvector((floatx2_t){p[0], p[1]}, bf16x2_t);
-                bf16x2_t q1 = __builtin_convertvector((floatx2_t){p[2], p[3]}, bf16x2_t);
-                bf16x2_t q2 = __builtin_convertvector((floatx2_t){p[4], p[5]}, bf16x2_t);
-                bf16x2_t q3 = __builtin_convertvector((floatx2_t){p[6], p[7]}, bf16x2_t);
-                pb[sub][h2] = bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
-            }
-        }
-        l_run += psum;
-
-        // O^T[d x q] += V^T[d x keys] P^T[keys x q]
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub) {
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const int col = 32 * dt + tr_col;
-                    const int key0 = sub * 32 + 16 * h2 + tr_key;
-                    const int key1 = key0 + 4;
-                    const int c = col >> 3;
-                    const uint8_t* p0 = vl + key0 * (D * 2) + ((c ^ v_swizzle<CH>(key0)) << 4) + (col & 7) * 2;
-                    const uint8_t* p1 = vl + key1 * (D * 2) + ((c ^ v_swizzle<CH>(key1)) << 4) + (col & 7) * 2;
-                    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
-                    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
-                    const v8s a = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[sub][h2],
-                                                                    o[dt], 0, 0, 0);
-                }
-            }
+            neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
         }
     };
+    const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // Double-buffered: tile t+1 streams into the other LDS buffers while tile t
-    // is computed; one barrier per tile.
-    floatx16_t s_cur[NSUB];
-    issue_k(k0, 0);
-    issue_v(k0, 0);
+    // Software pipeline over tiles, K two tiles ahead of V in LDS.  K(t) sits
+    // in k_lds[(t/KT)&1] and V(t) in v_lds[(t/KT)&1]; a buffer is refilled
+    // only after the barrier that follows its last read, and the loop is
+    // unrolled by two so that every LDS access names its buffer statically.
+    // Step t, after masking tile t and raising the reference if needed:
+    //   phase A: the QK^T products of tile t+1, each with the K read two
+    //            products ahead, a share of the block loads of K(t+2) and
+    //            V(t+1), and the weights of EPS scores of tile t (exp2, bf16
+    //            pack, row sum over the packed weights by dot2);
+    //   phase B: the PV products of tile t, each with the V read two products
+    //            ahead and a share of the maximum of tile t+1.
+    // Scheduling fences keep this order, so the matrix cores and the vector
+    // ALU work side by side within the wave.  Products of a tile past the
+    // split read stale or zero data and are never used.
+    constexpr int PF = 2;                        // operand reads in flight
+    constexpr int EPS = 16 * NSUB / NQK;         // scores weighted per QK^T product
+    constexpr int MX0 = NPV / 4;                 // first PV slot that takes max work
+    constexpr int NMX = NPV / 2;                 // PV slots that take max work
+    constexpr int EPM = 16 * NSUB / NMX;         // scores per max slot
+    static_assert(EPS % 2 == 0 && EPM % 2 == 0, "pairs");
+    auto step = [&](int t, const uint8_t* k_next, const uint8_t* v_cur, uint8_t* k_fill, uint8_t* v_fill,
+                    floatx16_t (&s_cur)[NSUB], floatx16_t (&s_next)[NSUB], float& mx_cur, float& mx_next) {
+        if (t + KT > L || t + KT > k1) {
+            mask_tile(t, s_cur);
+            mx_cur = tile_max(s_cur);
+        }
+        raise_reference(mx_cur);
+        bf16x8_t ka[NQK];
+        bf16x2_t wp[8 * NSUB];
+        float ps[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < PF; ++i) ka[i] = read_k(k_next, i);
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) {
+            if (i + PF < NQK) ka[i + PF] = read_k(k_next, i + PF);
+#pragma unroll
+            for (int l = 0; l < LOADS; ++l)
+                if (l * NQK / LOADS == i) issue_load(l, t + 2 * KT, k_fill, t + KT, v_fill);
+            s_next[i % NSUB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qb[i / NSUB],
+                                                                       i < NSUB ? zero16 : s_next[i % NSUB], 0, 0, 0);
+#pragma unroll
+            for (int f = EPS * i; f < EPS * (i + 1); f += 2) {
+                const float w0 = __builtin_amdgcn_exp2f(fmaf(s_cur[f / 16][f % 16], P.c, neg_m));
+                const float w1 = __builtin_amdgcn_exp2f(fmaf(s_cur[f / 16][f % 16 + 1], P.c, neg_m));
+                wp[f / 2] = __builtin_convertvector((floatx2_t){w0, w1}, bf16x2_t);
+                ps[(f / 2) & 1] = __builtin_amdgcn_fdot2_f32_bf16(wp[f / 2], ones2, ps[(f / 2) & 1], false);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run += ps[0] + ps[1];
+        bf16x8_t va[NPV];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) va[i] = read_v(v_cur, i);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            if (i + PF < NPV) va[i + PF] = read_v(v_cur, i + PF);
+            const int j = i / DT;   // 16-key step: pairs 4j .. 4j+3
+            const bf16x8_t pbj = {wp[4 * j][0], wp[4 * j][1], wp[4 * j + 1][0], wp[4 * j + 1][1],
+                                  wp[4 * j + 2][0], wp[4 * j + 2][1], wp[4 * j + 3][0], wp[4 * j + 3][1]};
+            o[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pbj, o[i % DT], 0, 0, 0);
+            if (i >= MX0 && i < MX0 + NMX) {
+#pragma unroll
+                for (int f = EPM * (i - MX0); f < EPM * (i - MX0 + 1); f += 2)
+                    mx = fmax3(mx, s_next[f / 16][f % 16], s_next[f / 16][f % 16 + 1]);
+                asm volatile("" : "+v"(mx));   // keeps this share of the maximum in its slot
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mx_next = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        __builtin_amdgcn_s_waitcnt(0);    // K(t+2) and V(t+1) have landed
+        __syncthreads();
+    };
+
+    floatx16_t sa[NSUB], sb[NSUB];
+    float mxa, mxb;
+#pragma unroll
+    for (int l = 0; l < LOADS; ++l) issue_load(l, k0, k_lds0, k0, v_lds0);
+#pragma unroll
+    for (int l = 0; l < LOADS / 2; ++l) issue_load(l, k0 + KT, k_lds1, 0, nullptr);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int it = 0;
-    for (int t = k0; t < k1; t += KT, ++it) {
-        const int cur = it & 1;
-        if (t + KT < k1) {
-            issue_k(t + KT, cur ^ 1);
-            issue_v(t + KT, cur ^ 1);
-        }
-        qk(cur, s_cur);
-        softmax_pv(t, cur, s_cur, t + KT > L || t + KT > k1);
-        __builtin_amdgcn_s_waitcnt(0);    // tile t+1 has landed
-        __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NQK; ++i)
+        sa[i % NSUB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_k(k_lds0, i), qb[i / NSUB],
+                                                               i < NSUB ? zero16 : sa[i % NSUB], 0, 0, 0);
+    mxa = tile_max(sa);
+    __builtin_amdgcn_s_waitcnt(0);       // every wave is done with K(k0) before it is refilled
+    __syncthreads();
+    for (int t = k0; t < k1; t += 2 * KT) {
+        step(t, k_lds1, v_lds0, k_lds0, v_lds1, sa, sb, mxa, mxb);
+        if (t + KT >= k1) break;
+        step(t + KT, k_lds0, v_lds1, k_lds1, v_lds0, sb, sa, mxb, mxa);
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
@@ -582,15 +629,14 @@ hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s) 
     if (p.rowblocks == 1) blocks = groups;
     else blocks = ((groups + 7) / 8) * 8 * p.rowblocks;
     dim3 grid(blocks);
-    constexpr int S = kAttnSubTiles;
     if (p.D == 128) {
-        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<128, 4, S>), grid, dim3(256), 0, s, p);
-        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<128, 2, S>), grid, dim3(128), 0, s, p);
-        else hipLaunchKernelGGL((attn_mfma_kernel<128, 1, S>), grid, dim3(64), 0, s, p);
+        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<128, 4>), grid, dim3(256), 0, s, p);
+        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, dim3(128), 0, s, p);
+        else hipLaunchKernelGGL((attn_mfma_kernel<128, 1>), grid, dim3(64), 0, s, p);
     } else {
-        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<64, 4, S>), grid, dim3(256), 0, s, p);
-        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<64, 2, S>), grid, dim3(128), 0, s, p);
-        else hipLaunchKernelGGL((attn_mfma_kernel<64, 1, S>), grid, dim3(64), 0, s, p);
+        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<64, 4>), grid, dim3(256), 0, s, p);
+        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, dim3(128), 0, s, p);
+        else hipLaunchKernelGGL((attn_mfma_kernel<64, 1>), grid, dim3(64), 0, s, p);
     }
     return hipGetLastError();
 }
