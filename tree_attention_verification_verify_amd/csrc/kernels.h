@@ -66,7 +66,10 @@ struct SelectParams {
     int32_t* status;
     uint8_t* node_accept;
     uint8_t* final_from_residual;
+    double2* slice_tot;   // [B][S] (residual, p-only) weight totals per slice of the final draw
+    int32_t* arrive;      // [B] slices done; reset to 0 by the last one
     int B, T, V, Lcap;
+    int S;                // slices per sequence: ceil(V / kSelectSlice)
     int sampling;
     float ilog;
 };
@@ -82,5 +85,8 @@ constexpr int kValuRows = 16;      // rows per block of the VALU attention kerne
 constexpr int kVocabThreads = 1024;               // register-resident row kernels
 constexpr int kVocabChunk = kVocabThreads * 32;   // logits held on chip per pass
 constexpr int kStatsThreads = 256;                // streaming row-statistics kernel
+constexpr int kSelectThreads = 256;               // selection / final draw workgroups
+constexpr int kSelectSlice = 2048;                // token ids per final-draw slice
+constexpr int kSelectMaxSlices = 2048;            // vocab <= 4194304
 
 }  // namespace sv

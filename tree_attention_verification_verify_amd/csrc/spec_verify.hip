@@ -92,6 +92,8 @@ struct spec_verify_handle {
     float* part_o = nullptr;
     float2* part_ml = nullptr;
     sv::RowStat* stats = nullptr;     // max_batch * 2 * max_nodes row statistics
+    double2* slice_tot = nullptr;     // max_batch * slices final-draw slice totals
+    int32_t* arrive = nullptr;        // max_batch final-draw arrival counters (zero between runs)
     bool timing = false;
     std::vector<hipEvent_t> events;   // kTimingRing * kEventsPerRun
     long runs_recorded = 0;           // since the last read
@@ -160,7 +162,15 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         }
     }
     e = hipMalloc((void**)&h->stats, (size_t)c.max_batch * 2 * c.max_nodes * sizeof(sv::RowStat));
+    const int slices = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
+    if (e == hipSuccess) e = hipMalloc((void**)&h->slice_tot, (size_t)c.max_batch * slices * sizeof(double2));
+    if (e == hipSuccess) e = hipMalloc((void**)&h->arrive, (size_t)c.max_batch * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMemset(h->arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
+        (void)hipFree(h->stats);
+        (void)hipFree(h->slice_tot);
+        (void)hipFree(h->arrive);
         (void)hipFree(h->part_o);
         (void)hipFree(h->part_ml);
         delete h;
@@ -193,6 +203,8 @@ int spec_verify_destroy(spec_verify_handle* h) {
     if (h->part_o) (void)hipFree(h->part_o);
     if (h->part_ml) (void)hipFree(h->part_ml);
     if (h->stats) (void)hipFree(h->stats);
+    if (h->slice_tot) (void)hipFree(h->slice_tot);
+    if (h->arrive) (void)hipFree(h->arrive);
     if (dev >= 0 && dev != h->device) (void)hipSetDevice(dev);
     delete h;
     return SPEC_VERIFY_OK;
@@ -305,6 +317,9 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     sp.Lcap = c.kv_capacity;
     sp.sampling = sampling ? 1 : 0;
     sp.ilog = tp.ilog;
+    sp.slice_tot = h->slice_tot;
+    sp.arrive = h->arrive;
+    sp.S = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
     e = sv::launch_select(sp, s);
     if (e != hipSuccess) return hip_fail(e, "select launch");
     if (int rc = mark(SPEC_VERIFY_STAGE_SELECT)) return rc;
