@@ -23,6 +23,8 @@
  *
  * All pointers in the input/output structs are DEVICE pointers unless noted;
  * the caller owns them and keeps them alive until the stream work is done.
+ * q, k_cache, v_cache and attn_out must be 16-byte aligned, every other array
+ * aligned to its element size (SPEC_VERIFY_ERR_INVALID_ARG otherwise).
  * Shapes use B = inputs.batch, T = inputs.nodes, Hq/Hkv/D/Lcap/V from the
  * config; arrays are dense, row-major, in the order of their dimensions.
  *

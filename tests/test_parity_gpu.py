@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import compare, note, run_gpu, sampled_attention
+from gpu_harness import compare, device_inputs, handle_config, note, run_gpu, sampled_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -161,3 +161,21 @@ def test_deterministic_across_runs():
     a, b = run_gpu(case, "determinism", repeat=2)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_misaligned_activation_pointer_is_rejected():
+    """q/k/v/attn_out must be 16-byte aligned: a 2-byte offset is refused before any launch."""
+    import torch
+    from tree_attention_verification_verify_amd import SpecVerify, SpecVerifyError, allocate_outputs
+
+    spec = synth.workload("70b-gqa-medusa", batch=1, prefix_len=64, vocab=512, seed=(9, 11))
+    case = synth.make_case(spec)
+    note("misaligned attn_out: expect an argument error, no launch")
+    ins = device_inputs(case)
+    outs = allocate_outputs(case.batch, case.nodes, spec.hq, spec.head_dim, spec.dtype)
+    flat = torch.empty(outs["attn_out"].numel() + 8, dtype=outs["attn_out"].dtype, device=outs["attn_out"].device)
+    outs["attn_out"] = flat[1:1 + outs["attn_out"].numel()].view(outs["attn_out"].shape)
+    with SpecVerify(**handle_config(spec)) as sv:
+        with pytest.raises(SpecVerifyError) as err:
+            sv.run(ins, outs)
+    assert err.value.code == -1 and "aligned" in str(err.value)

@@ -226,6 +226,17 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     if (!out->attn_out || !out->accept_len || !out->final_node || !out->path || !out->out_tokens || !out->status ||
         !out->node_p || !out->node_q || !out->node_accept || !out->final_from_residual || !out->row_token)
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an output pointer is NULL");
+    auto misaligned = [](const void* ptr, uintptr_t a) { return (((uintptr_t)ptr) & (a - 1)) != 0; };
+    if (misaligned(in->q, 16) || misaligned(in->k_cache, 16) || misaligned(in->v_cache, 16) ||
+        misaligned(out->attn_out, 16))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "q, k_cache, v_cache and attn_out must be 16-byte aligned");
+    if (misaligned(in->kv_len, 4) || misaligned(in->parent, 4) || misaligned(in->tokens, 4) ||
+        misaligned(in->target_logits, 4) || (sampling && misaligned(in->draft_logits, 4)) ||
+        misaligned(in->u_accept, 4) || misaligned(in->u_final, 4) || misaligned(out->accept_len, 4) ||
+        misaligned(out->final_node, 4) || misaligned(out->path, 4) || misaligned(out->out_tokens, 4) ||
+        misaligned(out->status, 4) || misaligned(out->node_p, 4) || misaligned(out->node_q, 4) ||
+        misaligned(out->row_token, 4))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "arrays must be aligned to their element size");
     hipStream_t s = (hipStream_t)stream;
 
     const int D = c.head_dim;
