@@ -64,12 +64,12 @@ extern "C" {
 #define SPEC_VERIFY_STATUS_ZERO_DRAFT 4   /* q_i(x_i) = 0 for a supplied draft (rejected) */
 #define SPEC_VERIFY_STATUS_BAD_KVLEN 8    /* kv_len[b] < 0 or kv_len[b] + T > Lcap        */
 
-/* Kernel stages reported by spec_verify_timing_read. */
-#define SPEC_VERIFY_STAGE_ATTENTION 0     /* tree attention main kernel              */
-#define SPEC_VERIFY_STAGE_COMBINE 1       /* merge of split-prefix partials          */
-#define SPEC_VERIFY_STAGE_VOCAB 2         /* per-row softmax statistics (one read)   */
-#define SPEC_VERIFY_STAGE_SELECT 3        /* ratios, decisions, path, final draw     */
-#define SPEC_VERIFY_NUM_STAGES 4
+/* Kernel stages (launches, in order) reported by spec_verify_timing_read. */
+#define SPEC_VERIFY_STAGE_ATTENTION 0     /* tree attention main kernel                   */
+#define SPEC_VERIFY_STAGE_VOCAB 1         /* per-row softmax statistics (one read)        */
+#define SPEC_VERIFY_STAGE_FINISH 2        /* ratios, decisions, path, final draw, and the
+                                             merge of split-prefix attention partials     */
+#define SPEC_VERIFY_NUM_STAGES 3
 
 typedef struct spec_verify_config {
     int32_t max_batch;      /* >= 1: largest B a run may pass                        */

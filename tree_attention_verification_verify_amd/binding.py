@@ -26,8 +26,8 @@ SPEC_VERIFY_BF16 = 1
 SPEC_VERIFY_GREEDY = 0
 SPEC_VERIFY_SAMPLING = 1
 SPEC_VERIFY_FLAG_TIMING = 1
-SPEC_VERIFY_NUM_STAGES = 4
-STAGES = ("attention", "combine", "vocab", "select")
+SPEC_VERIFY_NUM_STAGES = 3
+STAGES = ("attention", "vocab", "finish")
 
 EXPORTED = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
             "spec_verify_timing_read")

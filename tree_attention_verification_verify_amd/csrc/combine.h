@@ -1,0 +1,64 @@
+// Merge of split-prefix attention partials (internal to libspecverify).
+//
+// A row's splits s hold O_s (unnormalised), m_s (running max, log2 units) and
+// l_s (row sum); the merged row is sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// with M = max_s m_s over splits that saw a key (the usual log-sum-exp merge).
+// One thread per 8 consecutive head-dim columns of a row (two float4 reads
+// per split, one 16-byte store of bf16 or two of fp32): D/8 threads per row,
+// 256/(D/8) rows per 256-thread block.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace sv {
+
+template <int D>
+constexpr int combine_rows_per_block() { return 256 / (D / 8); }
+
+template <bool BF16, int D>
+__device__ __forceinline__ void combine_block(const AttnParams& P, long blk) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int TPR = D / 8;
+    constexpr int RPB = 256 / TPR;
+    const long row = (long)blk * RPB + threadIdx.x / TPR;
+    const int d0 = (threadIdx.x % TPR) * 8;
+    const long pairs = (long)P.B * P.Hkv;
+    if (row >= pairs * P.R) return;
+    const int pair = (int)(row / P.R), r = (int)(row - (long)pair * P.R);
+    const int b = pair / P.Hkv, kvh = pair - b * P.Hkv;
+    const int node = r / P.g, head = kvh * P.g + (r - node * P.g);
+
+    float mmax = -INFINITY;
+    for (int s = 0; s < P.nsplit; ++s) {
+        const float2 ml = P.part_ml[((size_t)pair * P.nsplit + s) * P.Rpad + r];
+        if (ml.y > 0.f) mmax = fmaxf(mmax, ml.x);
+    }
+    float lsum = 0.f;
+    floatx4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < P.nsplit; ++s) {
+        const size_t prow = ((size_t)pair * P.nsplit + s) * P.Rpad + r;
+        const float2 ml = P.part_ml[prow];
+        if (!(ml.y > 0.f)) continue;
+        const float w = exp2f(ml.x - mmax);
+        lsum += ml.y * w;
+        const floatx4_t* src = (const floatx4_t*)(P.part_o + prow * D + d0);
+        a0 += w * src[0];
+        a1 += w * src[1];
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    a0 *= inv;
+    a1 *= inv;
+    const size_t obase = ((size_t)(b * P.T + node) * P.Hq + head) * D + d0;
+    if constexpr (BF16) {
+        const u32x4_t w = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
+                           pack_bf16x2(a1[2], a1[3])};
+        *(u32x4_t*)((uint16_t*)P.out + obase) = w;
+    } else {
+        floatx4_t* dst = (floatx4_t*)((float*)P.out + obase);
+        dst[0] = a0;
+        dst[1] = a1;
+    }
+}
+
+}  // namespace sv

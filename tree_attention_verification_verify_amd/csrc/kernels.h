@@ -77,14 +77,16 @@ struct SelectParams {
 // Returns hipSuccess or the launch error.
 hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s);
 hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
-hipError_t launch_attention_combine(const AttnParams& p, bool bf16, hipStream_t s);
 hipError_t launch_row_stats(const StatsParams& p, hipStream_t s);
-hipError_t launch_select(const SelectParams& p, hipStream_t s);
+// The step's last launch: selection (decisions, path, final draw) and, when
+// `merge`, the merge of the attention splits.
+hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool merge, bool bf16, hipStream_t s);
 
 constexpr int kValuRows = 16;      // rows per block of the VALU attention kernel
 constexpr int kVocabThreads = 1024;               // register-resident row kernels
 constexpr int kVocabChunk = kVocabThreads * 32;   // logits held on chip per pass
 constexpr int kStatsThreads = 256;                // streaming row-statistics kernel
+constexpr int kStatsUnroll = 16;                  // float4 loads in flight per thread
 constexpr int kSelectThreads = 256;               // selection / final draw workgroups
 constexpr int kSelectSlice = 2048;                // token ids per final-draw slice
 constexpr int kSelectMaxSlices = 2048;            // vocab <= 4194304

@@ -27,6 +27,7 @@
 // order.  Every sum is taken in a fixed order, so the draw does not depend on
 // the order in which workgroups arrive.
 
+#include "combine.h"
 #include "row_block.h"
 
 namespace sv {
@@ -227,9 +228,8 @@ __device__ void slice_weights(const SelectParams& P, int b, int s, const SelectS
 }
 
 template <bool SAMPLING>
-__global__ __launch_bounds__(ST) void select_kernel(SelectParams P) {
+__device__ void select_block(const SelectParams& P, int s, int b) {
     __shared__ SelectShared sh;
-    const int s = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x;
     if (tid < kWave) decide(P, b, s == 0, sh);
     __syncthreads();
@@ -352,11 +352,41 @@ __global__ __launch_bounds__(ST) void select_kernel(SelectParams P) {
     }
 }
 
+// The launch that ends a step: the selection workgroups first (their
+// dependent loads start at once), then the merge of the attention splits,
+// which only streams memory and fills the GPU meanwhile.  Greedy mode uses one
+// selection workgroup per sequence, sampling mode one per (sequence, slice).
+template <bool SAMPLING, bool BF16, int D>
+__global__ __launch_bounds__(ST) void finish_kernel(SelectParams P, AttnParams A, int nsel) {
+    const int blk = blockIdx.x;
+    if (blk < nsel) {
+        if (SAMPLING) select_block<true>(P, blk % P.S, blk / P.S);
+        else select_block<false>(P, 0, blk);
+    } else {
+        combine_block<BF16, D>(A, blk - nsel);
+    }
+}
+
 }  // namespace
 
-hipError_t launch_select(const SelectParams& p, hipStream_t s) {
-    if (p.sampling) hipLaunchKernelGGL(select_kernel<true>, dim3(p.S, p.B), dim3(ST), 0, s, p);
-    else hipLaunchKernelGGL(select_kernel<false>, dim3(1, p.B), dim3(ST), 0, s, p);
+hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool merge, bool bf16, hipStream_t s) {
+    const int nsel = sp.sampling ? sp.S * sp.B : sp.B;
+    int nmerge = 0;
+    if (merge) {
+        const long rows = (long)ap.B * ap.Hkv * ap.R;
+        const long rpb = ap.D == 128 ? combine_rows_per_block<128>() : combine_rows_per_block<64>();
+        nmerge = (int)((rows + rpb - 1) / rpb);
+    }
+    const dim3 grid(nsel + nmerge), block(ST);
+#define SV_FINISH(S_, B_, D_) hipLaunchKernelGGL((finish_kernel<S_, B_, D_>), grid, block, 0, s, sp, ap, nsel)
+    if (sp.sampling) {
+        if (bf16) { if (ap.D == 128) SV_FINISH(true, true, 128); else SV_FINISH(true, true, 64); }
+        else { if (ap.D == 128) SV_FINISH(true, false, 128); else SV_FINISH(true, false, 64); }
+    } else {
+        if (bf16) { if (ap.D == 128) SV_FINISH(false, true, 128); else SV_FINISH(false, true, 64); }
+        else { if (ap.D == 128) SV_FINISH(false, false, 128); else SV_FINISH(false, false, 64); }
+    }
+#undef SV_FINISH
     return hipGetLastError();
 }
 

@@ -283,11 +283,6 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     hipError_t e = plan.mfma ? sv::launch_attention_mfma(ap, plan.waves, s) : sv::launch_attention_valu(ap, bf16, s);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     if (int rc = mark(SPEC_VERIFY_STAGE_ATTENTION)) return rc;
-    if (plan.nsplit > 1) {
-        e = sv::launch_attention_combine(ap, bf16, s);
-        if (e != hipSuccess) return hip_fail(e, "combine launch");
-    }
-    if (int rc = mark(SPEC_VERIFY_STAGE_COMBINE)) return rc;
 
     sv::StatsParams tp{};
     tp.target = in->target_logits;
@@ -331,9 +326,9 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     sp.slice_tot = h->slice_tot;
     sp.arrive = h->arrive;
     sp.S = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
-    e = sv::launch_select(sp, s);
-    if (e != hipSuccess) return hip_fail(e, "select launch");
-    if (int rc = mark(SPEC_VERIFY_STAGE_SELECT)) return rc;
+    e = sv::launch_finish(sp, ap, plan.nsplit > 1, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "finishing launch");
+    if (int rc = mark(SPEC_VERIFY_STAGE_FINISH)) return rc;
 
     if (h->timing) {
         ++h->ring_head;

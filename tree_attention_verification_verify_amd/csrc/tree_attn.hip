@@ -13,7 +13,7 @@
 // every tree node and every query head of the group.  The tree mask is a
 // per-node 64-bit ancestor set built in registers from parent[]; only tiles
 // that reach slot L_b pay for masking.  Online softmax runs in the log2
-// domain; splits are merged by attn_combine_kernel.
+// domain; the splits are merged by the finishing launch (combine.h).
 //
 // MFMA path (bf16, >= 16 rows per KV head): S^T = K Q^T and O^T = V^T P^T
 // with v_mfma_f32_32x32x16_bf16, so the query index is the MFMA column and a
@@ -560,52 +560,6 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams P) {
 
 // ---------------------------------------------------------------- split merge
 
-// One thread per 8 consecutive head-dim columns of a row (two float4 reads per
-// split, one 16-byte bf16 store): D/8 threads per row, 256/(D/8) rows per block.
-template <bool BF16, int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams P) {
-    constexpr int TPR = D / 8;
-    constexpr int RPB = 256 / TPR;
-    const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
-    const int d0 = (threadIdx.x % TPR) * 8;
-    const long pairs = (long)P.B * P.Hkv;
-    if (row >= pairs * P.R) return;
-    const int pair = (int)(row / P.R), r = (int)(row - (long)pair * P.R);
-    const int b = pair / P.Hkv, kvh = pair - b * P.Hkv;
-    const int node = r / P.g, head = kvh * P.g + (r - node * P.g);
-
-    float mmax = -INFINITY;
-    for (int s = 0; s < P.nsplit; ++s) {
-        const float2 ml = P.part_ml[((size_t)pair * P.nsplit + s) * P.Rpad + r];
-        if (ml.y > 0.f) mmax = fmaxf(mmax, ml.x);
-    }
-    float lsum = 0.f;
-    floatx4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < P.nsplit; ++s) {
-        const size_t prow = ((size_t)pair * P.nsplit + s) * P.Rpad + r;
-        const float2 ml = P.part_ml[prow];
-        if (!(ml.y > 0.f)) continue;
-        const float w = exp2f(ml.x - mmax);
-        lsum += ml.y * w;
-        const floatx4_t* src = (const floatx4_t*)(P.part_o + prow * D + d0);
-        a0 += w * src[0];
-        a1 += w * src[1];
-    }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    a0 *= inv;
-    a1 *= inv;
-    const size_t obase = ((size_t)(b * P.T + node) * P.Hq + head) * D + d0;
-    if constexpr (BF16) {
-        const u32x4 w = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
-                         pack_bf16x2(a1[2], a1[3])};
-        *(u32x4*)((uint16_t*)P.out + obase) = w;
-    } else {
-        floatx4_t* dst = (floatx4_t*)((float*)P.out + obase);
-        dst[0] = a0;
-        dst[1] = a1;
-    }
-}
-
 template <bool BF16, int D>
 hipError_t launch_valu_rows(const AttnParams& p, int maxr, dim3 grid, hipStream_t s) {
     switch (maxr) {
@@ -657,18 +611,5 @@ hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s) 
                       : launch_valu_rows<false, 64>(p, maxr, grid, s);
 }
 
-hipError_t launch_attention_combine(const AttnParams& p, bool bf16, hipStream_t s) {
-    const long rows = (long)p.B * p.Hkv * p.R;
-    const long rpb = 256 / (p.D / 8);
-    dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-    if (bf16) {
-        if (p.D == 128) hipLaunchKernelGGL((attn_combine_kernel<true, 128>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((attn_combine_kernel<true, 64>), grid, dim3(256), 0, s, p);
-    } else {
-        if (p.D == 128) hipLaunchKernelGGL((attn_combine_kernel<false, 128>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((attn_combine_kernel<false, 64>), grid, dim3(256), 0, s, p);
-    }
-    return hipGetLastError();
-}
 
 }  // namespace sv

@@ -39,8 +39,11 @@ __device__ __forceinline__ const float* row_ptr(const StatsParams& P, int b, int
 }
 
 // WITH_Z = false (greedy mode): only the largest logit and its id are needed.
+// Each step issues U float4 loads per thread before using any of them, so a
+// row of up to U * 4 * ST logits costs one memory round trip.
 template <bool WITH_Z>
 __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
+    constexpr int U = kStatsUnroll;
     __shared__ StatsSmem sm;
     const int nrows = P.sampling ? 2 * P.T : P.T;
     const int b = blockIdx.x / nrows, r = blockIdx.x - b * nrows;
@@ -57,56 +60,37 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
     float bv = -INFINITY;    // best logit and its smallest id (ids visited in increasing order)
     int bi = INT_MAX;
 
-    auto absorb = [&](const float* x, int n, int id0, int stride) {
+    // fold n logits with increasing ids (id_of(k)) into the thread's running statistics
+    auto absorb = [&](const float* x, int n, auto id_of) {
         float lm = -INFINITY;
         for (int k = 0; k < n; ++k) lm = fmaxf(lm, x[k]);
         for (int k = 0; k < n; ++k)
-            if (x[k] > bv) { bv = x[k]; bi = id0 + (k >> 2) * stride + (k & 3); }
+            if (x[k] > bv) { bv = x[k]; bi = id_of(k); }
         if (!WITH_Z) return;
         if (lm > m) {
             if (m != -INFINITY) s *= exp2((double)(m - lm) * (double)ilog);
             m = lm;
         }
+        if (m == -INFINITY) return;
         float part = 0.f;
-        for (int k = 0; k < n; ++k) part += exp2f((x[k] - m) * ilog);
+        for (int k = 0; k < n; ++k) part += __builtin_amdgcn_exp2f((x[k] - m) * ilog);
         s += (double)part;
     };
 
-    // 8 float4 per step per thread: 32 logits in flight
-    constexpr int U = 8;
-    int i4 = tid;
-    for (; i4 + (U - 1) * ST < nv4; i4 += U * ST) {
+    for (int base4 = 0; base4 < nv4; base4 += U * ST) {
         float x[4 * U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float4 v = *(const float4*)(row + 4 * (i4 + u * ST));
+            const int i4 = base4 + u * ST + tid;
+            float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            if (i4 < nv4) v = *(const float4*)(row + 4 * i4);
             x[4 * u] = v.x; x[4 * u + 1] = v.y; x[4 * u + 2] = v.z; x[4 * u + 3] = v.w;
         }
-        // ids: 4*(i4 + u*ST) + e, i.e. id0 = 4*i4, stride between float4 groups 4*ST
-        float lm = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < 4 * U; ++k) lm = fmaxf(lm, x[k]);
-#pragma unroll
-        for (int k = 0; k < 4 * U; ++k)
-            if (x[k] > bv) { bv = x[k]; bi = 4 * (i4 + (k >> 2) * ST) + (k & 3); }
-        if (!WITH_Z) continue;
-        if (lm > m) {
-            if (m != -INFINITY) s *= exp2((double)(m - lm) * (double)ilog);
-            m = lm;
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4 * U; ++k) part += exp2f((x[k] - m) * ilog);
-        s += (double)part;
+        absorb(x, 4 * U, [&](int k) { return 4 * (base4 + (k >> 2) * ST + tid) + (k & 3); });
     }
-    for (; i4 < nv4; i4 += ST) {
-        const float4 v = *(const float4*)(row + 4 * i4);
-        const float x[4] = {v.x, v.y, v.z, v.w};
-        absorb(x, 4, 4 * i4, 0);
-    }
-    for (int id = 4 * nv4 + tid; id < V; id += ST) {   // unaligned rows and the tail
-        const float x[1] = {row[id]};
-        absorb(x, 1, id, 0);
+    for (int i = 4 * nv4 + tid; i < V; i += ST) {   // unaligned rows and the tail
+        const float x[1] = {row[i]};
+        absorb(x, 1, [&](int) { return i; });
     }
 
     // merge: max, then the sums rescaled to it, then the argmax (fixed order)
