@@ -38,6 +38,9 @@ def parse():
                          "70b-gqa-medusa, longctx-bigvocab")
     ap.add_argument("--mode", default=None, help="sampling or greedy (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=5, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES"),
+                    help="write profiles/traffic_<kernel>_<workload>.json from rocprofv3 --pmc counter CSVs")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="instead of the verify step, run a plain device copy of this many bytes "
                          "(--steps times): the reference kernel for scaling HBM counters")
@@ -129,11 +132,67 @@ def copy_probe(nbytes, steps):
                       "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
 
 
+def synth_mode(name):
+    import synth
+
+    return synth.workload(name).mode
+
+
+def _counter_per_dispatch(csv_path, kernel_prefix, counter):
+    """Mean value of `counter` over the dispatches of kernels whose name starts with kernel_prefix."""
+    import csv
+
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and
+            r["Kernel_Name"].replace("void ", "").replace("sv::(anonymous namespace)::", "").startswith(kernel_prefix)]
+    if not vals:
+        raise SystemExit("no %s records for %s in %s" % (counter, kernel_prefix, csv_path))
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_summary(paths, workload, stage="attention"):
+    """Write the HBM traffic record of one kernel from rocprofv3 --pmc counter CSVs.
+
+    paths: FETCH_SIZE csv and WRITE_SIZE csv of a bench run, then FETCH_SIZE and
+    WRITE_SIZE csvs of the copy probe and the probe's byte count.  FETCH_SIZE and
+    WRITE_SIZE are in KiB per dispatch; each is scaled by the ratio of the copy's
+    known bytes to what the same counter reads for the copy.
+    """
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes = paths
+    copy_bytes = int(copy_bytes)
+    kname = KERNEL_NAMES[stage]
+    fetch_kib, nf = _counter_per_dispatch(fetch_csv, kname, "FETCH_SIZE")
+    write_kib, nw = _counter_per_dispatch(write_csv, kname, "WRITE_SIZE")
+    cf_kib, _ = _counter_per_dispatch(cfetch_csv, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
+    cw_kib, _ = _counter_per_dispatch(cwrite_csv, "__amd_rocclr_copyBuffer", "WRITE_SIZE")
+    f_scale = copy_bytes / (cf_kib * 1024.0)
+    w_scale = copy_bytes / (cw_kib * 1024.0)
+    read_b = fetch_kib * 1024.0 * f_scale
+    write_b = write_kib * 1024.0 * w_scale
+    rec = {"kernel": kname, "workload": workload, "source": KERNEL_SOURCES[stage],
+           "source_sha256_16": source_hash(stage),
+           "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
+           "dispatches": [nf, nw], "copy_probe_bytes": copy_bytes,
+           "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_read_bytes_per_launch": read_b, "hbm_write_bytes_per_launch": write_b,
+           "hbm_bytes_per_launch": read_b + write_b}
+    out = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kname, workload))
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary, "%s-%s" % (args.workload, args.mode or synth_mode(args.workload)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs the verify step on one GPU only; --gpus %d is not supported "
-              "(sequences shard across GPUs with no exchange; see the design notes)" % args.gpus)
+              "(sequences would shard across GPUs with no exchange, so one GPU's throughput is the unit)"
+              % args.gpus)
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps)
