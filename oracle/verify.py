@@ -174,11 +174,13 @@ def accept_and_select(parent: np.ndarray, tokens: np.ndarray, u_accept: np.ndarr
 def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final, *,
                  mode: str, temperature: float = 1.0, top_p: float = 1.0,
                  accept_band: float = NEAR_TIE, cdf_band: float = NEAR_TIE,
-                 topp_band: float = TOPP_NEAR_TIE) -> Dict[str, np.ndarray]:
+                 topp_band: float = TOPP_NEAR_TIE, rule: str = "independent") -> Dict[str, np.ndarray]:
     """Steps 2-4 for a batch: distributions, acceptance, final token and path.
 
     The *_band arguments set how close to its threshold a decision must be to
-    be flagged as a near-tie (defaults: the bands stated above).
+    be flagged as a near-tie (defaults: the bands stated above).  rule:
+    "independent" (each node tested against its parent's p, longest accepted
+    root path) or "lossless" (the sibling walk of oracle.lossless; sampling only).
     """
     target_logits = np.asarray(target_logits)
     B, T, V = target_logits.shape
@@ -194,6 +196,9 @@ def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final,
                 q_rows[b, 1:], dmargin[b, 1:] = row_distributions(
                     np.asarray(draft_logits)[b, 1:], temperature, top_p)
     greedy_rows = argmax_first(target_logits)
+    if rule == "lossless" and mode == "sampling":
+        return _lossless_vocab(parent, tokens, u_accept, u_final, p_rows, q_rows, greedy_rows,
+                               tmargin, dmargin, accept_band, cdf_band, topp_band)
     out = accept_and_select(parent, tokens, u_accept, u_final, mode, V, p_rows=p_rows,
                             q_rows=q_rows, greedy_rows=greedy_rows)
 
@@ -217,7 +222,33 @@ def verify_vocab(parent, tokens, target_logits, draft_logits, u_accept, u_final,
     return out
 
 
-def verify(case, *, attention: bool = True, seqs=None, **bands) -> Dict[str, np.ndarray]:
+def _lossless_vocab(parent, tokens, u_accept, u_final, p_rows, q_rows, greedy_rows, tmargin, dmargin,
+                    accept_band, cdf_band, topp_band):
+    """verify_vocab's result under the lossless sibling walk, with its near-tie flags."""
+    from .lossless import lossless_walk
+
+    out = lossless_walk(parent, tokens, u_accept, u_final, p_rows, q_rows)
+    B, T = np.asarray(parent).shape
+    out["row_token"] = np.asarray(greedy_rows, dtype=np.int32)
+    tested = out["tested"]
+    node_near = tested & (out["accept_margin"] < accept_band)
+    node_near[:, 0] = False
+    # every row the walk read: target rows of the path, draft rows of tested children
+    rows_near = np.zeros(B, dtype=bool)
+    for b in range(B):
+        path = out["path"][b]
+        on = path[path >= 0]
+        if len(on):
+            rows_near[b] |= bool((tmargin[b, on] < topp_band).any())
+        rows_near[b] |= bool((dmargin[b][tested[b]] < topp_band).any())
+    final_near = (out["cdf_margin"] < cdf_band) | rows_near
+    out.update(node_near=node_near, final_near=final_near, seq_near=node_near.any(axis=1) | final_near,
+               target_topp_margin=tmargin, draft_topp_margin=dmargin, p_rows=p_rows, q_rows=q_rows)
+    return out
+
+
+def verify(case, *, attention: bool = True, seqs=None, rule: str = "independent",
+           **bands) -> Dict[str, np.ndarray]:
     """The whole verify step on a case (any object with the synthetic-case fields).
 
     seqs: restrict to some sequence indices (outputs are for those, in order).
@@ -228,7 +259,7 @@ def verify(case, *, attention: bool = True, seqs=None, **bands) -> Dict[str, np.
     draft = None if case.draft_logits is None else case.draft_logits[seqs]
     out = verify_vocab(case.parent[seqs], case.tokens[seqs], case.target_logits[seqs], draft,
                        case.u_accept[seqs], case.u_final[seqs], mode=spec.mode,
-                       temperature=spec.temperature, top_p=spec.top_p, **bands)
+                       temperature=spec.temperature, top_p=spec.top_p, rule=rule, **bands)
     if attention:
         T = case.parent.shape[1]
         lcap = case.k_cache.shape[2]
