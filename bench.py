@@ -38,6 +38,8 @@ def parse():
                          "70b-gqa-medusa, longctx-bigvocab")
     ap.add_argument("--mode", default=None, help="sampling or greedy (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lossless-tree", action="store_true",
+                    help="time the lossless sibling walk (SPEC_VERIFY_FLAG_LOSSLESS_TREE) as the value")
     ap.add_argument("--traffic-summary", nargs=5, default=None,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES"),
                     help="write profiles/traffic_<kernel>_<workload>.json from rocprofv3 --pmc counter CSVs")
@@ -229,7 +231,8 @@ def main():
     outs = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
     cfg = dict(max_batch=B, max_nodes=T, num_q_heads=spec.hq, num_kv_heads=spec.hkv, head_dim=spec.head_dim,
                kv_capacity=spec.kv_capacity, vocab=spec.vocab, dtype=spec.dtype, mode=spec.mode,
-               temperature=spec.temperature, top_p=spec.top_p)
+               temperature=spec.temperature, top_p=spec.top_p,
+               lossless_tree=bool(args.lossless_tree and spec.mode == "sampling"))
     stream = torch.cuda.current_stream()
     work = algorithmic_work(case)
 
@@ -260,6 +263,35 @@ def main():
         ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     per_launch = {k: v / max(nruns, 1) for k, v in stage_ms.items()}
+
+    # the other tree rule on the same inputs (sampling): its step time and finishing stage
+    other = None
+    if spec.mode == "sampling":
+        ocfg = dict(cfg, lossless_tree=not cfg["lossless_tree"])
+        oouts = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
+        with SpecVerify(timing=True, **ocfg) as sv:
+            for _ in range(args.warmup):
+                sv.run(ins, oouts, stream)
+            torch.cuda.synchronize()
+            sv.timing_read()
+            for _ in range(args.steps):
+                sv.run(ins, oouts, stream)
+            torch.cuda.synchronize()
+            oms, on = sv.timing_read()
+        with SpecVerify(timing=False, **ocfg) as sv:
+            for _ in range(args.warmup):
+                sv.run(ins, oouts, stream)
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            for _ in range(args.steps):
+                sv.run(ins, oouts, stream)
+            torch.cuda.synchronize()
+            oms_step = (time.perf_counter() - t3) * 1e3 / args.steps
+        ores = {k: v.cpu().numpy() for k, v in oouts.items() if k in ("accept_len",)}
+        other = {"rule": "lossless sibling walk" if ocfg["lossless_tree"] else "independent per-node test",
+                 "value": B * T / (oms_step * 1e-3), "ms_per_step": oms_step,
+                 "stage_ms_per_launch": {k: v / max(on, 1) for k, v in oms.items()},
+                 "accepted_tokens_per_step": int(ores["accept_len"].sum() + B)}
     torch.cuda.synchronize()
     got = {k: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy() for k, v in outs.items()}
 
@@ -311,7 +343,10 @@ def main():
         "stage_ms_per_launch": per_launch,
         "ms_per_step_with_event_records": ms_with_events,
         "accepted_tokens_per_step": int(got["accept_len"].sum() + B),
+        "tree_rule": "lossless sibling walk" if cfg["lossless_tree"] else "independent per-node test",
     }
+    if other is not None:
+        result["other_tree_rule"] = other
     if not args.no_cpu_baseline:
         base, ok, err = cpu_baseline(case, got)
         result["cpu_baseline"] = base

@@ -57,6 +57,20 @@ extern "C" {
 /* config.flags: record HIP events around each kernel of every run (see
  * spec_verify_timing_read).  Costs a few event records per run. */
 #define SPEC_VERIFY_FLAG_TIMING 1u
+/* config.flags, sampling mode only: lossless multi-candidate tree sampling.
+ * Instead of testing every node independently against its parent's p and
+ * keeping the longest accepted root path, walk from the root: try the
+ * children of the current node in increasing id, accept child c when
+ * u_accept[c] < r(x_c)/q_c(x_c), otherwise set r <- norm([r - q_c]_+) (kept if
+ * that is all zero) and try the next child; r starts as p of the node reached
+ * and the final token is drawn from r.  The output then follows the target's
+ * law for any tree, not only for chains ("投机解码的五条路线", section 4:
+ * lossless verification; the featured article on the founding
+ * speculative-decoding paper, section 2.1, for one rejection step).  For
+ * chains both rules give the same outputs.  node_accept/node_p/node_q then
+ * describe the tests made (r(x) and q(x) at test time); children never tried
+ * get 0.  Costs one pass over the vocabulary per rejected child. */
+#define SPEC_VERIFY_FLAG_LOSSLESS_TREE 2u
 
 /* Status bits written to outputs.status[b]. */
 #define SPEC_VERIFY_STATUS_BAD_PARENT 1   /* parent[0] != -1 or not 0 <= parent[i] < i   */

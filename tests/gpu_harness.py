@@ -45,11 +45,11 @@ def device_inputs(case: synth.Case, device="cuda") -> Dict:
 
 
 def handle_config(spec: synth.CaseSpec, batch: Optional[int] = None, nodes: Optional[int] = None,
-                  timing: bool = False, kv_capacity: Optional[int] = None) -> Dict:
+                  timing: bool = False, kv_capacity: Optional[int] = None, lossless_tree: bool = False) -> Dict:
     return dict(max_batch=batch or spec.batch, max_nodes=nodes or spec.nodes, num_q_heads=spec.hq,
                 num_kv_heads=spec.hkv, head_dim=spec.head_dim, kv_capacity=kv_capacity or spec.kv_capacity,
                 vocab=spec.vocab, dtype=spec.dtype, mode=spec.mode, temperature=spec.temperature,
-                top_p=spec.top_p, timing=timing)
+                top_p=spec.top_p, timing=timing, lossless_tree=lossless_tree)
 
 
 def to_numpy(outputs: Dict) -> Dict[str, np.ndarray]:
@@ -64,7 +64,8 @@ def to_numpy(outputs: Dict) -> Dict[str, np.ndarray]:
     return res
 
 
-def run_gpu(case: synth.Case, label: str, repeat: int = 1) -> Sequence[Dict[str, np.ndarray]]:
+def run_gpu(case: synth.Case, label: str, repeat: int = 1,
+            lossless_tree: bool = False) -> Sequence[Dict[str, np.ndarray]]:
     import torch
     from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs
 
@@ -73,7 +74,7 @@ def run_gpu(case: synth.Case, label: str, repeat: int = 1) -> Sequence[Dict[str,
                                                     spec.vocab, spec.dtype, spec.mode))
     ins = device_inputs(case)
     results = []
-    with SpecVerify(**handle_config(spec, kv_capacity=case.k_cache.shape[2])) as sv:
+    with SpecVerify(**handle_config(spec, kv_capacity=case.k_cache.shape[2], lossless_tree=lossless_tree)) as sv:
         for r in range(repeat):
             outs = allocate_outputs(case.batch, case.nodes, spec.hq, spec.head_dim, spec.dtype)
             note("%s: run %d" % (label, r))
@@ -86,10 +87,12 @@ def run_gpu(case: synth.Case, label: str, repeat: int = 1) -> Sequence[Dict[str,
 
 def compare(case: synth.Case, got: Dict[str, np.ndarray], ref: Dict[str, np.ndarray],
             seqs: Optional[Sequence[int]] = None, attn: bool = True,
-            attn_rows: Optional[Sequence] = None) -> Dict[str, int]:
+            attn_rows: Optional[Sequence] = None, rule: str = "independent") -> Dict[str, int]:
     """Element-wise parity.  `ref` holds the oracle's outputs for `seqs` (in order).
 
     attn_rows: optional list of (seq, node, head, oracle row) to check instead of every row.
+    rule "lossless": which nodes are tested depends on earlier decisions, so a
+    sequence with any near-tie has no per-node comparison either.
     Returns counts of near-ties (excluded decisions).
     """
     spec = case.spec
@@ -106,6 +109,10 @@ def compare(case: synth.Case, got: Dict[str, np.ndarray], ref: Dict[str, np.ndar
         node_near = ref["node_near"][n]
         stats["node_near"] += int(node_near.sum())
         stats["final_near"] += int(ref["final_near"][n])
+        if rule == "lossless" and ref["seq_near"][n]:
+            stats["seq_near"] += 1
+            np.testing.assert_array_equal(got["row_token"][b], ref["row_token"][n], err_msg="row_token b=%d" % b)
+            continue
         # per-node decisions
         for i in range(T):
             if not node_near[i]:

@@ -72,6 +72,17 @@ def test_create_rejects_top_p_on_huge_vocab():
     assert e.value.code == binding.SPEC_VERIFY_ERR_UNSUPPORTED
 
 
+def test_create_rejects_lossless_tree_in_greedy_mode_and_unknown_flags():
+    with pytest.raises(sva.SpecVerifyError) as e:
+        sva.spec_verify_create(sva.make_config(**dict(GOOD, mode="greedy"), lossless_tree=True))
+    assert e.value.code == binding.SPEC_VERIFY_ERR_INVALID_ARG
+    cfg = sva.make_config(**GOOD)
+    cfg.flags = 0x80
+    with pytest.raises(sva.SpecVerifyError) as e:
+        sva.spec_verify_create(cfg)
+    assert e.value.code == binding.SPEC_VERIFY_ERR_INVALID_ARG
+
+
 def test_null_arguments():
     lib = sva.load_library()
     assert lib.spec_verify_create(None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG

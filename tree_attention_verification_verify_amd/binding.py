@@ -26,6 +26,7 @@ SPEC_VERIFY_BF16 = 1
 SPEC_VERIFY_GREEDY = 0
 SPEC_VERIFY_SAMPLING = 1
 SPEC_VERIFY_FLAG_TIMING = 1
+SPEC_VERIFY_FLAG_LOSSLESS_TREE = 2
 SPEC_VERIFY_NUM_STAGES = 3
 STAGES = ("attention", "vocab", "finish")
 
@@ -100,11 +101,12 @@ def _check(rc: int) -> None:
 
 def make_config(*, max_batch, max_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, vocab,
                 dtype="bf16", mode="sampling", temperature=1.0, top_p=1.0, softmax_scale=0.0,
-                timing=False) -> Config:
+                timing=False, lossless_tree=False) -> Config:
+    flags = (SPEC_VERIFY_FLAG_TIMING if timing else 0) | (SPEC_VERIFY_FLAG_LOSSLESS_TREE if lossless_tree else 0)
     return Config(max_batch, max_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, vocab,
                   SPEC_VERIFY_BF16 if dtype == "bf16" else SPEC_VERIFY_F32,
                   SPEC_VERIFY_SAMPLING if mode == "sampling" else SPEC_VERIFY_GREEDY,
-                  temperature, top_p, softmax_scale, SPEC_VERIFY_FLAG_TIMING if timing else 0)
+                  temperature, top_p, softmax_scale, flags)
 
 
 def spec_verify_create(cfg: Config) -> ctypes.c_void_p:

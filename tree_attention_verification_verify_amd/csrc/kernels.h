@@ -67,6 +67,7 @@ struct SelectParams {
     uint8_t* node_accept;
     uint8_t* final_from_residual;
     double2* slice_tot;   // [B][S] (residual, p-only) weight totals per slice of the final draw
+    float* resid_ws;      // [B][2][V] residual rows of the lossless sibling walk
     int32_t* arrive;      // [B] slices done; reset to 0 by the last one
     int B, T, V, Lcap;
     int S;                // slices per sequence: ceil(V / kSelectSlice)
@@ -80,7 +81,10 @@ hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
 hipError_t launch_row_stats(const StatsParams& p, hipStream_t s);
 // The step's last launch: selection (decisions, path, final draw) and, when
 // `merge`, the merge of the attention splits.
-hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool merge, bool bf16, hipStream_t s);
+hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool select, bool merge, bool bf16,
+                         hipStream_t s);
+// Lossless sibling walk (sampling mode, SPEC_VERIFY_FLAG_LOSSLESS_TREE): one workgroup per sequence.
+hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s);
 
 constexpr int kValuRows = 16;      // rows per block of the VALU attention kernel
 constexpr int kVocabThreads = 1024;               // register-resident row kernels

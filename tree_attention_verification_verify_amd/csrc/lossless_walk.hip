@@ -1,0 +1,295 @@
+// Lossless multi-candidate tree sampling: the sibling walk.
+//
+// Tree acceptance with one independent test per node keeps the target's
+// output law only when every node has at most one drafted child.  The walk
+// below keeps it for any tree ("投机解码的五条路线", section 4, separates
+// lossless verification from typical acceptance; the rejection step and its
+// residual are those of the featured article on the founding
+// speculative-decoding paper, section 2.1, applied once per sibling):
+//
+//   start at the root with r = p_root;
+//   at node v, try its children c in increasing node id:
+//       accept c when u_c < r(x_c) / q_c(x_c): emit x_c, move to c, r = p_c;
+//       otherwise r <- norm([r - q_c]_+) (kept if that is all zero) and try
+//       the next child;
+//   when v has no untried child, draw the final token from r with u_final
+//   (inverse CDF in token-id order).
+//
+// A chain gives exactly the independent rule: the first rejection ends the
+// walk, and its residual is computed with the same arithmetic.
+//
+// One 1024-thread workgroup per sequence.  Wave 0 checks the tree and sets
+// the status bits; each test is a gather by thread 0; each rejection is one
+// chunked pass over the vocabulary that writes the unnormalised residual to
+// one of two workspace rows of the sequence (so a residual that vanishes
+// leaves the previous one intact) and sums it in fp64 in a fixed order.
+
+#include "row_block.h"
+
+namespace sv {
+namespace {
+
+using namespace rows;
+
+struct WalkShared {
+    unsigned long long kids_of[64];   // children of every node, as a node bitmask
+    unsigned long long kids;          // untried children of v
+    double W;                         // total of the workspace residual (when r_ws)
+    int v, depth, r_ws, cur, accept, live, c;
+};
+
+__device__ __forceinline__ float walk_prob(const float* row, const RowStat& st, int x, float ilog) {
+    const float e = unnorm(row[x], st.zmax, ilog);
+    const Nucleus nu{st.thr, st.cutoff};
+    return in_nucleus(e, x, nu) ? (float)((double)e / st.Z) : 0.f;
+}
+
+// Unnormalised weights of the current r over one chunk: p_v in its nucleus
+// (from the logits), or the workspace residual.
+__device__ void r_weights(const SelectParams& P, int b, const WalkShared& ws, int cb, float4 (&w)[VPT4]) {
+    const int T = P.T, V = P.V;
+    if (ws.r_ws) {
+        const float* R = P.resid_ws + ((size_t)b * 2 + ws.cur) * V;
+        load_chunk(R, V, cb, (((uintptr_t)R) & 15) == 0, w);   // past V: -inf, a weight of 0 here
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (elem_index(cb, j, e) >= V) f4set(w[j], e, 0.f);
+    } else {
+        const float* zp = P.target + ((size_t)b * T + ws.v) * V;
+        load_chunk(zp, V, cb, (((uintptr_t)zp) & 15) == 0, w);
+        const RowStat sp = P.stats[(size_t)b * 2 * T + ws.v];
+        const Nucleus np{sp.thr, sp.cutoff};
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int idx = elem_index(cb, j, e);
+                float pe = unnorm(f4get(w[j], e), sp.zmax, P.ilog);
+                if (idx >= V || !in_nucleus(pe, idx, np)) pe = 0.f;
+                f4set(w[j], e, pe);
+            }
+    }
+}
+
+__device__ void store_chunk(float* row, int V, int cb, const float4 (&w)[VPT4]) {
+    const bool aligned = (((uintptr_t)row) & 15) == 0;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j) {
+        const int idx = elem_index(cb, j, 0);
+        if (aligned && idx + 3 < V) {
+            *(float4*)(row + idx) = w[j];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (idx + e < V) row[idx + e] = f4get(w[j], e);
+        }
+    }
+}
+
+// r <- [r - q_c]_+ over the whole row into the other workspace row; returns its fp64 total.
+__device__ double residual_pass(const SelectParams& P, int b, int c, const WalkShared& ws, Smem& sm) {
+    const int T = P.T, V = P.V;
+    const RowStat sq = P.stats[(size_t)b * 2 * T + T + c];
+    const Nucleus nq{sq.thr, sq.cutoff};
+    const float iq = (float)(1.0 / sq.Z);
+    const float ir = ws.r_ws ? (float)(1.0 / ws.W) : (float)(1.0 / P.stats[(size_t)b * 2 * T + ws.v].Z);
+    const float* zq = P.draft + ((size_t)b * T + c) * V;
+    const bool aq = (((uintptr_t)zq) & 15) == 0;
+    float* out = P.resid_ws + ((size_t)b * 2 + (ws.cur ^ 1)) * V;
+    double W = 0.0;
+    for (int cb = 0; cb < V; cb += CHUNK) {
+        float4 r[VPT4], q[VPT4];
+        r_weights(P, b, ws, cb, r);
+        load_chunk(zq, V, cb, aq, q);
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int idx = elem_index(cb, j, e);
+                float qe = unnorm(f4get(q[j], e), sq.zmax, P.ilog);
+                if (idx >= V || !in_nucleus(qe, idx, nq)) qe = 0.f;
+                f4set(q[j], e, idx < V ? resid_weight(f4get(r[j], e), ir, qe, iq) : 0.f);
+            }
+        store_chunk(out, V, cb, q);
+        W += slot_totals(q, sm);
+    }
+    return W;
+}
+
+// Inverse-CDF draw from r: y = min{k : u * W < C_k} in token-id order.
+__device__ int draw_from_r(const SelectParams& P, int b, const WalkShared& ws, double u, Smem& sm) {
+    const int V = P.V;
+    float4 w[VPT4];
+    if (V <= CHUNK) {
+        r_weights(P, b, ws, 0, w);
+        const double W = slot_totals(w, sm);
+        int y = locate_in_chunk(w, 0, V, 0.0, u * W, sm);
+        if (y < 0) {
+            int last = -1;
+#pragma unroll
+            for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (f4get(w[j], e) > 0.f) last = max(last, elem_index(0, j, e));
+            y = block_max_int(last, sm);
+        }
+        return y;
+    }
+    // streamed: chunk totals, then the chunk holding the draw again
+    double W = 0.0;
+    int nc = 0;
+    for (int cb = 0; cb < V; cb += CHUNK, ++nc) {
+        r_weights(P, b, ws, cb, w);
+        const double S = slot_totals(w, sm);
+        if (threadIdx.x == 0) sm.chunk_sum[nc] = S;
+        W += S;
+    }
+    __syncthreads();
+    const double target = u * W;
+    double cum = 0.0;
+    int cstar = -1;
+    for (int k = 0; k < nc; ++k) {
+        if (cum + sm.chunk_sum[k] > target) { cstar = k; break; }
+        cum += sm.chunk_sum[k];
+    }
+    if (cstar < 0) {   // rounding: the last chunk with weight
+        for (int k = nc - 1; k >= 0; --k)
+            if (sm.chunk_sum[k] > 0.0) { cstar = k; break; }
+        if (cstar < 0) return -1;
+        cum = 0.0;
+        for (int k = 0; k < cstar; ++k) cum += sm.chunk_sum[k];
+    }
+    const int cb = cstar * CHUNK;
+    r_weights(P, b, ws, cb, w);
+    (void)slot_totals(w, sm);
+    int y = locate_in_chunk(w, cb, V, cum, target, sm);
+    if (y < 0) {
+        int last = -1;
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (f4get(w[j], e) > 0.f) last = max(last, elem_index(cb, j, e));
+        y = block_max_int(last, sm);
+    }
+    return y;
+}
+
+__global__ __launch_bounds__(NT) void lossless_walk_kernel(SelectParams P) {
+    __shared__ Smem sm;
+    __shared__ WalkShared ws;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int T = P.T, V = P.V;
+    const size_t base = (size_t)b * T;
+    const RowStat* st = P.stats + (size_t)b * 2 * T;
+
+    if (tid < kWave) {
+        const int lane = tid;
+        const bool live = lane < T;
+        bool bad_parent;
+        (void)ancestor_mask(P.parent + base, T, &bad_parent);
+        const int tok = live ? P.tokens[base + lane] : 0;
+        const bool bad_token = __any(live && lane >= 1 && (tok < 0 || tok >= V));
+        const int L = P.kv_len[b];
+        const bool bad_kv = (L < 0) || (L > P.Lcap - T);
+        int status = (bad_parent ? 1 : 0) | (bad_token ? 2 : 0) | (bad_kv ? 8 : 0);
+        if (live) P.row_token[base + lane] = st[lane].argmax;
+        if (live) {
+            P.node_accept[base + lane] = (lane == 0) ? 1 : 0;
+            P.node_p[base + lane] = 0.f;
+            P.node_q[base + lane] = 0.f;
+            P.path[base + lane] = (lane == 0 && !bad_parent && !bad_token) ? 0 : -1;
+            P.out_tokens[base + lane] = -1;
+        }
+        if (bad_parent || bad_token) {
+            if (lane == 0) {
+                P.accept_len[b] = 0;
+                P.final_node[b] = -1;
+                P.final_from_residual[b] = 0;
+                P.status[b] = status;
+                ws.live = 0;
+            }
+        } else {
+            const int par = live ? P.parent[base + lane] : -1;
+            // status bit 4: some supplied draft gives its own token probability 0
+            const bool zero_q = live && lane >= 1 && !(walk_prob(P.draft + (base + lane) * V, st[T + lane], tok,
+                                                                 P.ilog) > 0.f);
+            if (__any(zero_q)) status |= 4;
+            for (int n = 0; n < T; ++n) {
+                const unsigned long long k = __ballot(live && lane >= 1 && par == n);
+                if (lane == 0) ws.kids_of[n] = k;
+            }
+            if (lane == 0) {
+                P.status[b] = status;
+                ws.live = 1;
+                ws.v = 0;
+                ws.depth = 0;
+                ws.r_ws = 0;
+                ws.cur = 0;
+                ws.W = 0.0;
+                ws.kids = ws.kids_of[0];
+            }
+        }
+    }
+    __syncthreads();
+    if (!ws.live) return;
+
+    // every round tests one child (accepting it or not) or ends the walk: at most 2T rounds
+    for (int round = 0; round < 2 * 64 + 1; ++round) {
+        const unsigned long long kids = ws.kids;
+        __syncthreads();   // every wave has read the state before thread 0 changes it
+        if (kids == 0ull) break;
+        if (tid == 0) {
+            const int c = __builtin_ctzll(kids);
+            const int x = P.tokens[base + c];
+            const float rx = ws.r_ws ? (float)((double)P.resid_ws[((size_t)b * 2 + ws.cur) * V + x] / ws.W)
+                                     : walk_prob(P.target + (base + ws.v) * V, st[ws.v], x, P.ilog);
+            const float qx = walk_prob(P.draft + (base + c) * V, st[T + c], x, P.ilog);
+            P.node_p[base + c] = rx;
+            P.node_q[base + c] = qx;
+            const bool acc = (qx > 0.f) && (P.u_accept[base + c] < rx / qx);
+            ws.accept = acc ? 1 : 0;
+            ws.c = c;
+            if (acc) {
+                P.node_accept[base + c] = 1;
+                P.out_tokens[base + ws.depth] = x;
+                ws.depth += 1;
+                P.path[base + ws.depth] = c;
+                ws.v = c;
+                ws.r_ws = 0;
+                ws.kids = ws.kids_of[c];
+            } else {
+                ws.kids &= ~(1ull << c);
+            }
+        }
+        __syncthreads();
+        if (ws.accept) continue;   // the next round's barrier follows this read
+        const double W = residual_pass(P, b, ws.c, ws, sm);
+        __syncthreads();
+        if (tid == 0 && W > 0.0) {   // a vanishing residual keeps r
+            ws.r_ws = 1;
+            ws.cur ^= 1;
+            ws.W = W;
+        }
+        __syncthreads();
+    }
+
+    const int y = draw_from_r(P, b, ws, (double)P.u_final[b], sm);
+    if (tid == 0) {
+        P.out_tokens[base + ws.depth] = y;
+        P.accept_len[b] = ws.depth;
+        P.final_node[b] = ws.v;
+        P.final_from_residual[b] = ws.kids_of[ws.v] != 0ull ? 1 : 0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(lossless_walk_kernel, dim3(p.B), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -369,14 +369,16 @@ __global__ __launch_bounds__(ST) void finish_kernel(SelectParams P, AttnParams A
 
 }  // namespace
 
-hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool merge, bool bf16, hipStream_t s) {
-    const int nsel = sp.sampling ? sp.S * sp.B : sp.B;
+hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool select, bool merge, bool bf16,
+                         hipStream_t s) {
+    const int nsel = !select ? 0 : (sp.sampling ? sp.S * sp.B : sp.B);
     int nmerge = 0;
     if (merge) {
         const long rows = (long)ap.B * ap.Hkv * ap.R;
         const long rpb = ap.D == 128 ? combine_rows_per_block<128>() : combine_rows_per_block<64>();
         nmerge = (int)((rows + rpb - 1) / rpb);
     }
+    if (nsel + nmerge == 0) return hipSuccess;
     const dim3 grid(nsel + nmerge), block(ST);
 #define SV_FINISH(S_, B_, D_) hipLaunchKernelGGL((finish_kernel<S_, B_, D_>), grid, block, 0, s, sp, ap, nsel)
     if (sp.sampling) {

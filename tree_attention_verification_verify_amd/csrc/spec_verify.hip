@@ -94,6 +94,7 @@ struct spec_verify_handle {
     sv::RowStat* stats = nullptr;     // max_batch * 2 * max_nodes row statistics
     double2* slice_tot = nullptr;     // max_batch * slices final-draw slice totals
     int32_t* arrive = nullptr;        // max_batch final-draw arrival counters (zero between runs)
+    float* resid_ws = nullptr;        // max_batch * 2 * vocab residual rows (lossless tree walk)
     bool timing = false;
     std::vector<hipEvent_t> events;   // kTimingRing * kEventsPerRun
     long runs_recorded = 0;           // since the last read
@@ -133,7 +134,10 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
     }
     if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-    if ((c.flags & ~SPEC_VERIFY_FLAG_TIMING) != 0u) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "unknown flag bits");
+    if ((c.flags & ~(SPEC_VERIFY_FLAG_TIMING | SPEC_VERIFY_FLAG_LOSSLESS_TREE)) != 0u)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "unknown flag bits");
+    if ((c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE) && c.mode != SPEC_VERIFY_SAMPLING)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "SPEC_VERIFY_FLAG_LOSSLESS_TREE needs sampling mode");
     const long long lcap_elems = (long long)c.kv_capacity * c.head_dim;
     if (lcap_elems > (1LL << 40)) return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "kv_capacity too large");
 
@@ -166,11 +170,14 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
     if (e == hipSuccess) e = hipMalloc((void**)&h->slice_tot, (size_t)c.max_batch * slices * sizeof(double2));
     if (e == hipSuccess) e = hipMalloc((void**)&h->arrive, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(h->arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
+    if (e == hipSuccess && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE))
+        e = hipMalloc((void**)&h->resid_ws, (size_t)c.max_batch * 2 * c.vocab * sizeof(float));
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         (void)hipFree(h->stats);
         (void)hipFree(h->slice_tot);
         (void)hipFree(h->arrive);
+        (void)hipFree(h->resid_ws);
         (void)hipFree(h->part_o);
         (void)hipFree(h->part_ml);
         delete h;
@@ -205,6 +212,7 @@ int spec_verify_destroy(spec_verify_handle* h) {
     if (h->stats) (void)hipFree(h->stats);
     if (h->slice_tot) (void)hipFree(h->slice_tot);
     if (h->arrive) (void)hipFree(h->arrive);
+    if (h->resid_ws) (void)hipFree(h->resid_ws);
     if (dev >= 0 && dev != h->device) (void)hipSetDevice(dev);
     delete h;
     return SPEC_VERIFY_OK;
@@ -326,8 +334,14 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     sp.slice_tot = h->slice_tot;
     sp.arrive = h->arrive;
     sp.S = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
-    e = sv::launch_finish(sp, ap, plan.nsplit > 1, bf16, s);
+    sp.resid_ws = h->resid_ws;
+    const bool walk = sampling && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE);
+    e = sv::launch_finish(sp, ap, !walk, plan.nsplit > 1, bf16, s);
     if (e != hipSuccess) return hip_fail(e, "finishing launch");
+    if (walk) {
+        e = sv::launch_lossless_walk(sp, s);
+        if (e != hipSuccess) return hip_fail(e, "lossless walk launch");
+    }
     if (int rc = mark(SPEC_VERIFY_STAGE_FINISH)) return rc;
 
     if (h->timing) {
