@@ -24,10 +24,13 @@ from .attention import tree_attention_node, tree_attention_sequence
 from .sampling import argmax_first, effective_distribution, inverse_cdf, inverse_cdf_rows, nucleus_margin
 from .verify import (NEAR_TIE, TOPP_NEAR_TIE, accept_and_select, row_distributions, verify, verify_vocab,
                      widen)
+from .lossless import lossless_walk
+from .commit import commit_kv
 
 __all__ = [
     "ancestors", "check_parent", "depths", "tree_mask",
     "tree_attention_node", "tree_attention_sequence",
     "argmax_first", "effective_distribution", "inverse_cdf", "inverse_cdf_rows", "nucleus_margin",
     "NEAR_TIE", "TOPP_NEAR_TIE", "accept_and_select", "row_distributions", "verify", "verify_vocab", "widen",
+    "lossless_walk", "commit_kv",
 ]
