@@ -264,6 +264,36 @@ def main():
 
     per_launch = {k: v / max(nruns, 1) for k, v in stage_ms.items()}
 
+    # KV commit of the accepted paths (spec_verify_commit) on this step's outputs: events
+    # around the call alone; kv_len is restored before each call
+    commit = None
+    with SpecVerify(timing=False, **cfg) as sv:
+        sv.run(ins, outs, stream)
+        kl0 = ins["kv_len"].clone()
+        kl = kl0.clone()
+        total_ms, reps = 0.0, max(args.steps // 4, 10)
+        for rep in range(reps + 3):
+            kl.copy_(kl0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sv.commit(ins["k_cache"], ins["v_cache"], kl, outs["path"], outs["accept_len"], outs["final_node"],
+                      stream)
+            e1.record(stream)
+            e1.synchronize()
+            if rep >= 3:
+                total_ms += e0.elapsed_time(e1)
+        path_np = outs["path"].cpu().numpy()
+        acc_np = outs["accept_len"].cpu().numpy()
+        moved = sum(int((path_np[b, 1:acc_np[b] + 1] != np.arange(1, acc_np[b] + 1)).sum()) for b in range(B))
+        elem = 2 if spec.dtype == "bf16" else 4
+        nbytes = moved * spec.hkv * spec.head_dim * elem * 2 * 2     # K and V, read and write
+        us = total_ms * 1e3 / reps
+        commit = {"us_per_call": us, "rows_moved": moved, "bytes_moved": nbytes,
+                  "GBps": nbytes / (us * 1e-6) / 1e9 if us > 0 else None}
+    # the caches were modified in place: restore them for any later use of `ins`
+    ins["k_cache"].copy_(up(case.k_cache, spec.dtype))
+    ins["v_cache"].copy_(up(case.v_cache, spec.dtype))
+
     # the other tree rule on the same inputs (sampling): its step time and finishing stage
     other = None
     if spec.mode == "sampling":
@@ -347,6 +377,7 @@ def main():
     }
     if other is not None:
         result["other_tree_rule"] = other
+    result["kv_commit"] = commit
     if not args.no_cpu_baseline:
         base, ok, err = cpu_baseline(case, got)
         result["cpu_baseline"] = base

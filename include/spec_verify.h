@@ -133,6 +133,18 @@ typedef struct spec_verify_outputs {
     int32_t* row_token;            /* [B,T]: best token of target row v (smallest id on ties) */
 } spec_verify_outputs;
 
+/* Arguments of spec_verify_commit (device pointers; B = batch, T = nodes). */
+typedef struct spec_verify_commit_args {
+    void* k_cache;              /* [B,Hkv,Lcap,D] dtype, 16-byte aligned: updated in place            */
+    void* v_cache;              /* [B,Hkv,Lcap,D] dtype, 16-byte aligned: updated in place            */
+    int32_t* kv_len;            /* [B] in: L_b; out: L_b + accept_len[b] + 1 (unchanged if skipped)    */
+    const int32_t* path;        /* [B,T] root..v* node ids then -1 (spec_verify_run's output)          */
+    const int32_t* accept_len;  /* [B] (spec_verify_run's output)                                     */
+    const int32_t* final_node;  /* [B] (spec_verify_run's output; < 0 = void sequence, skipped)        */
+    int32_t batch;              /* B: 1..max_batch                                                    */
+    int32_t nodes;              /* T: 1..max_nodes, the T of the run                                  */
+} spec_verify_commit_args;
+
 typedef struct spec_verify_handle spec_verify_handle;
 
 /* Validate cfg, size and allocate the workspace on the current HIP device.
@@ -148,6 +160,20 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out);
  * sampling mode), HIP (launch failure). */
 int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in,
                     const spec_verify_outputs* out, void* stream);
+
+/* Enqueue the KV commit of the accepted paths on `stream`: for every sequence,
+ * slot L_b+k of both caches (all KV heads) receives tree node path[b,k]
+ * (k = 1..accept_len[b]; the root already sits at slot L_b) and kv_len[b]
+ * becomes L_b + accept_len[b] + 1.  The caches are preallocated per sequence,
+ * so rolling back the rejected nodes is the new length alone (featured
+ * article on the founding speculative-decoding paper, section 4.3;
+ * "大模型推理加速：推测解码与MTP核心原理与工程实践", section 3.1 item 4 and
+ * section 6.3).  A sequence is skipped (caches and kv_len unchanged) when it
+ * is void (final_node < 0), L_b + T > Lcap, or path is not a root path
+ * (path[0] = 0, k <= path[k] < T).  Asynchronous; allocates nothing.
+ * Errors: INVALID_ARG (NULL or misaligned pointer, B or T out of range),
+ * HIP (launch failure). */
+int spec_verify_commit(spec_verify_handle* h, const spec_verify_commit_args* args, void* stream);
 
 /* Free the workspace and the handle.  The caller's streams must be idle. */
 int spec_verify_destroy(spec_verify_handle* h);

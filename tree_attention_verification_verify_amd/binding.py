@@ -31,7 +31,7 @@ SPEC_VERIFY_NUM_STAGES = 3
 STAGES = ("attention", "vocab", "finish")
 
 EXPORTED = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
-            "spec_verify_timing_read")
+            "spec_verify_timing_read", "spec_verify_commit")
 
 
 class SpecVerifyError(RuntimeError):
@@ -53,6 +53,12 @@ class Inputs(ctypes.Structure):
                 ("kv_len", ctypes.c_void_p), ("parent", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
                 ("target_logits", ctypes.c_void_p), ("draft_logits", ctypes.c_void_p),
                 ("u_accept", ctypes.c_void_p), ("u_final", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("nodes", ctypes.c_int32)]
+
+
+class CommitArgs(ctypes.Structure):
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("kv_len", ctypes.c_void_p),
+                ("path", ctypes.c_void_p), ("accept_len", ctypes.c_void_p), ("final_node", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("nodes", ctypes.c_int32)]
 
 
@@ -86,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_timing_read.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
                                             ctypes.POINTER(ctypes.c_int32)]
     lib.spec_verify_timing_read.restype = ctypes.c_int
+    lib.spec_verify_commit.argtypes = [ctypes.c_void_p, ctypes.POINTER(CommitArgs), ctypes.c_void_p]
+    lib.spec_verify_commit.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -139,6 +147,22 @@ def spec_verify_run(handle, inputs: Dict, outputs: Dict, stream=None) -> None:
     _check(load_library().spec_verify_run(handle, ctypes.byref(i), ctypes.byref(o), ctypes.c_void_p(stream)))
 
 
+def _stream_handle(stream):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def spec_verify_commit(handle, k_cache, v_cache, kv_len, path, accept_len, final_node, stream=None) -> None:
+    """KV commit of the accepted paths (device tensors; kv_len is updated in place)."""
+    B, T = path.shape
+    a = CommitArgs(_ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(path), _ptr(accept_len), _ptr(final_node),
+                   B, T)
+    _check(load_library().spec_verify_commit(handle, ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
+
+
 def spec_verify_timing_read(handle):
     """Summed per-stage kernel milliseconds over the runs since the last read, and the run count."""
     ms = (ctypes.c_float * SPEC_VERIFY_NUM_STAGES)()
@@ -181,6 +205,9 @@ class SpecVerify:
 
     def timing_read(self):
         return spec_verify_timing_read(self.handle)
+
+    def commit(self, k_cache, v_cache, kv_len, path, accept_len, final_node, stream=None) -> None:
+        spec_verify_commit(self.handle, k_cache, v_cache, kv_len, path, accept_len, final_node, stream)
 
     def close(self) -> None:
         if self.handle is not None:

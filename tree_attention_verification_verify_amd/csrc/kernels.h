@@ -75,6 +75,18 @@ struct SelectParams {
     float ilog;
 };
 
+struct CommitParams {
+    void* k;                 // [B,Hkv,Lcap,D] updated in place
+    void* v;
+    const int32_t* kv_len;   // [B] L before the commit
+    int32_t* kv_len_out;     // [B] L + accept_len + 1 (may be kv_len itself)
+    const int32_t* path;     // [B,T]
+    const int32_t* accept_len;
+    const int32_t* final_node;
+    int B, T, Hkv, Lcap;
+    int row_bytes;           // D * element size (a multiple of 16)
+};
+
 // Returns hipSuccess or the launch error.
 hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s);
 hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
@@ -85,6 +97,8 @@ hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool sele
                          hipStream_t s);
 // Lossless sibling walk (sampling mode, SPEC_VERIFY_FLAG_LOSSLESS_TREE): one workgroup per sequence.
 hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s);
+// KV commit of the accepted path: one workgroup per sequence.
+hipError_t launch_kv_commit(const CommitParams& p, hipStream_t s);
 
 constexpr int kValuRows = 16;      // rows per block of the VALU attention kernel
 constexpr int kVocabThreads = 1024;               // register-resident row kernels

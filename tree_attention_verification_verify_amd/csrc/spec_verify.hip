@@ -351,6 +351,38 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     return SPEC_VERIFY_OK;
 }
 
+int spec_verify_commit(spec_verify_handle* h, const spec_verify_commit_args* a, void* stream) {
+    g_err.clear();
+    if (!h || !a) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle and args must be non-NULL");
+    const spec_verify_config& c = h->cfg;
+    if (a->batch < 1 || a->batch > c.max_batch) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "batch out of range");
+    if (a->nodes < 1 || a->nodes > c.max_nodes) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes out of range");
+    if (!a->k_cache || !a->v_cache || !a->kv_len || !a->path || !a->accept_len || !a->final_node)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "a commit pointer is NULL");
+    auto misaligned = [](const void* ptr, uintptr_t al) { return (((uintptr_t)ptr) & (al - 1)) != 0; };
+    if (misaligned(a->k_cache, 16) || misaligned(a->v_cache, 16))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    if (misaligned(a->kv_len, 4) || misaligned(a->path, 4) || misaligned(a->accept_len, 4) ||
+        misaligned(a->final_node, 4))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "arrays must be aligned to their element size");
+    sv::CommitParams cp{};
+    cp.k = a->k_cache;
+    cp.v = a->v_cache;
+    cp.kv_len = a->kv_len;
+    cp.kv_len_out = a->kv_len;
+    cp.path = a->path;
+    cp.accept_len = a->accept_len;
+    cp.final_node = a->final_node;
+    cp.B = a->batch;
+    cp.T = a->nodes;
+    cp.Hkv = c.num_kv_heads;
+    cp.Lcap = c.kv_capacity;
+    cp.row_bytes = c.head_dim * (c.dtype == SPEC_VERIFY_BF16 ? 2 : 4);
+    const hipError_t e = sv::launch_kv_commit(cp, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "commit launch");
+    return SPEC_VERIFY_OK;
+}
+
 int spec_verify_timing_read(spec_verify_handle* h, float* stage_ms, int32_t* runs) {
     g_err.clear();
     if (!h || !stage_ms || !runs) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "NULL argument");
