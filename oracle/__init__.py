@@ -26,6 +26,7 @@ from .verify import (NEAR_TIE, TOPP_NEAR_TIE, accept_and_select, row_distributio
                      widen)
 from .lossless import lossless_walk
 from .commit import commit_kv
+from .paged import commit_kv_paged, gather_slots, kv_valid, pages_valid, slot_page_row, verify_paged
 
 __all__ = [
     "ancestors", "check_parent", "depths", "tree_mask",
@@ -33,4 +34,5 @@ __all__ = [
     "argmax_first", "effective_distribution", "inverse_cdf", "inverse_cdf_rows", "nucleus_margin",
     "NEAR_TIE", "TOPP_NEAR_TIE", "accept_and_select", "row_distributions", "verify", "verify_vocab", "widen",
     "lossless_walk", "commit_kv",
+    "commit_kv_paged", "gather_slots", "kv_valid", "pages_valid", "slot_page_row", "verify_paged",
 ]
