@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lossless-tree", action="store_true",
                     help="time the lossless sibling walk (SPEC_VERIFY_FLAG_LOSSLESS_TREE) as the value")
+    ap.add_argument("--paged-block-size", type=int, default=16,
+                    help="also time the step with the caches read through a block table of pages of this "
+                         "many slots (spec_verify_run_paged); 0 = skip")
     ap.add_argument("--traffic-summary", nargs=5, default=None,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES"),
                     help="write profiles/traffic_<kernel>_<workload>.json from rocprofv3 --pmc counter CSVs")
@@ -85,8 +88,9 @@ def measured_traffic(stage, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, got, nseq=2):
-    """The oracle, as it stands, on the first `nseq` sequences of the same workload.
+def cpu_baseline(case, got, min_seconds=10.0):
+    """The oracle, as it stands, on the first sequences of the same workload:
+    one sequence at a time until `min_seconds` of CPU work or the whole batch.
 
     Also a parity spot check of those sequences against the GPU run.
     """
@@ -99,10 +103,13 @@ def cpu_baseline(case, got, nseq=2):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    seqs = list(range(min(nseq, case.parent.shape[0])))
-    t0 = time.perf_counter()
-    ref = oracle.verify(case, attention=True, seqs=seqs)
-    dt = time.perf_counter() - t0
+    seqs, parts, dt = [], [], 0.0
+    while len(seqs) < case.parent.shape[0] and dt < min_seconds:
+        t0 = time.perf_counter()
+        parts.append(oracle.verify(case, attention=True, seqs=[len(seqs)]))
+        dt += time.perf_counter() - t0
+        seqs.append(len(seqs))
+    ref = {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
     T = case.parent.shape[1]
     ok = True
     err = 0.0
@@ -325,6 +332,43 @@ def main():
     torch.cuda.synchronize()
     got = {k: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy() for k, v in outs.items()}
 
+    # the same step with the caches read through a block table: pages of the
+    # given size scattered over a pool in random order (spec_verify_run_paged)
+    paged = None
+    if args.paged_block_size:
+        from tree_attention_verification_verify_amd import paged_kv
+
+        _, pg = synth.page_case(case, args.paged_block_size, seed=(1,))
+        pool_k, pool_v, table = up(pg.k_pool, spec.dtype), up(pg.v_pool, spec.dtype), up(pg.block_table)
+        pk = paged_kv(pool_k, pool_v, table)
+        pins = {k: v for k, v in ins.items() if k not in ("k_cache", "v_cache")}
+        pcfg = dict(cfg, kv_capacity=max(cfg["kv_capacity"], pg.capacity))
+        pouts = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
+        with SpecVerify(timing=True, **pcfg) as sv:
+            for _ in range(args.warmup):
+                sv.run_paged(pins, pk, pouts, stream)
+            torch.cuda.synchronize()
+            sv.timing_read()
+            for _ in range(args.steps):
+                sv.run_paged(pins, pk, pouts, stream)
+            torch.cuda.synchronize()
+            pms, pn = sv.timing_read()
+        with SpecVerify(timing=False, **pcfg) as sv:
+            for _ in range(args.warmup):
+                sv.run_paged(pins, pk, pouts, stream)
+            torch.cuda.synchronize()
+            t4 = time.perf_counter()
+            for _ in range(args.steps):
+                sv.run_paged(pins, pk, pouts, stream)
+            torch.cuda.synchronize()
+            pms_step = (time.perf_counter() - t4) * 1e3 / args.steps
+        same = all(bool(torch.equal(pouts[k], outs[k])) for k in outs)
+        paged = {"block_size": args.paged_block_size, "pages": int(pg.num_blocks),
+                 "value": B * T / (pms_step * 1e-3), "ms_per_step": pms_step,
+                 "stage_ms_per_launch": {k: v / max(pn, 1) for k, v in pms.items()},
+                 "outputs_equal_dense": same}
+        del pool_k, pool_v, table
+
     workload = "%s-%s" % (args.workload, spec.mode)
     # dominant kernel by measured time
     dominant = max(("attention", "vocab"), key=lambda k: per_launch[k])
@@ -378,6 +422,8 @@ def main():
     if other is not None:
         result["other_tree_rule"] = other
     result["kv_commit"] = commit
+    if paged is not None:
+        result["paged_kv"] = paged
     if not args.no_cpu_baseline:
         base, ok, err = cpu_baseline(case, got)
         result["cpu_baseline"] = base

@@ -145,6 +145,30 @@ typedef struct spec_verify_commit_args {
     int32_t nodes;              /* T: 1..max_nodes, the T of the run                                  */
 } spec_verify_commit_args;
 
+/* A paged KV cache: the slots of every sequence live in pages of a shared
+ * pool, found through a per-sequence block table ("大模型推理加速：推测解码与
+ * MTP核心原理与工程实践", section 4.2 on the candidates' KV memory and section
+ * 6.3: speculative KV is held in pages and released page by page).  Slot s of
+ * sequence b (prefix 0..L_b-1, tree node i at L_b+i, as in the dense cache) is
+ * row s % block_size of page block_table[b, s / block_size] of each pool.  The
+ * slots a sequence can address are table_width * block_size; pages may be
+ * shared between sequences (a common prefix): runs only read them, a commit
+ * writes slots L_b..L_b+accept_len, which the caller keeps in pages of that
+ * sequence alone.  Table entries past a sequence's slots in use are never read.
+ * A sequence whose entries for slots 0..L_b+T-1 are not all in
+ * [0, num_blocks), or whose L_b + T exceeds its slots, gets status bit
+ * SPEC_VERIFY_STATUS_BAD_KVLEN and zero attention output (its decisions are
+ * taken as usual). */
+typedef struct spec_verify_paged_kv {
+    void* k_pool;               /* [num_blocks,Hkv,block_size,D] dtype, 16-byte aligned    */
+    void* v_pool;               /* [num_blocks,Hkv,block_size,D] dtype, 16-byte aligned    */
+    const int32_t* block_table; /* [B,table_width]: page of slots j*block_size..+block_size-1 */
+    int32_t num_blocks;         /* pages in each pool, >= 1                                 */
+    int32_t block_size;         /* slots per page: a power of two in [16, 65536]            */
+    int32_t table_width;        /* entries per sequence, >= 1;
+                                   table_width * block_size <= config.kv_capacity          */
+} spec_verify_paged_kv;
+
 typedef struct spec_verify_handle spec_verify_handle;
 
 /* Validate cfg, size and allocate the workspace on the current HIP device.
@@ -174,6 +198,26 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in,
  * Errors: INVALID_ARG (NULL or misaligned pointer, B or T out of range),
  * HIP (launch failure). */
 int spec_verify_commit(spec_verify_handle* h, const spec_verify_commit_args* args, void* stream);
+
+/* spec_verify_run with the caches read through a block table: in->k_cache and
+ * in->v_cache are ignored, the keys and values of every slot come from
+ * paged->k_pool / v_pool (only read).  Every output is the one spec_verify_run
+ * gives for the dense caches holding the same slots.  Errors: as
+ * spec_verify_run, and INVALID_ARG for a NULL or misaligned pool or table, a
+ * block_size that is not a power of two in [16, 65536], or table_width *
+ * block_size > config.kv_capacity. */
+int spec_verify_run_paged(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_paged_kv* paged,
+                          const spec_verify_outputs* out, void* stream);
+
+/* spec_verify_commit through a block table: args->k_cache and args->v_cache
+ * are ignored; slot L_b+k (k = 1..accept_len[b]) of the pools receives tree
+ * node path[b,k]'s row, every KV head, and kv_len[b] becomes
+ * L_b + accept_len[b] + 1.  Skipped sequences as spec_verify_commit, and also
+ * those whose entries for slots 0..L_b+T-1 leave the pool.  The written slots
+ * must not lie in pages another sequence of the batch reads or writes.
+ * Errors: as spec_verify_commit, and the paged checks of spec_verify_run_paged. */
+int spec_verify_commit_paged(spec_verify_handle* h, const spec_verify_commit_args* args,
+                             const spec_verify_paged_kv* paged, void* stream);
 
 /* Free the workspace and the handle.  The caller's streams must be idle. */
 int spec_verify_destroy(spec_verify_handle* h);

@@ -38,6 +38,7 @@ def test_struct_layouts_match_the_header():
     assert ctypes.sizeof(binding.Inputs) == 10 * 8 + 2 * 4
     assert ctypes.sizeof(binding.Outputs) == 11 * 8
     assert ctypes.sizeof(binding.CommitArgs) == 6 * 8 + 2 * 4
+    assert ctypes.sizeof(binding.PagedKV) == 3 * 8 + 3 * 4 + 4   # padded to pointer alignment
 
 
 GOOD = dict(max_batch=2, max_nodes=8, num_q_heads=8, num_kv_heads=2, head_dim=128, kv_capacity=256,
@@ -90,6 +91,8 @@ def test_null_arguments():
     assert lib.spec_verify_run(None, None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
     assert lib.spec_verify_destroy(None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
     assert lib.spec_verify_commit(None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
+    assert lib.spec_verify_run_paged(None, None, None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
+    assert lib.spec_verify_commit_paged(None, None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
     ms = (ctypes.c_float * 4)()
     n = ctypes.c_int32()
     assert lib.spec_verify_timing_read(None, ms, ctypes.byref(n)) == binding.SPEC_VERIFY_ERR_INVALID_ARG

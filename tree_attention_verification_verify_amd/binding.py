@@ -1,7 +1,8 @@
 """ctypes binding of libspecverify.so: argument marshalling only.
 
 The functions mirror the C ABI in include/spec_verify.h one to one
-(spec_verify_create / spec_verify_run / spec_verify_destroy /
+(spec_verify_create / spec_verify_run / spec_verify_run_paged /
+spec_verify_commit / spec_verify_commit_paged / spec_verify_destroy /
 spec_verify_last_error / spec_verify_timing_read).  Tensors are PyTorch device
 tensors; only their data pointers cross the boundary.  Every step of the
 verify step runs in the library's HIP kernels: there is no fallback, and a
@@ -31,7 +32,7 @@ SPEC_VERIFY_NUM_STAGES = 3
 STAGES = ("attention", "vocab", "finish")
 
 EXPORTED = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
-            "spec_verify_timing_read", "spec_verify_commit")
+            "spec_verify_timing_read", "spec_verify_commit", "spec_verify_run_paged", "spec_verify_commit_paged")
 
 
 class SpecVerifyError(RuntimeError):
@@ -60,6 +61,11 @@ class CommitArgs(ctypes.Structure):
     _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("kv_len", ctypes.c_void_p),
                 ("path", ctypes.c_void_p), ("accept_len", ctypes.c_void_p), ("final_node", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("nodes", ctypes.c_int32)]
+
+
+class PagedKV(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("table_width", ctypes.c_int32)]
 
 
 class Outputs(ctypes.Structure):
@@ -94,6 +100,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_timing_read.restype = ctypes.c_int
     lib.spec_verify_commit.argtypes = [ctypes.c_void_p, ctypes.POINTER(CommitArgs), ctypes.c_void_p]
     lib.spec_verify_commit.restype = ctypes.c_int
+    lib.spec_verify_run_paged.argtypes = [ctypes.c_void_p, ctypes.POINTER(Inputs), ctypes.POINTER(PagedKV),
+                                          ctypes.POINTER(Outputs), ctypes.c_void_p]
+    lib.spec_verify_run_paged.restype = ctypes.c_int
+    lib.spec_verify_commit_paged.argtypes = [ctypes.c_void_p, ctypes.POINTER(CommitArgs), ctypes.POINTER(PagedKV),
+                                             ctypes.c_void_p]
+    lib.spec_verify_commit_paged.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -131,20 +143,36 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _inputs(inputs: Dict) -> Inputs:
+    B, T = inputs["parent"].shape
+    return Inputs(_ptr(inputs.get("q")), _ptr(inputs.get("k_cache")), _ptr(inputs.get("v_cache")),
+                  _ptr(inputs["kv_len"]), _ptr(inputs["parent"]), _ptr(inputs["tokens"]),
+                  _ptr(inputs["target_logits"]), _ptr(inputs.get("draft_logits")), _ptr(inputs["u_accept"]),
+                  _ptr(inputs["u_final"]), B, T)
+
+
+def _outputs(outputs: Dict) -> Outputs:
+    return Outputs(*[_ptr(outputs[f]) for f, _ in Outputs._fields_])
+
+
+def paged_kv(k_pool, v_pool, block_table) -> PagedKV:
+    """PagedKV from pools [num_blocks, Hkv, block_size, D] and a table [B, width] (device tensors)."""
+    nb, _, bs, _ = k_pool.shape
+    return PagedKV(_ptr(k_pool), _ptr(v_pool), _ptr(block_table), nb, bs, block_table.shape[1])
+
+
 def spec_verify_run(handle, inputs: Dict, outputs: Dict, stream=None) -> None:
     """inputs/outputs: dicts of device tensors named as the C struct fields."""
-    import torch
+    i, o = _inputs(inputs), _outputs(outputs)
+    _check(load_library().spec_verify_run(handle, ctypes.byref(i), ctypes.byref(o),
+                                          ctypes.c_void_p(_stream_handle(stream))))
 
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
-    B, T = inputs["parent"].shape
-    i = Inputs(_ptr(inputs["q"]), _ptr(inputs["k_cache"]), _ptr(inputs["v_cache"]), _ptr(inputs["kv_len"]),
-               _ptr(inputs["parent"]), _ptr(inputs["tokens"]), _ptr(inputs["target_logits"]),
-               _ptr(inputs.get("draft_logits")), _ptr(inputs["u_accept"]), _ptr(inputs["u_final"]), B, T)
-    o = Outputs(*[_ptr(outputs[f]) for f, _ in Outputs._fields_])
-    _check(load_library().spec_verify_run(handle, ctypes.byref(i), ctypes.byref(o), ctypes.c_void_p(stream)))
+
+def spec_verify_run_paged(handle, inputs: Dict, paged: PagedKV, outputs: Dict, stream=None) -> None:
+    """spec_verify_run with the caches read through a block table (inputs' k_cache/v_cache unused)."""
+    i, o = _inputs(inputs), _outputs(outputs)
+    _check(load_library().spec_verify_run_paged(handle, ctypes.byref(i), ctypes.byref(paged), ctypes.byref(o),
+                                                ctypes.c_void_p(_stream_handle(stream))))
 
 
 def _stream_handle(stream):
@@ -161,6 +189,14 @@ def spec_verify_commit(handle, k_cache, v_cache, kv_len, path, accept_len, final
     a = CommitArgs(_ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(path), _ptr(accept_len), _ptr(final_node),
                    B, T)
     _check(load_library().spec_verify_commit(handle, ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
+
+
+def spec_verify_commit_paged(handle, paged: PagedKV, kv_len, path, accept_len, final_node, stream=None) -> None:
+    """KV commit through a block table (the pools in `paged` and kv_len are updated in place)."""
+    B, T = path.shape
+    a = CommitArgs(None, None, _ptr(kv_len), _ptr(path), _ptr(accept_len), _ptr(final_node), B, T)
+    _check(load_library().spec_verify_commit_paged(handle, ctypes.byref(a), ctypes.byref(paged),
+                                                   ctypes.c_void_p(_stream_handle(stream))))
 
 
 def spec_verify_timing_read(handle):
@@ -203,11 +239,17 @@ class SpecVerify:
     def run(self, inputs: Dict, outputs: Dict, stream=None) -> None:
         spec_verify_run(self.handle, inputs, outputs, stream)
 
+    def run_paged(self, inputs: Dict, paged: PagedKV, outputs: Dict, stream=None) -> None:
+        spec_verify_run_paged(self.handle, inputs, paged, outputs, stream)
+
     def timing_read(self):
         return spec_verify_timing_read(self.handle)
 
     def commit(self, k_cache, v_cache, kv_len, path, accept_len, final_node, stream=None) -> None:
         spec_verify_commit(self.handle, k_cache, v_cache, kv_len, path, accept_len, final_node, stream)
+
+    def commit_paged(self, paged: PagedKV, kv_len, path, accept_len, final_node, stream=None) -> None:
+        spec_verify_commit_paged(self.handle, paged, kv_len, path, accept_len, final_node, stream)
 
     def close(self) -> None:
         if self.handle is not None:

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace sv {
 
 constexpr int kWave = 64;
@@ -83,6 +85,24 @@ __device__ __forceinline__ unsigned long long ancestor_mask(const int32_t* paren
     }
     *bad = __any(invalid);
     return a;
+}
+
+// Paged caches: whether some block-table entry of sequence b's slots
+// 0..n_slots-1 lies outside the pool, for the entries j = first, first + step,
+// ... this thread checks (the caller combines the threads' answers).  The
+// caller has checked n_slots <= width << bs_log2, so the row is not overrun.
+// Dense caches (no table): false.
+__device__ __forceinline__ bool page_entries_bad(const PageTable& pt, int b, int n_slots, int first, int step) {
+    if (!pt.table) return false;
+    const int used = (n_slots + (1 << pt.bs_log2) - 1) >> pt.bs_log2;
+    const int32_t* row = pt.table + (size_t)b * pt.width;
+    bool bad = false;
+#pragma unroll 8
+    for (int j = first; j < used; j += step) {
+        const int e = row[j];
+        bad |= (e < 0) | (e >= pt.num_blocks);
+    }
+    return bad;
 }
 
 }  // namespace sv

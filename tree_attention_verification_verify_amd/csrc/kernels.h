@@ -6,6 +6,16 @@
 
 namespace sv {
 
+// Block table of a paged KV cache (table == nullptr: dense caches).  Slot s of
+// sequence b is row s & (bs - 1) of page table[b * width + (s >> bs_log2)];
+// a page holds bs slots of every KV head: [pages][Hkv][bs][D].
+struct PageTable {
+    const int32_t* table;
+    int width;          // entries per sequence
+    int bs_log2;        // log2 of the slots per page
+    int num_blocks;     // pages in the pool
+};
+
 // Tree attention over the prefix split into `nsplit` key ranges of `chunk`
 // keys.  Rows of one (sequence, KV head) pair are r = node * g + (h % g).
 struct AttnParams {
@@ -25,6 +35,7 @@ struct AttnParams {
     int chunk;          // keys per split (multiple of 64)
     int groups_per_xcd; // XCD-aware block mapping (mfma path with rowblocks > 1)
     float c;            // softmax_scale * log2(e)
+    PageTable pt;       // paged caches: k, v are the pools; Lcap = pt.width << pt.bs_log2
 };
 
 // Statistics of one logits row under temperature (and top-p).
@@ -73,6 +84,7 @@ struct SelectParams {
     int S;                // slices per sequence: ceil(V / kSelectSlice)
     int sampling;
     float ilog;
+    PageTable pt;         // paged caches: table entries of the used slots count for status bit 8
 };
 
 struct CommitParams {
@@ -85,6 +97,7 @@ struct CommitParams {
     const int32_t* final_node;
     int B, T, Hkv, Lcap;
     int row_bytes;           // D * element size (a multiple of 16)
+    PageTable pt;            // paged caches: k, v are the pools; Lcap = pt.width << pt.bs_log2
 };
 
 // Returns hipSuccess or the launch error.

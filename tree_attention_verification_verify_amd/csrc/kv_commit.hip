@@ -15,6 +15,10 @@
 // moved rows (K and V) is loaded into registers before any is stored, since a
 // destination slot may be the source of an earlier row; rows already in
 // place are skipped.
+//
+// Paged caches: slot s lives in row s % bs of page table[s / bs]; a dense
+// cache is addressed the same way as one page of Lcap slots per sequence
+// (page b).  A sequence whose used table entries leave the pool is skipped.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -29,6 +33,7 @@ constexpr int MAXC = (2 * 63 * 32 + CT - 1) / CT;   // chunks per thread: K and 
 
 __global__ __launch_bounds__(CT) void kv_commit_kernel(CommitParams P) {
     __shared__ int src[64];
+    __shared__ size_t off_src[64], off_dst[64];   // byte offset of row k's source / destination slot, head 0
     __shared__ int sL, sA, sok;
     const int b = blockIdx.x, tid = threadIdx.x;
     const int T = P.T;
@@ -39,7 +44,18 @@ __global__ __launch_bounds__(CT) void kv_commit_kernel(CommitParams P) {
         bool ok = P.final_node[b] >= 0 && L >= 0 && L <= P.Lcap - T && A >= 0 && A < T;
         const bool bad = (lane == 0 && p != 0) || (lane >= 1 && lane <= A && !(lane <= p && p < T));
         ok = ok && !__any(bad);
+        ok = ok && !__any(page_entries_bad(P.pt, b, L + T, lane, kWave));
         src[lane] = p;
+        if (ok && lane >= 1 && lane <= A) {
+            auto slot_off = [&](int slot) -> size_t {
+                if (!P.pt.table) return ((size_t)b * P.Hkv * P.Lcap + slot) * P.row_bytes;
+                const int page = P.pt.table[(size_t)b * P.pt.width + (slot >> P.pt.bs_log2)];
+                return (((size_t)page * P.Hkv << P.pt.bs_log2) + (slot & ((1 << P.pt.bs_log2) - 1))) *
+                       P.row_bytes;
+            };
+            off_src[lane] = slot_off(L + p);
+            off_dst[lane] = slot_off(L + lane);
+        }
         if (lane == 0) {
             sL = L;
             sA = A;
@@ -51,8 +67,9 @@ __global__ __launch_bounds__(CT) void kv_commit_kernel(CommitParams P) {
     const int L = sL, A = sA;
     const int cpr = P.row_bytes / 16;             // chunks per row
     const int total = 2 * A * cpr;                 // K and V chunks of rows 1..A
+    const size_t head_stride = (size_t)(P.pt.table ? (1 << P.pt.bs_log2) : P.Lcap) * P.row_bytes;
     for (int h = 0; h < P.Hkv; ++h) {
-        const size_t head = ((size_t)b * P.Hkv + h) * P.Lcap;
+        const size_t head = (size_t)h * head_stride;
         u32x4 reg[MAXC];
 #pragma unroll
         for (int m = 0; m < MAXC; ++m) {
@@ -62,7 +79,7 @@ __global__ __launch_bounds__(CT) void kv_commit_kernel(CommitParams P) {
                 const int k = 1 + rest / cpr, c = rest - (k - 1) * cpr;
                 if (src[k] != k) {
                     const uint8_t* base = (const uint8_t*)(kv ? P.v : P.k);
-                    reg[m] = *(const u32x4*)(base + (head + L + src[k]) * P.row_bytes + c * 16);
+                    reg[m] = *(const u32x4*)(base + head + off_src[k] + c * 16);
                 }
             }
         }
@@ -75,7 +92,7 @@ __global__ __launch_bounds__(CT) void kv_commit_kernel(CommitParams P) {
                 const int k = 1 + rest / cpr, c = rest - (k - 1) * cpr;
                 if (src[k] != k) {
                     uint8_t* base = (uint8_t*)(kv ? P.v : P.k);
-                    *(u32x4*)(base + (head + L + k) * P.row_bytes + c * 16) = reg[m];
+                    *(u32x4*)(base + head + off_dst[k] + c * 16) = reg[m];
                 }
             }
         }

@@ -193,7 +193,8 @@ __global__ __launch_bounds__(NT) void lossless_walk_kernel(SelectParams P) {
         const int tok = live ? P.tokens[base + lane] : 0;
         const bool bad_token = __any(live && lane >= 1 && (tok < 0 || tok >= V));
         const int L = P.kv_len[b];
-        const bool bad_kv = (L < 0) || (L > P.Lcap - T);
+        bool bad_kv = (L < 0) || (L > P.Lcap - T);
+        bad_kv = bad_kv || __any(page_entries_bad(P.pt, b, L + T, lane, kWave));   // paged: L + T <= Lcap here
         int status = (bad_parent ? 1 : 0) | (bad_token ? 2 : 0) | (bad_kv ? 8 : 0);
         if (live) P.row_token[base + lane] = st[lane].argmax;
         if (live) {

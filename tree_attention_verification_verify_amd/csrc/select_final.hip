@@ -65,7 +65,9 @@ __device__ void decide(const SelectParams& P, int b, bool write, SelectShared& s
     const int tok = live ? P.tokens[base + lane] : 0;
     const bool bad_token = __any(live && lane >= 1 && (tok < 0 || tok >= V));
     const int L = P.kv_len[b];
-    const bool bad_kv = (L < 0) || (L > P.Lcap - T);
+    bool bad_kv = (L < 0) || (L > P.Lcap - T);
+    // paged caches: table entries of the used slots (L + T <= Lcap here); only the status needs it
+    bad_kv = bad_kv || (write && __any(page_entries_bad(P.pt, b, L + T, lane, kWave)));
     int status = (bad_parent ? 1 : 0) | (bad_token ? 2 : 0) | (bad_kv ? 8 : 0);
     if (write && live) P.row_token[base + lane] = st[lane].argmax;
 

@@ -83,6 +83,32 @@ AttnPlan plan_attention(const spec_verify_config& c, int B, int T) {
     return p;
 }
 
+// Checks of a paged cache description against the config; fills pt and the
+// slots a sequence can address.  SPEC_VERIFY_OK or INVALID_ARG.
+int check_paged(const spec_verify_config& c, const spec_verify_paged_kv* pg, sv::PageTable* pt, int* slots) {
+    if (!pg) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "paged is NULL");
+    if (!pg->k_pool || !pg->v_pool || !pg->block_table)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "k_pool, v_pool and block_table must be non-NULL");
+    if ((((uintptr_t)pg->k_pool) & 15u) || (((uintptr_t)pg->v_pool) & 15u))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "k_pool and v_pool must be 16-byte aligned");
+    if (((uintptr_t)pg->block_table) & 3u) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    if (pg->num_blocks < 1) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "num_blocks must be >= 1");
+    const int bs = pg->block_size;
+    if (bs < 16 || bs > 65536 || (bs & (bs - 1)) != 0)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "block_size must be a power of two in [16, 65536]");
+    if (pg->table_width < 1) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "table_width must be >= 1");
+    if ((long long)pg->table_width * bs > c.kv_capacity)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "table_width * block_size exceeds kv_capacity");
+    int lg = 0;
+    while ((1 << lg) < bs) ++lg;
+    pt->table = pg->block_table;
+    pt->width = pg->table_width;
+    pt->bs_log2 = lg;
+    pt->num_blocks = pg->num_blocks;
+    *slots = pg->table_width * bs;
+    return SPEC_VERIFY_OK;
+}
+
 }  // namespace
 
 struct spec_verify_handle {
@@ -218,16 +244,29 @@ int spec_verify_destroy(spec_verify_handle* h) {
     return SPEC_VERIFY_OK;
 }
 
-int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_outputs* out,
-                    void* stream) {
-    g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// One verify step; paged == nullptr reads the dense caches of `in`.
+int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_paged_kv* paged,
+             const spec_verify_outputs* out, void* stream) {
     if (!h || !in || !out) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle, inputs and outputs must be non-NULL");
     const spec_verify_config& c = h->cfg;
     const int B = in->batch, T = in->nodes;
     if (B < 1 || B > c.max_batch) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "batch out of range");
     if (T < 1 || T > c.max_nodes) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes out of range");
     const bool sampling = c.mode == SPEC_VERIFY_SAMPLING;
-    if (!in->q || !in->k_cache || !in->v_cache || !in->kv_len || !in->parent || !in->tokens ||
+    sv::PageTable pt{};
+    int slots = c.kv_capacity;
+    const void* kc = in->k_cache;
+    const void* vc = in->v_cache;
+    if (paged) {
+        if (int rc = check_paged(c, paged, &pt, &slots)) return rc;
+        kc = paged->k_pool;
+        vc = paged->v_pool;
+    }
+    if (!in->q || !kc || !vc || !in->kv_len || !in->parent || !in->tokens ||
         !in->target_logits || !in->u_accept || !in->u_final)
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an input pointer is NULL");
     if (sampling && !in->draft_logits) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "draft_logits is NULL in sampling mode");
@@ -235,8 +274,7 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
         !out->node_p || !out->node_q || !out->node_accept || !out->final_from_residual || !out->row_token)
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an output pointer is NULL");
     auto misaligned = [](const void* ptr, uintptr_t a) { return (((uintptr_t)ptr) & (a - 1)) != 0; };
-    if (misaligned(in->q, 16) || misaligned(in->k_cache, 16) || misaligned(in->v_cache, 16) ||
-        misaligned(out->attn_out, 16))
+    if (misaligned(in->q, 16) || misaligned(kc, 16) || misaligned(vc, 16) || misaligned(out->attn_out, 16))
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "q, k_cache, v_cache and attn_out must be 16-byte aligned");
     if (misaligned(in->kv_len, 4) || misaligned(in->parent, 4) || misaligned(in->tokens, 4) ||
         misaligned(in->target_logits, 4) || (sampling && misaligned(in->draft_logits, 4)) ||
@@ -266,8 +304,8 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
 
     sv::AttnParams ap{};
     ap.q = in->q;
-    ap.k = in->k_cache;
-    ap.v = in->v_cache;
+    ap.k = kc;
+    ap.v = vc;
     ap.kv_len = in->kv_len;
     ap.parent = in->parent;
     ap.out = out->attn_out;
@@ -279,7 +317,8 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     ap.Hkv = c.num_kv_heads;
     ap.g = c.num_q_heads / c.num_kv_heads;
     ap.D = D;
-    ap.Lcap = c.kv_capacity;
+    ap.Lcap = slots;
+    ap.pt = pt;
     ap.R = ap.g * T;
     ap.Rpad = plan.Rpad;
     ap.rowblocks = plan.rowblocks;
@@ -328,7 +367,8 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     sp.B = B;
     sp.T = T;
     sp.V = c.vocab;
-    sp.Lcap = c.kv_capacity;
+    sp.Lcap = slots;
+    sp.pt = pt;
     sp.sampling = sampling ? 1 : 0;
     sp.ilog = tp.ilog;
     sp.slice_tot = h->slice_tot;
@@ -351,23 +391,33 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const s
     return SPEC_VERIFY_OK;
 }
 
-int spec_verify_commit(spec_verify_handle* h, const spec_verify_commit_args* a, void* stream) {
-    g_err.clear();
+// KV commit; paged == nullptr writes the dense caches of `a`.
+int commit_impl(spec_verify_handle* h, const spec_verify_commit_args* a, const spec_verify_paged_kv* paged,
+                void* stream) {
     if (!h || !a) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle and args must be non-NULL");
     const spec_verify_config& c = h->cfg;
     if (a->batch < 1 || a->batch > c.max_batch) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "batch out of range");
     if (a->nodes < 1 || a->nodes > c.max_nodes) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes out of range");
-    if (!a->k_cache || !a->v_cache || !a->kv_len || !a->path || !a->accept_len || !a->final_node)
+    sv::PageTable pt{};
+    int slots = c.kv_capacity;
+    void* kc = a->k_cache;
+    void* vc = a->v_cache;
+    if (paged) {
+        if (int rc = check_paged(c, paged, &pt, &slots)) return rc;
+        kc = paged->k_pool;
+        vc = paged->v_pool;
+    }
+    if (!kc || !vc || !a->kv_len || !a->path || !a->accept_len || !a->final_node)
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "a commit pointer is NULL");
     auto misaligned = [](const void* ptr, uintptr_t al) { return (((uintptr_t)ptr) & (al - 1)) != 0; };
-    if (misaligned(a->k_cache, 16) || misaligned(a->v_cache, 16))
+    if (misaligned(kc, 16) || misaligned(vc, 16))
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
     if (misaligned(a->kv_len, 4) || misaligned(a->path, 4) || misaligned(a->accept_len, 4) ||
         misaligned(a->final_node, 4))
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "arrays must be aligned to their element size");
     sv::CommitParams cp{};
-    cp.k = a->k_cache;
-    cp.v = a->v_cache;
+    cp.k = kc;
+    cp.v = vc;
     cp.kv_len = a->kv_len;
     cp.kv_len_out = a->kv_len;
     cp.path = a->path;
@@ -376,11 +426,41 @@ int spec_verify_commit(spec_verify_handle* h, const spec_verify_commit_args* a, 
     cp.B = a->batch;
     cp.T = a->nodes;
     cp.Hkv = c.num_kv_heads;
-    cp.Lcap = c.kv_capacity;
+    cp.Lcap = slots;
     cp.row_bytes = c.head_dim * (c.dtype == SPEC_VERIFY_BF16 ? 2 : 4);
+    cp.pt = pt;
     const hipError_t e = sv::launch_kv_commit(cp, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "commit launch");
     return SPEC_VERIFY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_outputs* out,
+                    void* stream) {
+    g_err.clear();
+    return run_impl(h, in, nullptr, out, stream);
+}
+
+int spec_verify_run_paged(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_paged_kv* paged,
+                          const spec_verify_outputs* out, void* stream) {
+    g_err.clear();
+    if (!paged) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "paged is NULL");
+    return run_impl(h, in, paged, out, stream);
+}
+
+int spec_verify_commit(spec_verify_handle* h, const spec_verify_commit_args* a, void* stream) {
+    g_err.clear();
+    return commit_impl(h, a, nullptr, stream);
+}
+
+int spec_verify_commit_paged(spec_verify_handle* h, const spec_verify_commit_args* a,
+                             const spec_verify_paged_kv* paged, void* stream) {
+    g_err.clear();
+    if (!paged) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "paged is NULL");
+    return commit_impl(h, a, paged, stream);
 }
 
 int spec_verify_timing_read(spec_verify_handle* h, float* stage_ms, int32_t* runs) {

@@ -61,7 +61,7 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
 
 constexpr float kLazyMax = 8.f;   // log2 headroom of the lazily raised softmax reference
 
-template <int D, int WAVES>
+template <int D, int WAVES, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) {
     constexpr int NSUB = 2;                 // 32-key sub-tiles per tile
     constexpr int KT = 32 * NSUB;           // keys per tile
@@ -94,8 +94,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     const int b = pair / P.Hkv, kvh = pair - b * P.Hkv;
     const int T = P.T, g = P.g;
     const int L = P.kv_len[b];
-    const bool kv_ok = (L >= 0) && (L <= P.Lcap - T);
+    bool kv_ok = (L >= 0) && (L <= P.Lcap - T);
     const int N = L + T;
+    if constexpr (PAGED) {   // every table entry of the used slots must name a page of the pool
+        const bool bad = kv_ok && page_entries_bad(P.pt, b, N, tid, WAVES * 64);
+        kv_ok = kv_ok && !__syncthreads_or(bad);
+    }
     const int k0 = split * P.chunk;
     const int k1 = min(N, k0 + P.chunk);
     const int qcol = lane & 31, half = lane >> 5;
@@ -134,9 +138,6 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
             qb[ks] = as_bf16x8(v);
         }
     }
-    const uint16_t* kbase = (const uint16_t*)P.k + (size_t)(b * P.Hkv + kvh) * P.Lcap * D;
-    const uint16_t* vbase = (const uint16_t*)P.v + (size_t)(b * P.Hkv + kvh) * P.Lcap * D;
-
     __syncthreads();
     const unsigned long long anc_row = anc_lds[node];
 
@@ -157,23 +158,61 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     // applied on the global side: lane i of a 1 KB block loads the logical
     // chunk that belongs at its slot.  The buffer resources end at key k1, so
     // loads past the split read zeros (and those keys are masked or unused).
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, k1 * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, k1 * D * 2, 0x00020000);
+    //
+    // Paged caches: a 1 KB block (4 or 8 rows) never straddles a page (pages
+    // hold a power of two >= 16 slots), so each block load gets a resource of
+    // its own, based at the block's page and ending at key k1 or the page's
+    // end.  The page entries of a step's loads are fetched one step ahead:
+    // lane l of the fetched register holds the entry of block load l (-1 past
+    // the split); the step reads them into scalar registers.
+    constexpr uint32_t kRsrcFlags = 0x00020000;
+    const size_t head_off = PAGED ? (size_t)kvh * ((size_t)D << P.pt.bs_log2)
+                                  : (size_t)(b * P.Hkv + kvh) * P.Lcap * D;
+    const uint16_t* kbase = (const uint16_t*)P.k + head_off;
+    const uint16_t* vbase = (const uint16_t*)P.v + head_off;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, k1 * D * 2, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, k1 * D * 2, kRsrcFlags);
     constexpr int BLOCKS = KT * D * 2 / 1024;          // 1 KB blocks per tile and operand
     constexpr int ROWS_PER_BLOCK = 1024 / (D * 2);
     constexpr int LOADS = 2 * BLOCKS / WAVES;           // K and V blocks one wave loads per tile
+    static_assert(LOADS <= 64, "one page entry per lane");
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int32_t* trow = PAGED ? P.pt.table + (size_t)b * P.pt.width : nullptr;
+    // page entries of the block loads of a step that loads K at key tk and V at key tv
+    auto load_pages = [&](int tk, int tv) -> int {
+        int e = -1;
+        if (PAGED && lane < LOADS) {
+            const bool isk = lane < LOADS / 2;
+            const int blk = (isk ? lane : lane - LOADS / 2) * WAVES + wave_u;
+            const int key0 = (isk ? tk : tv) + blk * ROWS_PER_BLOCK;
+            if (key0 < k1) e = trow[key0 >> P.pt.bs_log2];
+        }
+        return e;
+    };
     // block load l of a tile: l < LOADS/2 -> K of the tile at key tk, else V at key tv
-    auto issue_load = [&](int l, int tk, uint8_t* kdst, int tv, uint8_t* vdst) {
+    auto issue_load = [&](int l, int tk, uint8_t* kdst, int tv, uint8_t* vdst, int page) {
         const bool isk = l < LOADS / 2;
         const int blk = (isk ? l : l - LOADS / 2) * WAVES + wave_u;
         const int row = blk * ROWS_PER_BLOCK + lane / CH;
         const int c = (lane % CH) ^ (isk ? (row & (CH - 1)) : v_swizzle<CH>(row));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            isk ? krs : vrs, (__attribute__((address_space(3))) void*)((isk ? kdst : vdst) + blk * 1024), 16,
-            ((isk ? tk : tv) + row) * (D * 2) + c * 16, 0, 0, 0);
+        auto* dst = (__attribute__((address_space(3))) void*)((isk ? kdst : vdst) + blk * 1024);
+        if constexpr (PAGED) {
+            const int key0 = (isk ? tk : tv) + blk * ROWS_PER_BLOCK;
+            const int in_page = key0 & ((1 << P.pt.bs_log2) - 1);
+            const int room = min(max(k1 - (key0 - in_page), 0), 1 << P.pt.bs_log2);
+            const size_t page_off = ((size_t)max(page, 0) * P.Hkv) * ((size_t)D << P.pt.bs_log2);
+            // every operand of the resource is wave-uniform: keep it in scalar registers
+            const uint64_t addr = (uint64_t)((isk ? kbase : vbase) + page_off);
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+            const int bytes = __builtin_amdgcn_readfirstlane(page >= 0 ? room * D * 2 : 0);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(((uint64_t)hi << 32) | lo), 0, bytes, kRsrcFlags);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (in_page + lane / CH) * (D * 2) + c * 16, 0, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16,
+                                                     ((isk ? tk : tv) + row) * (D * 2) + c * 16, 0, 0, 0);
+        }
     };
 
     // MFMA operands.  QK^T product i (i < NQK) is sub-tile i % NSUB, k-step
@@ -269,7 +308,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     constexpr int EPM = 16 * NSUB / NMX;         // scores per max slot
     static_assert(EPS % 2 == 0 && EPM % 2 == 0, "pairs");
     auto step = [&](int t, const uint8_t* k_next, const uint8_t* v_cur, uint8_t* k_fill, uint8_t* v_fill,
-                    floatx16_t (&s_cur)[NSUB], floatx16_t (&s_next)[NSUB], float& mx_cur, float& mx_next) {
+                    floatx16_t (&s_cur)[NSUB], floatx16_t (&s_next)[NSUB], float& mx_cur, float& mx_next,
+                    int pg_cur, int& pg_next) {
+        int pages[LOADS];   // wave-uniform page entries of this step's block loads
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l) pages[l] = PAGED ? __builtin_amdgcn_readlane(pg_cur, l) : -1;
+        if constexpr (PAGED) pg_next = load_pages(t + 3 * KT, t + 2 * KT);
         if (t + KT > L || t + KT > k1) {
             mask_tile(t, s_cur);
             mx_cur = tile_max(s_cur);
@@ -285,7 +329,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
             if (i + PF < NQK) ka[i + PF] = read_k(k_next, i + PF);
 #pragma unroll
             for (int l = 0; l < LOADS; ++l)
-                if (l * NQK / LOADS == i) issue_load(l, t + 2 * KT, k_fill, t + KT, v_fill);
+                if (l * NQK / LOADS == i) issue_load(l, t + 2 * KT, k_fill, t + KT, v_fill, pages[l]);
             s_next[i % NSUB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qb[i / NSUB],
                                                                        i < NSUB ? zero16 : s_next[i % NSUB], 0, 0, 0);
 #pragma unroll
@@ -324,10 +368,21 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
 
     floatx16_t sa[NSUB], sb[NSUB];
     float mxa, mxb;
+    int pga = -1, pgb = -1;
+    if constexpr (PAGED) {
+        const int p0 = load_pages(k0, k0), p1 = load_pages(k0 + KT, k0 + KT);
+        pga = load_pages(k0 + 2 * KT, k0 + KT);   // the first step's loads
+        __builtin_amdgcn_s_waitcnt(0);
+        pgb = p1;
 #pragma unroll
-    for (int l = 0; l < LOADS; ++l) issue_load(l, k0, k_lds0, k0, v_lds0);
+        for (int l = 0; l < LOADS; ++l) issue_load(l, k0, k_lds0, k0, v_lds0, __builtin_amdgcn_readlane(p0, l));
+    } else {
 #pragma unroll
-    for (int l = 0; l < LOADS / 2; ++l) issue_load(l, k0 + KT, k_lds1, 0, nullptr);
+        for (int l = 0; l < LOADS; ++l) issue_load(l, k0, k_lds0, k0, v_lds0, -1);
+    }
+#pragma unroll
+    for (int l = 0; l < LOADS / 2; ++l)
+        issue_load(l, k0 + KT, k_lds1, 0, nullptr, PAGED ? __builtin_amdgcn_readlane(pgb, l) : -1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -338,9 +393,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     __builtin_amdgcn_s_waitcnt(0);       // every wave is done with K(k0) before it is refilled
     __syncthreads();
     for (int t = k0; t < k1; t += 2 * KT) {
-        step(t, k_lds1, v_lds0, k_lds0, v_lds1, sa, sb, mxa, mxb);
+        step(t, k_lds1, v_lds0, k_lds0, v_lds1, sa, sb, mxa, mxb, pga, pgb);
         if (t + KT >= k1) break;
-        step(t + KT, k_lds0, v_lds1, k_lds1, v_lds0, sb, sa, mxb, mxa);
+        step(t + KT, k_lds0, v_lds1, k_lds1, v_lds0, sb, sa, mxb, mxa, pgb, pga);
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
@@ -376,7 +431,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
 
 // ---------------------------------------------------------------- VALU path
 
-template <bool BF16, int D, int MAXR>
+template <bool BF16, int D, int MAXR, bool PAGED>
 __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams P) {
     constexpr int KT = 64;
     constexpr int EB = BF16 ? 2 : 4;
@@ -388,6 +443,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams P) {
     __shared__ __align__(16) uint8_t k_lds[KT * ROWB];
     __shared__ __align__(16) float p_lds[KT * MAXR];
     __shared__ unsigned long long anc_lds[64];
+    __shared__ size_t row_lds[PAGED ? KT : 1];   // paged: byte offset of each key row of the tile
 
     const int lane = threadIdx.x;
     const int rb = blockIdx.x % P.rowblocks;
@@ -396,8 +452,9 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams P) {
     const int b = pair / P.Hkv, kvh = pair - b * P.Hkv;
     const int T = P.T, g = P.g;
     const int L = P.kv_len[b];
-    const bool kv_ok = (L >= 0) && (L <= P.Lcap - T);
+    bool kv_ok = (L >= 0) && (L <= P.Lcap - T);
     const int N = L + T;
+    if constexpr (PAGED) kv_ok = kv_ok && !__any(page_entries_bad(P.pt, b, N, lane, 64));
     const int k0 = split * P.chunk;
     const int k1 = min(N, k0 + P.chunk);
     const int rbase = rb * MAXR;
@@ -439,8 +496,17 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams P) {
         anc_r[j] = anc_lds[r < P.R ? r / g : 0];
     }
 
-    const uint8_t* kbase = (const uint8_t*)P.k + (size_t)(b * P.Hkv + kvh) * P.Lcap * ROWB;
-    const uint8_t* vbase = (const uint8_t*)P.v + (size_t)(b * P.Hkv + kvh) * P.Lcap * ROWB;
+    // Dense: row of key j at kbase + j * ROWB.  Paged: at kbase + row_lds[j - t]
+    // for the keys of tile t (page base of this KV head + row in the page).
+    const size_t head_off = PAGED ? (size_t)kvh * ((size_t)ROWB << P.pt.bs_log2)
+                                  : (size_t)(b * P.Hkv + kvh) * P.Lcap * ROWB;
+    const uint8_t* kbase = (const uint8_t*)P.k + head_off;
+    const uint8_t* vbase = (const uint8_t*)P.v + head_off;
+    const int32_t* trow = PAGED ? P.pt.table + (size_t)b * P.pt.width : nullptr;
+    auto row_off = [&](int t, int key) -> size_t {
+        if constexpr (PAGED) return row_lds[key];
+        else return (size_t)(t + key) * ROWB;
+    };
 
     float m_run[MAXR], l_run[MAXR], o[MAXR][DPL];
 #pragma unroll
@@ -452,10 +518,21 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams P) {
     }
 
     for (int t = k0; t < k1; t += KT) {
+        if constexpr (PAGED) {
+            const int slot = t + lane;
+            size_t off = 0;
+            if (slot < k1) {
+                const int page = trow[slot >> P.pt.bs_log2];
+                off = (size_t)page * P.Hkv * ((size_t)ROWB << P.pt.bs_log2) +
+                      (size_t)(slot & ((1 << P.pt.bs_log2) - 1)) * ROWB;
+            }
+            row_lds[lane] = off;
+            __syncthreads();
+        }
         for (int idx = lane; idx < KT * CH; idx += 64) {
             const int key = idx / CH, c = idx - key * CH;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (t + key < k1) v = *(const u32x4*)(kbase + (size_t)(t + key) * ROWB + c * 16);
+            if (t + key < k1) v = *(const u32x4*)(kbase + row_off(t, key) + c * 16);
             *(u32x4*)(k_lds + key * ROWB + ((c ^ (key & (CH - 1))) << 4)) = v;
         }
         __syncthreads();
@@ -509,7 +586,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams P) {
         const int nk = min(KT, k1 - t);
         for (int kk = 0; kk < nk; ++kk) {
             float v[DPL];
-            const uint8_t* vrow = vbase + (size_t)(t + kk) * ROWB;
+            const uint8_t* vrow = vbase + row_off(t, kk);
             if constexpr (BF16) {
                 if constexpr (DPL == 2) {
                     const uint32_t w = *(const uint32_t*)(vrow + lane * 4);
@@ -560,17 +637,30 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnParams P) {
 
 // ---------------------------------------------------------------- split merge
 
+template <bool BF16, int D, bool PAGED>
+void launch_valu_rows_p(const AttnParams& p, int maxr, dim3 grid, hipStream_t s) {
+    switch (maxr) {
+        case 2: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 2, PAGED>), grid, dim3(64), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 4, PAGED>), grid, dim3(64), 0, s, p); break;
+        case 6: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 6, PAGED>), grid, dim3(64), 0, s, p); break;
+        case 8: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 8, PAGED>), grid, dim3(64), 0, s, p); break;
+        case 12: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 12, PAGED>), grid, dim3(64), 0, s, p); break;
+        default: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 16, PAGED>), grid, dim3(64), 0, s, p); break;
+    }
+}
+
 template <bool BF16, int D>
 hipError_t launch_valu_rows(const AttnParams& p, int maxr, dim3 grid, hipStream_t s) {
-    switch (maxr) {
-        case 2: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 2>), grid, dim3(64), 0, s, p); break;
-        case 4: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 4>), grid, dim3(64), 0, s, p); break;
-        case 6: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 6>), grid, dim3(64), 0, s, p); break;
-        case 8: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 8>), grid, dim3(64), 0, s, p); break;
-        case 12: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 12>), grid, dim3(64), 0, s, p); break;
-        default: hipLaunchKernelGGL((attn_valu_kernel<BF16, D, 16>), grid, dim3(64), 0, s, p); break;
-    }
+    if (p.pt.table) launch_valu_rows_p<BF16, D, true>(p, maxr, grid, s);
+    else launch_valu_rows_p<BF16, D, false>(p, maxr, grid, s);
     return hipGetLastError();
+}
+
+template <int D, bool PAGED>
+void launch_mfma_waves(const AttnParams& p, int waves, dim3 grid, hipStream_t s) {
+    if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<D, 4, PAGED>), grid, dim3(256), 0, s, p);
+    else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<D, 2, PAGED>), grid, dim3(128), 0, s, p);
+    else hipLaunchKernelGGL((attn_mfma_kernel<D, 1, PAGED>), grid, dim3(64), 0, s, p);
 }
 
 }  // namespace
@@ -590,14 +680,12 @@ hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s) 
     if (p.rowblocks == 1) blocks = groups;
     else blocks = ((groups + 7) / 8) * 8 * p.rowblocks;
     dim3 grid(blocks);
-    if (p.D == 128) {
-        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<128, 4>), grid, dim3(256), 0, s, p);
-        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, dim3(128), 0, s, p);
-        else hipLaunchKernelGGL((attn_mfma_kernel<128, 1>), grid, dim3(64), 0, s, p);
+    if (p.pt.table) {
+        if (p.D == 128) launch_mfma_waves<128, true>(p, waves, grid, s);
+        else launch_mfma_waves<64, true>(p, waves, grid, s);
     } else {
-        if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<64, 4>), grid, dim3(256), 0, s, p);
-        else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, dim3(128), 0, s, p);
-        else hipLaunchKernelGGL((attn_mfma_kernel<64, 1>), grid, dim3(64), 0, s, p);
+        if (p.D == 128) launch_mfma_waves<128, false>(p, waves, grid, s);
+        else launch_mfma_waves<64, false>(p, waves, grid, s);
     }
     return hipGetLastError();
 }
