@@ -27,6 +27,7 @@ from .verify import (NEAR_TIE, TOPP_NEAR_TIE, accept_and_select, row_distributio
 from .lossless import lossless_walk
 from .commit import commit_kv
 from .paged import commit_kv_paged, gather_slots, kv_valid, pages_valid, slot_page_row, verify_paged
+from .tree_build import build_tree, topk_ids, tree_template
 
 __all__ = [
     "ancestors", "check_parent", "depths", "tree_mask",
@@ -35,4 +36,5 @@ __all__ = [
     "NEAR_TIE", "TOPP_NEAR_TIE", "accept_and_select", "row_distributions", "verify", "verify_vocab", "widen",
     "lossless_walk", "commit_kv",
     "commit_kv_paged", "gather_slots", "kv_valid", "pages_valid", "slot_page_row", "verify_paged",
+    "build_tree", "topk_ids", "tree_template",
 ]
