@@ -141,6 +141,52 @@ def copy_probe(nbytes, steps):
                       "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
 
 
+def time_tree_build(spec, B, steps, stream):
+    """Candidate-tree construction (spec_verify_build_tree) for the workload's tree shape:
+    per-depth top-k of B x depth logits rows (seeded N(0, 3^2)) and the template fill."""
+    import numpy as np
+    import torch
+
+    from tree_attention_verification_verify_amd import SpecVerify, spec_verify_tree_template
+
+    caps, T = spec.tree[1], spec.tree[2]
+    parent_t, rank_t = spec_verify_tree_template(caps, T)
+    depth = len(caps)
+    rng = np.random.default_rng(2024)
+    lg = torch.from_numpy(rng.normal(0.0, 3.0, size=(B, depth, spec.vocab)).astype(np.float32)).cuda()
+    root = torch.zeros(B, dtype=torch.int32, device="cuda")
+    par = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    tok = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    cfg = dict(max_batch=B, max_nodes=T, num_q_heads=spec.hq, num_kv_heads=spec.hkv, head_dim=spec.head_dim,
+               kv_capacity=spec.kv_capacity, vocab=spec.vocab, dtype=spec.dtype, mode=spec.mode,
+               temperature=spec.temperature, top_p=spec.top_p)
+    import ctypes
+
+    from tree_attention_verification_verify_amd import binding
+
+    lib = binding.load_library()
+    tp = (ctypes.c_int32 * T)(*parent_t)
+    tr = (ctypes.c_int32 * T)(*rank_t)
+    targs = binding.TreeArgs(lg.data_ptr(), root.data_ptr(), ctypes.cast(tp, ctypes.c_void_p),
+                             ctypes.cast(tr, ctypes.c_void_p), par.data_ptr(), tok.data_ptr(), B, T, depth)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    with SpecVerify(**cfg) as sv:
+        for _ in range(10):
+            sv.build_tree(lg, root, parent_t, rank_t, par, tok, stream)
+        torch.cuda.synchronize()
+        # prebuilt arguments: the host stays ahead of the kernels
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            lib.spec_verify_build_tree(sv.handle, ctypes.byref(targs), sh)
+        e1.record(stream)
+        e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = B * depth * spec.vocab * 4
+    return {"caps": list(caps), "nodes": T, "rows": B * depth, "us_per_call": us, "bytes_read": nbytes,
+            "GBps": nbytes / (us * 1e-6) / 1e9}
+
+
 def synth_mode(name):
     import synth
 
@@ -422,6 +468,8 @@ def main():
     if other is not None:
         result["other_tree_rule"] = other
     result["kv_commit"] = commit
+    if spec.tree[0] == "medusa":
+        result["tree_build"] = time_tree_build(spec, B, args.steps, stream)
     if paged is not None:
         result["paged_kv"] = paged
     if not args.no_cpu_baseline:

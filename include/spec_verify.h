@@ -169,6 +169,23 @@ typedef struct spec_verify_paged_kv {
                                    table_width * block_size <= config.kv_capacity          */
 } spec_verify_paged_kv;
 
+/* Arguments of spec_verify_build_tree (B = batch, T = nodes, V from the config). */
+typedef struct spec_verify_tree_args {
+    const float* cand_logits;   /* [B,depth,V] fp32, device: row d-1 holds the logits the depth-d
+                                   candidates are taken from (d = 1: the target's next-token
+                                   row; d >= 2: Medusa head d-1)                                */
+    const int32_t* root_token;  /* [B], device: token of node 0 (the current token)              */
+    const int32_t* tree_parent; /* [T], HOST: template parent[] (parent[0] = -1,
+                                   0 <= parent[i] < i)                                           */
+    const int32_t* tree_rank;   /* [T], HOST: node i >= 1 takes entry tree_rank[i] (0 = best) of
+                                   its depth's top-k list; tree_rank[0] is ignored              */
+    int32_t* parent;            /* [B,T], device, out: the template, for every sequence          */
+    int32_t* tokens;            /* [B,T], device, out: root_token, then the candidates           */
+    int32_t batch;              /* B: 1..max_batch                                              */
+    int32_t nodes;              /* T: 1..max_nodes                                              */
+    int32_t depth;              /* rows per sequence in cand_logits, >= the template's depth    */
+} spec_verify_tree_args;
+
 typedef struct spec_verify_handle spec_verify_handle;
 
 /* Validate cfg, size and allocate the workspace on the current HIP device.
@@ -218,6 +235,34 @@ int spec_verify_run_paged(spec_verify_handle* h, const spec_verify_inputs* in, c
  * Errors: as spec_verify_commit, and the paged checks of spec_verify_run_paged. */
 int spec_verify_commit_paged(spec_verify_handle* h, const spec_verify_commit_args* args,
                              const spec_verify_paged_kv* paged, void* stream);
+
+/* Build the candidate trees of a Medusa verify step: tokens[b,i] is entry
+ * tree_rank[i] of the top-k list of row depth(i)-1 of sequence b (larger
+ * logit first, equal logits by smaller token id, NaN below every number),
+ * tokens[b,0] = root_token[b], parent[b,:] = tree_parent.  The per-head top-k
+ * lists form the tree's levels and the template fixes which combinations are
+ * kept ("推测解码技术详解：加速LLM推理的关键", section "Tree Attention验证": the
+ * two-head top-2 product tree; "Medusa推测解码：为LLM推理加速2-3倍的工程实践",
+ * sections 2.2 and 4.2: top-k candidates per head).  The outputs are the
+ * parent/tokens inputs of spec_verify_run.  Asynchronous; allocates nothing.
+ * Errors: INVALID_ARG (NULL or misaligned pointer, B or T out of range, a
+ * template that is not topological, a negative rank, a template deeper than
+ * `depth`, or more entries needed at some depth than V), UNSUPPORTED (more
+ * than 32 entries of one depth's list), HIP (launch failure). */
+int spec_verify_build_tree(spec_verify_handle* h, const spec_verify_tree_args* args, void* stream);
+
+/* Host only, no GPU: the template of a pruned Medusa tree.  Candidates are
+ * rank tuples (r_1..r_d), 1 <= d <= ncaps, r_k < caps[k-1]; the nodes-1
+ * tuples with the smallest key (prod_k (r_k + 1), d, ranks lexicographically)
+ * are kept (a child's key exceeds its parent's, so ancestors are kept) and
+ * ordered by (d, ranks) after the root.  When nodes-1 is the size of the full
+ * Cartesian product nothing is pruned (the product tree of the page section
+ * cited above; the pages give no pruning rule, this ordering is this
+ * library's).  Writes parent[nodes] and rank[nodes] (host arrays; rank[0] =
+ * 0, rank[i] = r_d of node i).  Errors: INVALID_ARG (NULL pointer, ncaps not
+ * in [1, 63], a cap < 1, nodes not in [1, 64] or above 1 + the number of
+ * tuples). */
+int spec_verify_tree_template(const int32_t* caps, int32_t ncaps, int32_t nodes, int32_t* parent, int32_t* rank);
 
 /* Free the workspace and the handle.  The caller's streams must be idle. */
 int spec_verify_destroy(spec_verify_handle* h);

@@ -39,6 +39,7 @@ def test_struct_layouts_match_the_header():
     assert ctypes.sizeof(binding.Outputs) == 11 * 8
     assert ctypes.sizeof(binding.CommitArgs) == 6 * 8 + 2 * 4
     assert ctypes.sizeof(binding.PagedKV) == 3 * 8 + 3 * 4 + 4   # padded to pointer alignment
+    assert ctypes.sizeof(binding.TreeArgs) == 6 * 8 + 3 * 4 + 4
 
 
 GOOD = dict(max_batch=2, max_nodes=8, num_q_heads=8, num_kv_heads=2, head_dim=128, kv_capacity=256,
@@ -93,6 +94,41 @@ def test_null_arguments():
     assert lib.spec_verify_commit(None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
     assert lib.spec_verify_run_paged(None, None, None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
     assert lib.spec_verify_commit_paged(None, None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
+    assert lib.spec_verify_build_tree(None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
+    assert lib.spec_verify_tree_template(None, 1, 1, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
     ms = (ctypes.c_float * 4)()
     n = ctypes.c_int32()
     assert lib.spec_verify_timing_read(None, ms, ctypes.byref(n)) == binding.SPEC_VERIFY_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ host-only tree template
+
+@pytest.mark.parametrize("caps,nodes", [((2, 2), 7), ((10, 4, 2, 1, 1), 64), ((10, 4, 2, 1), 26), ((3, 3, 3), 40),
+                                        ((5, 5), 31), ((1, 1, 1, 1), 5), ((64,), 64), ((2,) * 6, 64),
+                                        ((7, 3), 1), ((4, 4, 4), 2)])
+def test_tree_template_matches_the_oracle(caps, nodes):
+    import oracle
+
+    par, rank = sva.spec_verify_tree_template(caps, nodes)
+    opar, orank = oracle.tree_template(caps, nodes)
+    assert par == [int(x) for x in opar]
+    assert rank == [int(x) for x in orank]
+
+
+def test_tree_template_huge_caps_stay_cheap():
+    import oracle
+
+    # every all-zero tuple has product 1: with 63 levels the 63 kept tuples are one chain
+    par, rank = sva.spec_verify_tree_template([1 << 30] * 63, 64)
+    assert par == [-1] + list(range(63)) and rank == [0] * 64
+    # two levels: a kept rank is at most 62, so caps of 64 keep the same tuples
+    par, rank = sva.spec_verify_tree_template([1 << 30] * 2, 64)
+    opar, orank = oracle.tree_template([64, 64], 64)
+    assert par == [int(x) for x in opar] and rank == [int(x) for x in orank]
+
+
+@pytest.mark.parametrize("caps,nodes", [((2, 2), 8), ((0, 2), 2), ((), 1), ((3,), 0), ((3,), 65)])
+def test_tree_template_rejects_bad_arguments(caps, nodes):
+    with pytest.raises(sva.SpecVerifyError) as e:
+        sva.spec_verify_tree_template(caps, nodes)
+    assert e.value.code == binding.SPEC_VERIFY_ERR_INVALID_ARG

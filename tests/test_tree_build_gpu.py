@@ -1,0 +1,118 @@
+"""GPU parity of the candidate-tree construction (spec_verify_build_tree) against oracle.build_tree.
+
+Tokens and parents are integer outputs: they must match bit for bit, on rows
+with many tied logits, infinities, NaN and signed zeros.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_harness import note
+
+pytestmark = pytest.mark.gpu
+
+
+def _config(B, T, V):
+    return dict(max_batch=B, max_nodes=max(T, 1), num_q_heads=8, num_kv_heads=8, head_dim=128,
+                kv_capacity=256, vocab=V, dtype="bf16", mode="greedy")
+
+
+def _run(logits, root, parent_t, rank_t, label):
+    import torch
+    from tree_attention_verification_verify_amd import SpecVerify
+
+    B, depth, V = logits.shape
+    T = len(parent_t)
+    note("%s: B=%d depth=%d V=%d T=%d" % (label, B, depth, V, T))
+    dev = "cuda"
+    lg = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).to(dev)
+    rt = torch.from_numpy(np.ascontiguousarray(root, dtype=np.int32)).to(dev)
+    par = torch.full((B, T), -9, dtype=torch.int32, device=dev)
+    tok = torch.full((B, T), -9, dtype=torch.int32, device=dev)
+    with SpecVerify(**_config(B, T, V)) as sv:
+        sv.build_tree(lg, rt, list(parent_t), list(rank_t), par, tok)
+        torch.cuda.synchronize()
+    return par.cpu().numpy(), tok.cpu().numpy()
+
+
+def _check(logits, root, caps, nodes, label):
+    parent_t, rank_t = oracle.tree_template(caps, nodes)
+    par, tok = _run(logits, root, parent_t, rank_t, label)
+    rpar, rtok = oracle.build_tree(logits.astype(np.float64), root, parent_t, rank_t)
+    np.testing.assert_array_equal(par, rpar)
+    np.testing.assert_array_equal(tok, rtok)
+    return tok
+
+
+@pytest.mark.parametrize("B,caps,nodes,V,step", [
+    (8, (10, 4, 2, 1, 1), 64, 32000, 0.125),     # the 70B-shaped GQA tree workload's tree
+    (1, (10, 4, 2, 1, 1), 64, 32000, 0.0),
+    (16, (10, 4, 2, 1), 26, 128256, 0.25),       # the long-context large-vocab workload's tree
+    (3, (2, 2), 7, 1000, 0.5),                   # the printed two-head top-2 tree
+    (2, (40,), 33, 5000, 1.0),                   # 32 entries of one list
+    (4, (3, 3, 3, 3), 64, 777, 0.0),
+])
+def test_tree_build_matches_oracle(B, caps, nodes, V, step):
+    rng = np.random.default_rng(B * 1000 + V)
+    logits = rng.normal(0.0, 3.0, size=(B, len(caps), V)).astype(np.float32)
+    if step:
+        logits = (np.round(logits / step) * step).astype(np.float32)   # many ties
+    root = rng.integers(0, V, size=B)
+    _check(logits, root, caps, nodes, "tree-%s-%d" % ("-".join(map(str, caps)), V))
+
+
+def test_tree_build_special_values_and_tiny_vocab():
+    rng = np.random.default_rng(11)
+    B, V = 5, 20
+    logits = np.round(rng.normal(size=(B, 3, V))).astype(np.float32)
+    logits[0, 0, :6] = [np.nan, -np.inf, np.inf, -0.0, 0.0, np.nan]
+    logits[1, 1, :] = -np.inf
+    logits[2, 2, :] = np.nan
+    logits[3, :, :] = 0.0
+    logits[3, :, ::3] = -0.0
+    root = np.arange(B)
+    _check(logits, root, (4, 3, 2), 40, "tree-special")
+
+
+def test_tree_build_crowded_row_takes_the_exact_path():
+    # the 4000 largest logits all sit in the first wave's share of the row
+    # (float4 columns 0..63 of each 1024-column stride), so far more entries
+    # pass the first pass's bound than the short list holds
+    rng = np.random.default_rng(13)
+    B, V = 2, 32000
+    logits = rng.normal(size=(B, 2, V)).astype(np.float32)
+    cols = np.arange(V)
+    crowd = ((cols // 4) % 1024) < 64
+    logits[:, :, crowd] += 100.0
+    _check(logits, np.array([1, 2]), (16, 16), 60, "tree-crowded")
+
+
+def test_tree_build_root_only_and_chain():
+    rng = np.random.default_rng(12)
+    logits = rng.normal(size=(2, 4, 300)).astype(np.float32)
+    tok = _check(logits, np.array([7, 8]), (5,), 1, "tree-root-only")
+    assert list(tok[:, 0]) == [7, 8]
+    _check(logits, np.array([7, 8]), (1, 1, 1, 1), 5, "tree-chain")   # greedy chain: argmax of each row
+
+
+def test_tree_build_rejects_bad_templates():
+    import torch
+    from tree_attention_verification_verify_amd import SpecVerify, SpecVerifyError
+
+    B, V = 2, 100
+    lg = torch.zeros((B, 2, V), dtype=torch.float32, device="cuda")
+    rt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    par = torch.zeros((B, 40), dtype=torch.int32, device="cuda")
+    tok = torch.zeros((B, 40), dtype=torch.int32, device="cuda")
+    with SpecVerify(**_config(B, 40, V)) as sv:
+        cases = [([-1, 0, 2], [0, 0, 0], -1),                  # not topological
+                 ([0, 0], [0, 0], -1),                          # root with a parent
+                 ([-1, 0, 1, 2], [0, 0, 0, 0], -1),             # deeper than the 2 rows given
+                 ([-1, 0, 0], [0, 0, -1], -1),                  # negative rank
+                 ([-1] + [0] * 33, [0] + list(range(33)), -2)]  # 33 entries of one list
+        for p, r, code in cases:
+            T = len(p)
+            with pytest.raises(SpecVerifyError) as e:
+                sv.build_tree(lg, rt, p, r, par[:, :T].contiguous(), tok[:, :T].contiguous())
+            assert e.value.code == code, (p, r)
+    torch.cuda.synchronize()

@@ -2,8 +2,9 @@
 
 The functions mirror the C ABI in include/spec_verify.h one to one
 (spec_verify_create / spec_verify_run / spec_verify_run_paged /
-spec_verify_commit / spec_verify_commit_paged / spec_verify_destroy /
-spec_verify_last_error / spec_verify_timing_read).  Tensors are PyTorch device
+spec_verify_commit / spec_verify_commit_paged / spec_verify_build_tree /
+spec_verify_tree_template / spec_verify_destroy / spec_verify_last_error /
+spec_verify_timing_read).  Tensors are PyTorch device
 tensors; only their data pointers cross the boundary.  Every step of the
 verify step runs in the library's HIP kernels: there is no fallback, and a
 missing library is an error.
@@ -32,7 +33,8 @@ SPEC_VERIFY_NUM_STAGES = 3
 STAGES = ("attention", "vocab", "finish")
 
 EXPORTED = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
-            "spec_verify_timing_read", "spec_verify_commit", "spec_verify_run_paged", "spec_verify_commit_paged")
+            "spec_verify_timing_read", "spec_verify_commit", "spec_verify_run_paged", "spec_verify_commit_paged",
+            "spec_verify_build_tree", "spec_verify_tree_template")
 
 
 class SpecVerifyError(RuntimeError):
@@ -66,6 +68,12 @@ class CommitArgs(ctypes.Structure):
 class PagedKV(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("table_width", ctypes.c_int32)]
+
+
+class TreeArgs(ctypes.Structure):
+    _fields_ = [("cand_logits", ctypes.c_void_p), ("root_token", ctypes.c_void_p), ("tree_parent", ctypes.c_void_p),
+                ("tree_rank", ctypes.c_void_p), ("parent", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("nodes", ctypes.c_int32), ("depth", ctypes.c_int32)]
 
 
 class Outputs(ctypes.Structure):
@@ -106,6 +114,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_commit_paged.argtypes = [ctypes.c_void_p, ctypes.POINTER(CommitArgs), ctypes.POINTER(PagedKV),
                                              ctypes.c_void_p]
     lib.spec_verify_commit_paged.restype = ctypes.c_int
+    lib.spec_verify_build_tree.argtypes = [ctypes.c_void_p, ctypes.POINTER(TreeArgs), ctypes.c_void_p]
+    lib.spec_verify_build_tree.restype = ctypes.c_int
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.spec_verify_tree_template.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, i32p, i32p]
+    lib.spec_verify_tree_template.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -199,6 +212,29 @@ def spec_verify_commit_paged(handle, paged: PagedKV, kv_len, path, accept_len, f
                                                    ctypes.c_void_p(_stream_handle(stream))))
 
 
+def spec_verify_tree_template(caps, nodes: int):
+    """Host-only template of a pruned Medusa tree: (parent, rank) as lists of `nodes` ints."""
+    ncaps = len(caps)
+    c = (ctypes.c_int32 * max(ncaps, 1))(*[int(x) for x in caps])
+    par = (ctypes.c_int32 * max(nodes, 1))()
+    rk = (ctypes.c_int32 * max(nodes, 1))()
+    _check(load_library().spec_verify_tree_template(c, ncaps, nodes, par, rk))
+    return list(par)[:nodes], list(rk)[:nodes]
+
+
+def spec_verify_build_tree(handle, cand_logits, root_token, tree_parent, tree_rank, parent, tokens,
+                           stream=None) -> None:
+    """Fill parent/tokens [B,T] (device) from cand_logits [B,depth,V] and root_token [B] (device)
+    with the host template tree_parent/tree_rank (sequences of T ints)."""
+    B, depth = cand_logits.shape[0], cand_logits.shape[1]
+    T = len(tree_parent)
+    tp = (ctypes.c_int32 * T)(*[int(x) for x in tree_parent])
+    tr = (ctypes.c_int32 * T)(*[int(x) for x in tree_rank])
+    a = TreeArgs(_ptr(cand_logits), _ptr(root_token), ctypes.cast(tp, ctypes.c_void_p),
+                 ctypes.cast(tr, ctypes.c_void_p), _ptr(parent), _ptr(tokens), B, T, depth)
+    _check(load_library().spec_verify_build_tree(handle, ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
+
+
 def spec_verify_timing_read(handle):
     """Summed per-stage kernel milliseconds over the runs since the last read, and the run count."""
     ms = (ctypes.c_float * SPEC_VERIFY_NUM_STAGES)()
@@ -250,6 +286,9 @@ class SpecVerify:
 
     def commit_paged(self, paged: PagedKV, kv_len, path, accept_len, final_node, stream=None) -> None:
         spec_verify_commit_paged(self.handle, paged, kv_len, path, accept_len, final_node, stream)
+
+    def build_tree(self, cand_logits, root_token, tree_parent, tree_rank, parent, tokens, stream=None) -> None:
+        spec_verify_build_tree(self.handle, cand_logits, root_token, tree_parent, tree_rank, parent, tokens, stream)
 
     def close(self) -> None:
         if self.handle is not None:

@@ -100,6 +100,21 @@ struct CommitParams {
     PageTable pt;            // paged caches: k, v are the pools; Lcap = pt.width << pt.bs_log2
 };
 
+// Candidate-tree construction: template by value (T <= 64, depth <= 63,
+// ranks < 32), one workgroup per (sequence, depth).
+struct TreeParams {
+    const float* logits;        // [B][rows][V]: row d-1 = distribution of depth-d candidates
+    const int32_t* root_token;  // [B]
+    int32_t* parent;            // [B][T] out
+    int32_t* tokens;            // [B][T] out
+    int B, T, V, rows;
+    int levels;                 // deepest template depth (0: root only)
+    int8_t tpar[64];            // template parent[] (-1 for the root)
+    int8_t trank[64];           // top-k entry each node takes
+    int8_t tdep[64];            // depth of each node
+    int8_t kd[64];              // entries needed at depth d (max rank + 1)
+};
+
 // Returns hipSuccess or the launch error.
 hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s);
 hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
@@ -112,6 +127,8 @@ hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool sele
 hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s);
 // KV commit of the accepted path: one workgroup per sequence.
 hipError_t launch_kv_commit(const CommitParams& p, hipStream_t s);
+// Candidate tree: kmax = largest kd over the depths (<= 32).
+hipError_t launch_tree_build(const TreeParams& p, int kmax, hipStream_t s);
 
 constexpr int kValuRows = 16;      // rows per block of the VALU attention kernel
 constexpr int kVocabThreads = 1024;               // register-resident row kernels

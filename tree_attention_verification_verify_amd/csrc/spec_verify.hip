@@ -463,6 +463,121 @@ int spec_verify_commit_paged(spec_verify_handle* h, const spec_verify_commit_arg
     return commit_impl(h, a, paged, stream);
 }
 
+int spec_verify_build_tree(spec_verify_handle* h, const spec_verify_tree_args* a, void* stream) {
+    g_err.clear();
+    if (!h || !a) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle and args must be non-NULL");
+    const spec_verify_config& c = h->cfg;
+    const int B = a->batch, T = a->nodes;
+    if (B < 1 || B > c.max_batch) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "batch out of range");
+    if (T < 1 || T > c.max_nodes) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes out of range");
+    if (!a->cand_logits || !a->root_token || !a->tree_parent || !a->tree_rank || !a->parent || !a->tokens)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "a tree-build pointer is NULL");
+    auto misaligned = [](const void* ptr) { return (((uintptr_t)ptr) & 3u) != 0; };
+    if (misaligned(a->cand_logits) || misaligned(a->root_token) || misaligned(a->parent) || misaligned(a->tokens))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "arrays must be aligned to their element size");
+    sv::TreeParams tp{};
+    int depth[64];
+    int levels = 0;
+    for (int i = 0; i < T; ++i) {
+        const int p = a->tree_parent[i];
+        if (i == 0 ? p != -1 : (p < 0 || p >= i))
+            return fail(SPEC_VERIFY_ERR_INVALID_ARG, "tree_parent is not a topologically ordered tree");
+        depth[i] = i == 0 ? 0 : depth[p] + 1;
+        levels = std::max(levels, depth[i]);
+        const int r = i == 0 ? 0 : a->tree_rank[i];
+        if (r < 0) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "tree_rank must be >= 0");
+        if (r >= 32) return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "a depth needs more than 32 top-k entries");
+        tp.tpar[i] = (int8_t)p;
+        tp.trank[i] = (int8_t)r;
+        tp.tdep[i] = (int8_t)depth[i];
+    }
+    if (levels > a->depth) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "the template is deeper than depth");
+    int kmax = 0;
+    for (int i = 1; i < T; ++i) {
+        tp.kd[depth[i]] = (int8_t)std::max<int>(tp.kd[depth[i]], tp.trank[i] + 1);
+        kmax = std::max<int>(kmax, tp.kd[depth[i]]);
+    }
+    if (kmax > c.vocab) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "more top-k entries needed than the vocabulary has");
+    tp.logits = a->cand_logits;
+    tp.root_token = a->root_token;
+    tp.parent = a->parent;
+    tp.tokens = a->tokens;
+    tp.B = B;
+    tp.T = T;
+    tp.V = c.vocab;
+    tp.rows = a->depth;
+    tp.levels = levels;
+    const hipError_t e = sv::launch_tree_build(tp, kmax, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "tree-build launch");
+    return SPEC_VERIFY_OK;
+}
+
+int spec_verify_tree_template(const int32_t* caps, int32_t ncaps, int32_t nodes, int32_t* parent, int32_t* rank) {
+    g_err.clear();
+    if (!caps || !parent || !rank) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "NULL argument");
+    if (ncaps < 1 || ncaps > 63) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "ncaps must be in [1, 63]");
+    if (nodes < 1 || nodes > 64) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes must be in [1, 64]");
+    long long tuples = 0, level = 1;
+    for (int k = 0; k < ncaps; ++k) {
+        if (caps[k] < 1) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "caps must be >= 1");
+        level = std::min<long long>(level * caps[k], 1LL << 40);
+        tuples = std::min<long long>(tuples + level, 1LL << 40);
+    }
+    if (nodes - 1 > tuples) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes exceed 1 + the number of rank tuples");
+    // Best-first over the rank tuples: every tuple but (0) is reached from a
+    // smaller key, as the first child t+(0) of t (same product, one deeper)
+    // or as the next sibling of (.., r) (larger product), so popping the
+    // smallest key and pushing those two successors yields the tuples in key order.
+    struct Cand {
+        unsigned long long prod;
+        std::vector<int> t;
+    };
+    auto less = [](const Cand& x, const Cand& y) {
+        if (x.prod != y.prod) return x.prod < y.prod;
+        if (x.t.size() != y.t.size()) return x.t.size() < y.t.size();
+        return x.t < y.t;
+    };
+    std::vector<Cand> open{Cand{1ull, {0}}};
+    std::vector<std::vector<int>> kept;
+    while ((int)kept.size() < nodes - 1) {
+        size_t best = 0;
+        for (size_t q = 1; q < open.size(); ++q)
+            if (less(open[q], open[best])) best = q;
+        Cand cur = open[best];
+        open.erase(open.begin() + best);
+        if ((int)cur.t.size() < ncaps) {
+            Cand child{cur.prod, cur.t};
+            child.t.push_back(0);
+            open.push_back(child);
+        }
+        const int r = cur.t.back();
+        if (r + 1 < caps[cur.t.size() - 1]) {
+            Cand sib{cur.prod / (unsigned long long)(r + 1) * (unsigned long long)(r + 2), cur.t};
+            sib.t.back() = r + 1;
+            open.push_back(sib);
+        }
+        kept.push_back(cur.t);
+    }
+    std::sort(kept.begin(), kept.end(), [](const std::vector<int>& x, const std::vector<int>& y) {
+        if (x.size() != y.size()) return x.size() < y.size();
+        return x < y;
+    });
+    parent[0] = -1;
+    rank[0] = 0;
+    for (int i = 1; i < nodes; ++i) {
+        const std::vector<int>& t = kept[i - 1];
+        int p = 0;
+        if (t.size() > 1) {
+            const std::vector<int> up(t.begin(), t.end() - 1);
+            for (int j = 1; j < i; ++j)
+                if (kept[j - 1] == up) p = j;
+        }
+        parent[i] = p;
+        rank[i] = t.back();
+    }
+    return SPEC_VERIFY_OK;
+}
+
 int spec_verify_timing_read(spec_verify_handle* h, float* stage_ms, int32_t* runs) {
     g_err.clear();
     if (!h || !stage_ms || !runs) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "NULL argument");
