@@ -131,6 +131,7 @@ hipError_t launch_kv_commit(const CommitParams& p, hipStream_t s);
 hipError_t launch_tree_build(const TreeParams& p, int kmax, hipStream_t s);
 
 constexpr int kValuRows = 16;      // rows per block of the VALU attention kernel
+constexpr int kMfmaHalves = 2;     // key halves per workgroup of the MFMA attention kernel
 constexpr int kVocabThreads = 1024;               // register-resident row kernels
 constexpr int kVocabChunk = kVocabThreads * 32;   // logits held on chip per pass
 constexpr int kStatsThreads = 256;                // streaming row-statistics kernel

@@ -69,7 +69,7 @@ AttnPlan plan_attention(const spec_verify_config& c, int B, int T) {
     p.rowblocks = (R + p.rows_per_block - 1) / p.rows_per_block;
     p.Rpad = p.rowblocks * p.rows_per_block;
     const long pairs = (long)B * c.num_kv_heads;
-    const long base_waves = pairs * p.rowblocks * p.waves;
+    const long base_waves = pairs * p.rowblocks * p.waves * (p.mfma ? sv::kMfmaHalves : 1);
     long want = (kTargetWaves + base_waves - 1) / base_waves;
     const long keys = c.kv_capacity;
     const long max_split = std::max(1L, keys / kMinSplitKeys);

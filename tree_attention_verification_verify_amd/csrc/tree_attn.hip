@@ -61,8 +61,14 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
 
 constexpr float kLazyMax = 8.f;   // log2 headroom of the lazily raised softmax reference
 
-template <int D, int WAVES, bool PAGED>
-__global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) {
+// H halves of WAVES waves each: with H = 2 the halves take the two halves of
+// the split's tiles and merge their (O, m, l) through LDS at the end, so a
+// workgroup of 8 waves covers what two 4-wave workgroups and a merge pass
+// would.  Both halves run the same number of steps (barriers are shared); a
+// half with one tile fewer runs its last step on a tile past its range,
+// whose loads read zeros and whose keys are all masked.
+template <int D, int WAVES, bool PAGED, int H>
+__global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams P) {   // 2 waves per SIMD
     constexpr int NSUB = 2;                 // 32-key sub-tiles per tile
     constexpr int KT = 32 * NSUB;           // keys per tile
     constexpr int CH = D / 8;               // 16-byte chunks per K/V row
@@ -73,13 +79,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     // Two buffers each for K and V, as four separate LDS objects: the compiler
     // then knows that the loads filling one buffer never alias the reads of
     // another and does not wait for the prefetch before reading the current tile.
-    __shared__ __align__(16) uint8_t k_lds0[KT * D * 2];
-    __shared__ __align__(16) uint8_t k_lds1[KT * D * 2];
-    __shared__ __align__(16) uint8_t v_lds0[KT * D * 2];
-    __shared__ __align__(16) uint8_t v_lds1[KT * D * 2];
+    __shared__ __align__(16) uint8_t k_lds0_all[H * KT * D * 2];
+    __shared__ __align__(16) uint8_t k_lds1_all[H * KT * D * 2];
+    __shared__ __align__(16) uint8_t v_lds0_all[H * KT * D * 2];
+    __shared__ __align__(16) uint8_t v_lds1_all[H * KT * D * 2];
     __shared__ unsigned long long anc_lds[64];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int hv = __builtin_amdgcn_readfirstlane((tid >> 6) / WAVES);   // which half of the split's tiles
+    const int wave = (tid >> 6) % WAVES;      // wave within the half
+    uint8_t* const k_lds0 = k_lds0_all + hv * (KT * D * 2);
+    uint8_t* const k_lds1 = k_lds1_all + hv * (KT * D * 2);
+    uint8_t* const v_lds0 = v_lds0_all + hv * (KT * D * 2);
+    uint8_t* const v_lds1 = v_lds1_all + hv * (KT * D * 2);
     int group, rb;
     if (P.rowblocks == 1) {
         group = blockIdx.x;
@@ -97,11 +109,14 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     bool kv_ok = (L >= 0) && (L <= P.Lcap - T);
     const int N = L + T;
     if constexpr (PAGED) {   // every table entry of the used slots must name a page of the pool
-        const bool bad = kv_ok && page_entries_bad(P.pt, b, N, tid, WAVES * 64);
+        const bool bad = kv_ok && page_entries_bad(P.pt, b, N, tid, WAVES * 64 * H);
         kv_ok = kv_ok && !__syncthreads_or(bad);
     }
-    const int k0 = split * P.chunk;
-    const int k1 = min(N, k0 + P.chunk);
+    const int s0 = split * P.chunk;            // the workgroup's keys [s0, s1)
+    const int s1 = min(N, s0 + P.chunk);
+    const int nsteps = (s1 - s0 + KT - 1) / KT / H + ((s1 - s0 + KT - 1) / KT % H ? 1 : 0);
+    const int k0 = s0 + hv * nsteps * KT;      // this half's keys [k0, k1)
+    const int k1 = (hv == H - 1) ? s1 : min(s1, k0 + nsteps * KT);
     const int qcol = lane & 31, half = lane >> 5;
     const int r = rb * (WAVES * 32) + wave * 32 + qcol;
     const bool row_ok = r < P.R;
@@ -109,7 +124,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     const int head = kvh * g + (row_ok ? r - node * g : 0);
     const size_t part_row = (size_t)group * P.Rpad + r;
 
-    if (!kv_ok || k0 >= k1) {
+    if (!kv_ok || s0 >= s1) {
+        if (hv != 0) return;
         if (P.nsplit == 1) {
             if (row_ok) {
                 uint16_t* o = (uint16_t*)P.out + ((size_t)(b * T + node) * P.Hq + head) * D;
@@ -121,7 +137,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
         return;
     }
 
-    if (wave == 0) {
+    if (tid < kWave) {
         bool bad;
         unsigned long long a = ancestor_mask(P.parent + (size_t)b * T, T, &bad);
         anc_lds[lane] = a;
@@ -256,8 +272,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
             for (int e = 0; e < 16; ++e) {
                 const int key = t + sub * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
                 const unsigned rel = (unsigned)(key - L);
-                const bool tree_vis = (key < k1) && ((anc_row >> (rel & 63u)) & 1ull);
-                const bool vis = (key < L) | (key >= L && tree_vis);
+                const bool tree_vis = (anc_row >> (rel & 63u)) & 1ull;
+                const bool vis = (key < k1) && ((key < L) | tree_vis);
                 s[sub][e] = vis ? s[sub][e] : -INFINITY;
             }
     };
@@ -392,13 +408,43 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_mfma_kernel(AttnParams P) 
     mxa = tile_max(sa);
     __builtin_amdgcn_s_waitcnt(0);       // every wave is done with K(k0) before it is refilled
     __syncthreads();
-    for (int t = k0; t < k1; t += 2 * KT) {
+    for (int st = 0; st < nsteps; st += 2) {
+        const int t = k0 + st * KT;
         step(t, k_lds1, v_lds0, k_lds0, v_lds1, sa, sb, mxa, mxb, pga, pgb);
-        if (t + KT >= k1) break;
+        if (st + 1 >= nsteps) break;
         step(t + KT, k_lds0, v_lds1, k_lds1, v_lds0, sb, sa, mxb, mxa, pgb, pga);
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+    float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+    if constexpr (H == 2) {
+        // half 1 hands (O, m, l) to half 0 through the (now idle) tile buffers:
+        // O tiles 0..DT/2-1 in the K buffers 0, the rest in K buffers 1, (m, l) in V buffers 0
+        auto xo = [&](int dt, int e) -> float* {
+            uint8_t* arr = dt < DT / 2 ? k_lds0_all : k_lds1_all;
+            return (float*)arr + ((wave * (DT / 2) + dt % (DT / 2)) * 16 + e) * kWave + lane;
+        };
+        float2* xml = (float2*)v_lds0_all + wave * kWave + lane;
+        if (hv == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) *xo(dt, e) = o[dt][e];
+            *xml = make_float2(m_run, l_tot);
+        }
+        __syncthreads();
+        if (hv == 1) return;
+        const float2 mlb = *xml;
+        const float ma = l_tot > 0.f ? m_run : -INFINITY, mb = mlb.y > 0.f ? mlb.x : -INFINITY;
+        const float mm = fmaxf(ma, mb);
+        const float wa = l_tot > 0.f ? __builtin_amdgcn_exp2f(ma - mm) : 0.f;
+        const float wb = mlb.y > 0.f ? __builtin_amdgcn_exp2f(mb - mm) : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[dt][e] = wa * o[dt][e] + wb * *xo(dt, e);
+        l_tot = wa * l_tot + wb * mlb.y;
+        m_run = mm;
+    }
     if (!row_ok) return;
     // O^T element e of tile dt: column d = 32*dt + 8*(e>>2) + 4*half + (e&3)
     if (P.nsplit == 1) {
@@ -658,9 +704,10 @@ hipError_t launch_valu_rows(const AttnParams& p, int maxr, dim3 grid, hipStream_
 
 template <int D, bool PAGED>
 void launch_mfma_waves(const AttnParams& p, int waves, dim3 grid, hipStream_t s) {
-    if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<D, 4, PAGED>), grid, dim3(256), 0, s, p);
-    else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<D, 2, PAGED>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((attn_mfma_kernel<D, 1, PAGED>), grid, dim3(64), 0, s, p);
+    constexpr int H = kMfmaHalves;
+    if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<D, 4, PAGED, H>), grid, dim3(256 * H), 0, s, p);
+    else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<D, 2, PAGED, H>), grid, dim3(128 * H), 0, s, p);
+    else hipLaunchKernelGGL((attn_mfma_kernel<D, 1, PAGED, H>), grid, dim3(64 * H), 0, s, p);
 }
 
 }  // namespace
