@@ -16,13 +16,14 @@ namespace sv {
 template <int D>
 constexpr int combine_rows_per_block() { return 256 / (D / 8); }
 
+// Merge block `blk` run by 256 threads, t = 0..255 this thread's index among them.
 template <bool BF16, int D>
-__device__ __forceinline__ void combine_block(const AttnParams& P, long blk) {
+__device__ __forceinline__ void combine_block(const AttnParams& P, long blk, int t) {
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     constexpr int TPR = D / 8;
     constexpr int RPB = 256 / TPR;
-    const long row = (long)blk * RPB + threadIdx.x / TPR;
-    const int d0 = (threadIdx.x % TPR) * 8;
+    const long row = (long)blk * RPB + t / TPR;
+    const int d0 = (t % TPR) * 8;
     const long pairs = (long)P.B * P.Hkv;
     if (row >= pairs * P.R) return;
     const int pair = (int)(row / P.R), r = (int)(row - (long)pair * P.R);

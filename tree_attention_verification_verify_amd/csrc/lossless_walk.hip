@@ -46,7 +46,7 @@ __device__ __forceinline__ float walk_prob(const float* row, const RowStat& st, 
 
 // Unnormalised weights of the current r over one chunk: p_v in its nucleus
 // (from the logits), or the workspace residual.
-__device__ void r_weights(const SelectParams& P, int b, const WalkShared& ws, int cb, float4 (&w)[VPT4]) {
+__device__ __forceinline__ void r_weights(const SelectParams& P, int b, const WalkShared& ws, int cb, float4 (&w)[VPT4]) {
     const int T = P.T, V = P.V;
     if (ws.r_ws) {
         const float* R = P.resid_ws + ((size_t)b * 2 + ws.cur) * V;
@@ -73,7 +73,7 @@ __device__ void r_weights(const SelectParams& P, int b, const WalkShared& ws, in
     }
 }
 
-__device__ void store_chunk(float* row, int V, int cb, const float4 (&w)[VPT4]) {
+__device__ __forceinline__ void store_chunk(float* row, int V, int cb, const float4 (&w)[VPT4]) {
     const bool aligned = (((uintptr_t)row) & 15) == 0;
 #pragma unroll
     for (int j = 0; j < VPT4; ++j) {
@@ -89,7 +89,7 @@ __device__ void store_chunk(float* row, int V, int cb, const float4 (&w)[VPT4]) 
 }
 
 // r <- [r - q_c]_+ over the whole row into the other workspace row; returns its fp64 total.
-__device__ double residual_pass(const SelectParams& P, int b, int c, const WalkShared& ws, Smem& sm) {
+__device__ __forceinline__ double residual_pass(const SelectParams& P, int b, int c, const WalkShared& ws, Smem& sm) {
     const int T = P.T, V = P.V;
     const RowStat sq = P.stats[(size_t)b * 2 * T + T + c];
     const Nucleus nq{sq.thr, sq.cutoff};
@@ -119,7 +119,7 @@ __device__ double residual_pass(const SelectParams& P, int b, int c, const WalkS
 }
 
 // Inverse-CDF draw from r: y = min{k : u * W < C_k} in token-id order.
-__device__ int draw_from_r(const SelectParams& P, int b, const WalkShared& ws, double u, Smem& sm) {
+__device__ __forceinline__ int draw_from_r(const SelectParams& P, int b, const WalkShared& ws, double u, Smem& sm) {
     const int V = P.V;
     float4 w[VPT4];
     if (V <= CHUNK) {

@@ -58,7 +58,7 @@ __device__ __forceinline__ void f4set(float4& v, int e, float x) {
 
 // Block reductions: each wave reduces, wave 0 reduces the wave results in a
 // fixed order and broadcasts one value (deterministic, two barriers).
-__device__ float block_max(float v, Smem& sm) {
+__device__ __forceinline__ float block_max(float v, Smem& sm) {
     v = wave_max(v);
     if (lane_() == 0) sm.f[wave_()] = v;
     __syncthreads();
@@ -70,7 +70,7 @@ __device__ float block_max(float v, Smem& sm) {
     return sm.fr;
 }
 
-__device__ double block_sum_d(double v, Smem& sm) {
+__device__ __forceinline__ double block_sum_d(double v, Smem& sm) {
     v = wave_sum_d(v);
     if (lane_() == 0) sm.d[wave_()] = v;
     __syncthreads();
@@ -82,7 +82,7 @@ __device__ double block_sum_d(double v, Smem& sm) {
     return sm.dr;
 }
 
-__device__ unsigned long long block_sum_u64(unsigned long long v, Smem& sm) {
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, Smem& sm) {
     v = wave_sum_u64(v);
     if (lane_() == 0) sm.u[wave_()] = v;
     __syncthreads();
@@ -94,7 +94,7 @@ __device__ unsigned long long block_sum_u64(unsigned long long v, Smem& sm) {
     return sm.ur;
 }
 
-__device__ int block_max_int(int v, Smem& sm) {
+__device__ __forceinline__ int block_max_int(int v, Smem& sm) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
     if (lane_() == 0) sm.i[wave_()] = v;
@@ -114,7 +114,7 @@ __device__ __forceinline__ void argmax_step(float& v, int& idx, float v2, int i2
 }
 
 // (value, index) max with the smallest index among equal values.
-__device__ int block_argmax(float v, int idx, Smem& sm) {
+__device__ __forceinline__ int block_argmax(float v, int idx, Smem& sm) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) argmax_step(v, idx, __shfl_xor(v, o, kWave), __shfl_xor(idx, o, kWave));
     if (lane_() == 0) { sm.f[wave_()] = v; sm.i[wave_()] = idx; }
@@ -133,7 +133,7 @@ __device__ int block_argmax(float v, int idx, Smem& sm) {
 // Inclusive scan of v over thread order; *excl receives the exclusive prefix.
 // Adjacent threads' bounds are bitwise equal (incl_t == excl_{t+1}): wave
 // offsets are accumulated sequentially from the waves' last inclusive values.
-__device__ unsigned long long block_scan_u64(unsigned long long v, unsigned long long* excl, Smem& sm) {
+__device__ __forceinline__ unsigned long long block_scan_u64(unsigned long long v, unsigned long long* excl, Smem& sm) {
     unsigned long long x = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -154,7 +154,7 @@ __device__ unsigned long long block_scan_u64(unsigned long long v, unsigned long
     return base + x;
 }
 
-__device__ double block_scan_d(double v, double* excl, Smem& sm) {
+__device__ __forceinline__ double block_scan_d(double v, double* excl, Smem& sm) {
     double x = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -176,22 +176,22 @@ __device__ double block_scan_d(double v, double* excl, Smem& sm) {
 }
 
 // Load chunk cb of a row: out-of-range entries become -inf.
-__device__ void load_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[VPT4]) {
+__device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[VPT4]) {
 #pragma unroll
     for (int j = 0; j < VPT4; ++j) {
         const int idx = elem_index(cb, j, 0);
         if (aligned && idx + 3 < V) {
             x[j] = *(const float4*)(row + idx);
         } else {
-            float4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) f4set(v, e, (idx + e < V) ? row[idx + e] : -INFINITY);
-            x[j] = v;
+            x[j].x = idx < V ? row[idx] : -INFINITY;
+            x[j].y = idx + 1 < V ? row[idx + 1] : -INFINITY;
+            x[j].z = idx + 2 < V ? row[idx + 2] : -INFINITY;
+            x[j].w = idx + 3 < V ? row[idx + 3] : -INFINITY;
         }
     }
 }
 
-__device__ float thread_max(const float4 (&x)[VPT4]) {
+__device__ __forceinline__ float thread_max(const float4 (&x)[VPT4]) {
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < VPT4; ++j) m = fmaxf(fmaxf(fmaxf(m, x[j].x), fmaxf(x[j].y, x[j].z)), x[j].w);
@@ -229,7 +229,7 @@ __device__ __forceinline__ unsigned long long fixmass(float e) { return (unsigne
 // elements whose bits above the level equal `prefix`, then the bucket where
 // the mass counted from the top first reaches `need`.  Returns the bucket;
 // *above receives the mass of the larger buckets.
-__device__ int radix_level(const float4 (&e)[VPT4], int cb, int V, int shift, uint32_t prefix, int prefix_shift,
+__device__ __forceinline__ int radix_level(const float4 (&e)[VPT4], int cb, int V, int shift, uint32_t prefix, int prefix_shift,
                            double need, unsigned long long* above, Smem& sm) {
     const int tid = tid_();
     sm.hist[tid] = 0ull;
@@ -266,7 +266,7 @@ __device__ int radix_level(const float4 (&e)[VPT4], int cb, int V, int shift, ui
     return 1023 - t;
 }
 
-__device__ Nucleus find_nucleus(const float4 (&e)[VPT4], int cb, int V, float top_p, Smem& sm) {
+__device__ __forceinline__ Nucleus find_nucleus(const float4 (&e)[VPT4], int cb, int V, float top_p, Smem& sm) {
     unsigned long long mine = 0;
 #pragma unroll
     for (int j = 0; j < VPT4; ++j)
@@ -321,7 +321,7 @@ __device__ Nucleus find_nucleus(const float4 (&e)[VPT4], int cb, int V, float to
 // Totals of the weights of every slot j (token ids cb + 4*(t + NT*j) + e over
 // all threads t), all slots in one reduction: stored in sm.slot_tot[j]; the
 // chunk total (fp64, fixed order) is returned.
-__device__ double slot_totals(const float4 (&w)[VPT4], Smem& sm) {
+__device__ __forceinline__ double slot_totals(const float4 (&w)[VPT4], Smem& sm) {
     double sj[VPT4];
 #pragma unroll
     for (int j = 0; j < VPT4; ++j)
@@ -346,7 +346,7 @@ __device__ double slot_totals(const float4 (&w)[VPT4], Smem& sm) {
 // Smallest token id k of this chunk with base + C_k > target (C = prefix sums
 // of w in id order within the chunk), or -1 if the chunk does not reach it.
 // Needs sm.slot_tot from slot_totals(w) on the same weights.
-__device__ int locate_in_chunk(const float4 (&w)[VPT4], int cb, int V, double base, double target, Smem& sm) {
+__device__ __forceinline__ int locate_in_chunk(const float4 (&w)[VPT4], int cb, int V, double base, double target, Smem& sm) {
     double cum = base;
     int jstar = -1;
 #pragma unroll
@@ -358,10 +358,17 @@ __device__ int locate_in_chunk(const float4 (&w)[VPT4], int cb, int V, double ba
         }
     }
     if (jstar < 0) return -1;
+    // component-wise selects keep w in registers (a copy of w[jstar] would
+    // need a pointer to a runtime slot, i.e. the array in scratch memory)
     float4 wv = w[0];
 #pragma unroll
-    for (int j = 1; j < VPT4; ++j)
-        if (j == jstar) wv = w[j];
+    for (int j = 1; j < VPT4; ++j) {
+        const bool hit = j == jstar;
+        wv.x = hit ? w[j].x : wv.x;
+        wv.y = hit ? w[j].y : wv.y;
+        wv.z = hit ? w[j].z : wv.z;
+        wv.w = hit ? w[j].w : wv.w;
+    }
     const double mysum = ((double)wv.x + (double)wv.y) + ((double)wv.z + (double)wv.w);
     double excl;
     double incl = block_scan_d(mysum, &excl, sm);

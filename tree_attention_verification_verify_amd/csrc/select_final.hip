@@ -53,7 +53,7 @@ __device__ __forceinline__ float prob_at(const float* row, const RowStat& st, in
 
 // Decisions and path of sequence b (wave 0).  Fills sh; writes the per-node
 // outputs only when `write`.
-__device__ void decide(const SelectParams& P, int b, bool write, SelectShared& sh) {
+__device__ __forceinline__ void decide(const SelectParams& P, int b, bool write, SelectShared& sh) {
     const int lane = threadIdx.x;
     const int T = P.T, V = P.V;
     const size_t base = (size_t)b * T;
@@ -143,7 +143,7 @@ __device__ void decide(const SelectParams& P, int b, bool write, SelectShared& s
 // thread's inclusive/exclusive prefixes and total the block totals.
 // Wave offsets are accumulated sequentially, so adjacent threads' bounds are
 // bitwise equal and a repeated scan of the same values gives the same bits.
-__device__ void block_scan2(const double (&v)[2], double (&incl)[2], double (&excl)[2], double (&total)[2],
+__device__ __forceinline__ void block_scan2(const double (&v)[2], double (&incl)[2], double (&excl)[2], double (&total)[2],
                             SelectShared& sh) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
 #pragma unroll
@@ -182,7 +182,7 @@ __device__ void block_scan2(const double (&v)[2], double (&incl)[2], double (&ex
 
 // Draw weights of this thread's EPT token ids of slice s: w[0] residual
 // max(0, p - q) (normalised; zero unless resid), w[1] p alone (unnormalised).
-__device__ void slice_weights(const SelectParams& P, int b, int s, const SelectShared& sh, float (&wr)[EPT],
+__device__ __forceinline__ void slice_weights(const SelectParams& P, int b, int s, const SelectShared& sh, float (&wr)[EPT],
                               float (&wp)[EPT]) {
     const int T = P.T, V = P.V;
     const int x0 = s * kSelectSlice + EPT * threadIdx.x;
@@ -230,7 +230,7 @@ __device__ void slice_weights(const SelectParams& P, int b, int s, const SelectS
 }
 
 template <bool SAMPLING>
-__device__ void select_block(const SelectParams& P, int s, int b) {
+__device__ __forceinline__ void select_block(const SelectParams& P, int s, int b) {
     __shared__ SelectShared sh;
     const int tid = threadIdx.x;
     if (tid < kWave) decide(P, b, s == 0, sh);
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(ST) void finish_kernel(SelectParams P, AttnParams A
         if (SAMPLING) select_block<true>(P, blk % P.S, blk / P.S);
         else select_block<false>(P, 0, blk);
     } else {
-        combine_block<BF16, D>(A, blk - nsel);
+        combine_block<BF16, D>(A, blk - nsel, threadIdx.x);
     }
 }
 

@@ -53,7 +53,7 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 // The block's k best keys (k <= K) from every thread's sorted list `lst`
 // (consumed): written to out[0..k-1], best first, visible after the call.
 template <int K>
-__device__ void block_topk(unsigned long long (&lst)[K], int k, unsigned long long (*wave_top)[K],
+__device__ __forceinline__ void block_topk(unsigned long long (&lst)[K], int k, unsigned long long (*wave_top)[K],
                            unsigned long long* out) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int r = 0; r < k; ++r) {
