@@ -315,6 +315,42 @@ def main():
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
+    # the same step captured once in a HIP graph (its three launches) and
+    # replayed: every replay is checked against the eager outputs above, with
+    # the outputs cleared in between
+    graph = None
+    with SpecVerify(timing=False, **cfg) as sv:
+        gouts = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                sv.run(ins, gouts)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sv.run(ins, gouts)
+        torch.cuda.synchronize()
+        equal = True
+        for _ in range(3):
+            for v in gouts.values():
+                v.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            equal &= all(bool(torch.equal(gouts[k], outs[k])) for k in outs)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t5 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t5) * 1e3 / args.steps
+        graph = {"ms_per_step": gms, "value": B * T / (gms * 1e-3), "replays_equal_eager": bool(equal)}
+        del g
+
     per_launch = {k: v / max(nruns, 1) for k, v in stage_ms.items()}
 
     # KV commit of the accepted paths (spec_verify_commit) on this step's outputs: events
@@ -467,6 +503,7 @@ def main():
     }
     if other is not None:
         result["other_tree_rule"] = other
+    result["hip_graph"] = graph
     result["kv_commit"] = commit
     if spec.tree[0] == "medusa":
         result["tree_build"] = time_tree_build(spec, B, args.steps, stream)
