@@ -39,16 +39,20 @@ __device__ __forceinline__ const float* row_ptr(const StatsParams& P, int b, int
 }
 
 // WITH_Z = false (greedy mode): only the largest logit and its id are needed.
-// Each step issues U float4 loads per thread before using any of them, so a
-// row of up to U * 4 * ST logits costs one memory round trip.
+// The row streams in batches of U float4 per thread; the next batch's loads
+// are in flight while the current one is folded in.  Per logit: one max3
+// half-step, one fma and one exp2 (Z); the argmax is located only when a
+// batch raises the thread's best value (first batch, then rarely), by the
+// first position holding the batch maximum (positions are in id order).
 template <bool WITH_Z>
 __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
-    constexpr int U = kStatsUnroll;
+    constexpr int U = kStatsUnroll / 2;
     __shared__ StatsSmem sm;
     const int nrows = P.sampling ? 2 * P.T : P.T;
     const int b = blockIdx.x / nrows, r = blockIdx.x - b * nrows;
-    const float* row = row_ptr(P, b, r);
-    if (!row) return;
+    if (r == P.T) return;   // no draft row for the root
+    const float* row = r < P.T ? P.target + ((size_t)b * P.T + r) * P.V
+                               : P.draft + ((size_t)b * P.T + (r - P.T)) * P.V;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int V = P.V;
     const float ilog = P.ilog;
@@ -57,36 +61,53 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
 
     float m = -INFINITY;     // running max of this thread's logits
     double s = 0.0;          // sum of exp2((z - m) * ilog) over this thread's logits
-    float bv = -INFINITY;    // best logit and its smallest id (ids visited in increasing order)
+    float bv = -INFINITY;    // best logit and its smallest id
     int bi = INT_MAX;
 
     // fold n logits with increasing ids (id_of(k)) into the thread's running statistics
     auto absorb = [&](const float* x, int n, auto id_of) {
         float lm = -INFINITY;
-        for (int k = 0; k < n; ++k) lm = fmaxf(lm, x[k]);
-        for (int k = 0; k < n; ++k)
-            if (x[k] > bv) { bv = x[k]; bi = id_of(k); }
+        for (int k = 0; k + 1 < n; k += 2) lm = __builtin_fmaxf(lm, __builtin_fmaxf(x[k], x[k + 1]));
+        if (n & 1) lm = fmaxf(lm, x[n - 1]);
+        if (lm > bv) {   // the first position holding lm has the smallest id
+            int at = -1;
+            for (int k = n - 1; k >= 0; --k) at = (x[k] == lm) ? k : at;
+            bv = lm;
+            bi = id_of(at);
+        }
         if (!WITH_Z) return;
         if (lm > m) {
             if (m != -INFINITY) s *= exp2((double)(m - lm) * (double)ilog);
             m = lm;
         }
         if (m == -INFINITY) return;
+        const float off = -m * ilog;
         float part = 0.f;
-        for (int k = 0; k < n; ++k) part += __builtin_amdgcn_exp2f((x[k] - m) * ilog);
+        for (int k = 0; k < n; ++k) part += __builtin_amdgcn_exp2f(fmaf(x[k], ilog, off));
         s += (double)part;
     };
 
-    for (int base4 = 0; base4 < nv4; base4 += U * ST) {
-        float x[4 * U];
+    auto load = [&](int base4, float (&x)[4 * U]) {
+        const bool full = base4 + U * ST <= nv4;   // every load of the batch in range: no guards
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i4 = base4 + u * ST + tid;
             float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-            if (i4 < nv4) v = *(const float4*)(row + 4 * i4);
+            if (full || i4 < nv4) v = *(const float4*)(row + 4 * i4);
             x[4 * u] = v.x; x[4 * u + 1] = v.y; x[4 * u + 2] = v.z; x[4 * u + 3] = v.w;
         }
-        absorb(x, 4 * U, [&](int k) { return 4 * (base4 + (k >> 2) * ST + tid) + (k & 3); });
+    };
+    if (nv4 > 0) {   // two register batches in turn (unrolled by two: no copies)
+        float xa[4 * U], xb[4 * U];
+        load(0, xa);
+        for (int base4 = 0; base4 < nv4; base4 += 2 * U * ST) {
+            const int b1 = base4 + U * ST, b2 = base4 + 2 * U * ST;
+            if (b1 < nv4) load(b1, xb);
+            absorb(xa, 4 * U, [&](int k) { return 4 * (base4 + (k >> 2) * ST + tid) + (k & 3); });
+            if (b1 >= nv4) break;
+            if (b2 < nv4) load(b2, xa);
+            absorb(xb, 4 * U, [&](int k) { return 4 * (b1 + (k >> 2) * ST + tid) + (k & 3); });
+        }
     }
     for (int i = 4 * nv4 + tid; i < V; i += ST) {   // unaligned rows and the tail
         const float x[1] = {row[i]};
