@@ -34,7 +34,7 @@ def _paged_device(paged, dtype, dev="cuda"):
                 block_table=torch.from_numpy(np.ascontiguousarray(paged.block_table, dtype=np.int32)).to(dev))
 
 
-def run_paged(case, paged, label, dense_too=False):
+def run_paged(case, paged, label, dense_too=False, lossless_tree=False):
     """Paged run (and optionally the dense run of the same case) on the GPU."""
     import torch
     from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs, paged_kv
@@ -47,7 +47,7 @@ def run_paged(case, paged, label, dense_too=False):
     pk = paged_kv(pd["k_pool"], pd["v_pool"], pd["block_table"])
     res = {}
     cap = max(case.k_cache.shape[2], paged.capacity)
-    with SpecVerify(**handle_config(spec, kv_capacity=cap)) as sv:
+    with SpecVerify(**handle_config(spec, kv_capacity=cap, lossless_tree=lossless_tree)) as sv:
         outs = allocate_outputs(case.batch, case.nodes, spec.hq, spec.head_dim, spec.dtype)
         paged_ins = {k: v for k, v in ins.items() if k not in ("k_cache", "v_cache")}
         note("%s: paged run" % label)
@@ -127,6 +127,15 @@ def test_paged_full_size_gqa_medusa_equals_dense():
     got, ref = check_paged(case, paged, "paged-gqa-medusa-full", attn_rows=rows, dense_too=True)
     for k, v in got["dense"].items():
         np.testing.assert_array_equal(got["paged"][k], v, err_msg=k)
+
+
+def test_paged_with_the_lossless_tree_rule():
+    spec = synth.workload("70b-gqa-medusa", batch=3, prefix_len=260, vocab=4000, ragged=(120, 260), seed=(16, 10))
+    case, paged = synth.page_case(synth.make_case(spec), 32, seed=(16, 10))
+    got = run_paged(case, paged, "paged-lossless", lossless_tree=True)
+    ref = oracle.verify_paged(case, paged, rule="lossless", **STRICT)
+    stats = compare(case, got["paged"], ref, attn=True, rule="lossless")
+    print("paged-lossless", stats, flush=True)
 
 
 # ------------------------------------------------------------------ commit through the table

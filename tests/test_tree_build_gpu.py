@@ -116,3 +116,47 @@ def test_tree_build_rejects_bad_templates():
                 sv.build_tree(lg, rt, p, r, par[:, :T].contiguous(), tok[:, :T].contiguous())
             assert e.value.code == code, (p, r)
     torch.cuda.synchronize()
+
+
+def test_built_tree_feeds_a_greedy_verify():
+    # the construction's outputs are the verify step's parent/tokens inputs:
+    # candidates of depth 1 come from the target's own row of the root, deeper
+    # ones from a noisy copy of the target row of the first node one level up,
+    # so greedy acceptance reaches past depth 1
+    import dataclasses
+
+    import torch
+    import synth
+    from gpu_harness import compare, device_inputs, handle_config, to_numpy
+    from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs
+
+    spec = synth.workload("70b-gqa-medusa", batch=4, prefix_len=300, vocab=3000, mode="greedy", seed=(18, 1))
+    case = synth.make_case(spec)
+    caps, T = spec.tree[1], spec.tree[2]
+    parent_t, rank_t = oracle.tree_template(caps, T)
+    np.testing.assert_array_equal(case.parent[0], parent_t)
+    depth = oracle.depths(parent_t)
+    first = [depth.index(k) for k in range(max(depth) + 1)]
+    rng = np.random.default_rng(181)
+    rows = [case.target_logits[:, first[k]] + (rng.normal(0.0, 0.5, size=case.target_logits[:, 0].shape) if k else 0.0)
+            for k in range(len(caps))]
+    cand = np.stack(rows, axis=1).astype(np.float32)
+    root = case.tokens[:, 0]
+    par_o, tok_o = oracle.build_tree(cand.astype(np.float64), root, parent_t, rank_t)
+    case2 = dataclasses.replace(case, parent=par_o.astype(np.int32), tokens=tok_o.astype(np.int32))
+
+    note("tree-then-verify: B=%d T=%d V=%d" % (case.batch, T, spec.vocab))
+    ins = device_inputs(case)
+    with SpecVerify(**handle_config(spec)) as sv:
+        lg = torch.from_numpy(cand).cuda()
+        rt = torch.from_numpy(root.astype(np.int32)).cuda()
+        sv.build_tree(lg, rt, list(parent_t), list(rank_t), ins["parent"], ins["tokens"])
+        outs = allocate_outputs(case.batch, T, spec.hq, spec.head_dim, spec.dtype)
+        sv.run(ins, outs)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ins["tokens"].cpu().numpy(), tok_o)
+        np.testing.assert_array_equal(ins["parent"].cpu().numpy(), par_o)
+        got = to_numpy(outs)
+    ref = oracle.verify(case2)
+    compare(case2, got, ref)
+    assert int(ref["accept_len"].max()) >= 2, ref["accept_len"]
