@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["tree_attn.hip", "vocab_stats.hip", "select_final.hip", "lossless_walk.hip", "kv_commit.hip", "tree_build.hip", "spec_verify.hip"]
+SOURCES = ["tree_attn.hip", "tree_attn_valu.hip", "vocab_stats.hip", "select_final.hip", "lossless_walk.hip", "kv_commit.hip", "tree_build.hip", "spec_verify.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 instructions stay off (compiler flag for the device pass)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

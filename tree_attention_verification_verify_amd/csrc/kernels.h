@@ -118,6 +118,10 @@ struct TreeParams {
 // Returns hipSuccess or the launch error.
 hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s);
 hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
+// VALU attention with 4 waves sharing double-buffered tiles: R <= 8 rows per KV
+// head, K/V rows of 128 or 256 bytes (valu_tiled_supported); Rpad = rows per block.
+bool valu_tiled_supported(bool bf16, int D, int R);
+hipError_t launch_attention_valu_tiled(const AttnParams& p, bool bf16, hipStream_t s);
 hipError_t launch_row_stats(const StatsParams& p, hipStream_t s);
 // The step's last launch: selection (decisions, path, final draw) and, when
 // `merge`, the merge of the attention splits.

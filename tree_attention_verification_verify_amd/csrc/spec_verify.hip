@@ -45,6 +45,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnPlan {
     bool mfma = false;
+    bool tiled = false;     // VALU path: 4-wave tiled kernel (few rows per KV head)
     int waves = 1;          // waves per block
     int rows_per_block = 0;
     int rowblocks = 1;
@@ -63,7 +64,8 @@ AttnPlan plan_attention(const spec_verify_config& c, int B, int T) {
         p.waves = std::min(4, (R + 31) / 32);
         p.rows_per_block = 32 * p.waves;
     } else {
-        p.waves = 1;
+        p.tiled = sv::valu_tiled_supported(c.dtype == SPEC_VERIFY_BF16, c.head_dim, R);
+        p.waves = p.tiled ? 4 : 1;
         p.rows_per_block = sv::valu_rows_for(R);
     }
     p.rowblocks = (R + p.rows_per_block - 1) / p.rows_per_block;
@@ -327,7 +329,9 @@ int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_ver
     const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt((float)D);
     ap.c = scale * kLog2e;
 
-    hipError_t e = plan.mfma ? sv::launch_attention_mfma(ap, plan.waves, s) : sv::launch_attention_valu(ap, bf16, s);
+    hipError_t e = plan.mfma    ? sv::launch_attention_mfma(ap, plan.waves, s)
+                   : plan.tiled ? sv::launch_attention_valu_tiled(ap, bf16, s)
+                                : sv::launch_attention_valu(ap, bf16, s);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     if (int rc = mark(SPEC_VERIFY_STAGE_ATTENTION)) return rc;
 
