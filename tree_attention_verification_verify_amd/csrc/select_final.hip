@@ -254,19 +254,23 @@ __device__ __forceinline__ void select_block(const SelectParams& P, int s, int b
     }
     double incl[2], excl[2], tot[2];
     block_scan2(mine, incl, excl, tot, sh);
+    // Publication without a device-wide fence (which would write back the whole
+    // L2 of this XCD): the totals are stored and later read as agent-scope
+    // atomics (write-through, and reads that bypass a stale L2 copy), and the
+    // counter is bumped only after both stores have completed (vmcnt 0).
     if (tid == 0) {
-        double2* slot = P.slice_tot + (size_t)b * P.S + s;
-        *slot = make_double2(tot[0], tot[1]);
-        __threadfence();
-        const int prev = atomicAdd(P.arrive + b, 1);
+        double* slot = (double*)(P.slice_tot + (size_t)b * P.S + s);
+        __hip_atomic_store(slot, tot[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(slot + 1, tot[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        const int prev = __hip_atomic_fetch_add(P.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sh.is_last = (prev == P.S - 1);
     }
     __syncthreads();
     if (!sh.is_last) return;
 
     // last arriver: prefix over the slice totals in slice order
-    __threadfence();
-    if (tid == 0) P.arrive[b] = 0;   // ready for the next launch
+    if (tid == 0) __hip_atomic_store(P.arrive + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next launch
     constexpr int SPT = (kSelectMaxSlices + ST - 1) / ST;
     double st_mine[2] = {0.0, 0.0};
     double st_vals[SPT][2];
@@ -274,7 +278,11 @@ __device__ __forceinline__ void select_block(const SelectParams& P, int s, int b
     for (int k = 0; k < SPT; ++k) {
         const int j = tid * SPT + k;
         double2 v = make_double2(0.0, 0.0);
-        if (j < P.S) v = P.slice_tot[(size_t)b * P.S + j];
+        if (j < P.S) {
+            const double* src = (const double*)(P.slice_tot + (size_t)b * P.S + j);
+            v.x = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v.y = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         st_vals[k][0] = v.x;
         st_vals[k][1] = v.y;
         st_mine[0] += v.x;
