@@ -89,6 +89,15 @@ def test_paged_matches_oracle(name, bs, kw):
     assert np.isfinite(got["paged"]["attn_out"]).all()
 
 
+def test_paged_tiled_valu_with_prefix_splits():
+    # one sequence, long prefix, few rows: the tiled VALU kernel over several splits, through the table
+    spec = synth.CaseSpec("valu-split", 2, "bf16", 4, 4, 128, 2500, 500, "sampling", ("chain", 5),
+                          ragged=(1500, 2500), seed=(16, 11))
+    case, paged = synth.page_case(synth.make_case(spec), 16, seed=(16, 11))
+    got, ref = check_paged(case, paged, "paged-valu-split")
+    assert np.isfinite(got["paged"]["attn_out"]).all()
+
+
 def test_paged_shared_prefix_pages():
     spec = synth.workload("70b-gqa-medusa", batch=3, prefix_len=300, ragged=(200, 300), seed=(16, 7))
     case, paged = synth.page_case(synth.make_case(spec), 32, share_prefix_pages=4, seed=(16, 7))

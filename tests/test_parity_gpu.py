@@ -117,6 +117,19 @@ def test_head_dim_64_and_unaligned_vocab():
     check(synth.make_case(spec), "d64-f32-greedy")
 
 
+def test_valu_tiled_rows_of_128_bytes_and_prefix_splits():
+    # few rows per KV head, bf16 D = 64 (128-byte K/V rows): the tiled VALU kernel
+    spec = synth.CaseSpec("d64-chain", 3, "bf16", 8, 4, 64, 300, 800, "sampling", ("chain", 3), seed=(9, 12))
+    check(synth.make_case(spec), "valu-tiled-d64")
+    # one sequence with a long prefix: the tiled kernel splits the prefix and the
+    # finishing launch merges the partials (bf16 D = 128 and fp32 D = 64)
+    spec = synth.CaseSpec("valu-split", 1, "bf16", 4, 4, 128, 3000, 500, "sampling", ("chain", 5), seed=(9, 13))
+    check(synth.make_case(spec), "valu-tiled-split")
+    spec = synth.CaseSpec("valu-split-f32", 2, "f32", 4, 4, 64, 2000, 500, "greedy", ("chain", 4),
+                          ragged=(900, 2000), seed=(9, 14))
+    check(synth.make_case(spec), "valu-tiled-split-f32")
+
+
 def test_valu_gqa_rows():
     spec = synth.CaseSpec("valu-gqa", 3, "bf16", 4, 2, 128, 777, 2000, "sampling", ("chain", 4), seed=(9, 6))
     check(synth.make_case(spec), "valu-gqa")
