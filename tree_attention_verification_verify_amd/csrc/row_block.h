@@ -1,6 +1,6 @@
 // Block-wide helpers for the 1024-thread row kernels (wave64, gfx950):
 // deterministic reductions and scans, register-resident logits chunks, the
-// top-p radix select and the inverse-CDF search.  Internal to the library.
+// top-p membership test and the inverse-CDF search.  Internal to the library.
 //
 // Element layout of a chunk: thread t holds float4 slots j = 0..VPT4-1 at
 // token ids cb + 4*(t + NT*j) + e, so (j, t, e) order is token-id order and
@@ -24,17 +24,10 @@ constexpr int MAX_CHUNKS = 128;
 constexpr float kFix = 1099511627776.0f;    // 2^40: fixed-point scale of top-p masses
 
 struct Smem {
-    float f[NW];
     double d[NW];
-    unsigned long long u[NW];
     int i[NW];
     double dpre[NW + 1];
-    unsigned long long upre[NW + 1];
-    float fr;
-    double dr;
-    unsigned long long ur;
     int ir;
-    unsigned long long hist[1024];
     double chunk_sum[MAX_CHUNKS];
     double slot_part[NW][VPT4];
     double slot_tot[VPT4];
@@ -56,44 +49,8 @@ __device__ __forceinline__ void f4set(float4& v, int e, float x) {
     if (e == 0) v.x = x; else if (e == 1) v.y = x; else if (e == 2) v.z = x; else v.w = x;
 }
 
-// Block reductions: each wave reduces, wave 0 reduces the wave results in a
-// fixed order and broadcasts one value (deterministic, two barriers).
-__device__ __forceinline__ float block_max(float v, Smem& sm) {
-    v = wave_max(v);
-    if (lane_() == 0) sm.f[wave_()] = v;
-    __syncthreads();
-    if (wave_() == 0) {
-        float x = wave_max(lane_() < NW ? sm.f[lane_()] : -INFINITY);
-        if (lane_() == 0) sm.fr = x;
-    }
-    __syncthreads();
-    return sm.fr;
-}
-
-__device__ __forceinline__ double block_sum_d(double v, Smem& sm) {
-    v = wave_sum_d(v);
-    if (lane_() == 0) sm.d[wave_()] = v;
-    __syncthreads();
-    if (wave_() == 0) {
-        double x = wave_sum_d(lane_() < NW ? sm.d[lane_()] : 0.0);
-        if (lane_() == 0) sm.dr = x;
-    }
-    __syncthreads();
-    return sm.dr;
-}
-
-__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, Smem& sm) {
-    v = wave_sum_u64(v);
-    if (lane_() == 0) sm.u[wave_()] = v;
-    __syncthreads();
-    if (wave_() == 0) {
-        unsigned long long x = wave_sum_u64(lane_() < NW ? sm.u[lane_()] : 0ull);
-        if (lane_() == 0) sm.ur = x;
-    }
-    __syncthreads();
-    return sm.ur;
-}
-
+// Block maximum: each wave reduces, wave 0 reduces the wave results and
+// broadcasts (two barriers).
 __device__ __forceinline__ int block_max_int(int v, Smem& sm) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
@@ -113,47 +70,9 @@ __device__ __forceinline__ void argmax_step(float& v, int& idx, float v2, int i2
     if (v2 > v || (v2 == v && i2 < idx)) { v = v2; idx = i2; }
 }
 
-// (value, index) max with the smallest index among equal values.
-__device__ __forceinline__ int block_argmax(float v, int idx, Smem& sm) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) argmax_step(v, idx, __shfl_xor(v, o, kWave), __shfl_xor(idx, o, kWave));
-    if (lane_() == 0) { sm.f[wave_()] = v; sm.i[wave_()] = idx; }
-    __syncthreads();
-    if (wave_() == 0) {
-        float x = lane_() < NW ? sm.f[lane_()] : -INFINITY;
-        int xi = lane_() < NW ? sm.i[lane_()] : INT_MAX;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) argmax_step(x, xi, __shfl_xor(x, o, kWave), __shfl_xor(xi, o, kWave));
-        if (lane_() == 0) sm.ir = xi;
-    }
-    __syncthreads();
-    return sm.ir;
-}
-
 // Inclusive scan of v over thread order; *excl receives the exclusive prefix.
 // Adjacent threads' bounds are bitwise equal (incl_t == excl_{t+1}): wave
 // offsets are accumulated sequentially from the waves' last inclusive values.
-__device__ __forceinline__ unsigned long long block_scan_u64(unsigned long long v, unsigned long long* excl, Smem& sm) {
-    unsigned long long x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const unsigned long long y = __shfl_up(x, o, kWave);
-        if (lane_() >= o) x += y;
-    }
-    if (lane_() == kWave - 1) sm.u[wave_()] = x;
-    unsigned long long prev = __shfl_up(x, 1, kWave);
-    if (lane_() == 0) prev = 0;
-    __syncthreads();
-    if (tid_() == 0) {
-        unsigned long long acc = 0;
-        for (int w = 0; w < NW; ++w) { sm.upre[w] = acc; acc += sm.u[w]; }
-    }
-    __syncthreads();
-    const unsigned long long base = sm.upre[wave_()];
-    *excl = base + prev;
-    return base + x;
-}
-
 __device__ __forceinline__ double block_scan_d(double v, double* excl, Smem& sm) {
     double x = v;
 #pragma unroll
@@ -191,13 +110,6 @@ __device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool
     }
 }
 
-__device__ __forceinline__ float thread_max(const float4 (&x)[VPT4]) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < VPT4; ++j) m = fmaxf(fmaxf(fmaxf(m, x[j].x), fmaxf(x[j].y, x[j].z)), x[j].w);
-    return m;
-}
-
 // Unnormalised probability of a logit: exp((z - zmax) / temperature).
 __device__ __forceinline__ float unnorm(float z, float zmax, float ilog) { return exp2f((z - zmax) * ilog); }
 
@@ -224,99 +136,6 @@ __device__ __forceinline__ bool in_nucleus(float e, int idx, const Nucleus& nu) 
 }
 
 __device__ __forceinline__ unsigned long long fixmass(float e) { return (unsigned long long)__float2ull_rn(e * kFix); }
-
-// One radix level: histogram (by `shift`/`width` bits) of the mass of the
-// elements whose bits above the level equal `prefix`, then the bucket where
-// the mass counted from the top first reaches `need`.  Returns the bucket;
-// *above receives the mass of the larger buckets.
-__device__ __forceinline__ int radix_level(const float4 (&e)[VPT4], int cb, int V, int shift, uint32_t prefix, int prefix_shift,
-                           double need, unsigned long long* above, Smem& sm) {
-    const int tid = tid_();
-    sm.hist[tid] = 0ull;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < VPT4; ++j) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int idx = elem_index(cb, j, c);
-            if (idx < V) {
-                const float v = f4get(e[j], c);
-                const uint32_t bits = __float_as_uint(v);
-                if ((bits >> prefix_shift) == prefix) {
-                    const int bucket = (bits >> shift) & 1023;
-                    atomicAdd(&sm.hist[bucket], fixmass(v));
-                }
-            }
-        }
-    }
-    __syncthreads();
-    // thread t holds bucket 1023 - t: scanning thread order = descending value
-    unsigned long long excl;
-    const unsigned long long incl = block_scan_u64(sm.hist[1023 - tid], &excl, sm);
-    if (tid == 0) sm.found = -1;
-    __syncthreads();
-    if ((double)excl < need && need <= (double)incl) atomicMax(&sm.found, tid);
-    __syncthreads();
-    int t = sm.found;
-    if (t < 0) t = NT - 1;   // need above every bucket: cannot happen for need <= total
-    if (tid == t) sm.u[0] = excl;
-    __syncthreads();
-    *above = sm.u[0];
-    __syncthreads();
-    return 1023 - t;
-}
-
-__device__ __forceinline__ Nucleus find_nucleus(const float4 (&e)[VPT4], int cb, int V, float top_p, Smem& sm) {
-    unsigned long long mine = 0;
-#pragma unroll
-    for (int j = 0; j < VPT4; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (elem_index(cb, j, c) < V) mine += fixmass(f4get(e[j], c));
-    const unsigned long long total = block_sum_u64(mine, sm);
-    const double need = (double)top_p * (double)total;
-    unsigned long long a1, a2, a3;
-    const int b1 = radix_level(e, cb, V, 20, 0u, 31, need, &a1, sm);
-    const int b2 = radix_level(e, cb, V, 10, (uint32_t)b1, 20, need - (double)a1, &a2, sm);
-    const int b3 = radix_level(e, cb, V, 0, ((uint32_t)b1 << 10) | (uint32_t)b2, 10, need - (double)a1 - (double)a2,
-                               &a3, sm);
-    Nucleus nu;
-    nu.thr = ((uint32_t)b1 << 20) | ((uint32_t)b2 << 10) | (uint32_t)b3;
-    nu.cutoff = INT_MAX;
-    const unsigned long long above = a1 + a2 + a3;
-    const unsigned long long tie_mass = fixmass(__uint_as_float(nu.thr));
-    int ties = 0;
-#pragma unroll
-    for (int j = 0; j < VPT4; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (elem_index(cb, j, c) < V && __float_as_uint(f4get(e[j], c)) == nu.thr) ++ties;
-    ties = (int)block_sum_u64((unsigned long long)ties, sm);
-    if (ties > 1 && tie_mass > 0) {
-        const double rest = need - (double)above;
-        long long k = (long long)ceil(rest / (double)tie_mass);
-        if (k < 1) k = 1;
-        if (k < ties) {
-            // smallest cutoff c with #ties(idx < c) >= k, by bisection on the token id
-            int lo = 0, hi = V;
-            while (lo < hi) {
-                const int mid = lo + (hi - lo) / 2;
-                int cnt = 0;
-#pragma unroll
-                for (int j = 0; j < VPT4; ++j)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int idx = elem_index(cb, j, c);
-                        if (idx < V && idx <= mid && __float_as_uint(f4get(e[j], c)) == nu.thr) ++cnt;
-                    }
-                cnt = (int)block_sum_u64((unsigned long long)cnt, sm);
-                if (cnt >= k) hi = mid; else lo = mid + 1;
-            }
-            nu.cutoff = lo + 1;
-        }
-    }
-    return nu;
-}
 
 // Totals of the weights of every slot j (token ids cb + 4*(t + NT*j) + e over
 // all threads t), all slots in one reduction: stored in sm.slot_tot[j]; the

@@ -14,7 +14,8 @@
 // max grows), merged in a fixed order.  With top-p the cut needs every
 // probability relative to the final max: the row (V <= 32768) is held in the
 // registers of a 1024-thread workgroup and cut by a 3-level radix select on
-// the fp32 bit patterns with integer mass histograms.
+// the fp32 bit patterns with integer mass histograms (eleven barriers in all
+// unless tied probabilities straddle the cut).
 
 #include "row_block.h"
 
@@ -148,19 +149,127 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
     }
 }
 
-// Top-p rows: the whole row in registers, cut, then the nucleus normaliser.
+// ---------------------------------------------------------------------------
+// Top-p rows.  The row stays in registers; the cut is a 3-level radix select
+// (10 bits per level, from the top) on the fp32 patterns of the unnormalised
+// probabilities, with exact integer mass histograms.  Each level costs three
+// barriers: histogram; scan of the buckets in descending order inside each
+// wave; wave offsets read by every thread (integer sums, so any order gives
+// the same result) and the crossing bucket published.  The first level sees
+// every logit, so its histogram has HK copies (lane & (HK - 1)), interleaved
+// per bucket so the copies of one bucket sit in different banks: a wave's
+// 64 atomics then collide HK times less on the crowded buckets.
+constexpr int HK = 4;
+constexpr int TNW = rows::NW;
+constexpr uint32_t kZeroMassBits = 0x2B000000u;   // 2^-41: rounds to mass 0 (ties to even)
+constexpr uint32_t kOneBits = 0x3F800000u;        // 1.0
+
+struct ToppSmem {
+    unsigned long long h1[1024 * HK];   // level 1: copy c of bucket k at k * HK + c
+    unsigned long long h2[1024];
+    unsigned long long h3[1024];
+    unsigned long long wt[3][TNW];      // per level: wave totals of the bucket scan
+    unsigned long long sel_above[3];    // per level: mass of the larger buckets
+    unsigned long long sel_mass[3];     // per level: mass of the crossing bucket
+    int sel_bucket[3];
+    float bv[TNW];
+    int bi[TNW];
+    double zp[TNW];
+    unsigned long long cnt[2][TNW];
+};
+
+// One level of the cut.  Elements whose pattern above bit `PSHIFT` equals
+// `prefix` add their mass to bucket (bits >> SHIFT) & 1023.  The crossing is
+// the bucket where the mass counted from the largest bucket down first
+// reaches need (for level 0 need is top_p times the row total, which only
+// the scan knows); without a crossing (need outside (0, total]) bucket 0.
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Returns need (level 0: the one it computed).
+template <int L>
+__device__ __forceinline__ double topp_level(const float4 (&e)[rows::VPT4], int V, uint32_t prefix, double need,
+                                             float top_p, ToppSmem& sm) {
+    using namespace rows;
+    constexpr int SHIFT = 20 - 10 * L;
+    constexpr int PSHIFT = L == 0 ? 31 : 30 - 10 * L;
+    constexpr int HC = L == 0 ? HK : 1;
+    unsigned long long* h = L == 0 ? sm.h1 : (L == 1 ? sm.h2 : sm.h3);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int copy = L == 0 ? (lane & (HK - 1)) : 0;
+    // only masses in (0, 2^40] count: entries past the row end (e = 0),
+    // probabilities at or below 2^-41 (zero in fixed point) and non-numbers
+    // add nothing
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float v = f4get(e[j], c);
+            const uint32_t bits = __float_as_uint(v);
+            if (bits > kZeroMassBits && bits <= kOneBits && (bits >> PSHIFT) == prefix)
+                atomicAdd(&h[((bits >> SHIFT) & 1023) * HC + copy], fixmass(v));
+        }
+    __syncthreads();
+    const int bk = 1023 - tid;   // thread order = descending bucket
+    unsigned long long x = 0;
+#pragma unroll
+    for (int c = 0; c < HC; ++c) x += h[bk * HC + c];
+    unsigned long long incl = x;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned long long y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) sm.wt[L][wave] = incl;
+    __syncthreads();
+    // lanes 0..TNW-1 scan the wave totals; this wave's offset and the total
+    // are then read from single lanes
+    unsigned long long wsc = lane < TNW ? sm.wt[L][lane] : 0ull;
+#pragma unroll
+    for (int o = 1; o < TNW; o <<= 1) {
+        const unsigned long long y = __shfl_up(wsc, o, kWave);
+        if (lane >= o) wsc += y;
+    }
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const unsigned long long total = readlane_u64(wsc, TNW - 1);
+    incl += wv > 0 ? readlane_u64(wsc, wv - 1) : 0ull;
+    const unsigned long long excl = incl - x;
+    if (L == 0) need = (double)top_p * (double)total;
+    // (double)excl and (double)incl tile (0, (double)total] without gaps, so a
+    // crossing exists exactly when need lies in that range, and is unique
+    const bool exists = 0.0 < need && need <= (double)total;
+    if (exists ? ((double)excl < need && need <= (double)incl) : tid == NT - 1) {
+        sm.sel_bucket[L] = bk;
+        sm.sel_above[L] = excl;
+        sm.sel_mass[L] = x;
+    }
+    __syncthreads();
+    return need;
+}
+
 __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P) {
     using namespace rows;
-    __shared__ Smem sm;
+    __shared__ ToppSmem sm;
     const int nrows = 2 * P.T;
     const int b = blockIdx.x / nrows, r = blockIdx.x - b * nrows;
     const float* row = row_ptr(P, b, r);
     if (!row) return;
     const int V = P.V;
     const float ilog = P.ilog;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const bool aligned = (((uintptr_t)row) & 15) == 0;
     float4 e[VPT4];
     load_chunk(row, V, 0, aligned, e);
+    // cleared histograms are ordered before their atomics by the next barrier
+#pragma unroll
+    for (int k = 0; k < HK; ++k) sm.h1[k * NT + tid] = 0ull;
+    sm.h2[tid] = 0ull;
+    sm.h3[tid] = 0ull;
+
+    // largest logit and its smallest id (the largest logit is zmax)
     float bv = -INFINITY;
     int bi = INT_MAX;
 #pragma unroll
@@ -171,13 +280,66 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
             const float v = f4get(e[j], c);
             if (idx < V && (v > bv || (v == bv && idx < bi))) { bv = v; bi = idx; }
         }
-    const int best = block_argmax(bv, bi, sm);
-    const float M = block_max(thread_max(e), sm);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) argmax_step(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
+    if (lane == 0) { sm.bv[wave] = bv; sm.bi[wave] = bi; }
+    __syncthreads();
+    float M = sm.bv[0];
+    int best = sm.bi[0];
+#pragma unroll
+    for (int w = 1; w < TNW; ++w) argmax_step(M, best, sm.bv[w], sm.bi[w]);
 #pragma unroll
     for (int j = 0; j < VPT4; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c) f4set(e[j], c, unnorm(f4get(e[j], c), M, ilog));
-    const Nucleus nu = find_nucleus(e, 0, V, P.top_p, sm);
+
+    // the cut
+    const double need = topp_level<0>(e, V, 0u, 0.0, P.top_p, sm);
+    const uint32_t b1 = (uint32_t)sm.sel_bucket[0];
+    const unsigned long long a1 = sm.sel_above[0];
+    topp_level<1>(e, V, b1, need - (double)a1, P.top_p, sm);
+    const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
+    const unsigned long long a2 = sm.sel_above[1];
+    topp_level<2>(e, V, (b1 << 10) | b2, need - (double)a1 - (double)a2, P.top_p, sm);
+    Nucleus nu;
+    nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
+    nu.cutoff = INT_MAX;
+    // every element of the last bucket has the pattern thr, so its mass is
+    // (number of ties) * (mass of one)
+    const unsigned long long tie_mass = fixmass(__uint_as_float(nu.thr));
+    if (tie_mass > 0) {
+        const unsigned long long ties = sm.sel_mass[2] / tie_mass;
+        const unsigned long long above = a1 + a2 + sm.sel_above[2];
+        long long k = (long long)ceil((need - (double)above) / (double)tie_mass);
+        if (k < 1) k = 1;
+        if (ties > 1 && (unsigned long long)k < ties) {
+            // ties straddle the cut: the smallest cutoff c with #ties(id < c) >= k,
+            // by bisection on the token id (block counts, alternating buffers)
+            int lo = 0, hi = V, par = 0;
+            while (lo < hi) {
+                const int mid = lo + (hi - lo) / 2;
+                unsigned long long cnt = 0;
+#pragma unroll
+                for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int idx = elem_index(0, j, c);
+                        if (idx < V && idx <= mid && __float_as_uint(f4get(e[j], c)) == nu.thr) ++cnt;
+                    }
+                cnt = wave_sum_u64(cnt);
+                if (lane == 0) sm.cnt[par][wave] = cnt;
+                __syncthreads();
+                unsigned long long tot = 0;
+#pragma unroll
+                for (int w = 0; w < TNW; ++w) tot += sm.cnt[par][w];
+                par ^= 1;
+                if (tot >= (unsigned long long)k) hi = mid; else lo = mid + 1;
+            }
+            nu.cutoff = lo + 1;
+        }
+    }
+
+    // normaliser of the nucleus: fp64, fixed order
     double s = 0.0;
 #pragma unroll
     for (int j = 0; j < VPT4; ++j)
@@ -186,8 +348,12 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
             const float v = f4get(e[j], c);
             if (in_nucleus(v, elem_index(0, j, c), nu)) s += (double)v;
         }
-    const double Z = block_sum_d(s, sm);
-    if (threadIdx.x == 0) {
+    s = wave_sum_d(s);
+    if (lane == 0) sm.zp[wave] = s;
+    __syncthreads();
+    if (tid == 0) {
+        double Z = 0.0;
+        for (int w = 0; w < TNW; ++w) Z += sm.zp[w];
         RowStat st;
         st.zmax = M;
         st.argmax = best;
