@@ -110,8 +110,12 @@ __device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool
     }
 }
 
-// Unnormalised probability of a logit: exp((z - zmax) / temperature).
-__device__ __forceinline__ float unnorm(float z, float zmax, float ilog) { return exp2f((z - zmax) * ilog); }
+// Unnormalised probability of a logit: exp((z - zmax) / temperature), by the
+// hardware base-2 exponential (results below 2^-126, far under any weight a
+// decision can resolve, may flush to zero).  Every kernel computes it here.
+__device__ __forceinline__ float unnorm(float z, float zmax, float ilog) {
+    return __builtin_amdgcn_exp2f((z - zmax) * ilog);
+}
 
 // max(0, p - q) from unnormalised values and inverse normalisers.  Both
 // products are rounded before the subtraction (contraction into a fused

@@ -14,8 +14,9 @@
 // max grows), merged in a fixed order.  With top-p the cut needs every
 // probability relative to the final max: the row (V <= 32768) is held in the
 // registers of a 1024-thread workgroup and cut by a 3-level radix select on
-// the fp32 bit patterns with integer mass histograms (eleven barriers in all
-// unless tied probabilities straddle the cut).
+// the fp32 bit patterns with integer mass histograms (ten barriers in all
+// unless tied probabilities straddle the cut); the nucleus normaliser is its
+// exact integer mass.
 
 #include "row_block.h"
 
@@ -174,7 +175,6 @@ struct ToppSmem {
     int sel_bucket[3];
     float bv[TNW];
     int bi[TNW];
-    double zp[TNW];
     unsigned long long cnt[2][TNW];
 };
 
@@ -269,16 +269,18 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
     sm.h2[tid] = 0ull;
     sm.h3[tid] = 0ull;
 
-    // largest logit and its smallest id (the largest logit is zmax)
+    // largest logit and its smallest id (the largest logit is zmax): the
+    // thread's maximum, then the first of its positions (in id order) holding it
     float bv = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j) bv = fmaxf(fmaxf(bv, fmaxf(e[j].x, e[j].y)), fmaxf(e[j].z, e[j].w));
     int bi = INT_MAX;
 #pragma unroll
-    for (int j = 0; j < VPT4; ++j)
+    for (int j = VPT4 - 1; j >= 0; --j)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 3; c >= 0; --c) {
             const int idx = elem_index(0, j, c);
-            const float v = f4get(e[j], c);
-            if (idx < V && (v > bv || (v == bv && idx < bi))) { bv = v; bi = idx; }
+            bi = (f4get(e[j], c) == bv && idx < V) ? idx : bi;
         }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) argmax_step(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
@@ -304,17 +306,19 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
     Nucleus nu;
     nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
     nu.cutoff = INT_MAX;
-    // every element of the last bucket has the pattern thr, so its mass is
-    // (number of ties) * (mass of one)
+    // masses above thr, and of the elements at thr (all of the last bucket:
+    // (number of ties) * (mass of one))
+    const unsigned long long above = a1 + a2 + sm.sel_above[2];
+    unsigned long long kept = sm.sel_mass[2];
     const unsigned long long tie_mass = fixmass(__uint_as_float(nu.thr));
     if (tie_mass > 0) {
-        const unsigned long long ties = sm.sel_mass[2] / tie_mass;
-        const unsigned long long above = a1 + a2 + sm.sel_above[2];
+        const unsigned long long ties = kept / tie_mass;
         long long k = (long long)ceil((need - (double)above) / (double)tie_mass);
         if (k < 1) k = 1;
         if (ties > 1 && (unsigned long long)k < ties) {
             // ties straddle the cut: the smallest cutoff c with #ties(id < c) >= k,
-            // by bisection on the token id (block counts, alternating buffers)
+            // by bisection on the token id (block counts, alternating buffers);
+            // exactly k ties then lie below the cutoff
             int lo = 0, hi = V, par = 0;
             while (lo < hi) {
                 const int mid = lo + (hi - lo) / 2;
@@ -336,30 +340,19 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
                 if (tot >= (unsigned long long)k) hi = mid; else lo = mid + 1;
             }
             nu.cutoff = lo + 1;
+            kept = (unsigned long long)k * tie_mass;
         }
     }
-
-    // normaliser of the nucleus: fp64, fixed order
-    double s = 0.0;
-#pragma unroll
-    for (int j = 0; j < VPT4; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float v = f4get(e[j], c);
-            if (in_nucleus(v, elem_index(0, j, c), nu)) s += (double)v;
-        }
-    s = wave_sum_d(s);
-    if (lane == 0) sm.zp[wave] = s;
-    __syncthreads();
     if (tid == 0) {
-        double Z = 0.0;
-        for (int w = 0; w < TNW; ++w) Z += sm.zp[w];
+        // normaliser of the nucleus from its exact fixed-point mass: each
+        // element is rounded by at most 2^-41 and the sum holds the top
+        // element (e = 1), so the relative error is at most V * 2^-41
         RowStat st;
         st.zmax = M;
         st.argmax = best;
         st.thr = nu.thr;
         st.cutoff = nu.cutoff;
-        st.Z = Z;
+        st.Z = (double)(above + kept) * (1.0 / (double)kFix);
         P.stats[(size_t)b * nrows + r] = st;
     }
 }
