@@ -61,13 +61,13 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 // rounds cover any depth below 64.  Lane i handles node i (T <= 64).  Nodes
 // whose parent entry is invalid (root not -1, or not 0 <= parent[i] < i) get
 // only their own bit; *bad is set for the whole wave in that case.
-__device__ __forceinline__ unsigned long long ancestor_mask(const int32_t* parent_row, int T,
-                                                            bool* bad) {
+// p_in: parent[lane] as loaded by the caller (ignored for lanes >= T).
+__device__ __forceinline__ unsigned long long ancestor_mask_of(int p_in, int T, bool* bad) {
     const int lane = threadIdx.x & (kWave - 1);
     int p = -1;
     bool invalid = false;
     if (lane < T) {
-        p = parent_row[lane];
+        p = p_in;
         if (lane == 0) invalid = (p != -1);
         else invalid = (p < 0 || p >= lane);
         if (invalid) p = -1;
@@ -85,6 +85,11 @@ __device__ __forceinline__ unsigned long long ancestor_mask(const int32_t* paren
     }
     *bad = __any(invalid);
     return a;
+}
+
+__device__ __forceinline__ unsigned long long ancestor_mask(const int32_t* parent_row, int T, bool* bad) {
+    const int lane = threadIdx.x & (kWave - 1);
+    return ancestor_mask_of(lane < T ? parent_row[lane] : -1, T, bad);
 }
 
 // Paged caches: whether some block-table entry of sequence b's slots

@@ -78,6 +78,7 @@ struct SelectParams {
     uint8_t* node_accept;
     uint8_t* final_from_residual;
     double2* slice_tot;   // [B][S] (residual, p-only) weight totals per slice of the final draw
+    double2* slice_pre;   // [B][S][kSelectThreads] per-thread exclusive prefixes (S <= kSelectKeepSlices)
     float* resid_ws;      // [B][2][V] residual rows of the lossless sibling walk
     int32_t* arrive;      // [B] slices done; reset to 0 by the last one
     int B, T, V, Lcap;
@@ -143,5 +144,6 @@ constexpr int kStatsUnroll = 16;                  // float4 loads in flight per 
 constexpr int kSelectThreads = 256;               // selection / final draw workgroups
 constexpr int kSelectSlice = 2048;                // token ids per final-draw slice
 constexpr int kSelectMaxSlices = 2048;            // vocab <= 4194304
+constexpr int kSelectKeepSlices = 64;             // up to this many slices the draw keeps slice prefixes
 
 }  // namespace sv

@@ -121,6 +121,7 @@ struct spec_verify_handle {
     float2* part_ml = nullptr;
     sv::RowStat* stats = nullptr;     // max_batch * 2 * max_nodes row statistics
     double2* slice_tot = nullptr;     // max_batch * slices final-draw slice totals
+    double2* slice_pre = nullptr;     // max_batch * slices * 256 per-thread slice prefixes (few slices only)
     int32_t* arrive = nullptr;        // max_batch final-draw arrival counters (zero between runs)
     float* resid_ws = nullptr;        // max_batch * 2 * vocab residual rows (lossless tree walk)
     bool timing = false;
@@ -196,6 +197,8 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
     e = hipMalloc((void**)&h->stats, (size_t)c.max_batch * 2 * c.max_nodes * sizeof(sv::RowStat));
     const int slices = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
     if (e == hipSuccess) e = hipMalloc((void**)&h->slice_tot, (size_t)c.max_batch * slices * sizeof(double2));
+    if (e == hipSuccess && c.mode == SPEC_VERIFY_SAMPLING && slices <= sv::kSelectKeepSlices)
+        e = hipMalloc((void**)&h->slice_pre, (size_t)c.max_batch * slices * sv::kSelectThreads * sizeof(double2));
     if (e == hipSuccess) e = hipMalloc((void**)&h->arrive, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(h->arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE))
@@ -204,6 +207,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
     if (e != hipSuccess) {
         (void)hipFree(h->stats);
         (void)hipFree(h->slice_tot);
+        (void)hipFree(h->slice_pre);
         (void)hipFree(h->arrive);
         (void)hipFree(h->resid_ws);
         (void)hipFree(h->part_o);
@@ -239,6 +243,7 @@ int spec_verify_destroy(spec_verify_handle* h) {
     if (h->part_ml) (void)hipFree(h->part_ml);
     if (h->stats) (void)hipFree(h->stats);
     if (h->slice_tot) (void)hipFree(h->slice_tot);
+    if (h->slice_pre) (void)hipFree(h->slice_pre);
     if (h->arrive) (void)hipFree(h->arrive);
     if (h->resid_ws) (void)hipFree(h->resid_ws);
     if (dev >= 0 && dev != h->device) (void)hipSetDevice(dev);
@@ -376,6 +381,7 @@ int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_ver
     sp.sampling = sampling ? 1 : 0;
     sp.ilog = tp.ilog;
     sp.slice_tot = h->slice_tot;
+    sp.slice_pre = h->slice_pre;
     sp.arrive = h->arrive;
     sp.S = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
     sp.resid_ws = h->resid_ws;
