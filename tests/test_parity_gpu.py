@@ -65,6 +65,14 @@ def test_large_vocab_tree_short_prefix():
     check(synth.make_case(spec), "bigvocab-L400")
 
 
+@pytest.mark.parametrize("vocab", [131072, 131073, 200000])
+def test_final_draw_slice_counts(vocab):
+    # up to 64 slices of 2048 ids the last workgroup reads the kept slice
+    # prefixes; beyond that it scans the chosen slice again
+    spec = synth.workload("longctx-bigvocab", batch=2, prefix_len=200, vocab=vocab, seed=(4, vocab % 997))
+    check(synth.make_case(spec), "draw-V%d" % vocab)
+
+
 # ------------------------------------------------------------------ full sizes, sampled attention rows
 
 def _full(name, picks, **kw):

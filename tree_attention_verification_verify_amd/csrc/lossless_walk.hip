@@ -286,10 +286,271 @@ __global__ __launch_bounds__(NT) void lossless_walk_kernel(SelectParams P) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Vocabularies of one chunk (V <= 32768): r stays in the workgroup's
+// registers.  Wave 0 first computes every first test of the walk (p of the
+// parent and q of the child at the child's token, as the independent rule
+// does), so a test needs no global load: p_parent(x_c) while r is still p_v,
+// else r(x_c) / W, which the thread holding x_c records during the residual
+// pass that produced r.  A rejection is then one read of q_c's row (and of
+// p_v's row at the first rejection under v) plus one fixed-order sum.
+
+struct WalkRes {
+    unsigned long long kids_of[64];
+    float pv0[64];              // p_parent(c)(x_c)
+    float qv[64];               // q_c(x_c)
+    float u[64];                // u_accept
+    int tok[64];
+    float qzmax[64];            // statistics of the draft row of each node
+    uint32_t qthr[64];
+    int qcut[64];
+    double qZ[64];
+    float rx[2][2];             // per pass (alternating): r_new and r_old at the next child's token
+    double wsum[2][NW];         // per pass (alternating): wave totals of the residual
+    int live;
+};
+
+// Total of w over the workgroup in a fixed order (one barrier): per thread in
+// slot order, per wave by the butterfly, then the wave totals in wave order.
+// Consecutive calls must alternate `buf`.
+__device__ __forceinline__ double block_total(const float4 (&w)[VPT4], double (&wsum)[2][NW], int buf) {
+    double t = 0.0;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j) t += ((double)w[j].x + (double)w[j].y) + ((double)w[j].z + (double)w[j].w);
+    t = wave_sum_d(t);
+    if (lane_() == 0) wsum[buf][wave_()] = t;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) tot += wsum[buf][k];
+    return tot;
+}
+
+__device__ __forceinline__ RowStat shfl_row_stat(const RowStat& s, int src) {
+    RowStat o;
+    o.zmax = __shfl(s.zmax, src, kWave);
+    o.argmax = __shfl(s.argmax, src, kWave);
+    o.thr = (uint32_t)__shfl((int)s.thr, src, kWave);
+    o.cutoff = __shfl(s.cutoff, src, kWave);
+    o.Z = __shfl(s.Z, src, kWave);
+    return o;
+}
+
+// w at slot (j, e) of this thread; j and e are the same in every lane
+__device__ __forceinline__ float pick(const float4 (&w)[VPT4], int j, int e) {
+    float r = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < VPT4; ++jj)
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) r = (jj == j && ee == e) ? f4get(w[jj], ee) : r;
+    return r;
+}
+
+__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// p_v's weights (unnormalised, in v's nucleus) over the single chunk; past V
+// the logits read as -inf and weigh 0 (a row without a finite logit weighs 0
+// everywhere)
+__device__ __forceinline__ void p_weights(const SelectParams& P, int b, int v, const RowStat& sp, float4 (&w)[VPT4]) {
+    const float* zp = P.target + ((size_t)b * P.T + v) * P.V;
+    load_chunk(zp, P.V, 0, (((uintptr_t)zp) & 15) == 0, w);
+    const Nucleus np{sp.thr, sp.cutoff};
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float pe = unnorm(f4get(w[j], e), sp.zmax, P.ilog);
+            f4set(w[j], e, (pe > 0.f && in_nucleus(pe, elem_index(0, j, e), np)) ? pe : 0.f);
+        }
+}
+
+__global__ __launch_bounds__(NT) void lossless_walk_resident_kernel(SelectParams P) {
+    __shared__ Smem sm;
+    __shared__ WalkRes ws;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int T = P.T, V = P.V;
+    const size_t base = (size_t)b * T;
+    const RowStat* st = P.stats + (size_t)b * 2 * T;
+
+    if (tid < kWave) {
+        const int lane = tid;
+        const bool live = lane < T;
+        const int par_in = live ? P.parent[base + lane] : -1;
+        const int tok = live ? P.tokens[base + lane] : 0;
+        RowStat sl{0.f, 0, 0u, 0, 1.0};
+        RowStat sq{0.f, 0, 0u, 0, 1.0};
+        float u = 0.f;
+        if (live) sl = st[lane];
+        if (live && lane >= 1) {
+            sq = st[T + lane];
+            u = P.u_accept[base + lane];
+        }
+        const int L = P.kv_len[b];
+        bool bad_parent;
+        (void)ancestor_mask_of(par_in, T, &bad_parent);
+        const bool bad_token = __any(live && lane >= 1 && (tok < 0 || tok >= V));
+        bool bad_kv = (L < 0) || (L > P.Lcap - T);
+        bad_kv = bad_kv || __any(page_entries_bad(P.pt, b, L + T, lane, kWave));   // paged: L + T <= Lcap here
+        int status = (bad_parent ? 1 : 0) | (bad_token ? 2 : 0) | (bad_kv ? 8 : 0);
+        if (live) {
+            P.row_token[base + lane] = sl.argmax;
+            P.node_accept[base + lane] = (lane == 0) ? 1 : 0;
+            P.node_p[base + lane] = 0.f;
+            P.node_q[base + lane] = 0.f;
+            P.path[base + lane] = (lane == 0 && !bad_parent && !bad_token) ? 0 : -1;
+            P.out_tokens[base + lane] = -1;
+        }
+        if (bad_parent || bad_token) {
+            if (lane == 0) {
+                P.accept_len[b] = 0;
+                P.final_node[b] = -1;
+                P.final_from_residual[b] = 0;
+                P.status[b] = status;
+                ws.live = 0;
+            }
+        } else {
+            const int par = par_in;   // valid: parent < node for every node >= 1
+            const RowStat spar = shfl_row_stat(sl, par >= 0 ? par : 0);
+            float pv = 0.f, qv = 0.f;
+            if (live && lane >= 1) {
+                const float zt = P.target[(base + par) * V + tok];
+                const float zd = P.draft[(base + lane) * V + tok];
+                const float et = unnorm(zt, spar.zmax, P.ilog), ed = unnorm(zd, sq.zmax, P.ilog);
+                const Nucleus nt{spar.thr, spar.cutoff}, nd{sq.thr, sq.cutoff};
+                pv = in_nucleus(et, tok, nt) ? (float)((double)et / spar.Z) : 0.f;
+                qv = in_nucleus(ed, tok, nd) ? (float)((double)ed / sq.Z) : 0.f;
+            }
+            // status bit 4: some supplied draft gives its own token probability 0
+            if (__any(live && lane >= 1 && !(qv > 0.f))) status |= 4;
+            for (int n = 0; n < T; ++n) {
+                const unsigned long long k = __ballot(live && lane >= 1 && par == n);
+                if (lane == 0) ws.kids_of[n] = k;
+            }
+            ws.pv0[lane] = pv;
+            ws.qv[lane] = qv;
+            ws.u[lane] = u;
+            ws.tok[lane] = tok;
+            ws.qzmax[lane] = sq.zmax;
+            ws.qthr[lane] = sq.thr;
+            ws.qcut[lane] = sq.cutoff;
+            ws.qZ[lane] = sq.Z;
+            if (lane == 0) {
+                P.status[b] = status;
+                ws.live = 1;
+            }
+        }
+    }
+    __syncthreads();
+    if (!ws.live) return;
+
+    // walk state, the same in every thread (kept in scalar registers)
+    int v = 0, depth = 0, pass = 0;
+    unsigned long long kids = uniform_u64(ws.kids_of[0]);
+    bool fresh = true;     // r = p_v
+    bool have_r = false;   // rr holds r's weights
+    double W = 0.0;        // total of r when it is a residual
+    float rx_next = 0.f;   // r(x) / W for the next child when r is a residual
+    float4 rr[VPT4];
+    for (int round = 0; round < 2 * 64 + 1; ++round) {
+        int c = -1;
+        if (kids != 0ull) {
+            c = __builtin_ctzll(kids);
+            const float rx = fresh ? ws.pv0[c] : rx_next;
+            const float qx = ws.qv[c];
+            const bool acc = (qx > 0.f) && (ws.u[c] < rx / qx);
+            if (tid == 0) {
+                P.node_p[base + c] = rx;
+                P.node_q[base + c] = qx;
+            }
+            if (acc) {
+                if (tid == 0) {
+                    P.node_accept[base + c] = 1;
+                    P.out_tokens[base + depth] = ws.tok[c];
+                    P.path[base + depth + 1] = c;
+                }
+                depth += 1;
+                v = c;
+                kids = uniform_u64(ws.kids_of[c]);
+                fresh = true;
+                have_r = false;
+                continue;
+            }
+            kids &= ~(1ull << c);
+        }
+        // a rejection, or the end of the walk: both need r's weights
+        if (!have_r) {
+            p_weights(P, b, v, st[v], rr);
+            have_r = true;
+        }
+        if (c < 0) break;
+        // r <- [r - q_c]_+ in registers
+        float4 q[VPT4];
+        const float* zq = P.draft + (base + c) * V;
+        load_chunk(zq, V, 0, (((uintptr_t)zq) & 15) == 0, q);
+        const Nucleus nq{ws.qthr[c], ws.qcut[c]};
+        const float qzmax = ws.qzmax[c];
+        const float iq = (float)(1.0 / ws.qZ[c]);
+        const float ir = fresh ? (float)(1.0 / st[v].Z) : (float)(1.0 / W);
+        // the next child's token x2 sits in slot (j2, e2) of thread t2
+        const int c2 = kids ? __builtin_ctzll(kids) : -1;
+        const int x2 = __builtin_amdgcn_readfirstlane(c2 >= 0 ? ws.tok[c2] : 0);
+        const int t2 = (x2 >> 2) & (NT - 1), j2 = x2 / (4 * NT), e2 = x2 & 3;
+        const int buf = pass & 1;
+        if (c2 >= 0 && tid == t2) ws.rx[buf][1] = pick(rr, j2, e2);   // r kept
+        // past V both weights are 0, so is the residual
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float qe = unnorm(f4get(q[j], e), qzmax, P.ilog);
+                if (!in_nucleus(qe, elem_index(0, j, e), nq)) qe = 0.f;
+                f4set(q[j], e, resid_weight(f4get(rr[j], e), ir, qe, iq));
+            }
+        if (c2 >= 0 && tid == t2) ws.rx[buf][0] = pick(q, j2, e2);    // r new
+        const double Wn = block_total(q, ws.wsum, buf);   // its barrier also publishes rx
+        if (Wn > 0.0) {
+#pragma unroll
+            for (int j = 0; j < VPT4; ++j) rr[j] = q[j];
+            W = Wn;
+            fresh = false;
+            if (c2 >= 0) rx_next = (float)((double)ws.rx[buf][0] / W);
+        } else if (!fresh && c2 >= 0) {   // a vanishing residual keeps r
+            rx_next = (float)((double)ws.rx[buf][1] / W);
+        }
+        ++pass;
+    }
+
+    // the final draw from r: y = min{k : u * W < C_k} in token-id order
+    const double Wd = slot_totals(rr, sm);
+    int y = locate_in_chunk(rr, 0, V, 0.0, (double)P.u_final[b] * Wd, sm);
+    if (y < 0) {
+        int last = -1;
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (f4get(rr[j], e) > 0.f) last = max(last, elem_index(0, j, e));
+        y = block_max_int(last, sm);
+    }
+    if (tid == 0) {
+        P.out_tokens[base + depth] = y;
+        P.accept_len[b] = depth;
+        P.final_node[b] = v;
+        P.final_from_residual[b] = ws.kids_of[v] != 0ull ? 1 : 0;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(lossless_walk_kernel, dim3(p.B), dim3(NT), 0, s, p);
+    if (p.V <= CHUNK)
+        hipLaunchKernelGGL(lossless_walk_resident_kernel, dim3(p.B), dim3(NT), 0, s, p);
+    else
+        hipLaunchKernelGGL(lossless_walk_kernel, dim3(p.B), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
