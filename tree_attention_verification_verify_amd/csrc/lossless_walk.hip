@@ -61,13 +61,14 @@ __device__ __forceinline__ void r_weights(const SelectParams& P, int b, const Wa
         load_chunk(zp, V, cb, (((uintptr_t)zp) & 15) == 0, w);
         const RowStat sp = P.stats[(size_t)b * 2 * T + ws.v];
         const Nucleus np{sp.thr, sp.cutoff};
+        const bool all = keeps_all(np);
 #pragma unroll
         for (int j = 0; j < VPT4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int idx = elem_index(cb, j, e);
                 float pe = unnorm(f4get(w[j], e), sp.zmax, P.ilog);
-                if (idx >= V || !in_nucleus(pe, idx, np)) pe = 0.f;
+                if (idx >= V || !(all || in_nucleus(pe, idx, np))) pe = 0.f;
                 f4set(w[j], e, pe);
             }
     }
@@ -93,6 +94,7 @@ __device__ __forceinline__ double residual_pass(const SelectParams& P, int b, in
     const int T = P.T, V = P.V;
     const RowStat sq = P.stats[(size_t)b * 2 * T + T + c];
     const Nucleus nq{sq.thr, sq.cutoff};
+    const bool all = keeps_all(nq);
     const float iq = (float)(1.0 / sq.Z);
     const float ir = ws.r_ws ? (float)(1.0 / ws.W) : (float)(1.0 / P.stats[(size_t)b * 2 * T + ws.v].Z);
     const float* zq = P.draft + ((size_t)b * T + c) * V;
@@ -109,7 +111,7 @@ __device__ __forceinline__ double residual_pass(const SelectParams& P, int b, in
             for (int e = 0; e < 4; ++e) {
                 const int idx = elem_index(cb, j, e);
                 float qe = unnorm(f4get(q[j], e), sq.zmax, P.ilog);
-                if (idx >= V || !in_nucleus(qe, idx, nq)) qe = 0.f;
+                if (idx >= V || !(all || in_nucleus(qe, idx, nq))) qe = 0.f;
                 f4set(q[j], e, idx < V ? resid_weight(f4get(r[j], e), ir, qe, iq) : 0.f);
             }
         store_chunk(out, V, cb, q);
@@ -359,12 +361,13 @@ __device__ __forceinline__ void p_weights(const SelectParams& P, int b, int v, c
     const float* zp = P.target + ((size_t)b * P.T + v) * P.V;
     load_chunk(zp, P.V, 0, (((uintptr_t)zp) & 15) == 0, w);
     const Nucleus np{sp.thr, sp.cutoff};
+    const bool all = keeps_all(np);
 #pragma unroll
     for (int j = 0; j < VPT4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float pe = unnorm(f4get(w[j], e), sp.zmax, P.ilog);
-            f4set(w[j], e, (pe > 0.f && in_nucleus(pe, elem_index(0, j, e), np)) ? pe : 0.f);
+            f4set(w[j], e, (pe > 0.f && (all || in_nucleus(pe, elem_index(0, j, e), np))) ? pe : 0.f);
         }
 }
 
@@ -505,11 +508,18 @@ __global__ __launch_bounds__(NT) void lossless_walk_resident_kernel(SelectParams
 #pragma unroll
         for (int j = 0; j < VPT4; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float qe = unnorm(f4get(q[j], e), qzmax, P.ilog);
-                if (!in_nucleus(qe, elem_index(0, j, e), nq)) qe = 0.f;
-                f4set(q[j], e, resid_weight(f4get(rr[j], e), ir, qe, iq));
-            }
+            for (int e = 0; e < 4; ++e) f4set(q[j], e, unnorm(f4get(q[j], e), qzmax, P.ilog));
+        if (!keeps_all(nq)) {
+#pragma unroll
+            for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!in_nucleus(f4get(q[j], e), elem_index(0, j, e), nq)) f4set(q[j], e, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f4set(q[j], e, resid_weight(f4get(rr[j], e), ir, f4get(q[j], e), iq));
         if (c2 >= 0 && tid == t2) ws.rx[buf][0] = pick(q, j2, e2);    // r new
         const double Wn = block_total(q, ws.wsum, buf);   // its barrier also publishes rx
         if (Wn > 0.0) {

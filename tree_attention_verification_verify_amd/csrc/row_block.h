@@ -94,19 +94,43 @@ __device__ __forceinline__ double block_scan_d(double v, double* excl, Smem& sm)
     return base + x;
 }
 
-// Load chunk cb of a row: out-of-range entries become -inf.
+// Buffer resource of a row of V floats (the row pointer is the same in every
+// lane; reads at or past V return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int V) {
+    const uint64_t a = (uint64_t)(uintptr_t)row;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, V * 4, 0x00020000);
+}
+
+// Load chunk cb of a row: out-of-range entries become -inf.  Whole float4s
+// when the row is 16-byte aligned and V is a multiple of 4 (the choice is
+// the same for the whole workgroup), else single floats.  Buffer loads with
+// one lane offset and the slot in the scalar offset; reads past the row
+// return 0 and are replaced afterwards, so there is no branch between the
+// loads: all of them are in flight before the first is used.
 __device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[VPT4]) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, V);
+    const int vo = 16 * tid_();
+    if (aligned && (V & 3) == 0) {
 #pragma unroll
-    for (int j = 0; j < VPT4; ++j) {
-        const int idx = elem_index(cb, j, 0);
-        if (aligned && idx + 3 < V) {
-            x[j] = *(const float4*)(row + idx);
-        } else {
-            x[j].x = idx < V ? row[idx] : -INFINITY;
-            x[j].y = idx + 1 < V ? row[idx + 1] : -INFINITY;
-            x[j].z = idx + 2 < V ? row[idx + 2] : -INFINITY;
-            x[j].w = idx + 3 < V ? row[idx + 3] : -INFINITY;
-        }
+        for (int j = 0; j < VPT4; ++j)
+            x[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 4 * cb + 16 * NT * j, 0));
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+            if (elem_index(cb, j, 0) >= V) x[j] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    } else {
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                f4set(x[j], e, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 4 * e, 4 * cb + 16 * NT * j, 0)));
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (elem_index(cb, j, e) >= V) f4set(x[j], e, -INFINITY);
     }
 }
 
@@ -138,6 +162,10 @@ __device__ __forceinline__ bool in_nucleus(float e, int idx, const Nucleus& nu) 
     const uint32_t bits = __float_as_uint(e);
     return bits > nu.thr || (bits == nu.thr && idx < nu.cutoff);
 }
+
+// Without top-p the cut keeps every token (thr 0, no tie cutoff): the
+// membership test can be skipped.
+__device__ __forceinline__ bool keeps_all(const Nucleus& nu) { return nu.thr == 0u && nu.cutoff == INT_MAX; }
 
 __device__ __forceinline__ unsigned long long fixmass(float e) { return (unsigned long long)__float2ull_rn(e * kFix); }
 

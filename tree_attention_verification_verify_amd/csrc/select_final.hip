@@ -243,18 +243,19 @@ __device__ __forceinline__ void slice_weights(const SelectParams& P, int b, int 
         }
     }
     const rows::Nucleus np{sp.thr, sp.cutoff}, nq{sq.thr, sq.cutoff};
+    const bool pall = rows::keeps_all(np), qall = rows::keeps_all(nq);
     const float ip = (float)(1.0 / sp.Z);
     const float iq = resid ? (float)(1.0 / sq.Z) : 0.f;
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
         const int x = x0 + k;
         float pe = rows::unnorm(lp[k], sp.zmax, P.ilog);
-        if (x >= V || !rows::in_nucleus(pe, x, np)) pe = 0.f;
+        if (x >= V || !(pall || rows::in_nucleus(pe, x, np))) pe = 0.f;
         wp[k] = pe;
         float r = 0.f;
         if (resid) {
             float qe = rows::unnorm(lq[k], sq.zmax, P.ilog);
-            if (x >= V || !rows::in_nucleus(qe, x, nq)) qe = 0.f;
+            if (x >= V || !(qall || rows::in_nucleus(qe, x, nq))) qe = 0.f;
             r = rows::resid_weight(pe, ip, qe, iq);
         }
         wr[k] = r;

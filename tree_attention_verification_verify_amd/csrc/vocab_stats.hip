@@ -89,25 +89,39 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
         s += (double)part;
     };
 
+    // buffer loads (tracked in order, so a batch's loads stay in flight while
+    // the previous batch is folded in); the slot is in the scalar offset.
+    // Reads past the row return 0; a batch that reaches past the aligned part
+    // is masked to -inf only when it is folded in, after the next batch's
+    // loads have been issued.
+    const __amdgpu_buffer_rsrc_t rs = rows::row_rsrc(row, V);
     auto load = [&](int base4, float (&x)[4 * U]) {
-        const bool full = base4 + U * ST <= nv4;   // every load of the batch in range: no guards
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i4 = base4 + u * ST + tid;
-            float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-            if (full || i4 < nv4) v = *(const float4*)(row + 4 * i4);
+            const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * tid, 16 * (base4 + u * ST), 0));
             x[4 * u] = v.x; x[4 * u + 1] = v.y; x[4 * u + 2] = v.z; x[4 * u + 3] = v.w;
         }
     };
+    auto mask_tail = [&](int base4, float (&x)[4 * U]) {
+        if (base4 + U * ST <= nv4) return;   // the whole batch is in range
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base4 + u * ST + tid >= nv4) x[4 * u] = x[4 * u + 1] = x[4 * u + 2] = x[4 * u + 3] = -INFINITY;
+    };
     if (nv4 > 0) {   // two register batches in turn (unrolled by two: no copies)
+        // the next batch is loaded unconditionally (past the row the loads
+        // return 0 and are unused): a conditional load would leave the waits
+        // after it counting as if it had not been issued
         float xa[4 * U], xb[4 * U];
         load(0, xa);
         for (int base4 = 0; base4 < nv4; base4 += 2 * U * ST) {
             const int b1 = base4 + U * ST, b2 = base4 + 2 * U * ST;
-            if (b1 < nv4) load(b1, xb);
+            load(b1, xb);
+            mask_tail(base4, xa);
             absorb(xa, 4 * U, [&](int k) { return 4 * (base4 + (k >> 2) * ST + tid) + (k & 3); });
             if (b1 >= nv4) break;
-            if (b2 < nv4) load(b2, xa);
+            load(b2, xa);
+            mask_tail(b1, xb);
             absorb(xb, 4 * U, [&](int k) { return 4 * (b1 + (k >> 2) * ST + tid) + (k & 3); });
         }
     }
