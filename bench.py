@@ -37,6 +37,7 @@ def parse():
                     help="one of: tiny-chain-f32, llama7b-medusa-greedy, chain-batch32-topp, "
                          "70b-gqa-medusa, longctx-bigvocab")
     ap.add_argument("--mode", default=None, help="sampling or greedy (default: the workload's own)")
+    ap.add_argument("--top-p", type=float, default=None, help="top-p of sampling mode (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lossless-tree", action="store_true",
                     help="time the lossless sibling walk (SPEC_VERIFY_FLAG_LOSSLESS_TREE) as the value")
@@ -263,6 +264,8 @@ def main():
     overrides = {}
     if args.mode:
         overrides["mode"] = args.mode
+    if args.top_p is not None:
+        overrides["top_p"] = args.top_p
     spec = synth.workload(args.workload, **overrides)
     t_gen = time.perf_counter()
     case = synth.make_case(spec)

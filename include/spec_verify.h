@@ -97,7 +97,7 @@ typedef struct spec_verify_config {
     int32_t dtype;          /* SPEC_VERIFY_F32 or SPEC_VERIFY_BF16: Q, K, V, attn_out */
     int32_t mode;           /* SPEC_VERIFY_GREEDY or SPEC_VERIFY_SAMPLING            */
     float temperature;      /* > 0 (sampling mode); applied to target and draft      */
-    float top_p;            /* (0,1]; 1 = off.  top_p < 1 needs V <= 32768           */
+    float top_p;            /* (0,1]; 1 = off                                        */
     float softmax_scale;    /* attention scale; 0 => 1/sqrt(D)                       */
     uint32_t flags;         /* SPEC_VERIFY_FLAG_*                                    */
 } spec_verify_config;
@@ -190,7 +190,8 @@ typedef struct spec_verify_handle spec_verify_handle;
 
 /* Validate cfg, size and allocate the workspace on the current HIP device.
  * *out receives the handle.  No kernel is launched.  Errors: INVALID_ARG
- * (bad field), UNSUPPORTED (top_p < 1 with V > 32768), OOM, HIP. */
+ * (bad field), UNSUPPORTED (a shape outside what the kernels handle: head_dim
+ * not 64 or 128, V > 4194304, ...), OOM, HIP. */
 int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out);
 
 /* Enqueue one verify step on `stream` (a hipStream_t; NULL = default stream).

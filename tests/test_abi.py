@@ -54,6 +54,7 @@ GOOD = dict(max_batch=2, max_nodes=8, num_q_heads=8, num_kv_heads=2, head_dim=12
     ("head_dim", 96, binding.SPEC_VERIFY_ERR_UNSUPPORTED),
     ("kv_capacity", 4, binding.SPEC_VERIFY_ERR_INVALID_ARG),
     ("vocab", 0, binding.SPEC_VERIFY_ERR_UNSUPPORTED),
+    ("vocab", 4194305, binding.SPEC_VERIFY_ERR_UNSUPPORTED),
     ("temperature", 0.0, binding.SPEC_VERIFY_ERR_INVALID_ARG),
     ("temperature", float("nan"), binding.SPEC_VERIFY_ERR_INVALID_ARG),
     ("top_p", 0.0, binding.SPEC_VERIFY_ERR_INVALID_ARG),
@@ -66,13 +67,6 @@ def test_create_rejects_bad_config(field, value, code):
         sva.spec_verify_create(sva.make_config(**cfg))
     assert e.value.code == code
     assert sva.spec_verify_last_error()
-
-
-def test_create_rejects_top_p_on_huge_vocab():
-    cfg = dict(GOOD, vocab=128256, top_p=0.9)
-    with pytest.raises(sva.SpecVerifyError) as e:
-        sva.spec_verify_create(sva.make_config(**cfg))
-    assert e.value.code == binding.SPEC_VERIFY_ERR_UNSUPPORTED
 
 
 def test_create_rejects_lossless_tree_in_greedy_mode_and_unknown_flags():

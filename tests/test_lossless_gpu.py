@@ -54,6 +54,9 @@ def test_lossless_streamed_vocab():
     # vocab above one on-chip chunk (32768): residual rows and the draw stream through the workspace
     spec = synth.workload("longctx-bigvocab", batch=2, prefix_len=128, vocab=40000, seed=(7, 4))
     check(synth.make_case(spec), "lossless-big-vocab")
+    # and with a top-p cut taken over the streamed rows
+    spec = synth.workload("longctx-bigvocab", batch=2, prefix_len=128, vocab=40000, top_p=0.9, seed=(7, 41))
+    check(synth.make_case(spec), "lossless-big-vocab-topp")
 
 
 def test_lossless_tree_with_temperature_and_top_p():

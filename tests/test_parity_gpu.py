@@ -73,6 +73,38 @@ def test_final_draw_slice_counts(vocab):
     check(synth.make_case(spec), "draw-V%d" % vocab)
 
 
+def test_top_p_large_vocab_streams_the_row():
+    # more than one on-chip chunk of 32768 logits: the cut is taken over the
+    # streamed row (maximum, then one pass per radix level)
+    spec = synth.workload("longctx-bigvocab", batch=2, prefix_len=160, top_p=0.9, seed=(4, 903))
+    check(synth.make_case(spec), "topp-V128256")
+    spec = synth.workload("chain-batch32-topp", batch=3, prefix_len=100, ragged=None, vocab=40001, seed=(4, 902))
+    check(synth.make_case(spec), "topp-V40001-unaligned")
+
+
+@pytest.mark.parametrize("vocab", [3000, 70000])
+def test_top_p_cut_inside_a_group_of_tied_probabilities(vocab):
+    # one large logit and a group of equal ones spread over the row: with
+    # top_p = 0.5 the cut falls inside the group, so only its first k members
+    # by token id are kept (the kernel's tie cutoff; at 70000 ids the group
+    # spans three chunks and the cutoff is found in the chunk holding the
+    # k-th member)
+    spec = synth.workload("chain-batch32-topp", batch=3, prefix_len=100, ragged=None, vocab=vocab, top_p=0.5,
+                          temperature=1.0, seed=(4, vocab))
+    case = synth.make_case(spec)
+    rng = np.random.default_rng(vocab)
+    B, T = case.batch, case.nodes
+    group = rng.choice(vocab, size=vocab // 3, replace=False)
+    for top, logits in ((group[0], case.target_logits), (group[1], case.draft_logits)):
+        logits[:] = -20.0
+        logits[:, :, group] = 0.0
+        logits[:, :, top] = 5.0      # p and q differ only in their top token
+    # drafted tokens: members of the group on both sides of the cutoff
+    case.tokens[:, 1:] = rng.choice(group[2:], size=(B, T - 1))
+    got, ref, _ = check(case, "topp-ties-V%d" % vocab)
+    assert int(got["node_accept"][:, 1:].sum()) > 0
+
+
 # ------------------------------------------------------------------ full sizes, sampled attention rows
 
 def _full(name, picks, **kw):

@@ -54,22 +54,20 @@ __device__ __forceinline__ void r_weights(const SelectParams& P, int b, const Wa
 #pragma unroll
         for (int j = 0; j < VPT4; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (elem_index(cb, j, e) >= V) f4set(w[j], e, 0.f);
+            for (int e = 0; e < 4; ++e) f4set(w[j], e, fmaxf(f4get(w[j], e), 0.f));
     } else {
         const float* zp = P.target + ((size_t)b * T + ws.v) * V;
         load_chunk(zp, V, cb, (((uintptr_t)zp) & 15) == 0, w);
         const RowStat sp = P.stats[(size_t)b * 2 * T + ws.v];
         const Nucleus np{sp.thr, sp.cutoff};
+        // past V the logits read -inf: weight 0 (0 also for a row without a finite logit)
         const bool all = keeps_all(np);
 #pragma unroll
         for (int j = 0; j < VPT4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int idx = elem_index(cb, j, e);
-                float pe = unnorm(f4get(w[j], e), sp.zmax, P.ilog);
-                if (idx >= V || !(all || in_nucleus(pe, idx, np))) pe = 0.f;
-                f4set(w[j], e, pe);
+                const float pe = unnorm(f4get(w[j], e), sp.zmax, P.ilog);
+                f4set(w[j], e, (pe > 0.f && (all || in_nucleus(pe, elem_index(cb, j, e), np))) ? pe : 0.f);
             }
     }
 }
@@ -105,14 +103,14 @@ __device__ __forceinline__ double residual_pass(const SelectParams& P, int b, in
         float4 r[VPT4], q[VPT4];
         r_weights(P, b, ws, cb, r);
         load_chunk(zq, V, cb, aq, q);
+        // past V both weights are 0, so is the residual
 #pragma unroll
         for (int j = 0; j < VPT4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int idx = elem_index(cb, j, e);
                 float qe = unnorm(f4get(q[j], e), sq.zmax, P.ilog);
-                if (idx >= V || !(all || in_nucleus(qe, idx, nq))) qe = 0.f;
-                f4set(q[j], e, idx < V ? resid_weight(f4get(r[j], e), ir, qe, iq) : 0.f);
+                if (!(all || in_nucleus(qe, elem_index(cb, j, e), nq))) qe = 0.f;
+                f4set(q[j], e, resid_weight(f4get(r[j], e), ir, qe, iq));
             }
         store_chunk(out, V, cb, q);
         W += slot_totals(q, sm);

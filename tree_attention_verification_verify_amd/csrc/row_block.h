@@ -94,43 +94,81 @@ __device__ __forceinline__ double block_scan_d(double v, double* excl, Smem& sm)
     return base + x;
 }
 
-// Buffer resource of a row of V floats (the row pointer is the same in every
-// lane; reads at or past V return 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int V) {
+// Row pointer and chunk base in scalar registers (they are the same in every
+// lane), so the per-slot resources below are built by scalar arithmetic.
+__device__ __forceinline__ uint64_t uniform_addr(const float* row) {
     const uint64_t a = (uint64_t)(uintptr_t)row;
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, V * 4, 0x00020000);
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// Load chunk cb of a row: out-of-range entries become -inf.  Whole float4s
-// when the row is 16-byte aligned and V is a multiple of 4 (the choice is
-// the same for the whole workgroup), else single floats.  Buffer loads with
-// one lane offset and the slot in the scalar offset; reads past the row
-// return 0 and are replaced afterwards, so there is no branch between the
-// loads: all of them are in flight before the first is used.
-__device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[VPT4]) {
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, V);
+// Buffer resource for floats first..V-1 of the row at scalar address a (none
+// left past the end).  Loads through it use only a lane offset and the
+// immediate offset, the parts the hardware checks against the resource size:
+// a read at or past V returns 0 without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tail_rsrc(uint64_t a, int V, int first) {
+    const int bytes = V > first ? (V - first) * 4 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a + 4ull * (uint64_t)(uint32_t)first), 0, bytes, 0x00020000);
+}
+
+// Issue the loads of chunk cb of a row: whole float4s when the row is
+// 16-byte aligned and V is a multiple of 4 (the choice is the same for the
+// whole workgroup), else single floats.  Each slot j has a resource based at
+// its first float (cb + 4 NT j), so one lane offset serves every load and
+// reads past the row return 0 (mask_chunk replaces them): a chunk past the
+// end may be loaded too.  There is no branch between the loads: all of them
+// are in flight before the first is used.
+__device__ __forceinline__ void issue_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[VPT4]) {
+    const uint64_t a = uniform_addr(row);
+    const int c0 = __builtin_amdgcn_readfirstlane(cb);
     const int vo = 16 * tid_();
     if (aligned && (V & 3) == 0) {
 #pragma unroll
         for (int j = 0; j < VPT4; ++j)
-            x[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 4 * cb + 16 * NT * j, 0));
-#pragma unroll
-        for (int j = 0; j < VPT4; ++j)
-            if (elem_index(cb, j, 0) >= V) x[j] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            x[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(tail_rsrc(a, V, c0 + 4 * NT * j), vo, 0, 0));
     } else {
 #pragma unroll
-        for (int j = 0; j < VPT4; ++j)
+        for (int j = 0; j < VPT4; ++j) {
+            const __amdgpu_buffer_rsrc_t rs = tail_rsrc(a, V, c0 + 4 * NT * j);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                f4set(x[j], e, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 4 * e, 4 * cb + 16 * NT * j, 0)));
+                f4set(x[j], e, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 4 * e, 0, 0)));
+        }
+    }
+}
+
+// Entries of chunk cb past V become -inf (nothing to do for a full chunk).
+__device__ __forceinline__ void mask_chunk(int V, int cb, float4 (&x)[VPT4]) {
+    if (cb + CHUNK <= V) return;
 #pragma unroll
-        for (int j = 0; j < VPT4; ++j)
+    for (int j = 0; j < VPT4; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (elem_index(cb, j, e) >= V) f4set(x[j], e, -INFINITY);
+        for (int e = 0; e < 4; ++e)
+            if (elem_index(cb, j, e) >= V) f4set(x[j], e, -INFINITY);
+}
+
+// Load chunk cb of a row: out-of-range entries become -inf.
+__device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[VPT4]) {
+    issue_chunk(row, V, cb, aligned, x);
+    mask_chunk(V, cb, x);
+}
+
+// f(x, cb) for every chunk of a row in order, each next chunk's loads in
+// flight while f runs (loaded unconditionally: a conditional load would make
+// the compiler's later waits count as if it had not been issued).
+template <class F>
+__device__ __forceinline__ void for_each_chunk(const float* row, int V, bool aligned, F&& f) {
+    float4 xa[VPT4], xb[VPT4];
+    issue_chunk(row, V, 0, aligned, xa);
+    for (int cb = 0; cb < V; cb += 2 * CHUNK) {
+        issue_chunk(row, V, cb + CHUNK, aligned, xb);
+        mask_chunk(V, cb, xa);
+        f(xa, cb);
+        if (cb + CHUNK >= V) break;
+        issue_chunk(row, V, cb + 2 * CHUNK, aligned, xa);
+        mask_chunk(V, cb + CHUNK, xb);
+        f(xb, cb + CHUNK);
     }
 }
 

@@ -158,8 +158,6 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         if (!(c.temperature > 0.f) || !std::isfinite(c.temperature))
             return fail(SPEC_VERIFY_ERR_INVALID_ARG, "temperature must be a finite value > 0");
         if (!(c.top_p > 0.f && c.top_p <= 1.f)) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "top_p must be in (0, 1]");
-        if (c.top_p < 1.f && c.vocab > sv::kVocabChunk)
-            return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "top_p < 1 needs vocab <= 32768");
     }
     if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");

@@ -90,15 +90,17 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
     };
 
     // buffer loads (tracked in order, so a batch's loads stay in flight while
-    // the previous batch is folded in); the slot is in the scalar offset.
-    // Reads past the row return 0; a batch that reaches past the aligned part
-    // is masked to -inf only when it is folded in, after the next batch's
-    // loads have been issued.
-    const __amdgpu_buffer_rsrc_t rs = rows::row_rsrc(row, V);
+    // the previous batch is folded in), each based at its slot with the lane
+    // offset alone checked against what is left of the row: reads past the
+    // row return 0 without touching memory.  A batch that reaches past the
+    // aligned part is masked to -inf only when it is folded in, after the
+    // next batch's loads have been issued.
+    const uint64_t row_a = rows::uniform_addr(row);
     auto load = [&](int base4, float (&x)[4 * U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * tid, 16 * (base4 + u * ST), 0));
+            const float4 v = __builtin_bit_cast(
+                float4, __builtin_amdgcn_raw_buffer_load_b128(rows::tail_rsrc(row_a, V, 4 * (base4 + u * ST)), 16 * tid, 0, 0));
             x[4 * u] = v.x; x[4 * u + 1] = v.y; x[4 * u + 2] = v.z; x[4 * u + 3] = v.w;
         }
     };
@@ -203,17 +205,16 @@ __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v,
     return ((unsigned long long)hi << 32) | lo;
 }
 
-// Returns need (level 0: the one it computed).
+// Histogram atomics of level L for one register chunk of unnormalised
+// probabilities e (no barrier: a row may take several chunks).
 template <int L>
-__device__ __forceinline__ double topp_level(const float4 (&e)[rows::VPT4], int V, uint32_t prefix, double need,
-                                             float top_p, ToppSmem& sm) {
+__device__ __forceinline__ void topp_accumulate(const float4 (&e)[rows::VPT4], uint32_t prefix, ToppSmem& sm) {
     using namespace rows;
     constexpr int SHIFT = 20 - 10 * L;
     constexpr int PSHIFT = L == 0 ? 31 : 30 - 10 * L;
     constexpr int HC = L == 0 ? HK : 1;
     unsigned long long* h = L == 0 ? sm.h1 : (L == 1 ? sm.h2 : sm.h3);
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    const int copy = L == 0 ? (lane & (HK - 1)) : 0;
+    const int copy = L == 0 ? (lane_() & (HK - 1)) : 0;
     // only masses in (0, 2^40] count: entries past the row end (e = 0),
     // probabilities at or below 2^-41 (zero in fixed point) and non-numbers
     // add nothing
@@ -226,6 +227,17 @@ __device__ __forceinline__ double topp_level(const float4 (&e)[rows::VPT4], int 
             if (bits > kZeroMassBits && bits <= kOneBits && (bits >> PSHIFT) == prefix)
                 atomicAdd(&h[((bits >> SHIFT) & 1023) * HC + copy], fixmass(v));
         }
+}
+
+// Scan of level L's histogram once every chunk has been accumulated; the
+// crossing bucket lands in sm.sel_*[L].  Returns need (level 0: the one it
+// computed).
+template <int L>
+__device__ __forceinline__ double topp_scan(double need, float top_p, ToppSmem& sm) {
+    using namespace rows;
+    constexpr int HC = L == 0 ? HK : 1;
+    unsigned long long* h = L == 0 ? sm.h1 : (L == 1 ? sm.h2 : sm.h3);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     __syncthreads();
     const int bk = 1023 - tid;   // thread order = descending bucket
     unsigned long long x = 0;
@@ -310,13 +322,16 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
         for (int c = 0; c < 4; ++c) f4set(e[j], c, unnorm(f4get(e[j], c), M, ilog));
 
     // the cut
-    const double need = topp_level<0>(e, V, 0u, 0.0, P.top_p, sm);
+    topp_accumulate<0>(e, 0u, sm);
+    const double need = topp_scan<0>(0.0, P.top_p, sm);
     const uint32_t b1 = (uint32_t)sm.sel_bucket[0];
     const unsigned long long a1 = sm.sel_above[0];
-    topp_level<1>(e, V, b1, need - (double)a1, P.top_p, sm);
+    topp_accumulate<1>(e, b1, sm);
+    topp_scan<1>(need - (double)a1, P.top_p, sm);
     const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
     const unsigned long long a2 = sm.sel_above[1];
-    topp_level<2>(e, V, (b1 << 10) | b2, need - (double)a1 - (double)a2, P.top_p, sm);
+    topp_accumulate<2>(e, (b1 << 10) | b2, sm);
+    topp_scan<2>(need - (double)a1 - (double)a2, P.top_p, sm);
     Nucleus nu;
     nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
     nu.cutoff = INT_MAX;
@@ -371,13 +386,157 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
     }
 }
 
+// Top-p rows longer than one register chunk (V > 32768).  The same cut, with
+// the row streamed chunk by chunk (each next chunk's loads in flight): one
+// pass for the maximum and its first position, one per radix level (the
+// repeated reads come from the caches), and, only when tied probabilities
+// straddle the cut, one pass counting the ties per chunk and a bisection
+// inside the chunk that holds the k-th tie.
+__global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsParams P) {
+    using namespace rows;
+    __shared__ ToppSmem sm;
+    __shared__ int chunk_ties[MAX_CHUNKS];
+    const int nrows = 2 * P.T;
+    const int b = blockIdx.x / nrows, r = blockIdx.x - b * nrows;
+    const float* row = row_ptr(P, b, r);
+    if (!row) return;
+    const int V = P.V;
+    const float ilog = P.ilog;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const bool aligned = (((uintptr_t)row) & 15) == 0;
+    // cleared histograms and counts are ordered before their atomics by the next barrier
+#pragma unroll
+    for (int k = 0; k < HK; ++k) sm.h1[k * NT + tid] = 0ull;
+    sm.h2[tid] = 0ull;
+    sm.h3[tid] = 0ull;
+    if (tid < MAX_CHUNKS) chunk_ties[tid] = 0;
+
+    // largest logit and its smallest id: per chunk the thread's maximum and
+    // the first of its positions holding it; chunks come in id order
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int cb) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j) m = fmaxf(fmaxf(m, fmaxf(x[j].x, x[j].y)), fmaxf(x[j].z, x[j].w));
+        int loc = INT_MAX;
+#pragma unroll
+        for (int j = VPT4 - 1; j >= 0; --j)
+#pragma unroll
+            for (int c = 3; c >= 0; --c) {
+                const int idx = elem_index(cb, j, c);
+                loc = (f4get(x[j], c) == m && idx < V) ? idx : loc;
+            }
+        if (m > bv || (m == bv && loc < bi)) { bv = m; bi = loc; }
+    });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) argmax_step(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
+    if (lane == 0) { sm.bv[wave] = bv; sm.bi[wave] = bi; }
+    __syncthreads();
+    float M = sm.bv[0];
+    int best = sm.bi[0];
+#pragma unroll
+    for (int w = 1; w < TNW; ++w) argmax_step(M, best, sm.bv[w], sm.bi[w]);
+    auto to_e = [&](float4 (&x)[VPT4]) {
+#pragma unroll
+        for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) f4set(x[j], c, unnorm(f4get(x[j], c), M, ilog));
+    };
+
+    // the cut: one streamed pass per level
+    for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int) { to_e(x); topp_accumulate<0>(x, 0u, sm); });
+    const double need = topp_scan<0>(0.0, P.top_p, sm);
+    const uint32_t b1 = (uint32_t)sm.sel_bucket[0];
+    const unsigned long long a1 = sm.sel_above[0];
+    for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int) { to_e(x); topp_accumulate<1>(x, b1, sm); });
+    topp_scan<1>(need - (double)a1, P.top_p, sm);
+    const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
+    const unsigned long long a2 = sm.sel_above[1];
+    const uint32_t p2 = (b1 << 10) | b2;
+    for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int) { to_e(x); topp_accumulate<2>(x, p2, sm); });
+    topp_scan<2>(need - (double)a1 - (double)a2, P.top_p, sm);
+    Nucleus nu;
+    nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
+    nu.cutoff = INT_MAX;
+    const unsigned long long above = a1 + a2 + sm.sel_above[2];
+    unsigned long long kept = sm.sel_mass[2];
+    const unsigned long long tie_mass = fixmass(__uint_as_float(nu.thr));
+    if (tie_mass > 0) {
+        const unsigned long long ties = kept / tie_mass;
+        long long k = (long long)ceil((need - (double)above) / (double)tie_mass);
+        if (k < 1) k = 1;
+        if (ties > 1 && (unsigned long long)k < ties) {
+            // ties straddle the cut: ties per chunk, then the smallest cutoff c
+            // with #ties(id < c) >= k by bisection inside the chunk holding
+            // the k-th tie (block counts, alternating buffers)
+            for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int cb) {
+                to_e(x);
+                unsigned long long cnt = 0;
+#pragma unroll
+                for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (elem_index(cb, j, c) < V && __float_as_uint(f4get(x[j], c)) == nu.thr) ++cnt;
+                cnt = wave_sum_u64(cnt);
+                if (lane == 0) atomicAdd(&chunk_ties[cb / CHUNK], (int)cnt);
+            });
+            __syncthreads();
+            const int nchunks = (V + CHUNK - 1) / CHUNK;
+            long long before = 0;
+            int cstar = nchunks - 1;
+            for (int c = 0; c < nchunks; ++c) {
+                if (before + chunk_ties[c] >= k) { cstar = c; break; }
+                before += chunk_ties[c];
+            }
+            const int cb = cstar * CHUNK;
+            float4 e[VPT4];
+            load_chunk(row, V, cb, aligned, e);
+            to_e(e);
+            int lo = cb, hi = min(V, cb + CHUNK) - 1, par = 0;
+            while (lo < hi) {
+                const int mid = lo + (hi - lo) / 2;
+                unsigned long long cnt = 0;
+#pragma unroll
+                for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int idx = elem_index(cb, j, c);
+                        if (idx < V && idx <= mid && __float_as_uint(f4get(e[j], c)) == nu.thr) ++cnt;
+                    }
+                cnt = wave_sum_u64(cnt);
+                if (lane == 0) sm.cnt[par][wave] = cnt;
+                __syncthreads();
+                unsigned long long tot = (unsigned long long)before;
+#pragma unroll
+                for (int w = 0; w < TNW; ++w) tot += sm.cnt[par][w];
+                par ^= 1;
+                if (tot >= (unsigned long long)k) hi = mid; else lo = mid + 1;
+            }
+            nu.cutoff = lo + 1;
+            kept = (unsigned long long)k * tie_mass;
+        }
+    }
+    if (tid == 0) {
+        RowStat st;
+        st.zmax = M;
+        st.argmax = best;
+        st.thr = nu.thr;
+        st.cutoff = nu.cutoff;
+        st.Z = (double)(above + kept) * (1.0 / (double)kFix);
+        P.stats[(size_t)b * nrows + r] = st;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_row_stats(const StatsParams& p, hipStream_t s) {
     const int nrows = p.sampling ? 2 * p.T : p.T;
     dim3 grid((unsigned)(p.B * nrows));
-    if (p.sampling && p.top_p < 1.f)
+    if (p.sampling && p.top_p < 1.f && p.V <= rows::CHUNK)
         hipLaunchKernelGGL(row_stats_topp_kernel, grid, dim3(rows::NT), 0, s, p);
+    else if (p.sampling && p.top_p < 1.f)
+        hipLaunchKernelGGL(row_stats_topp_chunked_kernel, grid, dim3(rows::NT), 0, s, p);
     else if (p.sampling)
         hipLaunchKernelGGL(row_stats_stream_kernel<true>, grid, dim3(ST), 0, s, p);
     else
