@@ -77,6 +77,9 @@ extern "C" {
 #define SPEC_VERIFY_STATUS_BAD_TOKEN 2    /* tokens[b,i] outside [0,V) for some i >= 1    */
 #define SPEC_VERIFY_STATUS_ZERO_DRAFT 4   /* q_i(x_i) = 0 for a supplied draft (rejected) */
 #define SPEC_VERIFY_STATUS_BAD_KVLEN 8    /* kv_len[b] < 0 or kv_len[b] + T > Lcap        */
+#define SPEC_VERIFY_STATUS_WALK_TIMEOUT 16 /* lossless walk: a wait for the sequence's other
+                                              workgroups ran out (another launch held the
+                                              GPU); that sequence's outputs are not valid */
 
 /* Kernel stages (launches, in order) reported by spec_verify_timing_read. */
 #define SPEC_VERIFY_STAGE_ATTENTION 0     /* tree attention main kernel                   */

@@ -59,6 +59,16 @@ def test_lossless_streamed_vocab():
     check(synth.make_case(spec), "lossless-big-vocab-topp")
 
 
+@pytest.mark.parametrize("batch,vocab", [(72, 32000), (16, 140000)])
+def test_lossless_grids_too_large_for_the_workgroup_walk(batch, vocab):
+    # batch * ceil(V / 4096) above two workgroups per CU: one workgroup per
+    # sequence instead (r in registers up to 32768 ids, in HBM rows above)
+    spec = synth.CaseSpec("walk-fallback", batch, "bf16", 8, 2, 64, 64, vocab, "sampling", ("medusa", (3, 2), 9),
+                          temperature=1.0, draft_sigma=2.0, seed=(7, 9, vocab))
+    _, ref, _ = check(synth.make_case(spec), "lossless-fallback-V%d" % vocab)
+    assert (ref["tested"] & (ref["node_accept"] == 0)).sum() > batch
+
+
 def test_lossless_tree_with_temperature_and_top_p():
     spec = synth.workload("70b-gqa-medusa", batch=4, prefix_len=128, vocab=3000, temperature=0.8, top_p=0.9,
                           seed=(7, 5))

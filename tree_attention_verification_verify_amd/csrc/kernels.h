@@ -80,6 +80,11 @@ struct SelectParams {
     double2* slice_tot;   // [B][S] (residual, p-only) weight totals per slice of the final draw
     double2* slice_pre;   // [B][S][kSelectThreads] per-thread exclusive prefixes (S <= kSelectKeepSlices)
     float* resid_ws;      // [B][2][V] residual rows of the lossless sibling walk
+    int32_t* walk_sync;   // [B][4] sibling walk across workgroups: arrivals, finished workgroups, timeout flag
+    double* walk_part;    // [B][2][walk_k] per-workgroup residual totals (two passes in turn)
+    float* walk_rx;       // [B][2][2] the next test's r (new, kept) from the workgroup holding its token
+    int walk_k;           // workgroups per sequence of the walk: ceil(V / kWalkSlice)
+    int walk_coop;        // 1: the walk over walk_k workgroups per sequence; 0: one workgroup per sequence
     int32_t* arrive;      // [B] slices done; reset to 0 by the last one
     int B, T, V, Lcap;
     int S;                // slices per sequence: ceil(V / kSelectSlice)
@@ -145,5 +150,7 @@ constexpr int kSelectThreads = 256;               // selection / final draw work
 constexpr int kSelectSlice = 2048;                // token ids per final-draw slice
 constexpr int kSelectMaxSlices = 2048;            // vocab <= 4194304
 constexpr int kSelectKeepSlices = 64;             // up to this many slices the draw keeps slice prefixes
+constexpr int kWalkThreads = 256;                 // sibling-walk workgroups
+constexpr int kWalkSlice = kWalkThreads * 16;     // token ids each walk workgroup holds in registers
 
 }  // namespace sv

@@ -552,10 +552,486 @@ __global__ __launch_bounds__(NT) void lossless_walk_resident_kernel(SelectParams
     }
 }
 
+// ---------------------------------------------------------------------------
+// The walk spread over K = ceil(V / 4096) workgroups per sequence: workgroup s
+// holds token ids 4096 s .. 4096 s + 4095 of r in registers (256 threads x 16).
+// Every workgroup takes the same decisions from the same values: the first
+// tests as above, and after each residual pass the sequence's K slice totals
+// (summed in slice order) and r at the next child's token, published by the
+// workgroup holding it.  A pass ends with an arrival barrier of the K
+// workgroups: agent-scope atomic stores of the totals, a `vmcnt(0)` wait, an
+// arrival count, and a bounded wait for the count (a wait that runs out sets
+// the status bit SPEC_VERIFY_STATUS_WALK_TIMEOUT and goes on, so every wave
+// ends).  The last workgroup to finish resets the counters for the next step.
+
+constexpr int CT = kWalkThreads;
+constexpr int CW = CT / kWave;
+constexpr int CV4 = kWalkSlice / (4 * CT);   // float4 per thread
+constexpr int kSpinLimit = 1 << 21;           // about 0.1 s of s_sleep
+
+struct CoopShared {
+    unsigned long long kids_of[64];
+    float pv0[64], qv[64], u[64];
+    int tok[64];
+    float qzmax[64];
+    uint32_t qthr[64];
+    int qcut[64];
+    double qZ[64];
+    double wsum[2][CW];          // wave totals of the block sums (alternating)
+    double slot_part[CW][CV4];
+    double slot_tot[CV4];
+    double W, cum, send;         // after a pass: the total; for the draw: prefixes around slice s*
+    float rx_new, rx_old;
+    int sstar, winner, found, live, status;
+};
+
+__device__ __forceinline__ int cidx(int first, int j, int e) { return first + 4 * (threadIdx.x + CT * j) + e; }
+
+// Slice [first, first + kWalkSlice) of a row into registers; past V: -inf.
+// One lane offset, a resource per slot based at the slot: reads past V
+// return 0 without touching memory.
+__device__ __forceinline__ void coop_load(const float* row, int V, int first, float4 (&x)[CV4]) {
+    const uint64_t a = rows::uniform_addr(row);
+    const int f0 = __builtin_amdgcn_readfirstlane(first);
+    const int vo = 16 * threadIdx.x;
+    const bool aligned = ((a & 15ull) == 0) && ((V & 3) == 0);
+    if (aligned) {
+#pragma unroll
+        for (int j = 0; j < CV4; ++j)
+            x[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rows::tail_rsrc(a, V, f0 + 4 * CT * j), vo, 0, 0));
+    } else {
+#pragma unroll
+        for (int j = 0; j < CV4; ++j) {
+            const __amdgpu_buffer_rsrc_t rs = rows::tail_rsrc(a, V, f0 + 4 * CT * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                f4set(x[j], e, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 4 * e, 0, 0)));
+        }
+    }
+    if (f0 + kWalkSlice > V) {
+#pragma unroll
+        for (int j = 0; j < CV4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (cidx(f0, j, e) >= V) f4set(x[j], e, -INFINITY);
+    }
+}
+
+__device__ __forceinline__ float coop_pick(const float4 (&w)[CV4], int j, int e) {
+    float r = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < CV4; ++jj)
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) r = (jj == j && ee == e) ? f4get(w[jj], ee) : r;
+    return r;
+}
+
+// Workgroup total of w (one barrier; consecutive calls alternate buf).
+__device__ __forceinline__ double coop_total(const float4 (&w)[CV4], CoopShared& cs, int buf) {
+    double t = 0.0;
+#pragma unroll
+    for (int j = 0; j < CV4; ++j) t += ((double)w[j].x + (double)w[j].y) + ((double)w[j].z + (double)w[j].w);
+    t = wave_sum_d(t);
+    if ((threadIdx.x & (kWave - 1)) == 0) cs.wsum[buf][threadIdx.x >> 6] = t;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int k = 0; k < CW; ++k) tot += cs.wsum[buf][k];
+    return tot;
+}
+
+// Arrival barrier of the sequence's K workgroups after this workgroup
+// published its pass-`pass` values; then wave 0 scans the K totals in slice
+// order.  With `target` >= 0 it also finds the slice s* whose running total
+// first exceeds target (rounding: the last slice with weight) and the
+// prefixes before and through it.  Results in cs (after a barrier).
+// With `arrived` the pass's values are already known to be published (the
+// scan of a pass that was synchronised before).
+__device__ __forceinline__ void coop_sync_scan(const SelectParams& P, int b, int pass, bool want_rx, double u_final,
+                                               bool draw, CoopShared& cs, bool arrived = false) {
+    const int K = P.walk_k;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    int32_t* sync = P.walk_sync + 4 * b;
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's published values have landed
+    __syncthreads();
+    if (tid < kWave) {
+        bool late = false;
+        if (tid == 0 && !arrived) {
+            __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int want = K * (pass + 1);
+            int it = 0;
+            while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+                if (++it > kSpinLimit) { late = true; break; }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (late) __hip_atomic_store(sync + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const double* part = P.walk_part + (size_t)(b * 2 + (pass & 1)) * K;
+        double run = 0.0;        // prefix of the earlier rounds of 64 slices
+        int sstar = -1, lastpos = -1;
+        double cum = 0.0, send = 0.0, lastcum = 0.0, lastend = 0.0;
+        // the target needs the total first: with a draw, two sweeps
+        double W = 0.0;
+        for (int sweep = 0; sweep < (draw ? 2 : 1); ++sweep) {
+            run = 0.0;
+            const double target = sweep == 1 ? u_final * W : -1.0;
+            for (int k0 = 0; k0 < K; k0 += kWave) {
+                const int k = k0 + lane;
+                const double v = k < K ? __hip_atomic_load(part + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
+                double inc = v;
+#pragma unroll
+                for (int o = 1; o < kWave; o <<= 1) {
+                    const double y = __shfl_up(inc, o, kWave);
+                    if (lane >= o) inc += y;
+                }
+                inc += run;
+                double exc = __shfl_up(inc, 1, kWave);
+                if (lane == 0) exc = run;
+                if (sweep == 1) {
+                    const unsigned long long past = __ballot(k < K && inc > target);
+                    const unsigned long long pos = __ballot(k < K && v > 0.0);
+                    if (sstar < 0 && past) {
+                        const int l = __builtin_ctzll(past);
+                        sstar = k0 + l;
+                        cum = __shfl(exc, l, kWave);
+                        send = __shfl(inc, l, kWave);
+                    }
+                    if (pos) {
+                        const int l = 63 - __builtin_clzll(pos);
+                        lastpos = k0 + l;
+                        lastcum = __shfl(exc, l, kWave);
+                        lastend = __shfl(inc, l, kWave);
+                    }
+                }
+                run = __shfl(inc, kWave - 1, kWave);
+            }
+            W = run;
+        }
+        if (tid == 0) {
+            cs.W = W;
+            if (draw) {
+                if (sstar < 0) { sstar = lastpos; cum = lastcum; send = lastend; }
+                cs.sstar = sstar;
+                cs.cum = cum;
+                cs.send = send;
+            }
+            if (want_rx) {
+                const float* rx = P.walk_rx + (size_t)(b * 2 + (pass & 1)) * 2;
+                cs.rx_new = __hip_atomic_load(rx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                cs.rx_old = __hip_atomic_load(rx + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(CT) void lossless_walk_coop_kernel(SelectParams P) {
+    __shared__ CoopShared cs;
+    const int K = P.walk_k;
+    const int b = blockIdx.x / K, s = blockIdx.x - b * K;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int T = P.T, V = P.V;
+    const size_t base = (size_t)b * T;
+    const RowStat* st = P.stats + (size_t)b * 2 * T;
+    const int first = s * kWalkSlice;   // this workgroup's token ids [first, first + kWalkSlice)
+    const bool lead = (s == 0);         // writes the per-node and per-sequence outputs
+
+    if (tid < kWave) {
+        const bool live = lane < T;
+        const int par_in = live ? P.parent[base + lane] : -1;
+        const int tok = live ? P.tokens[base + lane] : 0;
+        RowStat sl{0.f, 0, 0u, 0, 1.0};
+        RowStat sq{0.f, 0, 0u, 0, 1.0};
+        float u = 0.f;
+        if (live) sl = st[lane];
+        if (live && lane >= 1) {
+            sq = st[T + lane];
+            u = P.u_accept[base + lane];
+        }
+        const int L = P.kv_len[b];
+        bool bad_parent;
+        (void)ancestor_mask_of(par_in, T, &bad_parent);
+        const bool bad_token = __any(live && lane >= 1 && (tok < 0 || tok >= V));
+        bool bad_kv = (L < 0) || (L > P.Lcap - T);
+        bad_kv = bad_kv || (lead && __any(page_entries_bad(P.pt, b, L + T, lane, kWave)));   // paged: L + T <= Lcap here
+        int status = (bad_parent ? 1 : 0) | (bad_token ? 2 : 0) | (bad_kv ? 8 : 0);
+        // out_tokens: the lead writes the path's drafts and, at the end, -1 past
+        // the final position; the final position is written by the workgroup
+        // that draws it (stores of different workgroups to one address would
+        // not be ordered across XCD caches)
+        if (lead && live) {
+            P.row_token[base + lane] = sl.argmax;
+            P.node_accept[base + lane] = (lane == 0) ? 1 : 0;
+            P.node_p[base + lane] = 0.f;
+            P.node_q[base + lane] = 0.f;
+            P.path[base + lane] = (lane == 0 && !bad_parent && !bad_token) ? 0 : -1;
+        }
+        if (bad_parent || bad_token) {
+            if (lead && live) P.out_tokens[base + lane] = -1;
+            if (lane == 0) {
+                if (lead) {
+                    P.accept_len[b] = 0;
+                    P.final_node[b] = -1;
+                    P.final_from_residual[b] = 0;
+                    P.status[b] = status;
+                }
+                cs.live = 0;
+            }
+        } else {
+            const int par = par_in;   // valid: parent < node for every node >= 1
+            const RowStat spar = shfl_row_stat(sl, par >= 0 ? par : 0);
+            float pv = 0.f, qv = 0.f;
+            if (live && lane >= 1) {
+                const float zt = P.target[(base + par) * V + tok];
+                const float zd = P.draft[(base + lane) * V + tok];
+                const float et = unnorm(zt, spar.zmax, P.ilog), ed = unnorm(zd, sq.zmax, P.ilog);
+                const Nucleus nt{spar.thr, spar.cutoff}, nd{sq.thr, sq.cutoff};
+                pv = in_nucleus(et, tok, nt) ? (float)((double)et / spar.Z) : 0.f;
+                qv = in_nucleus(ed, tok, nd) ? (float)((double)ed / sq.Z) : 0.f;
+            }
+            // status bit 4: some supplied draft gives its own token probability 0
+            if (__any(live && lane >= 1 && !(qv > 0.f))) status |= 4;
+            for (int n = 0; n < T; ++n) {
+                const unsigned long long k = __ballot(live && lane >= 1 && par == n);
+                if (lane == 0) cs.kids_of[n] = k;
+            }
+            cs.pv0[lane] = pv;
+            cs.qv[lane] = qv;
+            cs.u[lane] = u;
+            cs.tok[lane] = tok;
+            cs.qzmax[lane] = sq.zmax;
+            cs.qthr[lane] = sq.thr;
+            cs.qcut[lane] = sq.cutoff;
+            cs.qZ[lane] = sq.Z;
+            if (lane == 0) {
+                cs.status = status;
+                cs.live = 1;
+            }
+        }
+    }
+    __syncthreads();
+    if (!cs.live) return;   // the same in every workgroup of the sequence: none waits
+
+    // walk state, the same in every workgroup of the sequence
+    int v = 0, depth = 0, pass = 0;
+    unsigned long long kids = uniform_u64(cs.kids_of[0]);
+    bool fresh = true;     // r = p_v
+    bool have_r = false;   // rr holds this workgroup's slice of r
+    double W = 0.0;        // total of r when it is a residual
+    float rx_next = 0.f;   // r(x) / W for the next child when r is a residual
+    bool last_kept = false;   // r is the residual the last pass produced
+    float4 rr[CV4];
+    for (int round = 0; round < 2 * 64 + 1; ++round) {
+        int c = -1;
+        if (kids != 0ull) {
+            last_kept = false;
+            c = __builtin_ctzll(kids);
+            const float rx = fresh ? cs.pv0[c] : rx_next;
+            const float qx = cs.qv[c];
+            const bool acc = (qx > 0.f) && (cs.u[c] < rx / qx);
+            if (lead && tid == 0) {
+                P.node_p[base + c] = rx;
+                P.node_q[base + c] = qx;
+            }
+            if (acc) {
+                if (lead && tid == 0) {
+                    P.node_accept[base + c] = 1;
+                    P.out_tokens[base + depth] = cs.tok[c];
+                    P.path[base + depth + 1] = c;
+                }
+                depth += 1;
+                v = c;
+                kids = uniform_u64(cs.kids_of[c]);
+                fresh = true;
+                have_r = false;
+                continue;
+            }
+            kids &= ~(1ull << c);
+        }
+        // a rejection, or the end of the walk: both need r's weights
+        const RowStat sp = st[v];
+        if (!have_r) {
+            coop_load(P.target + (base + v) * V, V, first, rr);
+            const Nucleus np{sp.thr, sp.cutoff};
+            const bool all = keeps_all(np);
+#pragma unroll
+            for (int j = 0; j < CV4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pe = unnorm(f4get(rr[j], e), sp.zmax, P.ilog);
+                    f4set(rr[j], e, (pe > 0.f && (all || in_nucleus(pe, cidx(first, j, e), np))) ? pe : 0.f);
+                }
+            have_r = true;
+        }
+        if (c < 0) break;
+        // r <- [r - q_c]_+ on this slice
+        float4 q[CV4];
+        coop_load(P.draft + (base + c) * V, V, first, q);
+        const Nucleus nq{cs.qthr[c], cs.qcut[c]};
+        const float qzmax = cs.qzmax[c];
+        const float iq = (float)(1.0 / cs.qZ[c]);
+        const float ir = fresh ? (float)(1.0 / sp.Z) : (float)(1.0 / W);
+        // the next child's token x2: slice s2, slot (j2, e2) of thread t2
+        const int c2 = kids ? __builtin_ctzll(kids) : -1;
+        const int x2 = __builtin_amdgcn_readfirstlane(c2 >= 0 ? cs.tok[c2] : 0);
+        const int s2 = x2 / kWalkSlice, loc2 = x2 - s2 * kWalkSlice;
+        const int t2 = (loc2 >> 2) & (CT - 1), j2 = loc2 / (4 * CT), e2 = loc2 & 3;
+        const bool owner = c2 >= 0 && s == s2 && tid == t2;
+        float* rxp = P.walk_rx + (size_t)(b * 2 + (pass & 1)) * 2;
+        if (owner) __hip_atomic_store(rxp + 1, coop_pick(rr, j2, e2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < CV4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f4set(q[j], e, unnorm(f4get(q[j], e), qzmax, P.ilog));
+        if (!keeps_all(nq)) {
+#pragma unroll
+            for (int j = 0; j < CV4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!in_nucleus(f4get(q[j], e), cidx(first, j, e), nq)) f4set(q[j], e, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < CV4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f4set(q[j], e, resid_weight(f4get(rr[j], e), ir, f4get(q[j], e), iq));
+        if (owner) __hip_atomic_store(rxp, coop_pick(q, j2, e2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const double t = coop_total(q, cs, pass & 1);
+        if (tid == 0)
+            __hip_atomic_store(P.walk_part + (size_t)(b * 2 + (pass & 1)) * K + s, t, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        coop_sync_scan(P, b, pass, c2 >= 0, 0.0, false, cs);
+        const double Wn = cs.W;
+        if (Wn > 0.0) {
+#pragma unroll
+            for (int j = 0; j < CV4; ++j) rr[j] = q[j];
+            W = Wn;
+            fresh = false;
+            last_kept = true;
+            if (c2 >= 0) rx_next = (float)((double)cs.rx_new / W);
+        } else if (!fresh && c2 >= 0) {   // a vanishing residual keeps r
+            rx_next = (float)((double)cs.rx_old / W);
+        }
+        ++pass;
+    }
+
+    // the final draw from r: y = min{k : u * W < C_k} in token-id order.  The
+    // slice totals in slice order give s*; the workgroup holding it locates y.
+    // When r is the residual of the last pass, that pass's totals are r's.
+    if (last_kept) {
+        coop_sync_scan(P, b, pass - 1, false, (double)P.u_final[b], true, cs, true);
+    } else {
+        const double t = coop_total(rr, cs, pass & 1);
+        if (tid == 0)
+            __hip_atomic_store(P.walk_part + (size_t)(b * 2 + (pass & 1)) * K + s, t, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        coop_sync_scan(P, b, pass, false, (double)P.u_final[b], true, cs);
+    }
+    const int sstar = cs.sstar;
+    const double target = (double)P.u_final[b] * cs.W;
+    const int draw_buf = last_kept ? (pass & 1) : ((pass + 1) & 1);   // not the last block sum's buffer
+    if (s == sstar) {
+        // slot totals of this slice (slot j: ids first + 1024 j ..), then the slot
+        // holding the target, then the thread, then the id
+        double sj[CV4];
+#pragma unroll
+        for (int j = 0; j < CV4; ++j)
+            sj[j] = wave_sum_d(((double)rr[j].x + (double)rr[j].y) + ((double)rr[j].z + (double)rr[j].w));
+        if (lane == 0)
+#pragma unroll
+            for (int j = 0; j < CV4; ++j) cs.slot_part[tid >> 6][j] = sj[j];
+        if (tid == 0) { cs.winner = 0; cs.found = -1; }
+        __syncthreads();
+        double cum = cs.cum;
+        int jstar = -1;
+#pragma unroll
+        for (int j = 0; j < CV4; ++j) {
+            double S = 0.0;
+#pragma unroll
+            for (int w2 = 0; w2 < CW; ++w2) S += cs.slot_part[w2][j];
+            if (jstar < 0) {
+                if (cum + S > target) jstar = j;
+                else cum += S;
+            }
+        }
+        float4 wv = rr[0];
+        int last_pos = -1;
+#pragma unroll
+        for (int j = 0; j < CV4; ++j) {
+            const bool hit = j == jstar;
+            wv.x = hit ? rr[j].x : wv.x;
+            wv.y = hit ? rr[j].y : wv.y;
+            wv.z = hit ? rr[j].z : wv.z;
+            wv.w = hit ? rr[j].w : wv.w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (f4get(rr[j], e) > 0.f) last_pos = max(last_pos, cidx(first, j, e));
+        }
+        const size_t out_at = base + depth;
+        if (jstar >= 0) {
+            // scan over the threads of slot j*: lane sums, wave offsets in order
+            const double mine = ((double)wv.x + (double)wv.y) + ((double)wv.z + (double)wv.w);
+            double x = mine;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const double y = __shfl_up(x, o, kWave);
+                if (lane >= o) x += y;
+            }
+            if (lane == kWave - 1) cs.wsum[draw_buf][tid >> 6] = x;
+            double prev = __shfl_up(x, 1, kWave);
+            if (lane == 0) prev = 0.0;
+            __syncthreads();
+            double wb = 0.0;
+#pragma unroll
+            for (int w2 = 0; w2 < CW; ++w2) wb += (w2 < (tid >> 6)) ? cs.wsum[draw_buf][w2] : 0.0;
+            const double lo = cum + (wb + prev), hi = cum + (wb + x);
+            if (lo <= target && target < hi) {
+                double run = lo;
+                int y = -1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    run += (double)f4get(wv, e);
+                    if (y < 0 && run > target) y = cidx(first, jstar, e);
+                }
+                int lp = -1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (f4get(wv, e) > 0.f) lp = cidx(first, jstar, e);
+                P.out_tokens[out_at] = (y >= 0) ? y : lp;
+                cs.winner = 1;
+            }
+        }
+        atomicMax(&cs.found, last_pos);
+        __syncthreads();
+        if (tid == 0 && !cs.winner) P.out_tokens[out_at] = cs.found;   // rounding left no winner
+    }
+    if (lead && tid < kWave && tid > depth && tid < T) P.out_tokens[base + tid] = -1;
+    if (lead && tid == 0) {
+        if (sstar < 0) P.out_tokens[base + depth] = -1;   // no weight at all
+        P.accept_len[b] = depth;
+        P.final_node[b] = v;
+        P.final_from_residual[b] = cs.kids_of[v] != 0ull ? 1 : 0;
+        const int late = __hip_atomic_load(P.walk_sync + 4 * b + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        P.status[b] = cs.status | (late ? 16 : 0);
+    }
+    // the last workgroup of the sequence to finish resets the counters
+    if (tid == 0) {
+        int32_t* sync = P.walk_sync + 4 * b;
+        __builtin_amdgcn_s_waitcnt(0);
+        const int prev = __hip_atomic_fetch_add(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == K - 1) {
+            __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sync + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sync + 2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s) {
-    if (p.V <= CHUNK)
+    if (p.walk_coop && p.V > CHUNK)
+        hipLaunchKernelGGL(lossless_walk_coop_kernel, dim3(p.B * p.walk_k), dim3(CT), 0, s, p);
+    else if (p.V <= CHUNK)
         hipLaunchKernelGGL(lossless_walk_resident_kernel, dim3(p.B), dim3(NT), 0, s, p);
     else
         hipLaunchKernelGGL(lossless_walk_kernel, dim3(p.B), dim3(NT), 0, s, p);

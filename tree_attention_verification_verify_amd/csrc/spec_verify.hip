@@ -124,6 +124,11 @@ struct spec_verify_handle {
     double2* slice_pre = nullptr;     // max_batch * slices * 256 per-thread slice prefixes (few slices only)
     int32_t* arrive = nullptr;        // max_batch final-draw arrival counters (zero between runs)
     float* resid_ws = nullptr;        // max_batch * 2 * vocab residual rows (lossless tree walk)
+    int32_t* walk_sync = nullptr;     // max_batch * 4 walk counters (lossless tree walk)
+    double* walk_part = nullptr;      // max_batch * 2 * walk_k walk slice totals
+    float* walk_rx = nullptr;         // max_batch * 4 walk test values
+    int walk_k = 0;
+    int walk_cap = 0;                 // largest B * walk_k launched across workgroups (2 per CU)
     bool timing = false;
     std::vector<hipEvent_t> events;   // kTimingRing * kEventsPerRun
     long runs_recorded = 0;           // since the last read
@@ -199,8 +204,22 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         e = hipMalloc((void**)&h->slice_pre, (size_t)c.max_batch * slices * sv::kSelectThreads * sizeof(double2));
     if (e == hipSuccess) e = hipMalloc((void**)&h->arrive, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(h->arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
-    if (e == hipSuccess && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE))
-        e = hipMalloc((void**)&h->resid_ws, (size_t)c.max_batch * 2 * c.vocab * sizeof(float));
+    if (e == hipSuccess && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE)) {
+        // the walk across workgroups waits for all of a sequence's workgroups,
+        // so it is launched only while the grid fits twice per CU; larger
+        // grids use one workgroup per sequence (with residual rows in HBM
+        // beyond one on-chip chunk)
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
+        h->walk_k = (c.vocab + sv::kWalkSlice - 1) / sv::kWalkSlice;
+        h->walk_cap = 2 * cus;
+        if (e == hipSuccess) e = hipMalloc((void**)&h->walk_sync, (size_t)c.max_batch * 4 * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMemset(h->walk_sync, 0, (size_t)c.max_batch * 4 * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMalloc((void**)&h->walk_part, (size_t)c.max_batch * 2 * h->walk_k * sizeof(double));
+        if (e == hipSuccess) e = hipMalloc((void**)&h->walk_rx, (size_t)c.max_batch * 4 * sizeof(float));
+        if (e == hipSuccess && (long)c.max_batch * h->walk_k > h->walk_cap && c.vocab > sv::kVocabChunk)
+            e = hipMalloc((void**)&h->resid_ws, (size_t)c.max_batch * 2 * c.vocab * sizeof(float));
+    }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         (void)hipFree(h->stats);
@@ -208,6 +227,9 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         (void)hipFree(h->slice_pre);
         (void)hipFree(h->arrive);
         (void)hipFree(h->resid_ws);
+        (void)hipFree(h->walk_sync);
+        (void)hipFree(h->walk_part);
+        (void)hipFree(h->walk_rx);
         (void)hipFree(h->part_o);
         (void)hipFree(h->part_ml);
         delete h;
@@ -244,6 +266,9 @@ int spec_verify_destroy(spec_verify_handle* h) {
     if (h->slice_pre) (void)hipFree(h->slice_pre);
     if (h->arrive) (void)hipFree(h->arrive);
     if (h->resid_ws) (void)hipFree(h->resid_ws);
+    if (h->walk_sync) (void)hipFree(h->walk_sync);
+    if (h->walk_part) (void)hipFree(h->walk_part);
+    if (h->walk_rx) (void)hipFree(h->walk_rx);
     if (dev >= 0 && dev != h->device) (void)hipSetDevice(dev);
     delete h;
     return SPEC_VERIFY_OK;
@@ -383,6 +408,11 @@ int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_ver
     sp.arrive = h->arrive;
     sp.S = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
     sp.resid_ws = h->resid_ws;
+    sp.walk_sync = h->walk_sync;
+    sp.walk_part = h->walk_part;
+    sp.walk_rx = h->walk_rx;
+    sp.walk_k = h->walk_k;
+    sp.walk_coop = ((long)B * h->walk_k <= h->walk_cap) ? 1 : 0;
     const bool walk = sampling && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE);
     e = sv::launch_finish(sp, ap, !walk, plan.nsplit > 1, bf16, s);
     if (e != hipSuccess) return hip_fail(e, "finishing launch");
