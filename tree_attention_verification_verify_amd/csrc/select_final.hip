@@ -307,6 +307,28 @@ __device__ __forceinline__ void select_block(const SelectParams& P, int s, int b
     }
     double incl[2], excl[2], tot[2];
     block_scan2(mine, incl, excl, tot, sh, 0);
+    if (P.S == 1) {
+        // one slice holds the whole row: this workgroup draws at once
+        const size_t out_at = base + sh.dstar;
+        const bool use_resid = (sh.c0 >= 0) && (tot[0] > 0.0);
+        const int col = use_resid ? 0 : 1;
+        const double target = (double)P.u_final[b] * tot[col];
+        float w[EPT];
+        int last_pos = -1;
+        const int x0 = EPT * tid;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            w[k] = use_resid ? wr[k] : wp[k];
+            if (w[k] > 0.f) last_pos = x0 + k;
+        }
+        if (tid == 0) { sh.winner = 0; sh.found = -1; }
+        __syncthreads();
+        if (locate_in_thread(P, out_at, x0, w, excl[col], incl[col], target, last_pos)) sh.winner = 1;
+        atomicMax(&sh.found, last_pos);
+        __syncthreads();
+        if (tid == 0 && !sh.winner) P.out_tokens[out_at] = sh.found;   // rounding left no winner
+        return;
+    }
     if (keep) {
         double* pre = (double*)(P.slice_pre + ((size_t)b * P.S + s) * ST + tid);
         __hip_atomic_store(pre, excl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
