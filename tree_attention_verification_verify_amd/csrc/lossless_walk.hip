@@ -18,11 +18,19 @@
 // A chain gives exactly the independent rule: the first rejection ends the
 // walk, and its residual is computed with the same arithmetic.
 //
-// One 1024-thread workgroup per sequence.  Wave 0 checks the tree and sets
-// the status bits; each test is a gather by thread 0; each rejection is one
-// chunked pass over the vocabulary that writes the unnormalised residual to
-// one of two workspace rows of the sequence (so a residual that vanishes
-// leaves the previous one intact) and sums it in fp64 in a fixed order.
+// Three kernels take the same walk (the host picks one per launch):
+//  * up to 32768 ids: one 1024-thread workgroup per sequence with r in
+//    registers (lossless_walk_resident_kernel);
+//  * more ids: the ids of each sequence split over workgroups of 4096 that
+//    meet at a barrier after every pass (lossless_walk_coop_kernel), while the
+//    grid fits twice per CU;
+//  * otherwise one 1024-thread workgroup per sequence that streams the rows
+//    chunk by chunk (lossless_walk_kernel below): wave 0 checks the tree and
+//    sets the status bits; each test is a gather by thread 0; each rejection
+//    is one chunked pass over the vocabulary that writes the unnormalised
+//    residual to one of two workspace rows of the sequence (so a residual
+//    that vanishes leaves the previous one intact) and sums it in fp64 in a
+//    fixed order.
 
 #include "row_block.h"
 
@@ -562,7 +570,10 @@ __global__ __launch_bounds__(NT) void lossless_walk_resident_kernel(SelectParams
 // workgroups: agent-scope atomic stores of the totals, a `vmcnt(0)` wait, an
 // arrival count, and a bounded wait for the count (a wait that runs out sets
 // the status bit SPEC_VERIFY_STATUS_WALK_TIMEOUT and goes on, so every wave
-// ends).  The last workgroup to finish resets the counters for the next step.
+// ends).  The draw takes r's slice totals from the last pass when r is that
+// pass's residual (else from one more synchronised pass), and the workgroup
+// holding the slice where u * W falls locates the token.  The last workgroup
+// to finish resets the counters for the next step.
 
 constexpr int CT = kWalkThreads;
 constexpr int CW = CT / kWave;

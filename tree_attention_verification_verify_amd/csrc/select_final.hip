@@ -29,7 +29,8 @@
 // totals in slice order (one wave), and each of its threads takes its own
 // bounds within that slice from the kept prefixes and re-weighs its 8 token
 // ids: the thread whose bounds hold the target locates the token.  Beyond 64
-// slices the last workgroup scans the slice again instead.  Every sum is
+// slices the last workgroup scans the slice again instead; with a single
+// slice (V <= 2048) its one workgroup draws at once.  Every sum is
 // taken in a fixed order, so the draw does not depend on the order in which
 // workgroups arrive.
 

@@ -12,10 +12,11 @@
 // Without top-p each row is streamed once by a 256-thread workgroup with an
 // online max / fp64 sum per thread (rescaled by fp64 exp2 when the running
 // max grows), merged in a fixed order.  With top-p the cut needs every
-// probability relative to the final max: the row (V <= 32768) is held in the
-// registers of a 1024-thread workgroup and cut by a 3-level radix select on
-// the fp32 bit patterns with integer mass histograms (ten barriers in all
-// unless tied probabilities straddle the cut); the nucleus normaliser is its
+// probability relative to the final max: a row of up to 32768 logits is held
+// in the registers of a 1024-thread workgroup and cut by a 3-level radix
+// select on the fp32 bit patterns with integer mass histograms (ten barriers
+// in all unless tied probabilities straddle the cut); a longer row is
+// streamed once per step of the same cut.  The nucleus normaliser is its
 // exact integer mass.
 
 #include "row_block.h"
@@ -194,19 +195,19 @@ struct ToppSmem {
     unsigned long long cnt[2][TNW];
 };
 
-// One level of the cut.  Elements whose pattern above bit `PSHIFT` equals
-// `prefix` add their mass to bucket (bits >> SHIFT) & 1023.  The crossing is
-// the bucket where the mass counted from the largest bucket down first
-// reaches need (for level 0 need is top_p times the row total, which only
-// the scan knows); without a crossing (need outside (0, total]) bucket 0.
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
     return ((unsigned long long)hi << 32) | lo;
 }
 
-// Histogram atomics of level L for one register chunk of unnormalised
-// probabilities e (no barrier: a row may take several chunks).
+// One level of the cut, in two parts.  Accumulate: elements whose pattern
+// above bit PSHIFT equals `prefix` add their mass to bucket
+// (bits >> SHIFT) & 1023 (no barrier: a row may take several chunks).  Scan:
+// the crossing is the bucket where the mass counted from the largest bucket
+// down first reaches need (for level 0 need is top_p times the row total,
+// which only the scan knows); without a crossing (need outside (0, total])
+// bucket 0.
 template <int L>
 __device__ __forceinline__ void topp_accumulate(const float4 (&e)[rows::VPT4], uint32_t prefix, ToppSmem& sm) {
     using namespace rows;
@@ -229,9 +230,8 @@ __device__ __forceinline__ void topp_accumulate(const float4 (&e)[rows::VPT4], u
         }
 }
 
-// Scan of level L's histogram once every chunk has been accumulated; the
-// crossing bucket lands in sm.sel_*[L].  Returns need (level 0: the one it
-// computed).
+// The crossing bucket lands in sm.sel_*[L].  Returns need (level 0: the one
+// it computed).
 template <int L>
 __device__ __forceinline__ double topp_scan(double need, float top_p, ToppSmem& sm) {
     using namespace rows;
