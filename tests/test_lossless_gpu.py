@@ -69,6 +69,25 @@ def test_lossless_grids_too_large_for_the_workgroup_walk(batch, vocab):
     assert (ref["tested"] & (ref["node_accept"] == 0)).sum() > batch
 
 
+def test_lossless_largest_vocabulary():
+    # 4194304 ids: 1024 workgroups of 4096 would not fit the GPU twice over,
+    # so the streamed one-workgroup kernel runs (128 chunks per pass); logits
+    # peaked on 40 ids keep the top-p cut far from the near-tie band
+    rng = np.random.default_rng(7)
+    spec = synth.CaseSpec("max-vocab", 1, "bf16", 8, 2, 64, 64, 4194304, "sampling", ("medusa", (2, 2), 5),
+                          temperature=1.0, top_p=0.9, seed=(7, 4194304))
+    case = synth.make_case(spec)
+    hot = rng.choice(spec.vocab, size=40, replace=False)
+    case.target_logits[:] = -30.0
+    case.draft_logits[:] = -30.0
+    z = rng.normal(0.0, 2.0, size=(1, case.nodes, hot.size)).astype(np.float32)
+    case.target_logits[:, :, hot] = z
+    case.draft_logits[:, :, hot] = z + rng.normal(0.0, 1.5, size=z.shape).astype(np.float32)
+    case.tokens[:, 1:] = rng.choice(hot, size=(1, case.nodes - 1))
+    _, ref, _ = check(case, "lossless-max-vocab")
+    assert not ref["seq_near"].any() and int(ref["tested"].sum()) >= 2
+
+
 def test_lossless_tree_with_temperature_and_top_p():
     spec = synth.workload("70b-gqa-medusa", batch=4, prefix_len=128, vocab=3000, temperature=0.8, top_p=0.9,
                           seed=(7, 5))

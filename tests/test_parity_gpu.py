@@ -82,6 +82,33 @@ def test_top_p_large_vocab_streams_the_row():
     check(synth.make_case(spec), "topp-V40001-unaligned")
 
 
+def _peaked(case, hot, rng):
+    """Logits -30 except on the `hot` ids (N(0, 2)), drafts near the target's,
+    drafted tokens among the hot ids: a nucleus of a few dozen ids whose cut
+    lies far from any 1e-6 band even over millions of ids."""
+    case.target_logits[:] = -30.0
+    case.draft_logits[:] = -30.0
+    B, T = case.batch, case.nodes
+    z = rng.normal(0.0, 2.0, size=(B, T, hot.size)).astype(np.float32)
+    case.target_logits[:, :, hot] = z
+    case.draft_logits[:, :, hot] = z + rng.normal(0.0, 1.0, size=z.shape).astype(np.float32)
+    case.tokens[:, 1:] = rng.choice(hot, size=(B, T - 1))
+
+
+def test_largest_vocabulary():
+    # 4194304 ids, the most a handle accepts: 128 chunks per streamed top-p
+    # pass and 2048 draw slices (the last workgroup scans its slice again)
+    rng = np.random.default_rng(4194304)
+    spec = synth.CaseSpec("max-vocab", 2, "bf16", 8, 2, 64, 64, 4194304, "sampling", ("chain", 2),
+                          temperature=0.9, top_p=0.9, seed=(4, 4194304))
+    case = synth.make_case(spec)
+    _peaked(case, rng.choice(spec.vocab, size=40, replace=False), rng)
+    _, ref, stats = check(case, "max-vocab-topp")
+    assert stats.get("seq_near", 0) == 0
+    spec = spec.replace(top_p=1.0, seed=(4, 4194305))
+    check(synth.make_case(spec), "max-vocab")
+
+
 @pytest.mark.parametrize("vocab", [3000, 70000])
 def test_top_p_cut_inside_a_group_of_tied_probabilities(vocab):
     # one large logit and a group of equal ones spread over the row: with
