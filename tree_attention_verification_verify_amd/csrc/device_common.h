@@ -55,6 +55,32 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
     return v;
 }
 
+// Data-parallel-primitive lane moves (gfx9 DPP controls): lanes without a
+// source, and rows outside ROWS, read 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+    const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)v), hi = dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Inclusive scan over the 64 lanes of a wave in VALU: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes (row_shr), then the last lane of row 0 into
+// row 1 and of row 2 into row 3 (row_bcast:15), then lane 31 into rows 2 and
+// 3 (row_bcast:31).  Integer sums: exact in any order.
+__device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x) {
+    x += dpp_u64<0x111>(x);
+    x += dpp_u64<0x112>(x);
+    x += dpp_u64<0x114>(x);
+    x += dpp_u64<0x118>(x);
+    x += dpp_u64<0x142, 0xa>(x);
+    x += dpp_u64<0x143, 0xc>(x);
+    return x;
+}
+
 // Per-node ancestor bitmasks anc*(i) (bit j set iff node j is on node i's
 // root path, i itself included), by pointer jumping over parent[] in one
 // wave: after k rounds each node has collected 2^k nodes of its chain, so 6

@@ -179,6 +179,7 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
 // 64 atomics then collide HK times less on the crowded buckets.
 constexpr int HK = 4;
 constexpr int TNW = rows::NW;
+constexpr int kListCap = 256;   // per-wave list of the elements in the first level's crossing bucket
 constexpr uint32_t kZeroMassBits = 0x2B000000u;   // 2^-41: rounds to mass 0 (ties to even)
 constexpr uint32_t kOneBits = 0x3F800000u;        // 1.0
 
@@ -193,6 +194,7 @@ struct ToppSmem {
     float bv[TNW];
     int bi[TNW];
     unsigned long long cnt[2][TNW];
+    uint32_t list[TNW][kListCap];       // per wave: patterns of its elements in the first-level bucket
 };
 
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
@@ -230,6 +232,44 @@ __device__ __forceinline__ void topp_accumulate(const float4 (&e)[rows::VPT4], u
         }
 }
 
+// Levels 1 and 2 from a wave's list instead of its registers (the same
+// elements: the list holds every one of the wave's nonzero masses in the
+// first level's crossing bucket); lanes take entries in turn.
+template <int L>
+__device__ __forceinline__ void topp_accumulate_list(const uint32_t* list, uint32_t n, uint32_t prefix, ToppSmem& sm) {
+    constexpr int SHIFT = 20 - 10 * L;
+    constexpr int PSHIFT = 30 - 10 * L;
+    static_assert(L == 1 || L == 2, "list levels");
+    unsigned long long* h = L == 1 ? sm.h2 : sm.h3;
+    for (uint32_t i = (uint32_t)rows::lane_(); i < n; i += kWave) {
+        const uint32_t bits = list[i];
+        if ((bits >> PSHIFT) == prefix) atomicAdd(&h[(bits >> SHIFT) & 1023], rows::fixmass(__uint_as_float(bits)));
+    }
+}
+
+// The wave's elements with a nonzero mass in first-level bucket b1, appended
+// to its list (positions by ballot); returns how many there are (the list
+// holds them when that is at most kListCap).  The same in every lane.
+__device__ __forceinline__ uint32_t topp_compact(const float4 (&e)[rows::VPT4], uint32_t b1, uint32_t* list) {
+    using namespace rows;
+    uint32_t n = 0;
+#pragma unroll
+    for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t bits = __float_as_uint(f4get(e[j], c));
+            const bool m = bits > kZeroMassBits && bits <= kOneBits && (bits >> 20) == b1;
+            const unsigned long long mask = __ballot(m);
+            if (m) {
+                const uint32_t pos = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                if (pos < (uint32_t)kListCap) list[pos] = bits;
+            }
+            n += (uint32_t)__popcll(mask);
+        }
+    return n;
+}
+
 // The crossing bucket lands in sm.sel_*[L].  Returns need (level 0: the one
 // it computed).
 template <int L>
@@ -243,22 +283,12 @@ __device__ __forceinline__ double topp_scan(double need, float top_p, ToppSmem& 
     unsigned long long x = 0;
 #pragma unroll
     for (int c = 0; c < HC; ++c) x += h[bk * HC + c];
-    unsigned long long incl = x;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const unsigned long long y = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += y;
-    }
+    unsigned long long incl = wave_scan_u64(x);
     if (lane == kWave - 1) sm.wt[L][wave] = incl;
     __syncthreads();
     // lanes 0..TNW-1 scan the wave totals; this wave's offset and the total
     // are then read from single lanes
-    unsigned long long wsc = lane < TNW ? sm.wt[L][lane] : 0ull;
-#pragma unroll
-    for (int o = 1; o < TNW; o <<= 1) {
-        const unsigned long long y = __shfl_up(wsc, o, kWave);
-        if (lane >= o) wsc += y;
-    }
+    const unsigned long long wsc = wave_scan_u64(lane < TNW ? sm.wt[L][lane] : 0ull);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const unsigned long long total = readlane_u64(wsc, TNW - 1);
     incl += wv > 0 ? readlane_u64(wsc, wv - 1) : 0ull;
@@ -326,11 +356,18 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
     const double need = topp_scan<0>(0.0, P.top_p, sm);
     const uint32_t b1 = (uint32_t)sm.sel_bucket[0];
     const unsigned long long a1 = sm.sel_above[0];
-    topp_accumulate<1>(e, b1, sm);
+    // levels 2 and 3 only see bucket b1: each wave lists its elements there
+    // once (writes and reads of a wave's own list need no barrier) and reads
+    // the list, or its registers when the list is too short for them
+    const uint32_t nlist = topp_compact(e, b1, sm.list[wave]);
+    const bool listed = nlist <= (uint32_t)kListCap;
+    if (listed) topp_accumulate_list<1>(sm.list[wave], nlist, b1, sm);
+    else topp_accumulate<1>(e, b1, sm);
     topp_scan<1>(need - (double)a1, P.top_p, sm);
     const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
     const unsigned long long a2 = sm.sel_above[1];
-    topp_accumulate<2>(e, (b1 << 10) | b2, sm);
+    if (listed) topp_accumulate_list<2>(sm.list[wave], nlist, (b1 << 10) | b2, sm);
+    else topp_accumulate<2>(e, (b1 << 10) | b2, sm);
     topp_scan<2>(need - (double)a1 - (double)a2, P.top_p, sm);
     Nucleus nu;
     nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
