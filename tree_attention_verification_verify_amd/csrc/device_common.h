@@ -67,6 +67,11 @@ __device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
     return ((unsigned long long)hi << 32) | lo;
 }
 
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ double dpp_d(double v) {
+    return __builtin_bit_cast(double, dpp_u64<CTRL, ROWS>(__builtin_bit_cast(unsigned long long, v)));
+}
+
 // Inclusive scan over the 64 lanes of a wave in VALU: shifts by 1, 2, 4, 8
 // inside each row of 16 lanes (row_shr), then the last lane of row 0 into
 // row 1 and of row 2 into row 3 (row_bcast:15), then lane 31 into rows 2 and
@@ -78,6 +83,18 @@ __device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x
     x += dpp_u64<0x118>(x);
     x += dpp_u64<0x142, 0xa>(x);
     x += dpp_u64<0x143, 0xc>(x);
+    return x;
+}
+
+// The same scan of doubles (a fixed order of additions per lane, so the same
+// bits on every run).
+__device__ __forceinline__ double wave_scan_d(double x) {
+    x += dpp_d<0x111>(x);
+    x += dpp_d<0x112>(x);
+    x += dpp_d<0x114>(x);
+    x += dpp_d<0x118>(x);
+    x += dpp_d<0x142, 0xa>(x);
+    x += dpp_d<0x143, 0xc>(x);
     return x;
 }
 

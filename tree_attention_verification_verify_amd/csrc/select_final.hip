@@ -186,12 +186,7 @@ __device__ __forceinline__ void block_scan2(const double (&v)[2], double (&incl)
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        double x = v[k];
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const double y = __shfl_up(x, o, kWave);
-            if (lane >= o) x += y;
-        }
+        const double x = wave_scan_d(v[k]);
         if (lane == kWave - 1) sh.wtot[bufi][wave][k] = x;
         double prev = __shfl_up(x, 1, kWave);
         if (lane == 0) prev = 0.0;
@@ -362,12 +357,7 @@ __device__ __forceinline__ void select_block(const SelectParams& P, int s, int b
                 v0 = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 v1 = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            double i0 = v0, i1 = v1;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const double y0 = __shfl_up(i0, o, kWave), y1 = __shfl_up(i1, o, kWave);
-                if (lane >= o) { i0 += y0; i1 += y1; }
-            }
+            const double i0 = wave_scan_d(v0), i1 = wave_scan_d(v1);
             const double t0 = __shfl(i0, kWave - 1, kWave), t1 = __shfl(i1, kWave - 1, kWave);
             const bool use_resid = (sh.c0 >= 0) && (t0 > 0.0);
             const double target = (double)P.u_final[b] * (use_resid ? t0 : t1);
