@@ -43,17 +43,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
 
 // Data-parallel-primitive lane moves (gfx9 DPP controls): lanes without a
 // source, and rows outside ROWS, read 0.
@@ -97,6 +86,18 @@ __device__ __forceinline__ double wave_scan_d(double x) {
     x += dpp_d<0x143, 0xc>(x);
     return x;
 }
+
+__device__ __forceinline__ unsigned long long lane63_u64(unsigned long long v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, kWave - 1);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), kWave - 1);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Wave totals, the same in every lane: the last lane of the scan.
+__device__ __forceinline__ double wave_sum_d(double v) {
+    return __builtin_bit_cast(double, lane63_u64(__builtin_bit_cast(unsigned long long, wave_scan_d(v))));
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) { return lane63_u64(wave_scan_u64(v)); }
 
 // Per-node ancestor bitmasks anc*(i) (bit j set iff node j is on node i's
 // root path, i itself included), by pointer jumping over parent[] in one
