@@ -119,17 +119,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tail_rsrc(uint64_t a, int V, i
 // reads past the row return 0 (mask_chunk replaces them): a chunk past the
 // end may be loaded too.  There is no branch between the loads: all of them
 // are in flight before the first is used.
-__device__ __forceinline__ void issue_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[VPT4]) {
+template <int N = VPT4>
+__device__ __forceinline__ void issue_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[N]) {
     const uint64_t a = uniform_addr(row);
     const int c0 = __builtin_amdgcn_readfirstlane(cb);
     const int vo = 16 * tid_();
     if (aligned && (V & 3) == 0) {
 #pragma unroll
-        for (int j = 0; j < VPT4; ++j)
+        for (int j = 0; j < N; ++j)
             x[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(tail_rsrc(a, V, c0 + 4 * NT * j), vo, 0, 0));
     } else {
 #pragma unroll
-        for (int j = 0; j < VPT4; ++j) {
+        for (int j = 0; j < N; ++j) {
             const __amdgpu_buffer_rsrc_t rs = tail_rsrc(a, V, c0 + 4 * NT * j);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -138,11 +139,12 @@ __device__ __forceinline__ void issue_chunk(const float* row, int V, int cb, boo
     }
 }
 
-// Entries of chunk cb past V become -inf (nothing to do for a full chunk).
-__device__ __forceinline__ void mask_chunk(int V, int cb, float4 (&x)[VPT4]) {
-    if (cb + CHUNK <= V) return;
+// Entries of the block at cb past V become -inf (nothing to do for a full block).
+template <int N = VPT4>
+__device__ __forceinline__ void mask_chunk(int V, int cb, float4 (&x)[N]) {
+    if (cb + NT * N * 4 <= V) return;
 #pragma unroll
-    for (int j = 0; j < VPT4; ++j)
+    for (int j = 0; j < N; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if (elem_index(cb, j, e) >= V) f4set(x[j], e, -INFINITY);
@@ -154,21 +156,23 @@ __device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool
     mask_chunk(V, cb, x);
 }
 
-// f(x, cb) for every chunk of a row in order, each next chunk's loads in
-// flight while f runs (loaded unconditionally: a conditional load would make
-// the compiler's later waits count as if it had not been issued).
-template <class F>
+// f(x, cb) for every block of N float4 per thread (4 N NT ids at cb) of a row
+// in order, each next block's loads in flight while f runs (loaded
+// unconditionally: a conditional load would make the compiler's later waits
+// count as if it had not been issued).
+template <int N = VPT4, class F>
 __device__ __forceinline__ void for_each_chunk(const float* row, int V, bool aligned, F&& f) {
-    float4 xa[VPT4], xb[VPT4];
-    issue_chunk(row, V, 0, aligned, xa);
-    for (int cb = 0; cb < V; cb += 2 * CHUNK) {
-        issue_chunk(row, V, cb + CHUNK, aligned, xb);
-        mask_chunk(V, cb, xa);
+    constexpr int STEP = 4 * NT * N;
+    float4 xa[N], xb[N];
+    issue_chunk<N>(row, V, 0, aligned, xa);
+    for (int cb = 0; cb < V; cb += 2 * STEP) {
+        issue_chunk<N>(row, V, cb + STEP, aligned, xb);
+        mask_chunk<N>(V, cb, xa);
         f(xa, cb);
-        if (cb + CHUNK >= V) break;
-        issue_chunk(row, V, cb + 2 * CHUNK, aligned, xa);
-        mask_chunk(V, cb + CHUNK, xb);
-        f(xb, cb + CHUNK);
+        if (cb + STEP >= V) break;
+        issue_chunk<N>(row, V, cb + 2 * STEP, aligned, xa);
+        mask_chunk<N>(V, cb + STEP, xb);
+        f(xb, cb + STEP);
     }
 }
 

@@ -210,8 +210,8 @@ __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v,
 // down first reaches need (for level 0 need is top_p times the row total,
 // which only the scan knows); without a crossing (need outside (0, total])
 // bucket 0.
-template <int L>
-__device__ __forceinline__ void topp_accumulate(const float4 (&e)[rows::VPT4], uint32_t prefix, ToppSmem& sm) {
+template <int L, int N = rows::VPT4>
+__device__ __forceinline__ void topp_accumulate(const float4 (&e)[N], uint32_t prefix, ToppSmem& sm) {
     using namespace rows;
     constexpr int SHIFT = 20 - 10 * L;
     constexpr int PSHIFT = L == 0 ? 31 : 30 - 10 * L;
@@ -222,7 +222,7 @@ __device__ __forceinline__ void topp_accumulate(const float4 (&e)[rows::VPT4], u
     // probabilities at or below 2^-41 (zero in fixed point) and non-numbers
     // add nothing
 #pragma unroll
-    for (int j = 0; j < VPT4; ++j)
+    for (int j = 0; j < N; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float v = f4get(e[j], c);
@@ -441,6 +441,7 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
     const float ilog = P.ilog;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const bool aligned = (((uintptr_t)row) & 15) == 0;
+    constexpr int HB = VPT4 / 2;   // float4 per thread per streamed block (two blocks in flight)
     // cleared histograms and counts are ordered before their atomics by the next barrier
 #pragma unroll
     for (int k = 0; k < HK; ++k) sm.h1[k * NT + tid] = 0ull;
@@ -452,13 +453,13 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
     // the first of its positions holding it; chunks come in id order
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int cb) {
+    for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int cb) {
         float m = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < VPT4; ++j) m = fmaxf(fmaxf(m, fmaxf(x[j].x, x[j].y)), fmaxf(x[j].z, x[j].w));
+        for (int j = 0; j < HB; ++j) m = fmaxf(fmaxf(m, fmaxf(x[j].x, x[j].y)), fmaxf(x[j].z, x[j].w));
         int loc = INT_MAX;
 #pragma unroll
-        for (int j = VPT4 - 1; j >= 0; --j)
+        for (int j = HB - 1; j >= 0; --j)
 #pragma unroll
             for (int c = 3; c >= 0; --c) {
                 const int idx = elem_index(cb, j, c);
@@ -474,24 +475,25 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
     int best = sm.bi[0];
 #pragma unroll
     for (int w = 1; w < TNW; ++w) argmax_step(M, best, sm.bv[w], sm.bi[w]);
-    auto to_e = [&](float4 (&x)[VPT4]) {
+    auto to_e = [&](auto& x) {
+        constexpr int n = (int)(sizeof(x) / sizeof(float4));
 #pragma unroll
-        for (int j = 0; j < VPT4; ++j)
+        for (int j = 0; j < n; ++j)
 #pragma unroll
             for (int c = 0; c < 4; ++c) f4set(x[j], c, unnorm(f4get(x[j], c), M, ilog));
     };
 
     // the cut: one streamed pass per level
-    for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int) { to_e(x); topp_accumulate<0>(x, 0u, sm); });
+    for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) { to_e(x); topp_accumulate<0, HB>(x, 0u, sm); });
     const double need = topp_scan<0>(0.0, P.top_p, sm);
     const uint32_t b1 = (uint32_t)sm.sel_bucket[0];
     const unsigned long long a1 = sm.sel_above[0];
-    for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int) { to_e(x); topp_accumulate<1>(x, b1, sm); });
+    for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) { to_e(x); topp_accumulate<1, HB>(x, b1, sm); });
     topp_scan<1>(need - (double)a1, P.top_p, sm);
     const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
     const unsigned long long a2 = sm.sel_above[1];
     const uint32_t p2 = (b1 << 10) | b2;
-    for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int) { to_e(x); topp_accumulate<2>(x, p2, sm); });
+    for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) { to_e(x); topp_accumulate<2, HB>(x, p2, sm); });
     topp_scan<2>(need - (double)a1 - (double)a2, P.top_p, sm);
     Nucleus nu;
     nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
@@ -507,11 +509,11 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
             // ties straddle the cut: ties per chunk, then the smallest cutoff c
             // with #ties(id < c) >= k by bisection inside the chunk holding
             // the k-th tie (block counts, alternating buffers)
-            for_each_chunk(row, V, aligned, [&](float4 (&x)[VPT4], int cb) {
+            for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int cb) {
                 to_e(x);
                 unsigned long long cnt = 0;
 #pragma unroll
-                for (int j = 0; j < VPT4; ++j)
+                for (int j = 0; j < HB; ++j)
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         if (elem_index(cb, j, c) < V && __float_as_uint(f4get(x[j], c)) == nu.thr) ++cnt;
