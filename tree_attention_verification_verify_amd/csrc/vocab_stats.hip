@@ -248,13 +248,14 @@ __device__ __forceinline__ void topp_accumulate_list(const uint32_t* list, uint3
 }
 
 // The wave's elements with a nonzero mass in first-level bucket b1, appended
-// to its list (positions by ballot); returns how many there are (the list
-// holds them when that is at most kListCap).  The same in every lane.
-__device__ __forceinline__ uint32_t topp_compact(const float4 (&e)[rows::VPT4], uint32_t b1, uint32_t* list) {
+// to its list after the n already there (positions by ballot); returns how
+// many there are now (the list holds them when that is at most kListCap).
+// The same in every lane.
+template <int N = rows::VPT4>
+__device__ __forceinline__ uint32_t topp_compact(const float4 (&e)[N], uint32_t b1, uint32_t* list, uint32_t n = 0) {
     using namespace rows;
-    uint32_t n = 0;
 #pragma unroll
-    for (int j = 0; j < VPT4; ++j)
+    for (int j = 0; j < N; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint32_t bits = __float_as_uint(f4get(e[j], c));
@@ -425,10 +426,11 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
 
 // Top-p rows longer than one register chunk (V > 32768).  The same cut, with
 // the row streamed chunk by chunk (each next chunk's loads in flight): one
-// pass for the maximum and its first position, one per radix level (the
-// repeated reads come from the caches), and, only when tied probabilities
-// straddle the cut, one pass counting the ties per chunk and a bisection
-// inside the chunk that holds the k-th tie.
+// pass for the maximum and its first position, one each for radix levels 1
+// and 2 (level 3 reads the entries of level 1's crossing bucket that the
+// level-2 pass listed, unless a wave's list overflowed), and, only when tied
+// probabilities straddle the cut, one pass counting the ties per chunk and a
+// bisection inside the chunk that holds the k-th tie.
 __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsParams P) {
     using namespace rows;
     __shared__ ToppSmem sm;
@@ -488,12 +490,23 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
     const double need = topp_scan<0>(0.0, P.top_p, sm);
     const uint32_t b1 = (uint32_t)sm.sel_bucket[0];
     const unsigned long long a1 = sm.sel_above[0];
-    for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) { to_e(x); topp_accumulate<1, HB>(x, b1, sm); });
+    // the level-2 pass also lists each wave's elements in bucket b1; level 3
+    // then reads the list, and only a wave whose list overflowed streams its
+    // part of the row once more
+    uint32_t nlist = 0;
+    for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) {
+        to_e(x);
+        topp_accumulate<1, HB>(x, b1, sm);
+        nlist = topp_compact<HB>(x, b1, sm.list[wave], nlist);
+    });
     topp_scan<1>(need - (double)a1, P.top_p, sm);
     const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
     const unsigned long long a2 = sm.sel_above[1];
     const uint32_t p2 = (b1 << 10) | b2;
-    for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) { to_e(x); topp_accumulate<2, HB>(x, p2, sm); });
+    if (nlist <= (uint32_t)kListCap)
+        topp_accumulate_list<2>(sm.list[wave], nlist, p2, sm);
+    else
+        for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) { to_e(x); topp_accumulate<2, HB>(x, p2, sm); });
     topp_scan<2>(need - (double)a1 - (double)a2, P.top_p, sm);
     Nucleus nu;
     nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
