@@ -24,8 +24,33 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 VALU_FP32_PEAK_TFLOPS = 157.3
 RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop/byte
-KERNEL_SOURCES = {"attention": "tree_attn.hip", "vocab": "vocab_stats.hip", "finish": "select_final.hip"}
-KERNEL_NAMES = {"attention": "attn_mfma_kernel", "vocab": "row_stats_stream_kernel", "finish": "finish_kernel"}
+KERNEL_SOURCES = {"attn_mfma_kernel": "tree_attn.hip", "attn_valu_kernel": "tree_attn.hip",
+                  "attn_valu_tiled_kernel": "tree_attn_valu.hip",
+                  "row_stats_stream_kernel": "vocab_stats.hip", "row_stats_topp_kernel": "vocab_stats.hip",
+                  "row_stats_topp_chunked_kernel": "vocab_stats.hip", "finish_kernel": "select_final.hip"}
+VOCAB_CHUNK = 32768   # vocabulary ids one row workgroup holds on chip (kVocabChunk)
+
+
+def stage_kernel(stage, spec):
+    """The kernel a stage launches for this workload, by the library's own dispatch rule.
+
+    Attention: the MFMA kernel when bf16 and the g*T query rows sharing one KV head
+    number at least 16; below that the tiled VALU kernel for at most 8 rows whose K/V
+    rows are 128 or 256 bytes, else the one-wave VALU kernel.  Row statistics: with
+    top-p in sampling mode, the row held on chip up to VOCAB_CHUNK ids and streamed
+    above; otherwise the streaming kernel.
+    """
+    if stage == "attention":
+        rows = spec.hq // spec.hkv * spec.nodes
+        if spec.dtype == "bf16" and rows >= 16:
+            return "attn_mfma_kernel"
+        rowb = spec.head_dim * (2 if spec.dtype == "bf16" else 4)
+        return "attn_valu_tiled_kernel" if rows <= 8 and rowb in (128, 256) else "attn_valu_kernel"
+    if stage == "vocab":
+        if spec.mode == "sampling" and spec.top_p < 1.0:
+            return "row_stats_topp_kernel" if spec.vocab <= VOCAB_CHUNK else "row_stats_topp_chunked_kernel"
+        return "row_stats_stream_kernel"
+    return "finish_kernel"
 
 
 def parse():
@@ -73,18 +98,18 @@ def algorithmic_work(case):
     return dict(attention_bytes=int(attn_bytes), attention_flops=int(attn_flops), vocab_bytes=int(vocab_bytes))
 
 
-def source_hash(stage):
-    path = os.path.join(ROOT, "tree_attention_verification_verify_amd", "csrc", KERNEL_SOURCES[stage])
+def source_hash(kname):
+    path = os.path.join(ROOT, "tree_attention_verification_verify_amd", "csrc", KERNEL_SOURCES[kname])
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(stage, workload):
+def measured_traffic(kname, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if the kernel is unchanged."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (KERNEL_NAMES[stage], workload))
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kname, workload))
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256_16") != source_hash(stage):
+    if rec.get("source_sha256_16") != source_hash(kname):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -188,12 +213,6 @@ def time_tree_build(spec, B, steps, stream):
             "GBps": nbytes / (us * 1e-6) / 1e9}
 
 
-def synth_mode(name):
-    import synth
-
-    return synth.workload(name).mode
-
-
 def _counter_per_dispatch(csv_path, kernel_prefix, counter):
     """Mean value of `counter` over the dispatches of kernels whose name starts with kernel_prefix."""
     import csv
@@ -206,7 +225,7 @@ def _counter_per_dispatch(csv_path, kernel_prefix, counter):
     return sum(vals) / len(vals), len(vals)
 
 
-def traffic_summary(paths, workload, stage="attention"):
+def traffic_summary(paths, workload, kname):
     """Write the HBM traffic record of one kernel from rocprofv3 --pmc counter CSVs.
 
     paths: FETCH_SIZE csv and WRITE_SIZE csv of a bench run, then FETCH_SIZE and
@@ -216,7 +235,6 @@ def traffic_summary(paths, workload, stage="attention"):
     """
     fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes = paths
     copy_bytes = int(copy_bytes)
-    kname = KERNEL_NAMES[stage]
     fetch_kib, nf = _counter_per_dispatch(fetch_csv, kname, "FETCH_SIZE")
     write_kib, nw = _counter_per_dispatch(write_csv, kname, "WRITE_SIZE")
     cf_kib, _ = _counter_per_dispatch(cfetch_csv, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
@@ -225,8 +243,8 @@ def traffic_summary(paths, workload, stage="attention"):
     w_scale = copy_bytes / (cw_kib * 1024.0)
     read_b = fetch_kib * 1024.0 * f_scale
     write_b = write_kib * 1024.0 * w_scale
-    rec = {"kernel": kname, "workload": workload, "source": KERNEL_SOURCES[stage],
-           "source_sha256_16": source_hash(stage),
+    rec = {"kernel": kname, "workload": workload, "source": KERNEL_SOURCES[kname],
+           "source_sha256_16": source_hash(kname),
            "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
            "dispatches": [nf, nw], "copy_probe_bytes": copy_bytes,
            "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
@@ -243,7 +261,9 @@ def traffic_summary(paths, workload, stage="attention"):
 def main():
     args = parse()
     if args.traffic_summary:
-        traffic_summary(args.traffic_summary, "%s-%s" % (args.workload, args.mode or synth_mode(args.workload)))
+        import synth
+        spec = synth.workload(args.workload, **({"mode": args.mode} if args.mode else {}))
+        traffic_summary(args.traffic_summary, "%s-%s" % (args.workload, spec.mode), stage_kernel("attention", spec))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs the verify step on one GPU only; --gpus %d is not supported "
@@ -471,9 +491,9 @@ def main():
     else:
         achieved = work["vocab_bytes"] / (per_launch["vocab"] * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS)
-    roof["kernel"] = KERNEL_NAMES[dominant]
+    roof["kernel"] = stage_kernel(dominant, spec)
     roof["ms_per_launch"] = per_launch[dominant]
-    roof["traffic"] = measured_traffic(dominant, workload)
+    roof["traffic"] = measured_traffic(roof["kernel"], workload)
 
     step_bytes = work["attention_bytes"] + work["vocab_bytes"]
     attn_t = per_launch["attention"] * 1e-3
