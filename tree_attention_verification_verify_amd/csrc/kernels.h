@@ -80,8 +80,9 @@ struct SelectParams {
     double2* slice_tot;   // [B][S] (residual, p-only) weight totals per slice of the final draw
     double2* slice_pre;   // [B][S][kSelectThreads] per-thread exclusive prefixes (S <= kSelectKeepSlices)
     float* resid_ws;      // [B][2][V] residual rows of the lossless sibling walk
-    int32_t* walk_sync;   // [B][4] sibling walk across workgroups: arrivals, finished workgroups, timeout flag
-    double* walk_part;    // [B][2][walk_k] per-workgroup residual totals (two passes in turn)
+    int32_t* walk_sync;   // [B][4] sibling walk across workgroups: (unused), finished workgroups, timeout flag
+    double* walk_part;    // [B][2][walk_k] per-workgroup residual totals tagged with their pass (two passes
+                          // in turn; zero between launches)
     float* walk_rx;       // [B][2][2] the next test's r (new, kept) from the workgroup holding its token
     int walk_k;           // workgroups per sequence of the walk: ceil(V / kWalkSlice)
     int walk_coop;        // 1: the walk over walk_k workgroups per sequence; 0: one workgroup per sequence

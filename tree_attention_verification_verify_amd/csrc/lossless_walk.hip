@@ -567,14 +567,15 @@ __global__ __launch_bounds__(NT) void lossless_walk_resident_kernel(SelectParams
 // Every workgroup takes the same decisions from the same values: the first
 // tests as above, and after each residual pass the sequence's K slice totals
 // (summed in slice order) and r at the next child's token, published by the
-// workgroup holding it.  A pass ends with an arrival barrier of the K
-// workgroups: agent-scope atomic stores of the totals, a `vmcnt(0)` wait, an
-// arrival count, and a bounded wait for the count (a wait that runs out sets
-// the status bit SPEC_VERIFY_STATUS_WALK_TIMEOUT and goes on, so every wave
+// workgroup holding it.  A pass ends with a barrier of the K workgroups:
+// each, once its other stores of the pass have landed (`vmcnt(0)`), stores
+// its total tagged with the pass as an agent-scope atomic, and reads the K
+// slots until all carry the pass's tag (a bounded wait: running out sets the
+// status bit SPEC_VERIFY_STATUS_WALK_TIMEOUT and goes on, so every wave
 // ends).  The draw takes r's slice totals from the last pass when r is that
 // pass's residual (else from one more synchronised pass), and the workgroup
 // holding the slice where u * W falls locates the token.  The last workgroup
-// to finish resets the counters for the next step.
+// to finish clears the slots and counters for the next step.
 
 constexpr int CT = kWalkThreads;
 constexpr int CW = CT / kWave;
@@ -594,7 +595,7 @@ struct CoopShared {
     double slot_tot[CV4];
     double W, cum, send;         // after a pass: the total; for the draw: prefixes around slice s*
     float rx_new, rx_old;
-    int sstar, winner, found, live, status;
+    int sstar, winner, found, live, status, last, timed_out;
 };
 
 __device__ __forceinline__ int cidx(int first, int j, int e) { return first + 4 * (threadIdx.x + CT * j) + e; }
@@ -652,33 +653,41 @@ __device__ __forceinline__ double coop_total(const float4 (&w)[CV4], CoopShared&
     return tot;
 }
 
-// Arrival barrier of the sequence's K workgroups after this workgroup
-// published its pass-`pass` values; then wave 0 scans the K totals in slice
-// order.  With `target` >= 0 it also finds the slice s* whose running total
-// first exceeds target (rounding: the last slice with weight) and the
-// prefixes before and through it.  Results in cs (after a barrier).
-// With `arrived` the pass's values are already known to be published (the
-// scan of a pass that was synchronised before).
+// Pass totals are published as tagged slots: the low 3 bits of a slice
+// total (a nonnegative double) are replaced by 1 + (pass & 3), so a slot
+// names the pass it belongs to (slots alternate by pass parity, and 0 is the
+// reset state).  Readers strip the tag: every workgroup sees the same totals,
+// each within 2^-49 (relative) of the one summed.
+__device__ __forceinline__ unsigned long long tag_total(double t, int pass) {
+    return (__double_as_longlong(t) & ~7ull) | (unsigned long long)(1 + (pass & 3));
+}
+__device__ __forceinline__ double untag_total(unsigned long long raw) {
+    return __longlong_as_double((long long)(raw & ~7ull));
+}
+
+// Barrier of the sequence's K workgroups for pass `pass`, then wave 0 scans
+// the K totals in slice order.  With `publish` this workgroup first stores
+// its total t in its slot (after its other stores of the pass have landed);
+// wave 0 then reads the K slots until each carries this pass's tag (the read
+// that sees the tag is the value read: no separate arrival count).  With
+// `draw` it also finds the slice s* whose running total first exceeds
+// u_final * W (rounding: the last slice with weight) and the prefixes before
+// and through it.  Results in cs (after a barrier).
 __device__ __forceinline__ void coop_sync_scan(const SelectParams& P, int b, int pass, bool want_rx, double u_final,
-                                               bool draw, CoopShared& cs, bool arrived = false) {
+                                               bool draw, CoopShared& cs, bool publish, double t) {
     const int K = P.walk_k;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    int32_t* sync = P.walk_sync + 4 * b;
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's published values have landed
-    __syncthreads();
+    unsigned long long* part = (unsigned long long*)(P.walk_part + (size_t)(b * 2 + (pass & 1)) * K);
+    const unsigned long long want = (unsigned long long)(1 + (pass & 3));
+    if (publish) {
+        __builtin_amdgcn_s_waitcnt(0);   // this workgroup's other stores of the pass have landed
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(part + (blockIdx.x % K), tag_total(t, pass), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (tid < kWave) {
-        bool late = false;
-        if (tid == 0 && !arrived) {
-            __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int want = K * (pass + 1);
-            int it = 0;
-            while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
-                if (++it > kSpinLimit) { late = true; break; }
-                __builtin_amdgcn_s_sleep(2);
-            }
-            if (late) __hip_atomic_store(sync + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        const double* part = P.walk_part + (size_t)(b * 2 + (pass & 1)) * K;
+        bool late = cs.timed_out != 0;   // after one wait has run out, later ones do not wait
+        int it = 0;
         double run = 0.0;        // prefix of the earlier rounds of 64 slices
         int sstar = -1, lastpos = -1;
         double cum = 0.0, send = 0.0, lastcum = 0.0, lastend = 0.0;
@@ -689,7 +698,18 @@ __device__ __forceinline__ void coop_sync_scan(const SelectParams& P, int b, int
             const double target = sweep == 1 ? u_final * W : -1.0;
             for (int k0 = 0; k0 < K; k0 += kWave) {
                 const int k = k0 + lane;
-                const double v = k < K ? __hip_atomic_load(part + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
+                unsigned long long raw = 0ull;
+                bool ok = k >= K;
+                while (true) {
+                    if (!ok) {
+                        raw = __hip_atomic_load(part + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ok = (raw & 7ull) == want;
+                    }
+                    if (__all(ok) || late) break;
+                    if (++it > kSpinLimit) late = true;   // a workgroup never arrived: go on, flag it
+                    else __builtin_amdgcn_s_sleep(1);
+                }
+                const double v = untag_total(raw);
                 double inc = v;
 #pragma unroll
                 for (int o = 1; o < kWave; o <<= 1) {
@@ -718,6 +738,10 @@ __device__ __forceinline__ void coop_sync_scan(const SelectParams& P, int b, int
                 run = __shfl(inc, kWave - 1, kWave);
             }
             W = run;
+        }
+        if (late && lane == 0) {
+            __hip_atomic_store(P.walk_sync + 4 * b + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            cs.timed_out = 1;
         }
         if (tid == 0) {
             cs.W = W;
@@ -818,6 +842,7 @@ __global__ __launch_bounds__(CT) void lossless_walk_coop_kernel(SelectParams P) 
             if (lane == 0) {
                 cs.status = status;
                 cs.live = 1;
+                cs.timed_out = 0;
             }
         }
     }
@@ -908,10 +933,7 @@ __global__ __launch_bounds__(CT) void lossless_walk_coop_kernel(SelectParams P) 
             for (int e = 0; e < 4; ++e) f4set(q[j], e, resid_weight(f4get(rr[j], e), ir, f4get(q[j], e), iq));
         if (owner) __hip_atomic_store(rxp, coop_pick(q, j2, e2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const double t = coop_total(q, cs, pass & 1);
-        if (tid == 0)
-            __hip_atomic_store(P.walk_part + (size_t)(b * 2 + (pass & 1)) * K + s, t, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        coop_sync_scan(P, b, pass, c2 >= 0, 0.0, false, cs);
+        coop_sync_scan(P, b, pass, c2 >= 0, 0.0, false, cs, true, t);
         const double Wn = cs.W;
         if (Wn > 0.0) {
 #pragma unroll
@@ -930,13 +952,10 @@ __global__ __launch_bounds__(CT) void lossless_walk_coop_kernel(SelectParams P) 
     // slice totals in slice order give s*; the workgroup holding it locates y.
     // When r is the residual of the last pass, that pass's totals are r's.
     if (last_kept) {
-        coop_sync_scan(P, b, pass - 1, false, (double)P.u_final[b], true, cs, true);
+        coop_sync_scan(P, b, pass - 1, false, (double)P.u_final[b], true, cs, false, 0.0);
     } else {
         const double t = coop_total(rr, cs, pass & 1);
-        if (tid == 0)
-            __hip_atomic_store(P.walk_part + (size_t)(b * 2 + (pass & 1)) * K + s, t, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        coop_sync_scan(P, b, pass, false, (double)P.u_final[b], true, cs);
+        coop_sync_scan(P, b, pass, false, (double)P.u_final[b], true, cs, true, t);
     }
     const int sstar = cs.sstar;
     const double target = (double)P.u_final[b] * cs.W;
@@ -1025,13 +1044,20 @@ __global__ __launch_bounds__(CT) void lossless_walk_coop_kernel(SelectParams P) 
         const int late = __hip_atomic_load(P.walk_sync + 4 * b + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         P.status[b] = cs.status | (late ? 16 : 0);
     }
-    // the last workgroup of the sequence to finish resets the counters
+    // the last workgroup of the sequence to finish (every workgroup has read
+    // its last slots by then) clears the slots and the counters for the next
+    // launch
+    int32_t* sync = P.walk_sync + 4 * b;
     if (tid == 0) {
-        int32_t* sync = P.walk_sync + 4 * b;
         __builtin_amdgcn_s_waitcnt(0);
         const int prev = __hip_atomic_fetch_add(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == K - 1) {
-            __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        cs.last = prev == K - 1;
+    }
+    __syncthreads();
+    if (cs.last) {
+        unsigned long long* slots = (unsigned long long*)(P.walk_part + (size_t)b * 2 * K);
+        for (int i = tid; i < 2 * K; i += CT) __hip_atomic_store(slots + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
             __hip_atomic_store(sync + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(sync + 2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

@@ -216,6 +216,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         if (e == hipSuccess) e = hipMalloc((void**)&h->walk_sync, (size_t)c.max_batch * 4 * sizeof(int32_t));
         if (e == hipSuccess) e = hipMemset(h->walk_sync, 0, (size_t)c.max_batch * 4 * sizeof(int32_t));
         if (e == hipSuccess) e = hipMalloc((void**)&h->walk_part, (size_t)c.max_batch * 2 * h->walk_k * sizeof(double));
+        if (e == hipSuccess) e = hipMemset(h->walk_part, 0, (size_t)c.max_batch * 2 * h->walk_k * sizeof(double));
         if (e == hipSuccess) e = hipMalloc((void**)&h->walk_rx, (size_t)c.max_batch * 4 * sizeof(float));
         if (e == hipSuccess && (long)c.max_batch * h->walk_k > h->walk_cap && c.vocab > sv::kVocabChunk)
             e = hipMalloc((void**)&h->resid_ws, (size_t)c.max_batch * 2 * c.vocab * sizeof(float));
