@@ -126,3 +126,26 @@ def test_tree_template_rejects_bad_arguments(caps, nodes):
     with pytest.raises(sva.SpecVerifyError) as e:
         sva.spec_verify_tree_template(caps, nodes)
     assert e.value.code == binding.SPEC_VERIFY_ERR_INVALID_ARG
+
+
+def test_paged_kv_keeps_its_tensors_alive():
+    """The PagedKV struct carries raw addresses; the tensors behind them must live
+    as long as it does (pools built from temporaries were freed while in use)."""
+    import gc
+    import weakref
+
+    import torch
+
+    k = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    t = torch.zeros((1, 4), dtype=torch.int32)
+    refs = [weakref.ref(x) for x in (k, v, t)]
+    pk = binding.paged_kv(k, v, t)
+    assert (pk.k_pool, pk.v_pool, pk.block_table) == (k.data_ptr(), v.data_ptr(), t.data_ptr())
+    assert (pk.num_blocks, pk.block_size, pk.table_width) == (4, 16, 4)
+    del k, v, t
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    del pk
+    gc.collect()
+    assert all(r() is None for r in refs)

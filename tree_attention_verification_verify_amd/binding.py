@@ -171,7 +171,10 @@ def _outputs(outputs: Dict) -> Outputs:
 def paged_kv(k_pool, v_pool, block_table) -> PagedKV:
     """PagedKV from pools [num_blocks, Hkv, block_size, D] and a table [B, width] (device tensors)."""
     nb, _, bs, _ = k_pool.shape
-    return PagedKV(_ptr(k_pool), _ptr(v_pool), _ptr(block_table), nb, bs, block_table.shape[1])
+    pk = PagedKV(_ptr(k_pool), _ptr(v_pool), _ptr(block_table), nb, bs, block_table.shape[1])
+    # the struct holds raw device addresses: keep the tensors alive as long as it is
+    pk._tensors = (k_pool, v_pool, block_table)
+    return pk
 
 
 def spec_verify_run(handle, inputs: Dict, outputs: Dict, stream=None) -> None:
