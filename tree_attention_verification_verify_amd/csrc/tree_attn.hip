@@ -186,8 +186,13 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
                                   : (size_t)(b * P.Hkv + kvh) * P.Lcap * D;
     const uint16_t* kbase = (const uint16_t*)P.k + head_off;
     const uint16_t* vbase = (const uint16_t*)P.v + head_off;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, k1 * D * 2, kRsrcFlags);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, k1 * D * 2, kRsrcFlags);
+    // paged: one resource per pool, based at this KV head's slice of page 0;
+    // a block wholly inside a page and the split is read through it with the
+    // page's offset as the scalar offset (when the pool spans < 4 GiB)
+    const int page_bytes = PAGED ? P.Hkv * (D << P.pt.bs_log2) * 2 : 0;
+    const bool pool_small = PAGED && (uint64_t)P.pt.num_blocks * (uint64_t)page_bytes < (1ull << 32);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, PAGED ? -1 : k1 * D * 2, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, PAGED ? -1 : k1 * D * 2, kRsrcFlags);
     constexpr int BLOCKS = KT * D * 2 / 1024;          // 1 KB blocks per tile and operand
     constexpr int ROWS_PER_BLOCK = 1024 / (D * 2);
     constexpr int LOADS = 2 * BLOCKS / WAVES;           // K and V blocks one wave loads per tile
@@ -215,6 +220,11 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
         if constexpr (PAGED) {
             const int key0 = (isk ? tk : tv) + blk * ROWS_PER_BLOCK;
             const int in_page = key0 & ((1 << P.pt.bs_log2) - 1);
+            if (pool_small && page >= 0 && key0 + ROWS_PER_BLOCK <= k1) {   // wave-uniform
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16, (in_page + lane / CH) * (D * 2) + c * 16,
+                                                         (uint32_t)page * (uint32_t)page_bytes, 0, 0);
+                return;
+            }
             const int room = min(max(k1 - (key0 - in_page), 0), 1 << P.pt.bs_log2);
             const size_t page_off = ((size_t)max(page, 0) * P.Hkv) * ((size_t)D << P.pt.bs_log2);
             // every operand of the resource is wave-uniform: keep it in scalar registers
