@@ -138,6 +138,44 @@ def test_paged_full_size_gqa_medusa_equals_dense():
         np.testing.assert_array_equal(got["paged"][k], v, err_msg=k)
 
 
+def test_paged_pool_beyond_4gib_equals_small_pool():
+    # a pool spanning more than 4 GiB takes the per-page buffer resources for
+    # every block (a pool under 4 GiB reads whole blocks through one resource
+    # with the page in the scalar offset): the same pages moved to the top of
+    # a 4 GiB + pool must give the small pool's outputs bit for bit
+    import torch
+    from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs, paged_kv
+
+    spec = synth.workload("70b-gqa-medusa", batch=2, prefix_len=333, seed=(16, 11))
+    case, paged = synth.page_case(synth.make_case(spec), 16, seed=(16, 11))
+    small = _paged_device(paged, spec.dtype)
+    nb, hkv, bs, d = paged.k_pool.shape
+    page_bytes = hkv * bs * d * 2
+    top = (1 << 32) // page_bytes + 1            # pages below the moved ones
+    note("paged-4gib: pool of %d pages (%.2f GiB per operand)" % (top + nb, (top + nb) * page_bytes / 2 ** 30))
+    big_k = torch.empty((top + nb, hkv, bs, d), dtype=torch.bfloat16, device="cuda")
+    big_v = torch.empty_like(big_k)
+    big_k[top:] = small["k_pool"]
+    big_v[top:] = small["v_pool"]
+    table = small["block_table"].clone()
+    table[table >= 0] += top
+    ins = {k: v for k, v in device_inputs(case).items() if k not in ("k_cache", "v_cache")}
+    got = {}
+    with SpecVerify(**handle_config(spec, kv_capacity=max(case.k_cache.shape[2], paged.capacity))) as sv:
+        for name, pk in (("small", paged_kv(small["k_pool"], small["v_pool"], small["block_table"])),
+                         ("big", paged_kv(big_k, big_v, table))):
+            outs = allocate_outputs(case.batch, case.nodes, spec.hq, spec.head_dim, spec.dtype)
+            note("paged-4gib: %s pool run" % name)
+            sv.run_paged(ins, pk, outs)
+            torch.cuda.synchronize()
+            got[name] = to_numpy(outs)
+    assert (got["big"]["status"] == 0).all()
+    for k, v in got["small"].items():
+        np.testing.assert_array_equal(got["big"][k], v, err_msg=k)
+    del big_k, big_v
+    torch.cuda.empty_cache()
+
+
 def test_paged_with_the_lossless_tree_rule():
     spec = synth.workload("70b-gqa-medusa", batch=3, prefix_len=260, vocab=4000, ragged=(120, 260), seed=(16, 10))
     case, paged = synth.page_case(synth.make_case(spec), 32, seed=(16, 10))
