@@ -138,7 +138,11 @@ def test_paged_full_size_gqa_medusa_equals_dense():
         np.testing.assert_array_equal(got["paged"][k], v, err_msg=k)
 
 
-def test_paged_pool_beyond_4gib_equals_small_pool():
+@pytest.mark.parametrize("name,kw", [
+    ("70b-gqa-medusa", dict(batch=2, prefix_len=333, seed=(16, 11))),                        # MFMA kernel
+    ("chain-batch32-topp", dict(batch=2, prefix_len=301, ragged=(150, 301), seed=(16, 12))),  # tiled VALU kernel
+])
+def test_paged_pool_beyond_4gib_equals_small_pool(name, kw):
     # a pool spanning more than 4 GiB takes the per-page buffer resources for
     # every block (a pool under 4 GiB reads whole blocks through one resource
     # with the page in the scalar offset): the same pages moved to the top of
@@ -146,8 +150,8 @@ def test_paged_pool_beyond_4gib_equals_small_pool():
     import torch
     from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs, paged_kv
 
-    spec = synth.workload("70b-gqa-medusa", batch=2, prefix_len=333, seed=(16, 11))
-    case, paged = synth.page_case(synth.make_case(spec), 16, seed=(16, 11))
+    spec = synth.workload(name, **kw)
+    case, paged = synth.page_case(synth.make_case(spec), 16, seed=kw["seed"])
     small = _paged_device(paged, spec.dtype)
     nb, hkv, bs, d = paged.k_pool.shape
     page_bytes = hkv * bs * d * 2

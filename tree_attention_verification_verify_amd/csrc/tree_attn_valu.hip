@@ -100,8 +100,13 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
                                   : (size_t)(b * P.Hkv + kvh) * P.Lcap * ROWB;
     const uint8_t* kbase = (const uint8_t*)P.k + head_off;
     const uint8_t* vbase = (const uint8_t*)P.v + head_off;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, k1 * ROWB, kRsrcFlags);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, k1 * ROWB, kRsrcFlags);
+    // paged: one resource per pool, based at this KV head's slice of page 0;
+    // a block wholly inside a page and the split is read through it with the
+    // page's offset as the scalar offset (when the pool spans < 4 GiB)
+    const int page_bytes = PAGED ? P.Hkv * (ROWB << P.pt.bs_log2) : 0;
+    const bool pool_small = PAGED && (uint64_t)P.pt.num_blocks * (uint64_t)page_bytes < (1ull << 32);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, PAGED ? -1 : k1 * ROWB, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, PAGED ? -1 : k1 * ROWB, kRsrcFlags);
     const int32_t* trow = PAGED ? P.pt.table + (size_t)b * P.pt.width : nullptr;
     // paged caches: lane l of the result holds the page entry of block load l
     // of the tile at key t (-1 past the split); fetched one step ahead
@@ -123,6 +128,11 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
         if constexpr (PAGED) {
             const int key0 = t + blk * RPB;   // first slot of the block (wave-uniform)
             const int in_page = key0 & ((1 << P.pt.bs_log2) - 1);
+            if (pool_small && page >= 0 && key0 + RPB <= k1) {   // wave-uniform
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16, (in_page + lane / CH) * ROWB + c * 16,
+                                                         (uint32_t)page * (uint32_t)page_bytes, 0, 0);
+                return;
+            }
             const int room = min(max(k1 - (key0 - in_page), 0), 1 << P.pt.bs_log2);
             const uint64_t addr = (uint64_t)((isk ? kbase : vbase) +
                                              (size_t)max(page, 0) * P.Hkv * ((size_t)ROWB << P.pt.bs_log2));
