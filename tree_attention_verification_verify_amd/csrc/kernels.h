@@ -105,6 +105,7 @@ struct CommitParams {
     int B, T, Hkv, Lcap;
     int row_bytes;           // D * element size (a multiple of 16)
     PageTable pt;            // paged caches: k, v are the pools; Lcap = pt.width << pt.bs_log2
+    int32_t* arrive;         // [B] finished workgroups per sequence (zero between calls)
 };
 
 // Candidate-tree construction: template by value (T <= 64, depth <= 63,

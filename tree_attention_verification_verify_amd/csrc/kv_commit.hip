@@ -11,10 +11,12 @@
 // section 6.3).  Void sequences, lengths out of range and paths that are not
 // root paths (path[0] = 0, k <= path[k] < T) are left unchanged.
 //
-// One workgroup per sequence.  For each KV head every 16-byte chunk of the
-// moved rows (K and V) is loaded into registers before any is stored, since a
-// destination slot may be the source of an earlier row; rows already in
-// place are skipped.
+// One workgroup per (sequence, KV head): heads touch disjoint memory.  Every
+// 16-byte chunk of the head's moved rows (K and V) is loaded into registers
+// before any is stored, since a destination slot may be the source of an
+// earlier row; rows already in place are skipped.  The new length is written
+// by the last workgroup of the sequence to finish (a per-sequence counter),
+// so no workgroup can read a length already updated.
 //
 // Paged caches: slot s lives in row s % bs of page table[s / bs]; a dense
 // cache is addressed the same way as one page of Lcap slots per sequence
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(CT) void kv_commit_kernel(CommitParams P) {
     __shared__ int src[64];
     __shared__ size_t off_src[64], off_dst[64];   // byte offset of row k's source / destination slot, head 0
     __shared__ int sL, sA, sok;
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int b = blockIdx.x / P.Hkv, h = blockIdx.x - b * P.Hkv, tid = threadIdx.x;
     const int T = P.T;
     if (tid < kWave) {
         const int lane = tid;
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(CT) void kv_commit_kernel(CommitParams P) {
     const int cpr = P.row_bytes / 16;             // chunks per row
     const int total = 2 * A * cpr;                 // K and V chunks of rows 1..A
     const size_t head_stride = (size_t)(P.pt.table ? (1 << P.pt.bs_log2) : P.Lcap) * P.row_bytes;
-    for (int h = 0; h < P.Hkv; ++h) {
+    {
         const size_t head = (size_t)h * head_stride;
         u32x4 reg[MAXC];
 #pragma unroll
@@ -97,13 +99,21 @@ __global__ __launch_bounds__(CT) void kv_commit_kernel(CommitParams P) {
             }
         }
     }
-    if (tid == 0) P.kv_len_out[b] = L + A + 1;
+    // every workgroup of the sequence has read the old length before it counts
+    // itself; a skipped sequence (the same decision in all of them) counts nothing
+    if (tid == 0) {
+        const int prev = __hip_atomic_fetch_add(P.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == P.Hkv - 1) {
+            __hip_atomic_store(P.arrive + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            P.kv_len_out[b] = L + A + 1;
+        }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_kv_commit(const CommitParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(kv_commit_kernel, dim3(p.B), dim3(CT), 0, s, p);
+    hipLaunchKernelGGL(kv_commit_kernel, dim3(p.B * p.Hkv), dim3(CT), 0, s, p);
     return hipGetLastError();
 }
 

@@ -123,6 +123,7 @@ struct spec_verify_handle {
     double2* slice_tot = nullptr;     // max_batch * slices final-draw slice totals
     double2* slice_pre = nullptr;     // max_batch * slices * 256 per-thread slice prefixes (few slices only)
     int32_t* arrive = nullptr;        // max_batch final-draw arrival counters (zero between runs)
+    int32_t* commit_arrive = nullptr; // max_batch KV-commit finish counters (zero between calls)
     float* resid_ws = nullptr;        // max_batch * 2 * vocab residual rows (lossless tree walk)
     int32_t* walk_sync = nullptr;     // max_batch * 4 walk counters (lossless tree walk)
     double* walk_part = nullptr;      // max_batch * 2 * walk_k walk slice totals
@@ -204,6 +205,8 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         e = hipMalloc((void**)&h->slice_pre, (size_t)c.max_batch * slices * sv::kSelectThreads * sizeof(double2));
     if (e == hipSuccess) e = hipMalloc((void**)&h->arrive, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(h->arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc((void**)&h->commit_arrive, (size_t)c.max_batch * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMemset(h->commit_arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE)) {
         // the walk across workgroups waits for all of a sequence's workgroups,
         // so it is launched only while the grid fits twice per CU; larger
@@ -227,6 +230,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         (void)hipFree(h->slice_tot);
         (void)hipFree(h->slice_pre);
         (void)hipFree(h->arrive);
+        (void)hipFree(h->commit_arrive);
         (void)hipFree(h->resid_ws);
         (void)hipFree(h->walk_sync);
         (void)hipFree(h->walk_part);
@@ -266,6 +270,7 @@ int spec_verify_destroy(spec_verify_handle* h) {
     if (h->slice_tot) (void)hipFree(h->slice_tot);
     if (h->slice_pre) (void)hipFree(h->slice_pre);
     if (h->arrive) (void)hipFree(h->arrive);
+    if (h->commit_arrive) (void)hipFree(h->commit_arrive);
     if (h->resid_ws) (void)hipFree(h->resid_ws);
     if (h->walk_sync) (void)hipFree(h->walk_sync);
     if (h->walk_part) (void)hipFree(h->walk_part);
@@ -468,6 +473,7 @@ int commit_impl(spec_verify_handle* h, const spec_verify_commit_args* a, const s
     cp.Lcap = slots;
     cp.row_bytes = c.head_dim * (c.dtype == SPEC_VERIFY_BF16 ? 2 : 4);
     cp.pt = pt;
+    cp.arrive = h->commit_arrive;
     const hipError_t e = sv::launch_kv_commit(cp, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "commit launch");
     return SPEC_VERIFY_OK;
