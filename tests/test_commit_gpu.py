@@ -21,11 +21,22 @@ def _gpu_commit(case, path, accept_len, final_node, kv_len=None):
     dev = ins["k_cache"].device
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
     kl = t(case.kv_len if kv_len is None else kv_len)
-    with SpecVerify(**handle_config(spec, kv_capacity=case.k_cache.shape[2])) as sv:
-        sv.commit(ins["k_cache"], ins["v_cache"], kl, t(path), t(accept_len), t(final_node))
-        torch.cuda.synchronize()
+    k0, v0, kl0 = ins["k_cache"].clone(), ins["v_cache"].clone(), kl.clone()
     as_np = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.cpu().numpy()
-    return as_np(ins["k_cache"]), as_np(ins["v_cache"]), kl.cpu().numpy()
+    res = []
+    # two calls on one handle from the same inputs: the second must repeat the
+    # first (the per-sequence counters that order the length update reset)
+    with SpecVerify(**handle_config(spec, kv_capacity=case.k_cache.shape[2])) as sv:
+        for _ in range(2):
+            ins["k_cache"].copy_(k0)
+            ins["v_cache"].copy_(v0)
+            kl.copy_(kl0)
+            sv.commit(ins["k_cache"], ins["v_cache"], kl, t(path), t(accept_len), t(final_node))
+            torch.cuda.synchronize()
+            res.append((as_np(ins["k_cache"]), as_np(ins["v_cache"]), kl.cpu().numpy()))
+    for a, b in zip(res[0], res[1]):
+        np.testing.assert_array_equal(a, b)
+    return res[1]
 
 
 def _check(case, path, accept_len, final_node, label, kv_len=None):
