@@ -121,6 +121,9 @@ struct TreeParams {
     int8_t trank[64];           // top-k entry each node takes
     int8_t tdep[64];            // depth of each node
     int8_t kd[64];              // entries needed at depth d (max rank + 1)
+    int slices;                 // workgroups per row (1: the whole row in one)
+    unsigned long long* cand;   // [B][levels][slices][32] per-slice best keys (slices > 1)
+    int32_t* arrive;            // [B][levels] finished slices per row (zero between calls)
 };
 
 // Returns hipSuccess or the launch error.
@@ -144,6 +147,7 @@ hipError_t launch_tree_build(const TreeParams& p, int kmax, hipStream_t s);
 
 constexpr int kValuRows = 16;      // rows per block of the VALU attention kernel
 constexpr int kMfmaHalves = 2;     // key halves per workgroup of the MFMA attention kernel
+constexpr int kTreeMaxSlices = 8;                  // tree building: workgroups per logits row at most
 constexpr int kVocabThreads = 1024;               // register-resident row kernels
 constexpr int kVocabChunk = kVocabThreads * 32;   // logits held on chip per pass
 constexpr int kStatsThreads = 256;                // streaming row-statistics kernel

@@ -124,6 +124,8 @@ struct spec_verify_handle {
     double2* slice_pre = nullptr;     // max_batch * slices * 256 per-thread slice prefixes (few slices only)
     int32_t* arrive = nullptr;        // max_batch final-draw arrival counters (zero between runs)
     int32_t* commit_arrive = nullptr; // max_batch KV-commit finish counters (zero between calls)
+    unsigned long long* tree_cand = nullptr;   // tree building: per-slice best keys of every row
+    int32_t* tree_arrive = nullptr;            // tree building: finished slices per row (zero between calls)
     float* resid_ws = nullptr;        // max_batch * 2 * vocab residual rows (lossless tree walk)
     int32_t* walk_sync = nullptr;     // max_batch * 4 walk counters (lossless tree walk)
     double* walk_part = nullptr;      // max_batch * 2 * walk_k walk slice totals
@@ -207,6 +209,12 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
     if (e == hipSuccess) e = hipMemset(h->arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess) e = hipMalloc((void**)&h->commit_arrive, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(h->commit_arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
+    {
+        const size_t rows = (size_t)c.max_batch * std::max(1, c.max_nodes - 1);   // (sequence, depth) rows
+        if (e == hipSuccess) e = hipMalloc((void**)&h->tree_cand, rows * sv::kTreeMaxSlices * 32 * sizeof(unsigned long long));
+        if (e == hipSuccess) e = hipMalloc((void**)&h->tree_arrive, rows * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMemset(h->tree_arrive, 0, rows * sizeof(int32_t));
+    }
     if (e == hipSuccess && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE)) {
         // the walk across workgroups waits for all of a sequence's workgroups,
         // so it is launched only while the grid fits twice per CU; larger
@@ -231,6 +239,8 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         (void)hipFree(h->slice_pre);
         (void)hipFree(h->arrive);
         (void)hipFree(h->commit_arrive);
+        (void)hipFree(h->tree_cand);
+        (void)hipFree(h->tree_arrive);
         (void)hipFree(h->resid_ws);
         (void)hipFree(h->walk_sync);
         (void)hipFree(h->walk_part);
@@ -271,6 +281,8 @@ int spec_verify_destroy(spec_verify_handle* h) {
     if (h->slice_pre) (void)hipFree(h->slice_pre);
     if (h->arrive) (void)hipFree(h->arrive);
     if (h->commit_arrive) (void)hipFree(h->commit_arrive);
+    if (h->tree_cand) (void)hipFree(h->tree_cand);
+    if (h->tree_arrive) (void)hipFree(h->tree_arrive);
     if (h->resid_ws) (void)hipFree(h->resid_ws);
     if (h->walk_sync) (void)hipFree(h->walk_sync);
     if (h->walk_part) (void)hipFree(h->walk_part);
@@ -552,6 +564,10 @@ int spec_verify_build_tree(spec_verify_handle* h, const spec_verify_tree_args* a
     tp.V = c.vocab;
     tp.rows = a->depth;
     tp.levels = levels;
+    // long rows are split over up to kTreeMaxSlices workgroups of >= 4096 ids
+    tp.slices = levels ? std::max(1, std::min(sv::kTreeMaxSlices, c.vocab / 4096)) : 1;
+    tp.cand = h->tree_cand;
+    tp.arrive = h->tree_arrive;
     const hipError_t e = sv::launch_tree_build(tp, kmax, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "tree-build launch");
     return SPEC_VERIFY_OK;

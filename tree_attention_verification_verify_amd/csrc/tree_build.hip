@@ -10,7 +10,11 @@
 // rank[i] of its depth's top-k list, so the kernel only has to find each
 // row's best few tokens and scatter them.
 //
-// One 1024-thread workgroup per (sequence, depth), two passes over the row.
+// Rows of at least 8192 ids are split over up to 8 workgroups (slices of
+// >= 4096 ids) that each find their slice's k best the way described below;
+// the last slice of a row to finish (a per-row counter) ranks the slices' k
+// best together.  One 1024-thread workgroup per (sequence, depth, slice),
+// two passes over its ids.
 // Pass 1: the c = ceil(k/16) best entries of each wave's share; the k-th
 // largest of those 16c distinct entries is a lower bound on the row's k-th
 // largest.  Pass 2 (from L2): each thread keeps the K best entries at or
@@ -92,7 +96,7 @@ __device__ __forceinline__ void block_topk(unsigned long long (&lst)[K], int k, 
 // Applies f(key) to every entry of the row in this thread's share: float4
 // loads when the row is 16-byte aligned, else scalar loads.
 template <typename F>
-__device__ __forceinline__ void for_row(const float* row, int V, F&& f) {
+__device__ __forceinline__ void for_row(const float* row, int V, int id0, F&& f) {
     const int tid = threadIdx.x;
     if ((((uintptr_t)row) & 15u) == 0) {
         const int V4 = V >> 2;
@@ -106,16 +110,16 @@ __device__ __forceinline__ void for_row(const float* row, int V, F&& f) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) f(order_key(v[u][e], 4 * (j + u * TB) + e));
+                for (int e = 0; e < 4; ++e) f(order_key(v[u][e], id0 + 4 * (j + u * TB) + e));
         }
         for (; j < V4; j += TB) {
             const floatx4_t v = row4[j];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) f(order_key(v[e], 4 * j + e));
+            for (int e = 0; e < 4; ++e) f(order_key(v[e], id0 + 4 * j + e));
         }
-        for (int x = 4 * V4 + tid; x < V; x += TB) f(order_key(row[x], x));
+        for (int x = 4 * V4 + tid; x < V; x += TB) f(order_key(row[x], id0 + x));
     } else {
-        for (int x = tid; x < V; x += TB) f(order_key(row[x], x));
+        for (int x = tid; x < V; x += TB) f(order_key(row[x], id0 + x));
     }
 }
 
@@ -134,20 +138,25 @@ __global__ __launch_bounds__(TB) void tree_build_kernel(TreeParams P) {
     __shared__ unsigned long long wave_top[NW][K];
     __shared__ unsigned long long best[K];
     __shared__ unsigned long long list[CAP];
-    __shared__ int nlist;
+    __shared__ int nlist, is_last;
     const int tid = threadIdx.x;
     const int levels = P.levels;
-    const int b = levels ? blockIdx.x / levels : blockIdx.x;
-    const int d = levels ? blockIdx.x - b * levels + 1 : 0;
+    const int G = P.slices;
+    const int rowid = blockIdx.x / G, sl = blockIdx.x - rowid * G;   // (sequence, depth) row and its slice
+    const int b = levels ? rowid / levels : rowid;
+    const int d = levels ? rowid - b * levels + 1 : 0;
     const size_t base = (size_t)b * P.T;
 
-    if (d <= 1 && tid < P.T) {   // the template and the root token, once per sequence
+    if (d <= 1 && sl == 0 && tid < P.T) {   // the template and the root token, once per sequence
         P.parent[base + tid] = P.tpar[tid];
         if (tid == 0) P.tokens[base] = P.root_token[b];
     }
     if (d == 0) return;
     const int k = P.kd[d];
-    const float* row = P.logits + ((size_t)b * P.rows + (d - 1)) * P.V;
+    // this workgroup's slice of the row: ids [lo, lo + len), lo a multiple of 4
+    const int span = ((P.V + G - 1) / G + 3) & ~3;
+    const int lo = min(sl * span, P.V), len = min(P.V - lo, span);
+    const float* row = P.logits + ((size_t)b * P.rows + (d - 1)) * P.V + lo;
 
     const int lane = tid & 63, wave = tid >> 6;
     unsigned long long lst[K];
@@ -155,10 +164,10 @@ __global__ __launch_bounds__(TB) void tree_build_kernel(TreeParams P) {
     // maxima, pulled by c wave-wide maxima); the k-th largest of them bounds the k-th best
     const int c = (k + NW - 1) / NW;
     unsigned long long m0 = 0ull, m1 = 0ull;   // the thread's two best
-    for_row(row, P.V, [&](unsigned long long key) {
-        const unsigned long long lo = key > m0 ? m0 : key;
+    for_row(row, len, lo, [&](unsigned long long key) {
+        const unsigned long long mn = key > m0 ? m0 : key;
         m0 = key > m0 ? key : m0;
-        m1 = lo > m1 ? lo : m1;
+        m1 = mn > m1 ? mn : m1;
     });
     if (tid == 0) {
         nlist = 0;
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(TB) void tree_build_kernel(TreeParams P) {
     // pass 2: the K best entries >= bound of this thread's share
 #pragma unroll
     for (int q = 0; q < K; ++q) lst[q] = 0ull;
-    for_row(row, P.V, [&](unsigned long long key) {
+    for_row(row, len, lo, [&](unsigned long long key) {
         if (key >= bound && key > lst[K - 1]) {
 #pragma unroll
             for (int q = 0; q < K; ++q) {
@@ -211,6 +220,27 @@ __global__ __launch_bounds__(TB) void tree_build_kernel(TreeParams P) {
     } else {
         block_topk<K>(lst, k, wave_top, best);
     }
+    if (G > 1) {
+        // each slice publishes its k best (agent-scope stores, landed before the
+        // count); the last slice of the row to finish ranks the G * k keys
+        // (unique: distinct ids; every slice has more than k entries)
+        unsigned long long* cand = P.cand + (size_t)rowid * G * 32;
+        if (tid < k) __hip_atomic_store(cand + sl * 32 + tid, best[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            const int prev = __hip_atomic_fetch_add(P.arrive + rowid, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            is_last = prev == G - 1;
+            if (is_last) __hip_atomic_store(P.arrive + rowid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!is_last) return;
+        for (int i = tid; i < G * k; i += TB)
+            list[i] = __hip_atomic_load(cand + (i / k) * 32 + i % k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        rank_place(list, G * k, k, best);
+        __syncthreads();
+    }
     if (tid >= 1 && tid < P.T && P.tdep[tid] == d)
         P.tokens[base + tid] = (int)(0xFFFFFFFFu - (uint32_t)(best[P.trank[tid]] & 0xFFFFFFFFull));
 }
@@ -218,7 +248,7 @@ __global__ __launch_bounds__(TB) void tree_build_kernel(TreeParams P) {
 }  // namespace
 
 hipError_t launch_tree_build(const TreeParams& p, int kmax, hipStream_t s) {
-    dim3 grid(p.B * (p.levels ? p.levels : 1));
+    dim3 grid(p.B * (p.levels ? p.levels : 1) * p.slices);
     if (kmax <= 8) hipLaunchKernelGGL(tree_build_kernel<8>, grid, dim3(TB), 0, s, p);
     else if (kmax <= 16) hipLaunchKernelGGL(tree_build_kernel<16>, grid, dim3(TB), 0, s, p);
     else hipLaunchKernelGGL(tree_build_kernel<32>, grid, dim3(TB), 0, s, p);
