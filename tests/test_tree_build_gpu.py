@@ -29,10 +29,19 @@ def _run(logits, root, parent_t, rank_t, label):
     rt = torch.from_numpy(np.ascontiguousarray(root, dtype=np.int32)).to(dev)
     par = torch.full((B, T), -9, dtype=torch.int32, device=dev)
     tok = torch.full((B, T), -9, dtype=torch.int32, device=dev)
+    res = []
+    # two builds on one handle: the second must repeat the first (the per-row
+    # counters that join a long row's slices reset)
     with SpecVerify(**_config(B, T, V)) as sv:
-        sv.build_tree(lg, rt, list(parent_t), list(rank_t), par, tok)
-        torch.cuda.synchronize()
-    return par.cpu().numpy(), tok.cpu().numpy()
+        for _ in range(2):
+            par.fill_(-9)
+            tok.fill_(-9)
+            sv.build_tree(lg, rt, list(parent_t), list(rank_t), par, tok)
+            torch.cuda.synchronize()
+            res.append((par.cpu().numpy(), tok.cpu().numpy()))
+    np.testing.assert_array_equal(res[0][0], res[1][0])
+    np.testing.assert_array_equal(res[0][1], res[1][1])
+    return res[1]
 
 
 def _check(logits, root, caps, nodes, label):
