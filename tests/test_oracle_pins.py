@@ -486,3 +486,25 @@ def test_inverse_cdf_boundaries():
     assert oracle.inverse_cdf(np.array([0.5, 0.5, 0.0]), 0.9999999)[0] == 1
     y, _ = oracle.inverse_cdf_rows(np.array([[0.25, 0.25, 0.5], [0.0, 0.5, 0.5]]), np.array([0.25, 0.0]))
     assert list(y) == [1, 1]
+
+
+def test_residual_uses_the_smallest_index_child():
+    """Root with two drafted children, both rejected: the correction is drawn from
+    [p_0 - q_c]_+ of the smallest-index child c (the reading taken where the pages
+    name only one draft per position).  p_0 = [1/2, 1/4, 1/8, 1/8];
+    q_1 uniform -> [p_0 - q_1]_+ = [1/4, 0, 0, 0]: token 0 for any uniform;
+    q_2 = [1/8, 1/8, 1/2, 1/4] -> [3/8, 1/8, 0, 0]: token 1 for u_final = 0.9."""
+    p0 = np.array([0.5, 0.25, 0.125, 0.125])
+    q1 = np.full(4, 0.25)
+    q2 = np.array([0.125, 0.125, 0.5, 0.25])
+    P = np.stack([p0, p0, p0])[None]
+    Q = np.stack([q1, q1, q2])[None]
+    # node 1 = token 2 (ratio 0.125/0.25), node 2 = token 3 (ratio 0.125/0.25): both rejected at u = 0.9
+    r = oracle.accept_and_select(np.array([[-1, 0, 0]]), np.array([[0, 2, 3]]), np.array([[0.0, 0.9, 0.9]]),
+                                 np.array([0.9]), "sampling", 4, p_rows=P, q_rows=Q)
+    assert r["accept_len"][0] == 0 and r["final_node"][0] == 0 and r["final_from_residual"][0] == 1
+    assert r["out_tokens"][0, 0] == 0
+    # with the children swapped the other draft row is the smallest-index child's
+    r = oracle.accept_and_select(np.array([[-1, 0, 0]]), np.array([[0, 3, 2]]), np.array([[0.0, 0.9, 0.9]]),
+                                 np.array([0.9]), "sampling", 4, p_rows=P, q_rows=np.stack([q1, q2, q1])[None])
+    assert r["out_tokens"][0, 0] == 1
