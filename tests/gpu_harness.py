@@ -139,27 +139,68 @@ def compare(case: synth.Case, got: Dict[str, np.ndarray], ref: Dict[str, np.ndar
         np.testing.assert_array_equal(got["out_tokens"][b], ref["out_tokens"][n], err_msg="out_tokens b=%d" % b)
     if attn:
         tol = ATTN_TOL[spec.dtype]
+        worst = 0.0
+        rows = 0
         if attn_rows is None:
             for n, b in enumerate(seqs):
                 if np.isnan(ref["attn_out"][n]).any():
                     continue
                 err = np.abs(got["attn_out"][b].astype(np.float64) - ref["attn_out"][n]).max()
+                worst = max(worst, float(err))
+                rows += ref["attn_out"][n].shape[0] * ref["attn_out"][n].shape[1]
                 assert err <= tol, ("attn_out", b, float(err))
         else:
             for (b, i, h, val) in attn_rows:
                 err = np.abs(got["attn_out"][b, i, h].astype(np.float64) - val).max()
+                worst = max(worst, float(err))
+                rows += 1
                 assert err <= tol, ("attn_out", b, i, h, float(err))
+        stats.update(attn_rows=rows, attn_max_err=worst, attn_tol=tol)
     return stats
 
 
 def sampled_attention(case: synth.Case, picks) -> list:
-    """Oracle attention for a few (seq, node, head) rows of a large case."""
+    """Oracle attention for some (seq, node, head) rows of a large case (one widening per sequence)."""
     rows = []
     spec = case.spec
+    by_seq = {}
     for (b, i, h) in picks:
-        q = oracle.widen(case.q[b, i], spec.dtype)
+        by_seq.setdefault(b, []).append((i, h))
+    for b, nh in by_seq.items():
         k = oracle.widen(case.k_cache[b], spec.dtype)
         v = oracle.widen(case.v_cache[b], spec.dtype)
-        out = oracle.tree_attention_node(q, k, v, int(case.kv_len[b]), case.parent[b], i, heads=[h])[0]
-        rows.append((b, i, h, out))
+        by_node = {}
+        for (i, h) in nh:
+            by_node.setdefault(i, []).append(h)
+        for i, heads in by_node.items():
+            q = oracle.widen(case.q[b, i], spec.dtype)
+            out = oracle.tree_attention_node(q, k, v, int(case.kv_len[b]), case.parent[b], i, heads=heads)
+            rows.extend((b, i, h, out[n]) for n, h in enumerate(heads))
     return rows
+
+
+def deepest_node_rows(case: synth.Case, seqs) -> list:
+    """(seq, node, head) for every head of the root and of every node at the tree's largest depth."""
+    out = []
+    for b in seqs:
+        d = oracle.depths(case.parent[b])
+        nodes = [0] + [i for i in range(len(d)) if d[i] == max(d) and i > 0]
+        out.extend((b, i, h) for i in nodes for h in range(case.spec.hq))
+    return out
+
+
+def scale_tree_keys(case: synth.Case, factor: float = 8.0) -> None:
+    """Multiply the keys of every tree slot (L_b .. L_b+T-1) by a power of two, in place.
+
+    Exact in bf16 and fp32.  The tree keys then carry a large share of every
+    node's attention weight, so a wrong tree mask changes the output by O(1)
+    even over a long prefix.
+    """
+    T = case.nodes
+    for b in range(case.batch):
+        L = int(case.kv_len[b])
+        sl = case.k_cache[b, :, L:L + T]
+        if case.spec.dtype == "bf16":
+            case.k_cache[b, :, L:L + T] = synth.bf16_round_bits(synth.bf16_bits_to_f32(sl) * np.float32(factor))
+        else:
+            case.k_cache[b, :, L:L + T] = sl * np.float32(factor)

@@ -10,7 +10,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import compare, device_inputs, handle_config, note, run_gpu, sampled_attention
+from gpu_harness import (compare, deepest_node_rows, device_inputs, handle_config, note, run_gpu,
+                         sampled_attention, scale_tree_keys)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,7 +22,13 @@ pytestmark = pytest.mark.gpu
 STRICT = dict(accept_band=2e-6, cdf_band=2e-6)
 
 
-def check(case, label, seqs=None, attn_rows=None):
+def check(case, label, seqs=None, attn_rows=None, max_near=0):
+    """Run the case on the GPU and compare it with the oracle.
+
+    max_near: the most sequences the oracle may exclude from the bit-exact
+    comparison as near-ties, in the stated 1e-5 band (the counts the oracle
+    gives on these seeded inputs); more would make the decision checks vacuous.
+    """
     got = run_gpu(case, label)[0]
     ref = oracle.verify(case, attention=attn_rows is None, seqs=seqs, **STRICT)
     stats = compare(case, got, ref, seqs=seqs, attn=True, attn_rows=attn_rows)
@@ -29,6 +36,7 @@ def check(case, label, seqs=None, attn_rows=None):
     stats.update(seq_near_1e5=int(loose["seq_near"].sum()), node_near_1e5=int(loose["node_near"].sum()),
                  final_near_1e5=int(loose["final_near"].sum()))
     print(label, stats, flush=True)
+    assert stats["seq_near"] <= stats["seq_near_1e5"] <= max_near, (label, stats)
     return got, ref, stats
 
 
@@ -57,7 +65,8 @@ def test_chain_topp_ragged_short_prefix():
 @pytest.mark.parametrize("mode", ["sampling", "greedy"])
 def test_gqa_medusa_tree_short_prefix(mode):
     spec = synth.workload("70b-gqa-medusa", batch=2, prefix_len=333, mode=mode, seed=(3, 333))
-    check(synth.make_case(spec), "gqa-medusa-%s-L333" % mode)
+    # one sampling decision of these inputs lies within 1e-5 (but not 2e-6) of its threshold
+    check(synth.make_case(spec), "gqa-medusa-%s-L333" % mode, max_near=1 if mode == "sampling" else 0)
 
 
 def test_large_vocab_tree_short_prefix():
@@ -106,7 +115,8 @@ def test_largest_vocabulary():
     _, ref, stats = check(case, "max-vocab-topp")
     assert stats.get("seq_near", 0) == 0
     spec = spec.replace(top_p=1.0, seed=(4, 4194305))
-    check(synth.make_case(spec), "max-vocab")
+    # one of the two final draws over 4194304 ids lies within 1e-5 (not 2e-6) of a CDF boundary
+    check(synth.make_case(spec), "max-vocab", max_near=1)
 
 
 @pytest.mark.parametrize("vocab", [3000, 70000])
@@ -134,31 +144,85 @@ def test_top_p_cut_inside_a_group_of_tied_probabilities(vocab):
 
 # ------------------------------------------------------------------ full sizes, sampled attention rows
 
-def _full(name, picks, **kw):
+def _full(name, picks, deep_seqs=(0,), max_near=0, **kw):
+    """Full-size workload: every decision, and the oracle's attention for the
+    picked rows plus every head of the root and of the deepest nodes of the
+    sequences in deep_seqs."""
     spec = synth.workload(name, **kw)
     case = synth.make_case(spec)
-    rows = sampled_attention(case, picks)
-    return check(case, "%s-full-%s" % (name, spec.mode), attn_rows=rows)
+    want = sorted(set(picks) | set(deepest_node_rows(case, deep_seqs)))
+    rows = sampled_attention(case, want)
+    return check(case, "%s-full-%s" % (name, spec.mode), attn_rows=rows, max_near=max_near)
 
 
 def test_llama7b_medusa_greedy_full():
-    _full("llama7b-medusa-greedy", [(0, 0, 0), (0, 63, 31), (0, 17, 5), (0, 52, 20)])
+    # every (node, head) row: 7 prefix splits merged
+    _full("llama7b-medusa-greedy", [(0, i, h) for i in range(64) for h in range(32)])
 
 
 def test_chain_batch32_topp_full():
-    _full("chain-batch32-topp", [(0, 0, 0), (31, 5, 31), (7, 3, 12), (19, 2, 7)])
+    # three sequences of these inputs hold a decision within 1e-5 of its threshold
+    _full("chain-batch32-topp", [(0, 0, 0), (31, 5, 31), (7, 3, 12), (19, 2, 7)], deep_seqs=(0, 31), max_near=3)
 
 
 def test_70b_gqa_medusa_full_sampling():
-    _full("70b-gqa-medusa", [(0, 0, 0), (7, 63, 63), (3, 40, 17), (5, 11, 36)])
+    _full("70b-gqa-medusa", [(0, 0, 0), (7, 63, 63), (3, 40, 17), (5, 11, 36)], deep_seqs=(0, 7))
 
 
 def test_70b_gqa_medusa_full_greedy():
-    _full("70b-gqa-medusa", [(1, 1, 8), (6, 50, 55)], mode="greedy")
+    _full("70b-gqa-medusa", [(1, 1, 8), (6, 50, 55)], mode="greedy", deep_seqs=(3,))
 
 
 def test_longctx_bigvocab_full():
-    _full("longctx-bigvocab", [(0, 0, 0), (15, 25, 31), (8, 12, 9)])
+    _full("longctx-bigvocab", [(0, 0, 0), (15, 25, 31), (8, 12, 9)], deep_seqs=(0, 15))
+
+
+def test_70b_gqa_medusa_full_tree_mask_sensitive():
+    # the tree slots' keys scaled by 8: the tree carries a large share of every
+    # node's attention weight, so a node seeing a sibling (or not itself) moves
+    # its output by O(1) over the 8192-slot prefix, far above the tolerance
+    spec = synth.workload("70b-gqa-medusa", mode="greedy")
+    case = synth.make_case(spec)
+    scale_tree_keys(case)
+    rows = sampled_attention(case, [(b, i, h) for b in (0, 5) for i in range(case.nodes) for h in range(spec.hq)])
+    check(case, "70b-gqa-medusa-full-treekeys-x8", attn_rows=rows)
+
+
+# ------------------------------------------------------------------ prefix splits and tree tiles, every row
+
+def test_dense_mfma_eight_prefix_splits_every_row():
+    # the 70b-gqa-medusa shape at one sequence plans 8 prefix splits (merged by
+    # the finishing launch); every (node, head) row is compared
+    spec = synth.workload("70b-gqa-medusa", batch=1, prefix_len=4096, seed=(3, 4096))
+    check(synth.make_case(spec), "gqa-medusa-B1-L4096-8splits")
+
+
+def test_split_boundary_inside_the_tree_slots():
+    # capacity 4608 -> 8 splits of 576 slots; L = 4000 puts the split (and tile)
+    # boundary at slot 4032 between tree nodes 31 and 32, so the tree's keys
+    # are read by two splits; tree keys scaled by 8 so the tree part matters
+    spec = synth.workload("70b-gqa-medusa", batch=2, prefix_len=4544, ragged=(4000, 4000), seed=(3, 4002))
+    case = synth.make_case(spec)
+    scale_tree_keys(case)
+    check(case, "gqa-medusa-split-in-tree")
+    spec = synth.workload("70b-gqa-medusa", batch=2, prefix_len=4544, ragged=(3990, 4040), mode="greedy",
+                          seed=(3, 4001))
+    case = synth.make_case(spec)
+    scale_tree_keys(case)
+    check(case, "gqa-medusa-ragged-split-in-tree")
+
+
+def test_branching_tree_over_an_empty_prefix():
+    # MFMA path (bf16, 512 rows per KV head) and VALU paths (fp32; bf16 with
+    # 12 rows per KV head): the tree's own keys are all there is
+    spec = synth.workload("70b-gqa-medusa", batch=2, prefix_len=0, seed=(3, 1))
+    check(synth.make_case(spec), "gqa-medusa-L0")
+    spec = synth.CaseSpec("tree-f32-L0", 2, "f32", 8, 2, 128, 0, 700, "sampling", ("medusa", (4, 3, 2), 12),
+                          seed=(9, 20))
+    check(synth.make_case(spec), "tree-f32-L0")
+    spec = synth.CaseSpec("tree-bf16-valu-L0", 2, "bf16", 4, 4, 128, 0, 700, "greedy", ("medusa", (4, 3, 2), 12),
+                          seed=(9, 21))
+    check(synth.make_case(spec), "tree-bf16-valu-L0")
 
 
 # ------------------------------------------------------------------ edge cases
