@@ -71,6 +71,26 @@ extern "C" {
  * describe the tests made (r(x) and q(x) at test time); children never tried
  * get 0.  Costs one pass over the vocabulary per rejected child. */
 #define SPEC_VERIFY_FLAG_LOSSLESS_TREE 2u
+/* config.flags: run without step 1 (tree attention).  q, k_cache, v_cache
+ * (or the paged pools) and attn_out are not read or written and may be NULL;
+ * parent and kv_len are still read (status bits 1 and 8). */
+#define SPEC_VERIFY_FLAG_SKIP_ATTENTION 4u
+/* config.flags: run step 1 only.  target_logits, draft_logits, tokens,
+ * u_accept, u_final and every output except attn_out are not read or written
+ * and may be NULL.  Not together with SKIP_ATTENTION. */
+#define SPEC_VERIFY_FLAG_SKIP_VOCAB 8u
+/* config.flags, sampling mode only: also write outputs.probs[B,T,V], the
+ * effective target distribution of every row, TopP(softmax(z / temperature))
+ * (the full probability rows the page's sampler takes as its input:
+ * "推测解码技术详解：加速LLM推理的关键", section "数学保证：无损输出质量").  A
+ * debug output: it writes 4 bytes per logit.  probs[b, parent[b,i], x_i]
+ * equals node_p[b, i] bit for bit. */
+#define SPEC_VERIFY_FLAG_WRITE_PROBS 16u
+/* config.flags, for tests of the lossless walk's time-out path only: every
+ * wait of the walk for the sequence's other workgroups gives up after one
+ * poll (status bit 16 and invalid outputs for a sequence whose workgroups
+ * were not all there yet).  Every kernel still runs to its end. */
+#define SPEC_VERIFY_FLAG_WALK_NO_WAIT 32u
 
 /* Status bits written to outputs.status[b]. */
 #define SPEC_VERIFY_STATUS_BAD_PARENT 1   /* parent[0] != -1 or not 0 <= parent[i] < i   */
@@ -134,6 +154,8 @@ typedef struct spec_verify_outputs {
     uint8_t* node_accept;          /* [B,T]: per-node test result (node 0 = 1)               */
     uint8_t* final_from_residual;  /* [B]: 1 if the final token came from norm([p-q]_+)      */
     int32_t* row_token;            /* [B,T]: best token of target row v (smallest id on ties) */
+    float* probs;                  /* [B,T,V] fp32 with SPEC_VERIFY_FLAG_WRITE_PROBS (else unused,
+                                      may be NULL): row v = effective target distribution p_v   */
 } spec_verify_outputs;
 
 /* Arguments of spec_verify_commit (device pointers; B = batch, T = nodes). */
@@ -192,17 +214,34 @@ typedef struct spec_verify_tree_args {
 typedef struct spec_verify_handle spec_verify_handle;
 
 /* Validate cfg, size and allocate the workspace on the current HIP device.
- * *out receives the handle.  No kernel is launched.  Errors: INVALID_ARG
- * (bad field), UNSUPPORTED (a shape outside what the kernels handle: head_dim
- * not 64 or 128, V > 4194304, ...), OOM, HIP. */
+ * *out receives the handle.  No kernel is launched.  The fields follow the
+ * verifier's inputs on the pages: the target's sampling settings (temperature,
+ * top-p) of the generation config in "Medusa推测解码：为LLM推理加速2-3倍的工程实践",
+ * section 4.2, which must also be the settings the drafts were sampled with
+ * ("投机解码的五条路线", section on exact verification); the tree size of the
+ * candidate tree of "推测解码技术详解：加速LLM推理的关键", section "Tree Attention验证".
+ * The handle owns only its workspace (allocated here, freed by destroy); the
+ * caller owns every array it passes to the other calls.
+ * Errors: INVALID_ARG (bad field, unknown or conflicting flags),
+ * UNSUPPORTED (a shape outside what the kernels handle: head_dim not 64 or
+ * 128, V > 4194304, one (sequence, KV head) slice of the cache of 2 GiB or
+ * more, i.e. kv_capacity * head_dim * element size >= 2^31, ...), OOM, HIP. */
 int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out);
 
-/* Enqueue one verify step on `stream` (a hipStream_t; NULL = default stream).
+/* Enqueue one verify step on `stream` (a hipStream_t; NULL = default stream):
+ * the four parts listed at the top of this file, for every sequence of the
+ * batch.  The call shape follows the page's sampler, which takes the draft
+ * and target probability rows and the draft tokens and returns the emitted
+ * tokens and their count ("推测解码技术详解：加速LLM推理的关键", section
+ * "数学保证：无损输出质量"); here the rows come as logits, the tree as parent[],
+ * and the random draws as the uniforms u_accept and u_final.
  * Asynchronous: allocates nothing, never synchronises.  All output arrays are
- * written (entries past T or past a sequence's path are -1).  One run per
- * handle may be in flight at a time unless runs share the same stream.
+ * written (entries past T or past a sequence's path are -1), except those a
+ * SKIP flag leaves out.  One run per handle may be in flight at a time unless
+ * runs share the same stream (the workspace is the handle's).
  * Errors: INVALID_ARG (NULL pointer, B or T out of range, draft_logits NULL in
- * sampling mode), HIP (launch failure). */
+ * sampling mode, probs NULL with SPEC_VERIFY_FLAG_WRITE_PROBS), HIP (launch
+ * failure). */
 int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in,
                     const spec_verify_outputs* out, void* stream);
 
@@ -215,7 +254,10 @@ int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in,
  * "大模型推理加速：推测解码与MTP核心原理与工程实践", section 3.1 item 4 and
  * section 6.3).  A sequence is skipped (caches and kv_len unchanged) when it
  * is void (final_node < 0), L_b + T > Lcap, or path is not a root path
- * (path[0] = 0, k <= path[k] < T).  Asynchronous; allocates nothing.
+ * (path[0] = 0, k <= path[k] < T).  Asynchronous; allocates nothing.  The
+ * caches and kv_len must not be in use by another call in flight; one commit
+ * per handle may be in flight at a time unless commits share the same
+ * stream (a per-handle counter joins the KV heads of a sequence).
  * Errors: INVALID_ARG (NULL or misaligned pointer, B or T out of range),
  * HIP (launch failure). */
 int spec_verify_commit(spec_verify_handle* h, const spec_verify_commit_args* args, void* stream);
@@ -249,6 +291,8 @@ int spec_verify_commit_paged(spec_verify_handle* h, const spec_verify_commit_arg
  * two-head top-2 product tree; "Medusa推测解码：为LLM推理加速2-3倍的工程实践",
  * sections 2.2 and 4.2: top-k candidates per head).  The outputs are the
  * parent/tokens inputs of spec_verify_run.  Asynchronous; allocates nothing.
+ * One tree build per handle may be in flight at a time unless builds share
+ * the same stream (per-handle slots join the slices of a long row).
  * Errors: INVALID_ARG (NULL or misaligned pointer, B or T out of range, a
  * template that is not topological, a negative rank, a template deeper than
  * `depth`, or more entries needed at some depth than V), UNSUPPORTED (more
@@ -268,14 +312,20 @@ int spec_verify_build_tree(spec_verify_handle* h, const spec_verify_tree_args* a
  * tuples). */
 int spec_verify_tree_template(const int32_t* caps, int32_t ncaps, int32_t nodes, int32_t* parent, int32_t* rank);
 
-/* Free the workspace and the handle.  The caller's streams must be idle. */
+/* Free the workspace and the handle (the counterpart of spec_verify_create;
+ * the pages' verifier keeps no state between calls beyond the KV cache, which
+ * the caller owns).  The caller's streams must be idle. */
 int spec_verify_destroy(spec_verify_handle* h);
 
 /* Message of the last error on this thread ("" if none).  Valid until the
- * next call into the library on this thread. */
+ * next call into the library on this thread.  No exception or abort crosses
+ * the boundary: every failure is a return code plus this message. */
 const char* spec_verify_last_error(void);
 
-/* With SPEC_VERIFY_FLAG_TIMING: wait for the runs recorded since the last
+/* Per-round latency of the verify step, by stage (the pages ask for the
+ * latency of each round next to the accept lengths: "投机解码的五条路线",
+ * section "怎么选,以及怎么算收益").
+ * With SPEC_VERIFY_FLAG_TIMING: wait for the runs recorded since the last
  * read, then write into stage_ms[SPEC_VERIFY_NUM_STAGES] the summed kernel
  * time of each stage over those runs (HIP events on the run's stream) and the
  * run count into *runs (host pointers).  At most 1024 runs are kept between

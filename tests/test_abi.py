@@ -36,7 +36,7 @@ def test_struct_layouts_match_the_header():
     # the C structs are plain 4-byte fields / pointers: sizes follow from the field lists
     assert ctypes.sizeof(binding.Config) == 13 * 4
     assert ctypes.sizeof(binding.Inputs) == 10 * 8 + 2 * 4
-    assert ctypes.sizeof(binding.Outputs) == 11 * 8
+    assert ctypes.sizeof(binding.Outputs) == 12 * 8
     assert ctypes.sizeof(binding.CommitArgs) == 6 * 8 + 2 * 4
     assert ctypes.sizeof(binding.PagedKV) == 3 * 8 + 3 * 4 + 4   # padded to pointer alignment
     assert ctypes.sizeof(binding.TreeArgs) == 6 * 8 + 3 * 4 + 4
@@ -59,6 +59,8 @@ GOOD = dict(max_batch=2, max_nodes=8, num_q_heads=8, num_kv_heads=2, head_dim=12
     ("temperature", float("nan"), binding.SPEC_VERIFY_ERR_INVALID_ARG),
     ("top_p", 0.0, binding.SPEC_VERIFY_ERR_INVALID_ARG),
     ("top_p", 1.5, binding.SPEC_VERIFY_ERR_INVALID_ARG),
+    # one (sequence, KV head) slice of the cache must stay below 2 GiB
+    ("kv_capacity", (1 << 30) // 128, binding.SPEC_VERIFY_ERR_UNSUPPORTED),
 ])
 def test_create_rejects_bad_config(field, value, code):
     cfg = dict(GOOD)
@@ -149,3 +151,115 @@ def test_paged_kv_keeps_its_tensors_alive():
     del pk
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def test_create_bounds_the_cache_slice_below_two_gib():
+    # bf16, D = 128: 8388607 slots (2^31 - 256 bytes) are not refused for size;
+    # 8388608 slots (2^31 bytes) are
+    cfg = dict(GOOD, kv_capacity=(1 << 23))
+    with pytest.raises(sva.SpecVerifyError) as e:
+        sva.spec_verify_create(sva.make_config(**cfg))
+    assert e.value.code == binding.SPEC_VERIFY_ERR_UNSUPPORTED and "2^31" in str(e.value)
+    cfg = dict(GOOD, kv_capacity=(1 << 22), dtype="f32")        # fp32: 4 bytes per element
+    with pytest.raises(sva.SpecVerifyError) as e:
+        sva.spec_verify_create(sva.make_config(**cfg))
+    assert e.value.code == binding.SPEC_VERIFY_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("flags,msg", [
+    (dict(skip_attention=True, skip_vocab=True), "nothing to run"),
+    (dict(write_probs=True, mode="greedy"), "sampling"),
+    (dict(write_probs=True, skip_vocab=True), "vocabulary pass"),
+    (dict(walk_no_wait=True), "LOSSLESS"),
+])
+def test_create_rejects_conflicting_flags(flags, msg):
+    cfg = dict(GOOD)
+    cfg.update(flags)
+    with pytest.raises(sva.SpecVerifyError) as e:
+        sva.spec_verify_create(sva.make_config(**cfg))
+    assert e.value.code == binding.SPEC_VERIFY_ERR_INVALID_ARG and msg in str(e.value)
+
+
+# ------------------------------------------------------------------ binding argument checks (no GPU)
+
+def _cpu_args(cfg, B=2, T=5, probs=False):
+    import torch
+
+    act = torch.bfloat16 if cfg.dtype == binding.SPEC_VERIFY_BF16 else torch.float32
+    Hq, Hkv, D, L, V = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.kv_capacity, cfg.vocab
+    i32, f32 = torch.int32, torch.float32
+    ins = dict(q=torch.zeros(B, T, Hq, D, dtype=act), k_cache=torch.zeros(B, Hkv, L, D, dtype=act),
+               v_cache=torch.zeros(B, Hkv, L, D, dtype=act), kv_len=torch.zeros(B, dtype=i32),
+               parent=torch.zeros(B, T, dtype=i32), tokens=torch.zeros(B, T, dtype=i32),
+               target_logits=torch.zeros(B, T, V, dtype=f32), draft_logits=torch.zeros(B, T, V, dtype=f32),
+               u_accept=torch.zeros(B, T, dtype=f32), u_final=torch.zeros(B, dtype=f32))
+    outs = sva.allocate_outputs(B, T, Hq, D, "bf16" if act == torch.bfloat16 else "f32", device="cpu",
+                                vocab=V if probs else None)
+    return ins, outs
+
+
+def test_binding_checks_shapes_dtypes_and_layout_before_the_library():
+    import torch
+
+    cfg = sva.make_config(**GOOD)
+    ins, outs = _cpu_args(cfg)
+    # everything well formed: only the device is wrong (CPU tensors)
+    with pytest.raises(sva.SpecVerifyError) as e:
+        binding.check_run_args(cfg, ins, outs)
+    assert "device tensor" in str(e.value)
+
+    def expect(mutate, words):
+        i, o = _cpu_args(cfg)
+        mutate(i, o)
+        with pytest.raises(sva.SpecVerifyError) as e:
+            binding.check_run_args(cfg, i, o)
+        assert e.value.code == binding.SPEC_VERIFY_ERR_INVALID_ARG
+        for w in words:
+            assert w in str(e.value), (str(e.value), w)
+
+    # a transposed (non-contiguous) view of the right shape
+    expect(lambda i, o: i.__setitem__("q", torch.zeros(2, 5, 128, 8, dtype=torch.bfloat16).transpose(2, 3)),
+           ["q", "contiguous"])
+    expect(lambda i, o: i.__setitem__("tokens", torch.zeros(2, 5, dtype=torch.int64)), ["tokens", "i32"])
+    expect(lambda i, o: i.__setitem__("target_logits", torch.zeros(2, 5, 999)), ["target_logits", "shape"])
+    expect(lambda i, o: i.__setitem__("k_cache", torch.zeros(2, 2, 256, 128, dtype=torch.float32)), ["k_cache", "bf16"])
+    expect(lambda i, o: i.__setitem__("kv_len", torch.zeros(1, dtype=torch.int32)), ["kv_len", "shape"])
+    expect(lambda i, o: i.__setitem__("draft_logits", None), ["draft_logits", "required"])
+    expect(lambda i, o: o.__setitem__("path", torch.zeros(2, 6, dtype=torch.int32)), ["path", "shape"])
+    expect(lambda i, o: o.__setitem__("node_accept", torch.zeros(2, 5, dtype=torch.int32)), ["node_accept", "u8"])
+    expect(lambda i, o: o.__setitem__("attn_out", torch.zeros(2, 5, 8, 128)), ["attn_out", "bf16"])
+    # more sequences of room than the batch uses is fine (first dimension only)
+    i, o = _cpu_args(cfg)
+    i["u_final"] = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises(sva.SpecVerifyError) as e:
+        binding.check_run_args(cfg, i, o)
+    assert "device tensor" in str(e.value)
+
+
+def test_binding_checks_follow_the_skip_and_probs_flags():
+    import torch
+
+    cfg = sva.make_config(**dict(GOOD, skip_attention=True))
+    ins, outs = _cpu_args(cfg)
+    for k in ("q", "k_cache", "v_cache"):
+        ins[k] = None
+    outs["attn_out"] = None
+    with pytest.raises(sva.SpecVerifyError) as e:
+        binding.check_run_args(cfg, ins, outs)
+    assert "device tensor" in str(e.value)          # nothing else missing
+    cfg = sva.make_config(**dict(GOOD, skip_vocab=True))
+    ins, _ = _cpu_args(cfg)
+    for k in ("tokens", "target_logits", "draft_logits", "u_accept", "u_final"):
+        ins[k] = None
+    with pytest.raises(sva.SpecVerifyError) as e:
+        binding.check_run_args(cfg, ins, dict(attn_out=torch.zeros(2, 5, 8, 128, dtype=torch.bfloat16)))
+    assert "device tensor" in str(e.value)
+    cfg = sva.make_config(**dict(GOOD, write_probs=True))
+    ins, outs = _cpu_args(cfg)
+    with pytest.raises(sva.SpecVerifyError) as e:
+        binding.check_run_args(cfg, ins, outs)
+    assert "probs" in str(e.value) and "required" in str(e.value)
+    ins, outs = _cpu_args(cfg, probs=True)
+    with pytest.raises(sva.SpecVerifyError) as e:
+        binding.check_run_args(cfg, ins, outs)
+    assert "device tensor" in str(e.value)

@@ -91,7 +91,7 @@ def test_commit_moves_rows_across_a_medusa_tree():
 
 def test_commit_rejects_a_misaligned_cache():
     import torch
-    from tree_attention_verification_verify_amd import SpecVerify, SpecVerifyError
+    from tree_attention_verification_verify_amd import SpecVerify, SpecVerifyError, spec_verify_commit
 
     spec = synth.workload("70b-gqa-medusa", batch=1, prefix_len=64, vocab=500, seed=(8, 4))
     case = synth.make_case(spec)
@@ -99,8 +99,14 @@ def test_commit_rejects_a_misaligned_cache():
     flat = ins["k_cache"].reshape(-1)
     bad = flat[1:1 + flat.numel() - 8]
     z = torch.zeros(1, dtype=torch.int32, device=flat.device)
+    path = torch.zeros((1, case.nodes), dtype=torch.int32, device=flat.device)
     with SpecVerify(**handle_config(spec)) as sv:
+        # the binding's shape check refuses the flat view first ...
         with pytest.raises(SpecVerifyError) as e:
-            sv.commit(bad, ins["v_cache"], z.clone(), torch.zeros((1, case.nodes), dtype=torch.int32,
-                                                                   device=flat.device), z, z)
-    assert e.value.code == -1
+            sv.commit(bad, ins["v_cache"], z.clone(), path, z, z)
+        assert e.value.code == -1 and "shape" in str(e.value)
+        # ... and without the config the library's own alignment check does
+        note("misaligned cache: expect an argument error, no launch")
+        with pytest.raises(SpecVerifyError) as e:
+            spec_verify_commit(sv.handle, bad, ins["v_cache"], z.clone(), path, z, z)
+        assert e.value.code == -1 and "aligned" in str(e.value)

@@ -29,6 +29,10 @@ SPEC_VERIFY_GREEDY = 0
 SPEC_VERIFY_SAMPLING = 1
 SPEC_VERIFY_FLAG_TIMING = 1
 SPEC_VERIFY_FLAG_LOSSLESS_TREE = 2
+SPEC_VERIFY_FLAG_SKIP_ATTENTION = 4
+SPEC_VERIFY_FLAG_SKIP_VOCAB = 8
+SPEC_VERIFY_FLAG_WRITE_PROBS = 16
+SPEC_VERIFY_FLAG_WALK_NO_WAIT = 32
 SPEC_VERIFY_NUM_STAGES = 3
 STAGES = ("attention", "vocab", "finish")
 
@@ -80,7 +84,8 @@ class Outputs(ctypes.Structure):
     _fields_ = [("attn_out", ctypes.c_void_p), ("accept_len", ctypes.c_void_p), ("final_node", ctypes.c_void_p),
                 ("path", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("status", ctypes.c_void_p),
                 ("node_p", ctypes.c_void_p), ("node_q", ctypes.c_void_p), ("node_accept", ctypes.c_void_p),
-                ("final_from_residual", ctypes.c_void_p), ("row_token", ctypes.c_void_p)]
+                ("final_from_residual", ctypes.c_void_p), ("row_token", ctypes.c_void_p),
+                ("probs", ctypes.c_void_p)]
 
 
 _lib = None
@@ -134,8 +139,13 @@ def _check(rc: int) -> None:
 
 def make_config(*, max_batch, max_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, vocab,
                 dtype="bf16", mode="sampling", temperature=1.0, top_p=1.0, softmax_scale=0.0,
-                timing=False, lossless_tree=False) -> Config:
-    flags = (SPEC_VERIFY_FLAG_TIMING if timing else 0) | (SPEC_VERIFY_FLAG_LOSSLESS_TREE if lossless_tree else 0)
+                timing=False, lossless_tree=False, skip_attention=False, skip_vocab=False,
+                write_probs=False, walk_no_wait=False) -> Config:
+    flags = ((SPEC_VERIFY_FLAG_TIMING if timing else 0) | (SPEC_VERIFY_FLAG_LOSSLESS_TREE if lossless_tree else 0)
+             | (SPEC_VERIFY_FLAG_SKIP_ATTENTION if skip_attention else 0)
+             | (SPEC_VERIFY_FLAG_SKIP_VOCAB if skip_vocab else 0)
+             | (SPEC_VERIFY_FLAG_WRITE_PROBS if write_probs else 0)
+             | (SPEC_VERIFY_FLAG_WALK_NO_WAIT if walk_no_wait else 0))
     return Config(max_batch, max_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, vocab,
                   SPEC_VERIFY_BF16 if dtype == "bf16" else SPEC_VERIFY_F32,
                   SPEC_VERIFY_SAMPLING if mode == "sampling" else SPEC_VERIFY_GREEDY,
@@ -156,20 +166,122 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+# ------------------------------------------------------------------ argument checks
+#
+# The library sees raw addresses only, so a non-contiguous view, a wrong dtype
+# or a wrong shape would make it read or write the wrong memory.  These checks
+# run before any call into the library; they use only tensor metadata.
+
+def _torch_dtype(name):
+    import torch
+
+    return {"bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32, "u8": torch.uint8}[name]
+
+
+def _check_tensor(name: str, t, dtype: str, shape, optional: bool = False, seen: Optional[list] = None) -> None:
+    """shape: sizes per dimension; the first may be exceeded (room for more sequences), None = any.
+
+    With `seen`, the tensor is appended to it and its device is left for
+    _check_devices (so every shape is checked before any device)."""
+    if t is None:
+        if optional:
+            return
+        raise SpecVerifyError(SPEC_VERIFY_ERR_INVALID_ARG, "%s is required" % name)
+    if not hasattr(t, "data_ptr") or not hasattr(t, "is_contiguous"):
+        raise SpecVerifyError(SPEC_VERIFY_ERR_INVALID_ARG, "%s must be a torch tensor" % name)
+    if t.dtype != _torch_dtype(dtype):
+        raise SpecVerifyError(SPEC_VERIFY_ERR_INVALID_ARG, "%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != len(shape):
+        raise SpecVerifyError(SPEC_VERIFY_ERR_INVALID_ARG,
+                              "%s must have %d dimensions, got shape %s" % (name, len(shape), tuple(t.shape)))
+    for k, (got, want) in enumerate(zip(t.shape, shape)):
+        if want is None:
+            continue
+        if (got < want) if k == 0 else (got != want):
+            raise SpecVerifyError(SPEC_VERIFY_ERR_INVALID_ARG,
+                                  "%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise SpecVerifyError(SPEC_VERIFY_ERR_INVALID_ARG, "%s must be contiguous" % name)
+    if seen is not None:
+        seen.append((name, t))
+    else:
+        _check_devices([(name, t)])
+
+
+def _check_devices(named) -> None:
+    for name, t in named:
+        if t.device.type != "cuda":
+            raise SpecVerifyError(SPEC_VERIFY_ERR_INVALID_ARG,
+                                  "%s must be a device tensor, got %s" % (name, t.device))
+
+
+def _cfg_dims(cfg: Config):
+    act = "bf16" if cfg.dtype == SPEC_VERIFY_BF16 else "f32"
+    return act, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.kv_capacity, cfg.vocab
+
+
+def check_run_args(cfg: Config, inputs: Dict, outputs: Dict, paged: bool = False) -> None:
+    """Every tensor of a run against the handle's config (raises SpecVerifyError).
+
+    Dtypes, shapes and contiguity of all tensors are checked first, then that
+    each one lives on the GPU."""
+    seen = []
+    chk = lambda name, t, dtype, shape, optional=False: _check_tensor(name, t, dtype, shape, optional, seen)
+    parent = inputs.get("parent")
+    chk("parent", parent, "i32", (None, None))
+    B, T = parent.shape
+    act, Hq, Hkv, D, Lcap, V = _cfg_dims(cfg)
+    flags = cfg.flags
+    attn = not flags & SPEC_VERIFY_FLAG_SKIP_ATTENTION
+    vocab = not flags & SPEC_VERIFY_FLAG_SKIP_VOCAB
+    sampling = cfg.mode == SPEC_VERIFY_SAMPLING
+    chk("kv_len", inputs.get("kv_len"), "i32", (B,))
+    if attn:
+        chk("q", inputs.get("q"), act, (B, T, Hq, D))
+        if not paged:
+            chk("k_cache", inputs.get("k_cache"), act, (B, Hkv, Lcap, D))
+            chk("v_cache", inputs.get("v_cache"), act, (B, Hkv, Lcap, D))
+        chk("attn_out", outputs.get("attn_out"), act, (B, T, Hq, D))
+    if vocab:
+        chk("tokens", inputs.get("tokens"), "i32", (B, T))
+        chk("target_logits", inputs.get("target_logits"), "f32", (B, T, V))
+        chk("draft_logits", inputs.get("draft_logits"), "f32", (B, T, V), optional=not sampling)
+        chk("u_accept", inputs.get("u_accept"), "f32", (B, T))
+        chk("u_final", inputs.get("u_final"), "f32", (B,))
+        for name in ("accept_len", "final_node", "status"):
+            chk(name, outputs.get(name), "i32", (B,))
+        for name in ("path", "out_tokens", "row_token"):
+            chk(name, outputs.get(name), "i32", (B, T))
+        for name in ("node_p", "node_q"):
+            chk(name, outputs.get(name), "f32", (B, T))
+        chk("node_accept", outputs.get("node_accept"), "u8", (B, T))
+        chk("final_from_residual", outputs.get("final_from_residual"), "u8", (B,))
+        if flags & SPEC_VERIFY_FLAG_WRITE_PROBS:
+            chk("probs", outputs.get("probs"), "f32", (B, T, V))
+    _check_devices(seen)
+
+
 def _inputs(inputs: Dict) -> Inputs:
     B, T = inputs["parent"].shape
     return Inputs(_ptr(inputs.get("q")), _ptr(inputs.get("k_cache")), _ptr(inputs.get("v_cache")),
-                  _ptr(inputs["kv_len"]), _ptr(inputs["parent"]), _ptr(inputs["tokens"]),
-                  _ptr(inputs["target_logits"]), _ptr(inputs.get("draft_logits")), _ptr(inputs["u_accept"]),
-                  _ptr(inputs["u_final"]), B, T)
+                  _ptr(inputs["kv_len"]), _ptr(inputs["parent"]), _ptr(inputs.get("tokens")),
+                  _ptr(inputs.get("target_logits")), _ptr(inputs.get("draft_logits")), _ptr(inputs.get("u_accept")),
+                  _ptr(inputs.get("u_final")), B, T)
 
 
 def _outputs(outputs: Dict) -> Outputs:
-    return Outputs(*[_ptr(outputs[f]) for f, _ in Outputs._fields_])
+    return Outputs(*[_ptr(outputs.get(f)) for f, _ in Outputs._fields_])
 
 
 def paged_kv(k_pool, v_pool, block_table) -> PagedKV:
     """PagedKV from pools [num_blocks, Hkv, block_size, D] and a table [B, width] (device tensors)."""
+    if k_pool is None or v_pool is None or block_table is None:
+        raise SpecVerifyError(SPEC_VERIFY_ERR_INVALID_ARG, "k_pool, v_pool and block_table are required")
+    # layout checks here; the device and the config are checked when a call uses it
+    act = "bf16" if str(k_pool.dtype).endswith("bfloat16") else "f32"
+    _check_tensor("k_pool", k_pool, act, (None, None, None, None), seen=[])
+    _check_tensor("v_pool", v_pool, act, tuple(k_pool.shape), seen=[])
+    _check_tensor("block_table", block_table, "i32", (None, None), seen=[])
     nb, _, bs, _ = k_pool.shape
     pk = PagedKV(_ptr(k_pool), _ptr(v_pool), _ptr(block_table), nb, bs, block_table.shape[1])
     # the struct holds raw device addresses: keep the tensors alive as long as it is
@@ -177,15 +289,31 @@ def paged_kv(k_pool, v_pool, block_table) -> PagedKV:
     return pk
 
 
-def spec_verify_run(handle, inputs: Dict, outputs: Dict, stream=None) -> None:
-    """inputs/outputs: dicts of device tensors named as the C struct fields."""
+def _check_paged(cfg: Config, paged: PagedKV) -> None:
+    k_pool, v_pool, table = paged._tensors
+    act, _, Hkv, D, _, _ = _cfg_dims(cfg)
+    _check_tensor("k_pool", k_pool, act, (None, Hkv, None, D), seen=[])
+    _check_devices([("k_pool", k_pool), ("v_pool", v_pool), ("block_table", table)])
+
+
+def spec_verify_run(handle, inputs: Dict, outputs: Dict, stream=None, config: Optional[Config] = None) -> None:
+    """inputs/outputs: dicts of device tensors named as the C struct fields.
+
+    With `config` (the handle's Config) every tensor is checked against it first.
+    """
+    if config is not None:
+        check_run_args(config, inputs, outputs)
     i, o = _inputs(inputs), _outputs(outputs)
     _check(load_library().spec_verify_run(handle, ctypes.byref(i), ctypes.byref(o),
                                           ctypes.c_void_p(_stream_handle(stream))))
 
 
-def spec_verify_run_paged(handle, inputs: Dict, paged: PagedKV, outputs: Dict, stream=None) -> None:
+def spec_verify_run_paged(handle, inputs: Dict, paged: PagedKV, outputs: Dict, stream=None,
+                          config: Optional[Config] = None) -> None:
     """spec_verify_run with the caches read through a block table (inputs' k_cache/v_cache unused)."""
+    if config is not None:
+        check_run_args(config, inputs, outputs, paged=True)
+        _check_paged(config, paged)
     i, o = _inputs(inputs), _outputs(outputs)
     _check(load_library().spec_verify_run_paged(handle, ctypes.byref(i), ctypes.byref(paged), ctypes.byref(o),
                                                 ctypes.c_void_p(_stream_handle(stream))))
@@ -199,16 +327,34 @@ def _stream_handle(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
-def spec_verify_commit(handle, k_cache, v_cache, kv_len, path, accept_len, final_node, stream=None) -> None:
+def _check_commit(cfg: Optional[Config], k_cache, v_cache, kv_len, path, accept_len, final_node, paged=False):
+    _check_tensor("path", path, "i32", (None, None))
+    B, T = path.shape
+    _check_tensor("kv_len", kv_len, "i32", (B,))
+    _check_tensor("accept_len", accept_len, "i32", (B,))
+    _check_tensor("final_node", final_node, "i32", (B,))
+    if cfg is not None and not paged:
+        act, _, Hkv, D, Lcap, _ = _cfg_dims(cfg)
+        _check_tensor("k_cache", k_cache, act, (B, Hkv, Lcap, D))
+        _check_tensor("v_cache", v_cache, act, (B, Hkv, Lcap, D))
+
+
+def spec_verify_commit(handle, k_cache, v_cache, kv_len, path, accept_len, final_node, stream=None,
+                       config: Optional[Config] = None) -> None:
     """KV commit of the accepted paths (device tensors; kv_len is updated in place)."""
+    _check_commit(config, k_cache, v_cache, kv_len, path, accept_len, final_node)
     B, T = path.shape
     a = CommitArgs(_ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(path), _ptr(accept_len), _ptr(final_node),
                    B, T)
     _check(load_library().spec_verify_commit(handle, ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
 
 
-def spec_verify_commit_paged(handle, paged: PagedKV, kv_len, path, accept_len, final_node, stream=None) -> None:
+def spec_verify_commit_paged(handle, paged: PagedKV, kv_len, path, accept_len, final_node, stream=None,
+                             config: Optional[Config] = None) -> None:
     """KV commit through a block table (the pools in `paged` and kv_len are updated in place)."""
+    _check_commit(config, None, None, kv_len, path, accept_len, final_node, paged=True)
+    if config is not None:
+        _check_paged(config, paged)
     B, T = path.shape
     a = CommitArgs(None, None, _ptr(kv_len), _ptr(path), _ptr(accept_len), _ptr(final_node), B, T)
     _check(load_library().spec_verify_commit_paged(handle, ctypes.byref(a), ctypes.byref(paged),
@@ -226,11 +372,17 @@ def spec_verify_tree_template(caps, nodes: int):
 
 
 def spec_verify_build_tree(handle, cand_logits, root_token, tree_parent, tree_rank, parent, tokens,
-                           stream=None) -> None:
+                           stream=None, config: Optional[Config] = None) -> None:
     """Fill parent/tokens [B,T] (device) from cand_logits [B,depth,V] and root_token [B] (device)
     with the host template tree_parent/tree_rank (sequences of T ints)."""
+    _check_tensor("cand_logits", cand_logits, "f32", (None, None, None if config is None else config.vocab))
     B, depth = cand_logits.shape[0], cand_logits.shape[1]
     T = len(tree_parent)
+    if len(tree_rank) != T:
+        raise SpecVerifyError(SPEC_VERIFY_ERR_INVALID_ARG, "tree_rank and tree_parent differ in length")
+    _check_tensor("root_token", root_token, "i32", (B,))
+    _check_tensor("parent", parent, "i32", (B, T))
+    _check_tensor("tokens", tokens, "i32", (B, T))
     tp = (ctypes.c_int32 * T)(*[int(x) for x in tree_parent])
     tr = (ctypes.c_int32 * T)(*[int(x) for x in tree_rank])
     a = TreeArgs(_ptr(cand_logits), _ptr(root_token), ctypes.cast(tp, ctypes.c_void_p),
@@ -246,13 +398,15 @@ def spec_verify_timing_read(handle):
     return dict(zip(STAGES, list(ms))), int(n.value)
 
 
-def allocate_outputs(batch: int, nodes: int, num_q_heads: int, head_dim: int, dtype: str, device="cuda"):
-    """Device output tensors for one run (PyTorch is only the allocator here)."""
+def allocate_outputs(batch: int, nodes: int, num_q_heads: int, head_dim: int, dtype: str, device="cuda",
+                     vocab: Optional[int] = None):
+    """Device output tensors for one run (PyTorch is only the allocator here); with `vocab`,
+    also probs [B,T,V] for SPEC_VERIFY_FLAG_WRITE_PROBS."""
     import torch
 
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     B, T = batch, nodes
-    return dict(
+    out = dict(
         attn_out=torch.empty((B, T, num_q_heads, head_dim), dtype=dt, device=device),
         accept_len=torch.empty(B, dtype=torch.int32, device=device),
         final_node=torch.empty(B, dtype=torch.int32, device=device),
@@ -265,6 +419,9 @@ def allocate_outputs(batch: int, nodes: int, num_q_heads: int, head_dim: int, dt
         final_from_residual=torch.empty(B, dtype=torch.uint8, device=device),
         row_token=torch.empty((B, T), dtype=torch.int32, device=device),
     )
+    if vocab is not None:
+        out["probs"] = torch.empty((B, T, vocab), dtype=torch.float32, device=device)
+    return out
 
 
 class SpecVerify:
@@ -276,22 +433,24 @@ class SpecVerify:
         self.handle = spec_verify_create(self.cfg)
 
     def run(self, inputs: Dict, outputs: Dict, stream=None) -> None:
-        spec_verify_run(self.handle, inputs, outputs, stream)
+        spec_verify_run(self.handle, inputs, outputs, stream, config=self.cfg)
 
     def run_paged(self, inputs: Dict, paged: PagedKV, outputs: Dict, stream=None) -> None:
-        spec_verify_run_paged(self.handle, inputs, paged, outputs, stream)
+        spec_verify_run_paged(self.handle, inputs, paged, outputs, stream, config=self.cfg)
 
     def timing_read(self):
         return spec_verify_timing_read(self.handle)
 
     def commit(self, k_cache, v_cache, kv_len, path, accept_len, final_node, stream=None) -> None:
-        spec_verify_commit(self.handle, k_cache, v_cache, kv_len, path, accept_len, final_node, stream)
+        spec_verify_commit(self.handle, k_cache, v_cache, kv_len, path, accept_len, final_node, stream,
+                           config=self.cfg)
 
     def commit_paged(self, paged: PagedKV, kv_len, path, accept_len, final_node, stream=None) -> None:
-        spec_verify_commit_paged(self.handle, paged, kv_len, path, accept_len, final_node, stream)
+        spec_verify_commit_paged(self.handle, paged, kv_len, path, accept_len, final_node, stream, config=self.cfg)
 
     def build_tree(self, cand_logits, root_token, tree_parent, tree_rank, parent, tokens, stream=None) -> None:
-        spec_verify_build_tree(self.handle, cand_logits, root_token, tree_parent, tree_rank, parent, tokens, stream)
+        spec_verify_build_tree(self.handle, cand_logits, root_token, tree_parent, tree_rank, parent, tokens, stream,
+                               config=self.cfg)
 
     def close(self) -> None:
         if self.handle is not None:

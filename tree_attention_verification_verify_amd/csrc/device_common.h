@@ -99,6 +99,18 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) { return lane63_u64(wave_scan_u64(v)); }
 
+// Arrival count of a group of G workgroups at a per-group counter: true for
+// the G-th arrival.  The increment wraps to 0 in the same atomic (an old
+// value >= G-1 becomes 0), so no reset store follows and the counter stays in
+// [0, G): every completed group leaves it where it was, and calls that were
+// (wrongly) interleaved leave it at 0 again once all their workgroups have
+// counted, instead of poisoning every later call.  The caller makes its
+// published stores land before it counts (vmcnt(0) and a barrier).
+__device__ __forceinline__ bool arrive_last(int32_t* counter, int G) {
+    const uint32_t old = __builtin_amdgcn_atomic_inc32((uint32_t*)counter, (uint32_t)(G - 1), __ATOMIC_RELAXED, "agent");
+    return old == (uint32_t)(G - 1);
+}
+
 // Per-node ancestor bitmasks anc*(i) (bit j set iff node j is on node i's
 // root path, i itself included), by pointer jumping over parent[] in one
 // wave: after k rounds each node has collected 2^k nodes of its chain, so 6

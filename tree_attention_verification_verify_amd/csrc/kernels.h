@@ -86,7 +86,8 @@ struct SelectParams {
     float* walk_rx;       // [B][2][2] the next test's r (new, kept) from the workgroup holding its token
     int walk_k;           // workgroups per sequence of the walk: ceil(V / kWalkSlice)
     int walk_coop;        // 1: the walk over walk_k workgroups per sequence; 0: one workgroup per sequence
-    int32_t* arrive;      // [B] slices done; reset to 0 by the last one
+    int walk_spin;        // polls of a walk wait before it gives up (status bit 16)
+    int32_t* arrive;      // [B] slices done (wraps to 0 at the last one)
     int B, T, V, Lcap;
     int S;                // slices per sequence: ceil(V / kSelectSlice)
     int sampling;
@@ -134,12 +135,18 @@ hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
 bool valu_tiled_supported(bool bf16, int D, int R);
 hipError_t launch_attention_valu_tiled(const AttnParams& p, bool bf16, hipStream_t s);
 hipError_t launch_row_stats(const StatsParams& p, hipStream_t s);
+// probs[B,T,V] = effective target distribution of every row (after launch_row_stats).
+hipError_t launch_write_probs(const StatsParams& p, float* probs, hipStream_t s);
 // The step's last launch: selection (decisions, path, final draw) and, when
 // `merge`, the merge of the attention splits.
 hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool select, bool merge, bool bf16,
                          hipStream_t s);
 // Lossless sibling walk (sampling mode, SPEC_VERIFY_FLAG_LOSSLESS_TREE): one workgroup per sequence.
 hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s);
+// Workgroups of the walk across workgroups one CU holds at once (its register,
+// LDS and wave use, from the runtime's occupancy calculation).
+hipError_t walk_coop_blocks_per_cu(int* blocks);
+constexpr int kWalkSpinLimit = 1 << 21;   // polls (s_sleep 1 each, about 0.1 s) before a walk wait gives up
 // KV commit of the accepted path: one workgroup per sequence.
 hipError_t launch_kv_commit(const CommitParams& p, hipStream_t s);
 // Candidate tree: kmax = largest kd over the depths (<= 32).

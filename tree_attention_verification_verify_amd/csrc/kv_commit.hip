@@ -102,11 +102,7 @@ __global__ __launch_bounds__(CT) void kv_commit_kernel(CommitParams P) {
     // every workgroup of the sequence has read the old length before it counts
     // itself; a skipped sequence (the same decision in all of them) counts nothing
     if (tid == 0) {
-        const int prev = __hip_atomic_fetch_add(P.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == P.Hkv - 1) {
-            __hip_atomic_store(P.arrive + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            P.kv_len_out[b] = L + A + 1;
-        }
+        if (arrive_last(P.arrive + b, P.Hkv)) P.kv_len_out[b] = L + A + 1;
     }
 }
 

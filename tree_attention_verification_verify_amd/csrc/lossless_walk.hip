@@ -580,7 +580,6 @@ __global__ __launch_bounds__(NT) void lossless_walk_resident_kernel(SelectParams
 constexpr int CT = kWalkThreads;
 constexpr int CW = CT / kWave;
 constexpr int CV4 = kWalkSlice / (4 * CT);   // float4 per thread
-constexpr int kSpinLimit = 1 << 21;           // about 0.1 s of s_sleep
 
 struct CoopShared {
     unsigned long long kids_of[64];
@@ -706,7 +705,7 @@ __device__ __forceinline__ void coop_sync_scan(const SelectParams& P, int b, int
                         ok = (raw & 7ull) == want;
                     }
                     if (__all(ok) || late) break;
-                    if (++it > kSpinLimit) late = true;   // a workgroup never arrived: go on, flag it
+                    if (++it > P.walk_spin) late = true;   // a workgroup never arrived: go on, flag it
                     else __builtin_amdgcn_s_sleep(1);
                 }
                 const double v = untag_total(raw);
@@ -1041,8 +1040,9 @@ __global__ __launch_bounds__(CT) void lossless_walk_coop_kernel(SelectParams P) 
         P.accept_len[b] = depth;
         P.final_node[b] = v;
         P.final_from_residual[b] = cs.kids_of[v] != 0ull ? 1 : 0;
+        // agent-scope store: the last workgroup to finish may add the time-out bit below
         const int late = __hip_atomic_load(P.walk_sync + 4 * b + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        P.status[b] = cs.status | (late ? 16 : 0);
+        __hip_atomic_store(P.status + b, cs.status | (late ? 16 : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // the last workgroup of the sequence to finish (every workgroup has read
     // its last slots by then) clears the slots and the counters for the next
@@ -1050,21 +1050,27 @@ __global__ __launch_bounds__(CT) void lossless_walk_coop_kernel(SelectParams P) 
     int32_t* sync = P.walk_sync + 4 * b;
     if (tid == 0) {
         __builtin_amdgcn_s_waitcnt(0);
-        const int prev = __hip_atomic_fetch_add(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        cs.last = prev == K - 1;
+        cs.last = arrive_last(sync + 1, K);
     }
     __syncthreads();
     if (cs.last) {
         unsigned long long* slots = (unsigned long long*)(P.walk_part + (size_t)b * 2 * K);
         for (int i = tid; i < 2 * K; i += CT) __hip_atomic_store(slots + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (tid == 0) {
-            __hip_atomic_store(sync + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // a wait that ran out after the lead wrote the status (the drawing
+            // workgroup's, say) still marks the sequence
+            if (__hip_atomic_load(sync + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                __hip_atomic_fetch_or(P.status + b, 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(sync + 2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
 }  // namespace
+
+hipError_t walk_coop_blocks_per_cu(int* blocks) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, lossless_walk_coop_kernel, CT, 0);
+}
 
 hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s) {
     if (p.walk_coop && p.V > kWalkSlice)

@@ -338,12 +338,10 @@ __device__ __forceinline__ void select_block(const SelectParams& P, int s, int b
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const int prev = __hip_atomic_fetch_add(P.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sh.is_last = (prev == P.S - 1);
+        sh.is_last = arrive_last(P.arrive + b, P.S);
     }
     __syncthreads();
     if (!sh.is_last) return;
-    if (tid == 0) __hip_atomic_store(P.arrive + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next launch
     const size_t out_at = base + sh.dstar;
 
     if (keep) {

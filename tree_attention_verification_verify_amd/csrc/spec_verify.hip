@@ -55,7 +55,9 @@ struct AttnPlan {
     size_t part_rows = 0;   // pairs * nsplit * Rpad
 };
 
-AttnPlan plan_attention(const spec_verify_config& c, int B, int T) {
+// max_part_rows: the split partials must fit this many rows (fewer splits
+// otherwise; one split needs none).
+AttnPlan plan_attention(const spec_verify_config& c, int B, int T, size_t max_part_rows = SIZE_MAX) {
     AttnPlan p;
     const int g = c.num_q_heads / c.num_kv_heads;
     const int R = g * T;
@@ -76,12 +78,16 @@ AttnPlan plan_attention(const spec_verify_config& c, int B, int T) {
     const long keys = c.kv_capacity;
     const long max_split = std::max(1L, keys / kMinSplitKeys);
     long ns = std::max(1L, std::min(want, max_split));
-    long chunk = (keys + ns - 1) / ns;
-    chunk = ((chunk + 63) / 64) * 64;
-    ns = (keys + chunk - 1) / chunk;
-    p.nsplit = (int)ns;
-    p.chunk = (int)chunk;
-    p.part_rows = p.nsplit > 1 ? (size_t)pairs * p.nsplit * p.Rpad : 0;
+    for (;;) {
+        long chunk = (keys + ns - 1) / ns;
+        chunk = ((chunk + 63) / 64) * 64;
+        const long n = (keys + chunk - 1) / chunk;
+        p.nsplit = (int)n;
+        p.chunk = (int)chunk;
+        p.part_rows = n > 1 ? (size_t)pairs * n * p.Rpad : 0;
+        if (p.part_rows <= max_part_rows || ns == 1) break;
+        --ns;
+    }
     return p;
 }
 
@@ -111,42 +117,8 @@ int check_paged(const spec_verify_config& c, const spec_verify_paged_kv* pg, sv:
     return SPEC_VERIFY_OK;
 }
 
-}  // namespace
-
-struct spec_verify_handle {
-    spec_verify_config cfg;
-    int device = 0;
-    size_t part_rows_cap = 0;
-    float* part_o = nullptr;
-    float2* part_ml = nullptr;
-    sv::RowStat* stats = nullptr;     // max_batch * 2 * max_nodes row statistics
-    double2* slice_tot = nullptr;     // max_batch * slices final-draw slice totals
-    double2* slice_pre = nullptr;     // max_batch * slices * 256 per-thread slice prefixes (few slices only)
-    int32_t* arrive = nullptr;        // max_batch final-draw arrival counters (zero between runs)
-    int32_t* commit_arrive = nullptr; // max_batch KV-commit finish counters (zero between calls)
-    unsigned long long* tree_cand = nullptr;   // tree building: per-slice best keys of every row
-    int32_t* tree_arrive = nullptr;            // tree building: finished slices per row (zero between calls)
-    float* resid_ws = nullptr;        // max_batch * 2 * vocab residual rows (lossless tree walk)
-    int32_t* walk_sync = nullptr;     // max_batch * 4 walk counters (lossless tree walk)
-    double* walk_part = nullptr;      // max_batch * 2 * walk_k walk slice totals
-    float* walk_rx = nullptr;         // max_batch * 4 walk test values
-    int walk_k = 0;
-    int walk_cap = 0;                 // largest B * walk_k launched across workgroups (2 per CU)
-    bool timing = false;
-    std::vector<hipEvent_t> events;   // kTimingRing * kEventsPerRun
-    long runs_recorded = 0;           // since the last read
-    long ring_head = 0;               // total runs recorded
-};
-
-extern "C" {
-
-const char* spec_verify_last_error(void) { return g_err.c_str(); }
-
-int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) {
-    g_err.clear();
-    if (!cfg || !out) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "cfg and out must be non-NULL");
-    *out = nullptr;
-    const spec_verify_config& c = *cfg;
+// Every host-checkable fault of a configuration (before any HIP call).
+int validate_config(const spec_verify_config& c) {
     if (c.max_batch < 1) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "max_batch must be >= 1");
     if (c.max_nodes < 1 || c.max_nodes > 64) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "max_nodes must be in [1, 64]");
     if (c.num_q_heads < 1 || c.num_kv_heads < 1) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "head counts must be >= 1");
@@ -169,12 +141,73 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
     }
     if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-    if ((c.flags & ~(SPEC_VERIFY_FLAG_TIMING | SPEC_VERIFY_FLAG_LOSSLESS_TREE)) != 0u)
-        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "unknown flag bits");
+    constexpr uint32_t kKnownFlags = SPEC_VERIFY_FLAG_TIMING | SPEC_VERIFY_FLAG_LOSSLESS_TREE |
+                                     SPEC_VERIFY_FLAG_SKIP_ATTENTION | SPEC_VERIFY_FLAG_SKIP_VOCAB |
+                                     SPEC_VERIFY_FLAG_WRITE_PROBS | SPEC_VERIFY_FLAG_WALK_NO_WAIT;
+    if ((c.flags & ~kKnownFlags) != 0u) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "unknown flag bits");
     if ((c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE) && c.mode != SPEC_VERIFY_SAMPLING)
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "SPEC_VERIFY_FLAG_LOSSLESS_TREE needs sampling mode");
-    const long long lcap_elems = (long long)c.kv_capacity * c.head_dim;
-    if (lcap_elems > (1LL << 40)) return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "kv_capacity too large");
+    if ((c.flags & SPEC_VERIFY_FLAG_SKIP_ATTENTION) && (c.flags & SPEC_VERIFY_FLAG_SKIP_VOCAB))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "SKIP_ATTENTION and SKIP_VOCAB together leave nothing to run");
+    if ((c.flags & SPEC_VERIFY_FLAG_WRITE_PROBS) && c.mode != SPEC_VERIFY_SAMPLING)
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "SPEC_VERIFY_FLAG_WRITE_PROBS needs sampling mode");
+    if ((c.flags & SPEC_VERIFY_FLAG_WRITE_PROBS) && (c.flags & SPEC_VERIFY_FLAG_SKIP_VOCAB))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "SPEC_VERIFY_FLAG_WRITE_PROBS needs the vocabulary pass");
+    if ((c.flags & SPEC_VERIFY_FLAG_WALK_NO_WAIT) && !(c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "SPEC_VERIFY_FLAG_WALK_NO_WAIT needs SPEC_VERIFY_FLAG_LOSSLESS_TREE");
+    // the attention kernels address one (sequence, KV head) slice of a cache
+    // through a buffer resource with a 32-bit byte range
+    const long long slab_bytes = (long long)c.kv_capacity * c.head_dim * (c.dtype == SPEC_VERIFY_BF16 ? 2 : 4);
+    if (slab_bytes >= (1LL << 31))
+        return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "kv_capacity * head_dim * element size must be below 2^31 bytes");
+
+    return SPEC_VERIFY_OK;
+}
+
+}  // namespace
+
+// Device workspace of a run: the handle's (allocated by create) or carved out
+// of the static scratch array (spec_verify_run_noalloc).
+struct Workspace {
+    size_t part_rows_cap = 0;
+    float* part_o = nullptr;
+    float2* part_ml = nullptr;
+    sv::RowStat* stats = nullptr;     // batch * 2 * nodes row statistics
+    double2* slice_tot = nullptr;     // batch * slices final-draw slice totals
+    double2* slice_pre = nullptr;     // batch * slices * 256 per-thread slice prefixes (few slices only; may be NULL)
+    int32_t* arrive = nullptr;        // batch final-draw arrival counters (zero between runs)
+    float* resid_ws = nullptr;        // max_batch * 2 * vocab residual rows (lossless tree walk)
+    int32_t* walk_sync = nullptr;     // max_batch * 4 walk counters (lossless tree walk)
+    double* walk_part = nullptr;      // max_batch * 2 * walk_k walk slice totals
+    float* walk_rx = nullptr;         // max_batch * 4 walk test values
+    int walk_k = 0;
+    int walk_cap = 0;                 // largest B * walk_k launched across workgroups (all resident at once)
+    int walk_spin = 0;                // polls of a walk wait before it gives up
+};
+
+struct spec_verify_handle {
+    spec_verify_config cfg;
+    int device = 0;
+    Workspace ws;
+    int32_t* commit_arrive = nullptr; // max_batch KV-commit finish counters (zero between calls)
+    unsigned long long* tree_cand = nullptr;   // tree building: per-slice best keys of every row
+    int32_t* tree_arrive = nullptr;            // tree building: finished slices per row (zero between calls)
+    bool timing = false;
+    std::vector<hipEvent_t> events;   // kTimingRing * kEventsPerRun
+    long runs_recorded = 0;           // since the last read
+    long ring_head = 0;               // total runs recorded
+};
+
+extern "C" {
+
+const char* spec_verify_last_error(void) { return g_err.c_str(); }
+
+int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) {
+    g_err.clear();
+    if (!cfg || !out) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "cfg and out must be non-NULL");
+    *out = nullptr;
+    const spec_verify_config& c = *cfg;
+    if (int rc = validate_config(c)) return rc;
 
     // workspace: the largest split-prefix partial buffer over every (B, T) a run may use
     size_t cap = 0;
@@ -189,24 +222,24 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         delete h;
         return hip_fail(e, "hipGetDevice");
     }
-    h->part_rows_cap = cap;
+    h->ws.part_rows_cap = cap;
     if (cap > 0) {
-        e = hipMalloc((void**)&h->part_o, cap * c.head_dim * sizeof(float));
-        if (e == hipSuccess) e = hipMalloc((void**)&h->part_ml, cap * sizeof(float2));
+        e = hipMalloc((void**)&h->ws.part_o, cap * c.head_dim * sizeof(float));
+        if (e == hipSuccess) e = hipMalloc((void**)&h->ws.part_ml, cap * sizeof(float2));
         if (e != hipSuccess) {
-            (void)hipFree(h->part_o);
+            (void)hipFree(h->ws.part_o);
             delete h;
             (void)hipGetLastError();
             return fail(SPEC_VERIFY_ERR_OOM, "workspace allocation failed");
         }
     }
-    e = hipMalloc((void**)&h->stats, (size_t)c.max_batch * 2 * c.max_nodes * sizeof(sv::RowStat));
+    e = hipMalloc((void**)&h->ws.stats, (size_t)c.max_batch * 2 * c.max_nodes * sizeof(sv::RowStat));
     const int slices = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
-    if (e == hipSuccess) e = hipMalloc((void**)&h->slice_tot, (size_t)c.max_batch * slices * sizeof(double2));
+    if (e == hipSuccess) e = hipMalloc((void**)&h->ws.slice_tot, (size_t)c.max_batch * slices * sizeof(double2));
     if (e == hipSuccess && c.mode == SPEC_VERIFY_SAMPLING && slices <= sv::kSelectKeepSlices)
-        e = hipMalloc((void**)&h->slice_pre, (size_t)c.max_batch * slices * sv::kSelectThreads * sizeof(double2));
-    if (e == hipSuccess) e = hipMalloc((void**)&h->arrive, (size_t)c.max_batch * sizeof(int32_t));
-    if (e == hipSuccess) e = hipMemset(h->arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
+        e = hipMalloc((void**)&h->ws.slice_pre, (size_t)c.max_batch * slices * sv::kSelectThreads * sizeof(double2));
+    if (e == hipSuccess) e = hipMalloc((void**)&h->ws.arrive, (size_t)c.max_batch * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMemset(h->ws.arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess) e = hipMalloc((void**)&h->commit_arrive, (size_t)c.max_batch * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(h->commit_arrive, 0, (size_t)c.max_batch * sizeof(int32_t));
     {
@@ -222,31 +255,35 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         // beyond one on-chip chunk)
         int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
-        h->walk_k = (c.vocab + sv::kWalkSlice - 1) / sv::kWalkSlice;
-        h->walk_cap = 2 * cus;
-        if (e == hipSuccess) e = hipMalloc((void**)&h->walk_sync, (size_t)c.max_batch * 4 * sizeof(int32_t));
-        if (e == hipSuccess) e = hipMemset(h->walk_sync, 0, (size_t)c.max_batch * 4 * sizeof(int32_t));
-        if (e == hipSuccess) e = hipMalloc((void**)&h->walk_part, (size_t)c.max_batch * 2 * h->walk_k * sizeof(double));
-        if (e == hipSuccess) e = hipMemset(h->walk_part, 0, (size_t)c.max_batch * 2 * h->walk_k * sizeof(double));
-        if (e == hipSuccess) e = hipMalloc((void**)&h->walk_rx, (size_t)c.max_batch * 4 * sizeof(float));
-        if (e == hipSuccess && (long)c.max_batch * h->walk_k > h->walk_cap && c.vocab > sv::kVocabChunk)
-            e = hipMalloc((void**)&h->resid_ws, (size_t)c.max_batch * 2 * c.vocab * sizeof(float));
+        h->ws.walk_k = (c.vocab + sv::kWalkSlice - 1) / sv::kWalkSlice;
+        // as many workgroups as the CUs hold at once by the kernel's own resource use
+        int per_cu = 0;
+        if (e == hipSuccess) e = sv::walk_coop_blocks_per_cu(&per_cu);
+        h->ws.walk_cap = per_cu * cus;
+        h->ws.walk_spin = (c.flags & SPEC_VERIFY_FLAG_WALK_NO_WAIT) ? 0 : sv::kWalkSpinLimit;
+        if (e == hipSuccess) e = hipMalloc((void**)&h->ws.walk_sync, (size_t)c.max_batch * 4 * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMemset(h->ws.walk_sync, 0, (size_t)c.max_batch * 4 * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMalloc((void**)&h->ws.walk_part, (size_t)c.max_batch * 2 * h->ws.walk_k * sizeof(double));
+        if (e == hipSuccess) e = hipMemset(h->ws.walk_part, 0, (size_t)c.max_batch * 2 * h->ws.walk_k * sizeof(double));
+        if (e == hipSuccess) e = hipMalloc((void**)&h->ws.walk_rx, (size_t)c.max_batch * 4 * sizeof(float));
+        if (e == hipSuccess && (long)c.max_batch * h->ws.walk_k > h->ws.walk_cap && c.vocab > sv::kVocabChunk)
+            e = hipMalloc((void**)&h->ws.resid_ws, (size_t)c.max_batch * 2 * c.vocab * sizeof(float));
     }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
-        (void)hipFree(h->stats);
-        (void)hipFree(h->slice_tot);
-        (void)hipFree(h->slice_pre);
-        (void)hipFree(h->arrive);
+        (void)hipFree(h->ws.stats);
+        (void)hipFree(h->ws.slice_tot);
+        (void)hipFree(h->ws.slice_pre);
+        (void)hipFree(h->ws.arrive);
         (void)hipFree(h->commit_arrive);
         (void)hipFree(h->tree_cand);
         (void)hipFree(h->tree_arrive);
-        (void)hipFree(h->resid_ws);
-        (void)hipFree(h->walk_sync);
-        (void)hipFree(h->walk_part);
-        (void)hipFree(h->walk_rx);
-        (void)hipFree(h->part_o);
-        (void)hipFree(h->part_ml);
+        (void)hipFree(h->ws.resid_ws);
+        (void)hipFree(h->ws.walk_sync);
+        (void)hipFree(h->ws.walk_part);
+        (void)hipFree(h->ws.walk_rx);
+        (void)hipFree(h->ws.part_o);
+        (void)hipFree(h->ws.part_ml);
         delete h;
         (void)hipGetLastError();
         return fail(SPEC_VERIFY_ERR_OOM, "workspace allocation failed");
@@ -274,19 +311,19 @@ int spec_verify_destroy(spec_verify_handle* h) {
     if (dev != h->device) (void)hipSetDevice(h->device);
     for (auto& ev : h->events)
         if (ev) (void)hipEventDestroy(ev);
-    if (h->part_o) (void)hipFree(h->part_o);
-    if (h->part_ml) (void)hipFree(h->part_ml);
-    if (h->stats) (void)hipFree(h->stats);
-    if (h->slice_tot) (void)hipFree(h->slice_tot);
-    if (h->slice_pre) (void)hipFree(h->slice_pre);
-    if (h->arrive) (void)hipFree(h->arrive);
+    if (h->ws.part_o) (void)hipFree(h->ws.part_o);
+    if (h->ws.part_ml) (void)hipFree(h->ws.part_ml);
+    if (h->ws.stats) (void)hipFree(h->ws.stats);
+    if (h->ws.slice_tot) (void)hipFree(h->ws.slice_tot);
+    if (h->ws.slice_pre) (void)hipFree(h->ws.slice_pre);
+    if (h->ws.arrive) (void)hipFree(h->ws.arrive);
     if (h->commit_arrive) (void)hipFree(h->commit_arrive);
     if (h->tree_cand) (void)hipFree(h->tree_cand);
     if (h->tree_arrive) (void)hipFree(h->tree_arrive);
-    if (h->resid_ws) (void)hipFree(h->resid_ws);
-    if (h->walk_sync) (void)hipFree(h->walk_sync);
-    if (h->walk_part) (void)hipFree(h->walk_part);
-    if (h->walk_rx) (void)hipFree(h->walk_rx);
+    if (h->ws.resid_ws) (void)hipFree(h->ws.resid_ws);
+    if (h->ws.walk_sync) (void)hipFree(h->ws.walk_sync);
+    if (h->ws.walk_part) (void)hipFree(h->ws.walk_part);
+    if (h->ws.walk_rx) (void)hipFree(h->ws.walk_rx);
     if (dev >= 0 && dev != h->device) (void)hipSetDevice(dev);
     delete h;
     return SPEC_VERIFY_OK;
@@ -296,11 +333,18 @@ int spec_verify_destroy(spec_verify_handle* h) {
 
 namespace {
 
-// One verify step; paged == nullptr reads the dense caches of `in`.
-int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_paged_kv* paged,
+// Event ring of a handle created with SPEC_VERIFY_FLAG_TIMING.
+struct TimingRing {
+    std::vector<hipEvent_t>* events;
+    long* ring_head;
+    long* runs_recorded;
+};
+
+// One verify step with workspace ws; paged == nullptr reads the dense caches of `in`.
+int run_impl(const spec_verify_config& c, const Workspace& ws, const TimingRing* timing,
+             const spec_verify_inputs* in, const spec_verify_paged_kv* paged,
              const spec_verify_outputs* out, void* stream) {
-    if (!h || !in || !out) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle, inputs and outputs must be non-NULL");
-    const spec_verify_config& c = h->cfg;
+    if (!in || !out) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "inputs and outputs must be non-NULL");
     const int B = in->batch, T = in->nodes;
     if (B < 1 || B > c.max_batch) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "batch out of range");
     if (T < 1 || T > c.max_nodes) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes out of range");
@@ -314,33 +358,45 @@ int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_ver
         kc = paged->k_pool;
         vc = paged->v_pool;
     }
-    if (!in->q || !kc || !vc || !in->kv_len || !in->parent || !in->tokens ||
-        !in->target_logits || !in->u_accept || !in->u_final)
-        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an input pointer is NULL");
-    if (sampling && !in->draft_logits) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "draft_logits is NULL in sampling mode");
-    if (!out->attn_out || !out->accept_len || !out->final_node || !out->path || !out->out_tokens || !out->status ||
-        !out->node_p || !out->node_q || !out->node_accept || !out->final_from_residual || !out->row_token)
-        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an output pointer is NULL");
+    const bool do_attn = !(c.flags & SPEC_VERIFY_FLAG_SKIP_ATTENTION);
+    const bool do_vocab = !(c.flags & SPEC_VERIFY_FLAG_SKIP_VOCAB);
+    const bool do_probs = (c.flags & SPEC_VERIFY_FLAG_WRITE_PROBS) != 0u;
+    if (!in->kv_len || !in->parent) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an input pointer is NULL");
+    if (do_attn && (!in->q || !kc || !vc || !out->attn_out))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an attention pointer is NULL");
+    if (do_vocab) {
+        if (!in->tokens || !in->target_logits || !in->u_accept || !in->u_final)
+            return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an input pointer is NULL");
+        if (sampling && !in->draft_logits)
+            return fail(SPEC_VERIFY_ERR_INVALID_ARG, "draft_logits is NULL in sampling mode");
+        if (!out->accept_len || !out->final_node || !out->path || !out->out_tokens || !out->status ||
+            !out->node_p || !out->node_q || !out->node_accept || !out->final_from_residual || !out->row_token)
+            return fail(SPEC_VERIFY_ERR_INVALID_ARG, "an output pointer is NULL");
+        if (do_probs && !out->probs)
+            return fail(SPEC_VERIFY_ERR_INVALID_ARG, "probs is NULL with SPEC_VERIFY_FLAG_WRITE_PROBS");
+    }
     auto misaligned = [](const void* ptr, uintptr_t a) { return (((uintptr_t)ptr) & (a - 1)) != 0; };
-    if (misaligned(in->q, 16) || misaligned(kc, 16) || misaligned(vc, 16) || misaligned(out->attn_out, 16))
+    if (do_attn && (misaligned(in->q, 16) || misaligned(kc, 16) || misaligned(vc, 16) || misaligned(out->attn_out, 16)))
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "q, k_cache, v_cache and attn_out must be 16-byte aligned");
-    if (misaligned(in->kv_len, 4) || misaligned(in->parent, 4) || misaligned(in->tokens, 4) ||
-        misaligned(in->target_logits, 4) || (sampling && misaligned(in->draft_logits, 4)) ||
-        misaligned(in->u_accept, 4) || misaligned(in->u_final, 4) || misaligned(out->accept_len, 4) ||
-        misaligned(out->final_node, 4) || misaligned(out->path, 4) || misaligned(out->out_tokens, 4) ||
-        misaligned(out->status, 4) || misaligned(out->node_p, 4) || misaligned(out->node_q, 4) ||
-        misaligned(out->row_token, 4))
+    if (misaligned(in->kv_len, 4) || misaligned(in->parent, 4))
+        return fail(SPEC_VERIFY_ERR_INVALID_ARG, "arrays must be aligned to their element size");
+    if (do_vocab &&
+        (misaligned(in->tokens, 4) || misaligned(in->target_logits, 4) || (sampling && misaligned(in->draft_logits, 4)) ||
+         misaligned(in->u_accept, 4) || misaligned(in->u_final, 4) || misaligned(out->accept_len, 4) ||
+         misaligned(out->final_node, 4) || misaligned(out->path, 4) || misaligned(out->out_tokens, 4) ||
+         misaligned(out->status, 4) || misaligned(out->node_p, 4) || misaligned(out->node_q, 4) ||
+         misaligned(out->row_token, 4) || (do_probs && misaligned(out->probs, 4))))
         return fail(SPEC_VERIFY_ERR_INVALID_ARG, "arrays must be aligned to their element size");
     hipStream_t s = (hipStream_t)stream;
 
     const int D = c.head_dim;
     const bool bf16 = c.dtype == SPEC_VERIFY_BF16;
-    AttnPlan plan = plan_attention(c, B, T);
-    if (plan.part_rows > h->part_rows_cap) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "workspace too small (internal)");
+    AttnPlan plan = plan_attention(c, B, T, ws.part_rows_cap);
+    if (plan.part_rows > ws.part_rows_cap) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "workspace too small (internal)");
 
     hipEvent_t* ev = nullptr;
-    if (h->timing) {
-        ev = &h->events[(size_t)(h->ring_head % kTimingRing) * kEventsPerRun];
+    if (timing) {
+        ev = &(*timing->events)[(size_t)(*timing->ring_head % kTimingRing) * kEventsPerRun];
         hipError_t e = hipEventRecord(ev[0], s);
         if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
@@ -357,8 +413,8 @@ int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_ver
     ap.kv_len = in->kv_len;
     ap.parent = in->parent;
     ap.out = out->attn_out;
-    ap.part_o = h->part_o;
-    ap.part_ml = h->part_ml;
+    ap.part_o = ws.part_o;
+    ap.part_ml = ws.part_ml;
     ap.B = B;
     ap.T = T;
     ap.Hq = c.num_q_heads;
@@ -375,30 +431,39 @@ int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_ver
     const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt((float)D);
     ap.c = scale * kLog2e;
 
-    hipError_t e = plan.mfma    ? sv::launch_attention_mfma(ap, plan.waves, s)
-                   : plan.tiled ? sv::launch_attention_valu_tiled(ap, bf16, s)
-                                : sv::launch_attention_valu(ap, bf16, s);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    hipError_t e = hipSuccess;
+    if (do_attn) {
+        e = plan.mfma    ? sv::launch_attention_mfma(ap, plan.waves, s)
+            : plan.tiled ? sv::launch_attention_valu_tiled(ap, bf16, s)
+                         : sv::launch_attention_valu(ap, bf16, s);
+        if (e != hipSuccess) return hip_fail(e, "attention launch");
+    }
     if (int rc = mark(SPEC_VERIFY_STAGE_ATTENTION)) return rc;
 
     sv::StatsParams tp{};
     tp.target = in->target_logits;
     tp.draft = in->draft_logits;
-    tp.stats = h->stats;
+    tp.stats = ws.stats;
     tp.B = B;
     tp.T = T;
     tp.V = c.vocab;
     tp.sampling = sampling ? 1 : 0;
     tp.ilog = sampling ? kLog2e / c.temperature : kLog2e;
     tp.top_p = sampling ? c.top_p : 1.f;
-    e = sv::launch_row_stats(tp, s);
-    if (e != hipSuccess) return hip_fail(e, "row statistics launch");
+    if (do_vocab) {
+        e = sv::launch_row_stats(tp, s);
+        if (e != hipSuccess) return hip_fail(e, "row statistics launch");
+        if (do_probs) {
+            e = sv::launch_write_probs(tp, out->probs, s);
+            if (e != hipSuccess) return hip_fail(e, "probs launch");
+        }
+    }
     if (int rc = mark(SPEC_VERIFY_STAGE_VOCAB)) return rc;
 
     sv::SelectParams sp{};
     sp.target = in->target_logits;
     sp.draft = in->draft_logits;
-    sp.stats = h->stats;
+    sp.stats = ws.stats;
     sp.parent = in->parent;
     sp.tokens = in->tokens;
     sp.kv_len = in->kv_len;
@@ -421,18 +486,19 @@ int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_ver
     sp.pt = pt;
     sp.sampling = sampling ? 1 : 0;
     sp.ilog = tp.ilog;
-    sp.slice_tot = h->slice_tot;
-    sp.slice_pre = h->slice_pre;
-    sp.arrive = h->arrive;
+    sp.slice_tot = ws.slice_tot;
+    sp.slice_pre = ws.slice_pre;
+    sp.arrive = ws.arrive;
     sp.S = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
-    sp.resid_ws = h->resid_ws;
-    sp.walk_sync = h->walk_sync;
-    sp.walk_part = h->walk_part;
-    sp.walk_rx = h->walk_rx;
-    sp.walk_k = h->walk_k;
-    sp.walk_coop = ((long)B * h->walk_k <= h->walk_cap) ? 1 : 0;
-    const bool walk = sampling && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE);
-    e = sv::launch_finish(sp, ap, !walk, plan.nsplit > 1, bf16, s);
+    sp.resid_ws = ws.resid_ws;
+    sp.walk_sync = ws.walk_sync;
+    sp.walk_part = ws.walk_part;
+    sp.walk_rx = ws.walk_rx;
+    sp.walk_k = ws.walk_k;
+    sp.walk_coop = ((long)B * ws.walk_k <= ws.walk_cap) ? 1 : 0;
+    sp.walk_spin = ws.walk_spin;
+    const bool walk = do_vocab && sampling && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE);
+    e = sv::launch_finish(sp, ap, do_vocab && !walk, do_attn && plan.nsplit > 1, bf16, s);
     if (e != hipSuccess) return hip_fail(e, "finishing launch");
     if (walk) {
         e = sv::launch_lossless_walk(sp, s);
@@ -440,9 +506,9 @@ int run_impl(spec_verify_handle* h, const spec_verify_inputs* in, const spec_ver
     }
     if (int rc = mark(SPEC_VERIFY_STAGE_FINISH)) return rc;
 
-    if (h->timing) {
-        ++h->ring_head;
-        h->runs_recorded = std::min<long>(h->runs_recorded + 1, kTimingRing);
+    if (timing) {
+        ++*timing->ring_head;
+        *timing->runs_recorded = std::min<long>(*timing->runs_recorded + 1, kTimingRing);
     }
     return SPEC_VERIFY_OK;
 }
@@ -498,14 +564,18 @@ extern "C" {
 int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_outputs* out,
                     void* stream) {
     g_err.clear();
-    return run_impl(h, in, nullptr, out, stream);
+    if (!h) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle is NULL");
+    TimingRing tr{&h->events, &h->ring_head, &h->runs_recorded};
+    return run_impl(h->cfg, h->ws, h->timing ? &tr : nullptr, in, nullptr, out, stream);
 }
 
 int spec_verify_run_paged(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_paged_kv* paged,
                           const spec_verify_outputs* out, void* stream) {
     g_err.clear();
+    if (!h) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "handle is NULL");
     if (!paged) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "paged is NULL");
-    return run_impl(h, in, paged, out, stream);
+    TimingRing tr{&h->events, &h->ring_head, &h->runs_recorded};
+    return run_impl(h->cfg, h->ws, h->timing ? &tr : nullptr, in, paged, out, stream);
 }
 
 int spec_verify_commit(spec_verify_handle* h, const spec_verify_commit_args* a, void* stream) {

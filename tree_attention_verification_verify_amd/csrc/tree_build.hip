@@ -229,9 +229,7 @@ __global__ __launch_bounds__(TB) void tree_build_kernel(TreeParams P) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
-            const int prev = __hip_atomic_fetch_add(P.arrive + rowid, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            is_last = prev == G - 1;
-            if (is_last) __hip_atomic_store(P.arrive + rowid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            is_last = arrive_last(P.arrive + rowid, G);
         }
         __syncthreads();
         if (!is_last) return;

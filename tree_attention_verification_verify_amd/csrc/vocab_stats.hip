@@ -580,6 +580,32 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
     }
 }
 
+// Debug output: the effective target distribution of every row, p =
+// TopP(softmax(z / temperature)), from the row's statistics (same weight,
+// nucleus test and fp64 division as the probability the acceptance test
+// reads, so probs[b, parent(i), x_i] equals node_p[b, i] bit for bit).  One
+// workgroup per (row, slice of kProbSlice ids); consecutive lanes write
+// consecutive ids.  HBM-bound: reads and writes 4 bytes per logit.
+constexpr int kProbSlice = ST * 8;
+
+__global__ __launch_bounds__(ST) void write_probs_kernel(StatsParams P, float* probs) {
+    const int row = blockIdx.x;                 // b * T + i
+    const int b = row / P.T, i = row - b * P.T;
+    const RowStat st = P.stats[(size_t)b * 2 * P.T + i];
+    const rows::Nucleus nu{st.thr, st.cutoff};
+    const float* z = P.target + (size_t)row * P.V;
+    float* out = probs + (size_t)row * P.V;
+    const int first = blockIdx.y * kProbSlice + threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kProbSlice / ST; ++j) {
+        const int k = first + j * ST;
+        if (k < P.V) {
+            const float e = rows::unnorm(z[k], st.zmax, P.ilog);
+            out[k] = rows::in_nucleus(e, k, nu) ? (float)((double)e / st.Z) : 0.f;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_row_stats(const StatsParams& p, hipStream_t s) {
@@ -593,6 +619,16 @@ hipError_t launch_row_stats(const StatsParams& p, hipStream_t s) {
         hipLaunchKernelGGL(row_stats_stream_kernel<true>, grid, dim3(ST), 0, s, p);
     else
         hipLaunchKernelGGL(row_stats_stream_kernel<false>, grid, dim3(ST), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace sv
+
+namespace sv {
+
+hipError_t launch_write_probs(const StatsParams& p, float* probs, hipStream_t s) {
+    const dim3 grid((unsigned)(p.B * p.T), (unsigned)((p.V + kProbSlice - 1) / kProbSlice));
+    hipLaunchKernelGGL(write_probs_kernel, grid, dim3(ST), 0, s, p, probs);
     return hipGetLastError();
 }
 
