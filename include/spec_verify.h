@@ -245,6 +245,26 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out);
 int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in,
                     const spec_verify_outputs* out, void* stream);
 
+/* spec_verify_run for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no handle, no hipMalloc/hipFree, no allocating library call.  The
+ * workspace (row statistics, final-draw totals, arrival counters, split
+ * partials) lives in a 16 MiB array of static device memory that every GPU
+ * the library runs on holds from the library's first use there until the
+ * process ends; the first call on a GPU looks its address up and clears its
+ * counters on `stream`.  Outputs equal spec_verify_run's for the same cfg
+ * (decisions and tokens bit for bit; attention within the stated tolerance:
+ * when the split partials would not fit, the prefix is split fewer times).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and give wrong results; calls on
+ * one stream are ordered.  cfg is validated as in spec_verify_create.
+ * Errors: INVALID_ARG (as spec_verify_create and spec_verify_run),
+ * UNSUPPORTED (SPEC_VERIFY_FLAG_TIMING or SPEC_VERIFY_FLAG_LOSSLESS_TREE,
+ * more than 1024 sequences, or row statistics and draw totals for the batch
+ * above 16 MiB), HIP. */
+int spec_verify_run_noalloc(const spec_verify_config* cfg, const spec_verify_inputs* in,
+                            const spec_verify_outputs* out, void* stream);
+
 /* Enqueue the KV commit of the accepted paths on `stream`: for every sequence,
  * slot L_b+k of both caches (all KV heads) receives tree node path[b,k]
  * (k = 1..accept_len[b]; the root already sits at slot L_b) and kv_len[b]

@@ -263,3 +263,30 @@ def test_binding_checks_follow_the_skip_and_probs_flags():
     with pytest.raises(sva.SpecVerifyError) as e:
         binding.check_run_args(cfg, ins, outs)
     assert "device tensor" in str(e.value)
+
+
+def test_noalloc_entry_point_refuses_before_touching_the_device():
+    """Host-checkable refusals of spec_verify_run_noalloc happen before any HIP call."""
+    lib = sva.load_library()
+    ins, outs = binding.Inputs(), binding.Outputs()
+    cfg = sva.make_config(**dict(GOOD, max_batch=2000))
+    ins.batch, ins.nodes = 1025, 4
+    assert lib.spec_verify_run_noalloc(ctypes.byref(cfg), ctypes.byref(ins), ctypes.byref(outs), None) == \
+        binding.SPEC_VERIFY_ERR_UNSUPPORTED
+    assert "1024" in sva.spec_verify_last_error()
+    ins.batch = 2
+    for flags in (dict(timing=True), dict(lossless_tree=True)):
+        cfg = sva.make_config(**dict(GOOD, **flags))
+        assert lib.spec_verify_run_noalloc(ctypes.byref(cfg), ctypes.byref(ins), ctypes.byref(outs), None) == \
+            binding.SPEC_VERIFY_ERR_UNSUPPORTED
+    cfg = sva.make_config(**dict(GOOD, head_dim=96))            # validated as create does
+    assert lib.spec_verify_run_noalloc(ctypes.byref(cfg), ctypes.byref(ins), ctypes.byref(outs), None) == \
+        binding.SPEC_VERIFY_ERR_UNSUPPORTED
+    assert lib.spec_verify_run_noalloc(None, ctypes.byref(ins), ctypes.byref(outs), None) == \
+        binding.SPEC_VERIFY_ERR_INVALID_ARG
+    # row statistics of 1024 sequences of 64 nodes fit; the 4194304-id draw totals of 1024 do not
+    cfg = sva.make_config(**dict(GOOD, max_batch=1024, max_nodes=64, vocab=4194304))
+    ins.batch, ins.nodes = 1024, 64
+    assert lib.spec_verify_run_noalloc(ctypes.byref(cfg), ctypes.byref(ins), ctypes.byref(outs), None) == \
+        binding.SPEC_VERIFY_ERR_UNSUPPORTED
+    assert "16 MiB" in sva.spec_verify_last_error()

@@ -1,7 +1,7 @@
 """ctypes binding of libspecverify.so: argument marshalling only.
 
 The functions mirror the C ABI in include/spec_verify.h one to one
-(spec_verify_create / spec_verify_run / spec_verify_run_paged /
+(spec_verify_create / spec_verify_run / spec_verify_run_noalloc / spec_verify_run_paged /
 spec_verify_commit / spec_verify_commit_paged / spec_verify_build_tree /
 spec_verify_tree_template / spec_verify_destroy / spec_verify_last_error /
 spec_verify_timing_read).  Tensors are PyTorch device
@@ -38,7 +38,7 @@ STAGES = ("attention", "vocab", "finish")
 
 EXPORTED = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
             "spec_verify_timing_read", "spec_verify_commit", "spec_verify_run_paged", "spec_verify_commit_paged",
-            "spec_verify_build_tree", "spec_verify_tree_template")
+            "spec_verify_build_tree", "spec_verify_tree_template", "spec_verify_run_noalloc")
 
 
 class SpecVerifyError(RuntimeError):
@@ -104,6 +104,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(Inputs), ctypes.POINTER(Outputs),
                                     ctypes.c_void_p]
     lib.spec_verify_run.restype = ctypes.c_int
+    lib.spec_verify_run_noalloc.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Inputs), ctypes.POINTER(Outputs),
+                                            ctypes.c_void_p]
+    lib.spec_verify_run_noalloc.restype = ctypes.c_int
     lib.spec_verify_destroy.argtypes = [ctypes.c_void_p]
     lib.spec_verify_destroy.restype = ctypes.c_int
     lib.spec_verify_last_error.argtypes = []
@@ -306,6 +309,15 @@ def spec_verify_run(handle, inputs: Dict, outputs: Dict, stream=None, config: Op
     i, o = _inputs(inputs), _outputs(outputs)
     _check(load_library().spec_verify_run(handle, ctypes.byref(i), ctypes.byref(o),
                                           ctypes.c_void_p(_stream_handle(stream))))
+
+
+def spec_verify_run_noalloc(config: Config, inputs: Dict, outputs: Dict, stream=None) -> None:
+    """spec_verify_run without a handle and without any device allocation: the
+    workspace is the library's static per-GPU scratch (see the C declaration)."""
+    check_run_args(config, inputs, outputs)
+    i, o = _inputs(inputs), _outputs(outputs)
+    _check(load_library().spec_verify_run_noalloc(ctypes.byref(config), ctypes.byref(i), ctypes.byref(o),
+                                                  ctypes.c_void_p(_stream_handle(stream))))
 
 
 def spec_verify_run_paged(handle, inputs: Dict, paged: PagedKV, outputs: Dict, stream=None,

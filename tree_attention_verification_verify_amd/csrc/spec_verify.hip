@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -559,6 +560,85 @@ int commit_impl(spec_verify_handle* h, const spec_verify_commit_args* a, const s
 
 }  // namespace
 
+namespace {
+
+// ------------------------------------------------------------------ workspace without allocation
+//
+// spec_verify_run_noalloc takes its workspace from this array instead of a
+// handle's hipMalloc'd buffers.  Each GPU the library runs on holds its own
+// copy (placed by the runtime when the code object is loaded there) until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(16) << 20;   // 16 MiB per GPU
+constexpr int kNoallocMaxBatch = 1024;               // sequences per call (one arrival counter each)
+constexpr size_t kCounterBytes = kNoallocMaxBatch * sizeof(int32_t);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_words_kernel(int32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// Device address of this GPU's scratch array.  The first call on a device
+// looks it up and clears the arrival counters on `stream` (every complete run
+// leaves them at 0 again: the last workgroup's increment wraps them).
+int scratch_for_device(int dev, hipStream_t stream, unsigned char** out) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "device index out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(SPEC_VERIFY_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        hipLaunchKernelGGL(zero_words_kernel, dim3(4), dim3(256), 0, stream, (int32_t*)ptr, kNoallocMaxBatch);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+        g_scratch_ptr[dev] = (unsigned char*)ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPEC_VERIFY_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Carve a run's workspace for (B, T) out of the scratch at `base`: arrival
+// counters, row statistics and final-draw totals first, the per-thread slice
+// prefixes when they fit in half of what is left, and split partials in the
+// rest (the attention plan then takes as many prefix splits as fit).
+int carve_scratch(const spec_verify_config& c, int B, int T, unsigned char* base, Workspace* ws) {
+    const int slices = (c.vocab + sv::kSelectSlice - 1) / sv::kSelectSlice;
+    const uintptr_t b0 = (uintptr_t)base;   // 0 for a size check only
+    size_t off = kCounterBytes;
+    const size_t stats_bytes = round_up((size_t)B * 2 * T * sizeof(sv::RowStat), 256);
+    const size_t tot_bytes = round_up((size_t)B * slices * sizeof(double2), 256);
+    if (off + stats_bytes + tot_bytes > kScratchBytes)
+        return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "the batch needs more than the 16 MiB scratch of spec_verify_run_noalloc");
+    ws->arrive = (int32_t*)b0;
+    ws->stats = (sv::RowStat*)(b0 + off);
+    off += stats_bytes;
+    ws->slice_tot = (double2*)(b0 + off);
+    off += tot_bytes;
+    const size_t pre_bytes = round_up((size_t)B * slices * sv::kSelectThreads * sizeof(double2), 256);
+    ws->slice_pre = nullptr;
+    if (c.mode == SPEC_VERIFY_SAMPLING && slices <= sv::kSelectKeepSlices && 2 * pre_bytes <= kScratchBytes - off) {
+        ws->slice_pre = (double2*)(b0 + off);
+        off += pre_bytes;
+    }
+    // partial rows: D floats of O and one (m, l) pair each; 256 bytes kept for aligning the pairs
+    const size_t row_bytes = (size_t)c.head_dim * sizeof(float) + sizeof(float2);
+    const size_t left = kScratchBytes - off;
+    ws->part_rows_cap = left > 256 ? (left - 256) / row_bytes : 0;
+    ws->part_o = (float*)(b0 + off);
+    ws->part_ml = (float2*)(b0 + off + round_up(ws->part_rows_cap * c.head_dim * sizeof(float), 256));
+    return SPEC_VERIFY_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int spec_verify_run(spec_verify_handle* h, const spec_verify_inputs* in, const spec_verify_outputs* out,
@@ -576,6 +656,30 @@ int spec_verify_run_paged(spec_verify_handle* h, const spec_verify_inputs* in, c
     if (!paged) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "paged is NULL");
     TimingRing tr{&h->events, &h->ring_head, &h->runs_recorded};
     return run_impl(h->cfg, h->ws, h->timing ? &tr : nullptr, in, paged, out, stream);
+}
+
+int spec_verify_run_noalloc(const spec_verify_config* cfg, const spec_verify_inputs* in,
+                            const spec_verify_outputs* out, void* stream) {
+    g_err.clear();
+    if (!cfg || !in || !out) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "cfg, inputs and outputs must be non-NULL");
+    const spec_verify_config& c = *cfg;
+    if (int rc = validate_config(c)) return rc;
+    if (c.flags & (SPEC_VERIFY_FLAG_TIMING | SPEC_VERIFY_FLAG_LOSSLESS_TREE | SPEC_VERIFY_FLAG_WALK_NO_WAIT))
+        return fail(SPEC_VERIFY_ERR_UNSUPPORTED,
+                    "spec_verify_run_noalloc takes neither SPEC_VERIFY_FLAG_TIMING nor SPEC_VERIFY_FLAG_LOSSLESS_TREE");
+    if (in->batch < 1 || in->batch > c.max_batch) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "batch out of range");
+    if (in->nodes < 1 || in->nodes > c.max_nodes) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes out of range");
+    if (in->batch > kNoallocMaxBatch)
+        return fail(SPEC_VERIFY_ERR_UNSUPPORTED, "spec_verify_run_noalloc takes at most 1024 sequences");
+    Workspace ws;
+    if (int rc = carve_scratch(c, in->batch, in->nodes, nullptr, &ws)) return rc;   // size check only
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    unsigned char* base = nullptr;
+    if (int rc = scratch_for_device(dev, (hipStream_t)stream, &base)) return rc;
+    carve_scratch(c, in->batch, in->nodes, base, &ws);
+    return run_impl(c, ws, nullptr, in, nullptr, out, stream);
 }
 
 int spec_verify_commit(spec_verify_handle* h, const spec_verify_commit_args* a, void* stream) {
