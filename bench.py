@@ -2,18 +2,35 @@
 """Verify-step benchmark on one MI355X.
 
 One step = one spec_verify_run over a batch of synthetic inputs already resident
-in HBM: tree attention + split merge + vocab pass + selection.  The default
-workload is the 70B-shaped GQA Medusa-tree verify (batch 8, 64 query / 8 KV
-heads x 128, prefix 8192, 64-node tree, vocab 32000) in sampling mode.
+in HBM: tree attention (+ split merge), vocabulary pass and selection.  The
+headline workload is the 70B-shaped GQA Medusa-tree verify (batch 8, 64 query /
+8 KV heads x 128, prefix 8192, 64-node tree, vocab 32000) in sampling mode; the
+other four workloads (and the headline in greedy mode) are reported as
+sub-records under "configs".
 
-Prints one JSON line: verified candidate tokens/s (B*T per step), the roofline
-of the dominant kernel (HIP events on the run's stream), HBM GB/s of the whole
-step, and the CPU oracle timed on a bounded sample of the same workload.
+For every workload, before anything is timed, the GPU outputs are compared
+with the CPU oracle (every decision and token, bit for bit outside the
+near-tie band; attention rows of the root and the deepest nodes of a sequence
+within the stated tolerance): a mismatch ends the run with exit status 3.
+
+Timing (HIP events on the run's stream, inputs resident in HBM; every timed
+part starts after at least 0.2 s of untimed steps, which bring the GPU out of
+its idle clocks after the host-side parity check):
+  value          B*T candidate tokens / mean time of `steps` back-to-back steps
+                 (host clock around a synchronised region, as the driver's contract asks);
+  warm           the same steps in 20 blocks with events only between blocks: median / min per step;
+  cold           single steps, each after writing a 1 GiB buffer (flushes L2 and the
+                 Infinity Cache) outside the events: median / min;
+  roofline       the dominant kernel (the attention) timed alone, back to back, with a
+                 handle that skips the vocabulary pass: no event between its launches.
+
+Prints one JSON line.
 """
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -28,29 +45,11 @@ KERNEL_SOURCES = {"attn_mfma_kernel": "tree_attn.hip", "attn_valu_kernel": "tree
                   "attn_valu_tiled_kernel": "tree_attn_valu.hip",
                   "row_stats_stream_kernel": "vocab_stats.hip", "row_stats_topp_kernel": "vocab_stats.hip",
                   "row_stats_topp_chunked_kernel": "vocab_stats.hip", "finish_kernel": "select_final.hip"}
-VOCAB_CHUNK = 32768   # vocabulary ids one row workgroup holds on chip (kVocabChunk)
-
-
-def stage_kernel(stage, spec):
-    """The kernel a stage launches for this workload, by the library's own dispatch rule.
-
-    Attention: the MFMA kernel when bf16 and the g*T query rows sharing one KV head
-    number at least 16; below that the tiled VALU kernel for at most 8 rows whose K/V
-    rows are 128 or 256 bytes, else the one-wave VALU kernel.  Row statistics: with
-    top-p in sampling mode, the row held on chip up to VOCAB_CHUNK ids and streamed
-    above; otherwise the streaming kernel.
-    """
-    if stage == "attention":
-        rows = spec.hq // spec.hkv * spec.nodes
-        if spec.dtype == "bf16" and rows >= 16:
-            return "attn_mfma_kernel"
-        rowb = spec.head_dim * (2 if spec.dtype == "bf16" else 4)
-        return "attn_valu_tiled_kernel" if rows <= 8 and rowb in (128, 256) else "attn_valu_kernel"
-    if stage == "vocab":
-        if spec.mode == "sampling" and spec.top_p < 1.0:
-            return "row_stats_topp_kernel" if spec.vocab <= VOCAB_CHUNK else "row_stats_topp_chunked_kernel"
-        return "row_stats_stream_kernel"
-    return "finish_kernel"
+HEADLINE = ("70b-gqa-medusa", None)
+SUBRECORDS = [("tiny-chain-f32", None), ("llama7b-medusa-greedy", None), ("chain-batch32-topp", None),
+              ("70b-gqa-medusa", "greedy"), ("longctx-bigvocab", None)]
+ATTN_TOL = {"bf16": 2e-2, "f32": 1e-4}
+STRICT = dict(accept_band=2e-6, cdf_band=2e-6)   # as the GPU parity tests
 
 
 def parse():
@@ -58,12 +57,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="70b-gqa-medusa",
-                    help="one of: tiny-chain-f32, llama7b-medusa-greedy, chain-batch32-topp, "
+    ap.add_argument("--workload", default=HEADLINE[0],
+                    help="headline workload: tiny-chain-f32, llama7b-medusa-greedy, chain-batch32-topp, "
                          "70b-gqa-medusa, longctx-bigvocab")
     ap.add_argument("--mode", default=None, help="sampling or greedy (default: the workload's own)")
     ap.add_argument("--top-p", type=float, default=None, help="top-p of sampling mode (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-subrecords", action="store_true", help="time the headline workload only")
+    ap.add_argument("--profile", action="store_true",
+                    help="only warm-up and `steps` back-to-back steps of the headline workload, after the "
+                         "parity check (for rocprofv3 traces and counters)")
+    ap.add_argument("--cold-iters", type=int, default=20, help="single steps timed after a cache flush")
+    ap.add_argument("--flush-bytes", type=int, default=1 << 30, help="bytes written between cold steps")
     ap.add_argument("--lossless-tree", action="store_true",
                     help="time the lossless sibling walk (SPEC_VERIFY_FLAG_LOSSLESS_TREE) as the value")
     ap.add_argument("--paged-block-size", type=int, default=16,
@@ -71,15 +76,26 @@ def parse():
                          "many slots (spec_verify_run_paged); 0 = skip")
     ap.add_argument("--traffic-summary", nargs=5, default=None,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES"),
-                    help="write profiles/traffic_<kernel>_<workload>.json from rocprofv3 --pmc counter CSVs")
+                    help="write profiles/traffic_<kernel>_<workload>.json from rocprofv3 --pmc counter CSVs "
+                         "(kernel: --kernel)")
+    ap.add_argument("--kernel", default="attn_mfma_kernel", help="kernel of --traffic-summary")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="instead of the verify step, run a plain device copy of this many bytes "
                          "(--steps times): the reference kernel for scaling HBM counters")
     return ap.parse_args()
 
 
+# ------------------------------------------------------------------ algorithmic work
+
 def algorithmic_work(case):
-    """Bytes and flops the method itself must move / do, per step (see the design notes)."""
+    """Bytes and flops the method itself must move / do, per step.
+
+    Attention per sequence: K and V of the L_b + T visible slots read once, Q read
+    and O written once: 2*Hkv*D*e*(L_b+T) + 2*T*Hq*D*e bytes; flops 4*Hq*D per
+    visible (query, key) pair, node i seeing L_b + depth(i) + 1 keys.
+    Vocabulary: every target row (and every draft row in sampling mode) read once,
+    4*V bytes per row.
+    """
     spec = case.spec
     e = 2 if spec.dtype == "bf16" else 4
     B, T = case.parent.shape
@@ -88,7 +104,7 @@ def algorithmic_work(case):
     for b in range(B):
         L = int(case.kv_len[b])
         attn_bytes += 2 * spec.hkv * spec.head_dim * e * (L + T) + 2 * T * spec.hq * spec.head_dim * e
-        depth = [0] * T          # node i sees the prefix and its depth(i) + 1 root-path nodes
+        depth = [0] * T
         for i in range(1, T):
             depth[i] = depth[int(case.parent[b, i])] + 1
         visible = sum(L + d + 1 for d in depth)
@@ -96,6 +112,45 @@ def algorithmic_work(case):
     rows = T + (T - 1 if spec.mode == "sampling" else 0)
     vocab_bytes = 4 * spec.vocab * rows * B
     return dict(attention_bytes=int(attn_bytes), attention_flops=int(attn_flops), vocab_bytes=int(vocab_bytes))
+
+
+def acceptance_stats(parent, node_accept, accept_len):
+    """Accept-length histogram and the per-depth conditional acceptance rate.
+
+    conditional rate at depth d: among the nodes of depth d whose parent lies on
+    an accepted root path, the fraction whose own test passed (the chance a step
+    goes one node deeper, given it got to the parent).  "acceptance_rate" is the
+    mean accepted length over the deepest depth a tree offers.
+    """
+    import numpy as np
+
+    parent = np.asarray(parent)
+    node_accept = np.asarray(node_accept).astype(bool)
+    accept_len = np.asarray(accept_len)
+    B, T = parent.shape
+    hist = {}
+    for a in accept_len.tolist():
+        hist[str(int(a))] = hist.get(str(int(a)), 0) + 1
+    tried, passed = {}, {}
+    max_depth = 0
+    for b in range(B):
+        acc = [True] + [False] * (T - 1)
+        depth = [0] * T
+        for i in range(1, T):
+            p = int(parent[b, i])
+            depth[i] = depth[p] + 1
+            acc[i] = bool(node_accept[b, i]) and acc[p]
+            if acc[p]:
+                tried[depth[i]] = tried.get(depth[i], 0) + 1
+                passed[depth[i]] = passed.get(depth[i], 0) + int(bool(node_accept[b, i]))
+        max_depth = max(max_depth, max(depth))
+    cond = {str(d): passed[d] / tried[d] for d in sorted(tried)}
+    return {"accept_len_histogram": dict(sorted(hist.items(), key=lambda kv: int(kv[0]))),
+            "mean_accept_len": float(accept_len.mean()),
+            "accepted_tokens_per_step": int(accept_len.sum() + B),
+            "acceptance_rate": float(accept_len.mean()) / max(max_depth, 1),
+            "conditional_acceptance_by_depth": cond,
+            "nodes_tested_by_depth": {str(d): tried[d] for d in sorted(tried)}}
 
 
 def source_hash(kname):
@@ -114,14 +169,453 @@ def measured_traffic(kname, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, got, min_seconds=10.0):
-    """The oracle, as it stands, on the first sequences of the same workload:
-    one sequence at a time until `min_seconds` of CPU work or the whole batch.
+# ------------------------------------------------------------------ helpers on the GPU
 
-    Also a parity spot check of those sequences against the GPU run.
-    """
+def upload(case, dev):
+    import numpy as np
+    import torch
+
+    def up(a, dtype=None):
+        a = np.ascontiguousarray(a)
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    spec = case.spec
+    return dict(q=up(case.q, spec.dtype), k_cache=up(case.k_cache, spec.dtype), v_cache=up(case.v_cache, spec.dtype),
+                kv_len=up(case.kv_len), parent=up(case.parent), tokens=up(case.tokens),
+                target_logits=up(case.target_logits),
+                draft_logits=None if case.draft_logits is None else up(case.draft_logits),
+                u_accept=up(case.u_accept), u_final=up(case.u_final)), up
+
+
+def handle_cfg(spec, case, **flags):
+    B, T = case.parent.shape
+    cfg = dict(max_batch=B, max_nodes=T, num_q_heads=spec.hq, num_kv_heads=spec.hkv, head_dim=spec.head_dim,
+               kv_capacity=case.k_cache.shape[2], vocab=spec.vocab, dtype=spec.dtype, mode=spec.mode,
+               temperature=spec.temperature, top_p=spec.top_p)
+    cfg.update(flags)
+    return cfg
+
+
+def to_host(outs):
+    import torch
+
+    return {k: (v.float() if v.dtype == torch.bfloat16 else v).cpu().numpy() for k, v in outs.items()}
+
+
+def parity_check(case, got):
+    """The GPU outputs against the oracle on the same inputs (raises SystemExit(3) on a mismatch).
+
+    Every decision and token of every sequence, outside the near-tie band;
+    node_p/node_q to relative 1e-4; attention rows of the root and the deepest
+    nodes of sequence 0 (all heads) within 2e-2 (bf16) / 1e-4 (fp32)."""
     import numpy as np
 
+    import oracle
+
+    spec = case.spec
+    ref = oracle.verify(case, attention=False, **STRICT)
+    bad = []
+    B, T = case.parent.shape
+    for b in range(B):
+        if int(got["status"][b]) != int(ref["status"][b]):
+            bad.append("status b=%d" % b)
+            continue
+        near = ref["node_near"][b]
+        for i in range(T):
+            if not near[i] and got["node_accept"][b, i] != ref["node_accept"][b, i]:
+                bad.append("node_accept b=%d i=%d" % (b, i))
+        if not (got["row_token"][b] == ref["row_token"][b]).all():
+            bad.append("row_token b=%d" % b)
+        if spec.mode == "sampling":
+            for name in ("node_p", "node_q"):
+                g, r = got[name][b, 1:].astype(np.float64), ref[name][b, 1:]
+                m = ~near[1:] & (r >= 1e-30)
+                if m.any() and (np.abs(g[m] - r[m]) / r[m]).max() > 1e-4:
+                    bad.append("%s b=%d" % (name, b))
+        if ref["seq_near"][b]:
+            continue
+        for k in ("accept_len", "final_node", "final_from_residual"):
+            if int(got[k][b]) != int(ref[k][b]):
+                bad.append("%s b=%d" % (k, b))
+        for k in ("path", "out_tokens"):
+            if not (got[k][b] == ref[k][b]).all():
+                bad.append("%s b=%d" % (k, b))
+    d = oracle.depths(case.parent[0])
+    nodes = [0] + [i for i in range(T) if d[i] == max(d) and i > 0]
+    err = 0.0
+    q = oracle.widen(case.q[0], spec.dtype)
+    k = oracle.widen(case.k_cache[0], spec.dtype)
+    v = oracle.widen(case.v_cache[0], spec.dtype)
+    for i in nodes:
+        row = oracle.tree_attention_node(q[i], k, v, int(case.kv_len[0]), case.parent[0], i)
+        err = max(err, float(np.abs(got["attn_out"][0, i].astype(np.float64) - row).max()))
+    if err > ATTN_TOL[spec.dtype]:
+        bad.append("attn_out max err %.3g" % err)
+    if bad:
+        print("bench.py: GPU outputs differ from the oracle on %s: %s" % (spec.name, ", ".join(bad[:10])),
+              file=sys.stderr, flush=True)
+        raise SystemExit(3)
+    return {"ok": True, "sequences": B, "near_tie_sequences": int(ref["seq_near"].sum()),
+            "attn_rows_checked": len(nodes) * spec.hq, "attn_max_abs_err": err, "attn_tol": ATTN_TOL[spec.dtype]}
+
+
+def clock_ramp(run, seconds=0.2):
+    """Steps for `seconds` of wall time (untimed): brings the GPU out of its idle
+    clocks after host-side work (the parity check) before anything is timed."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+        n += 10
+    return n
+
+
+def time_back_to_back(run, steps, warmup, stream):
+    """Mean ms per step of `steps` back-to-back runs, host clock around a synchronised region."""
+    import torch
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_blocks(run, steps, stream, blocks=20):
+    """Per-step ms of back-to-back runs in `blocks` blocks, events only between blocks: median and min."""
+    import torch
+
+    per = max(1, steps // blocks)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+    ev[0].record(stream)
+    for j in range(blocks):
+        for _ in range(per):
+            run()
+        ev[j + 1].record(stream)
+    ev[-1].synchronize()
+    ms = [ev[j].elapsed_time(ev[j + 1]) / per for j in range(blocks)]
+    return {"median_ms": statistics.median(ms), "min_ms": min(ms), "blocks": blocks, "steps_per_block": per}
+
+
+def time_cold(run, iters, flush, stream):
+    """Single steps, each after a write of the flush buffer (outside the events): median and min ms."""
+    import torch
+
+    ms = []
+    pair = []
+    for _ in range(iters):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        # an empty event pair after the same flush: what the two records alone add
+        flush.fill_(2)
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        e3.record(stream)
+        e3.synchronize()
+        pair.append(e2.elapsed_time(e3))
+    return {"median_ms": statistics.median(ms), "min_ms": min(ms), "iters": iters,
+            "flush_bytes": flush.numel() * flush.element_size(), "empty_event_pair_ms": statistics.median(pair)}
+
+
+def roofline(work, us, spec, kernel):
+    """Roofline record of the attention kernel from its own time per launch (us)."""
+    t = us * 1e-6
+    ai = work["attention_flops"] / work["attention_bytes"]
+    if ai > RIDGE and spec.dtype == "bf16":
+        achieved = work["attention_flops"] / t / 1e12
+        rec = dict(bound="mfma", achieved=achieved, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                   frac=achieved / MFMA_BF16_PEAK_TFLOPS)
+    else:
+        achieved = work["attention_bytes"] / t / 1e9
+        rec = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS)
+    rec.update(kernel=kernel, us_per_launch=us, arithmetic_intensity=ai,
+               method="the attention alone (handle with SPEC_VERIFY_FLAG_SKIP_VOCAB), back-to-back launches "
+                      "between two events on the run's stream")
+    return rec
+
+
+def measure(name, mode, args, headline=False):
+    """Every figure of one workload (see the module docstring).  Returns (record, state)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs
+
+    overrides = {}
+    if mode:
+        overrides["mode"] = mode
+    if headline and args.top_p is not None:
+        overrides["top_p"] = args.top_p
+    spec = synth.workload(name, **overrides)
+    t_gen = time.perf_counter()
+    case = synth.make_case(spec)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda")
+    ins, up = upload(case, dev)
+    B, T = case.parent.shape
+    stream = torch.cuda.current_stream()
+    lossless = bool(headline and args.lossless_tree and spec.mode == "sampling")
+    cfg = handle_cfg(spec, case, lossless_tree=lossless)
+    outs = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
+    work = algorithmic_work(case)
+    rec = {"workload": name, "mode": spec.mode, "batch": B, "nodes": T, "q_heads": spec.hq, "kv_heads": spec.hkv,
+           "head_dim": spec.head_dim, "prefix": int(case.kv_len.max()), "vocab": spec.vocab,
+           "temperature": spec.temperature, "top_p": spec.top_p, "dtype": spec.dtype,
+           "tree_rule": "lossless sibling walk" if lossless else "independent per-node test"}
+    with SpecVerify(**cfg) as sv:
+        plan = sv.describe(B, T)
+        run = sv.prepare(ins, outs, stream)      # checked and marshalled once
+        for _ in range(max(args.warmup, 1)):
+            run()
+        torch.cuda.synchronize()
+        got = to_host(outs)
+        rec["parity"] = parity_check(case, got)       # before any timing; exits on a mismatch
+        ramp = clock_ramp(run)
+        if args.profile:
+            ms = time_back_to_back(run, args.steps, 0, stream)
+            return dict(rec, ms_per_step=ms, value=B * T / (ms * 1e-3), plan=plan), None
+        ms = time_back_to_back(run, args.steps, args.warmup, stream)
+        warm = time_blocks(run, args.steps, stream)
+        flush = torch.empty(args.flush_bytes // 4, dtype=torch.int32, device=dev)
+        cold = time_cold(run, args.cold_iters, flush, stream)
+        del flush
+    rec.update(plan=plan, value=B * T / (ms * 1e-3), unit="candidate tokens/s", ms_per_step=ms,
+               warm=warm, cold=cold, clock_ramp_steps=ramp, input_generation_s=t_gen)
+
+    # per-stage event times (events around each launch: each record adds a gap, so these
+    # are upper bounds on the kernels' own times)
+    with SpecVerify(timing=True, **cfg) as sv:
+        trun = sv.prepare(ins, outs, stream)
+        clock_ramp(trun)
+        for _ in range(args.warmup):
+            trun()
+        torch.cuda.synchronize()
+        sv.timing_read()
+        for _ in range(args.steps):
+            trun()
+        torch.cuda.synchronize()
+        stage_ms, nruns = sv.timing_read()
+    stage = {k: v / max(nruns, 1) for k, v in stage_ms.items()}
+    rec["stage_ms_per_launch_with_events"] = stage
+
+    # the attention alone, back to back (kernel time per launch for the roofline)
+    acfg = dict(cfg, skip_vocab=True, lossless_tree=False)
+    aouts = dict(attn_out=torch.empty_like(outs["attn_out"]))
+    with SpecVerify(**acfg) as sv:
+        aplan = sv.describe(B, T)
+        arun = sv.prepare(ins, aouts, stream)
+        clock_ramp(arun)
+        for _ in range(args.warmup):
+            arun()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            arun()
+        e1.record(stream)
+        e1.synchronize()
+        attn_us = e0.elapsed_time(e1) * 1e3 / args.steps
+        same = bool(torch.equal(aouts["attn_out"], outs["attn_out"]))
+    kernels = [aplan["attention"]] + (["finish_kernel (split merge)"] if aplan["merge"] else [])
+    roof = roofline(work, attn_us, spec, aplan["attention"])
+    roof["launches_timed"] = kernels
+    roof["traffic"] = measured_traffic(aplan["attention"], "%s-%s" % (name, spec.mode))
+    rec["roofline"] = roof
+    rec["attention_alone_equals_full_run"] = same
+    vocab_ms = stage["vocab"]
+    step_bytes = work["attention_bytes"] + work["vocab_bytes"]
+    rec["hbm"] = dict(step_GBps=step_bytes / (ms * 1e-3) / 1e9,
+                      step_frac=step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                      attention_GBps=work["attention_bytes"] / (attn_us * 1e-6) / 1e9,
+                      attention_TFLOPs=work["attention_flops"] / (attn_us * 1e-6) / 1e12,
+                      vocab_kernel=plan["vocab"],
+                      vocab_GBps_with_events=work["vocab_bytes"] / (vocab_ms * 1e-3) / 1e9,
+                      vocab_frac_with_events=work["vocab_bytes"] / (vocab_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                      algorithmic_bytes_per_step=step_bytes, attention_bytes_per_step=work["attention_bytes"],
+                      vocab_bytes_per_step=work["vocab_bytes"], attention_flops_per_step=work["attention_flops"])
+    rec["acceptance"] = acceptance_stats(case.parent, got["node_accept"], got["accept_len"])
+    return rec, dict(case=case, ins=ins, outs=outs, got=got, cfg=cfg, up=up, spec=spec, stream=stream)
+
+
+# ------------------------------------------------------------------ headline extras
+
+def time_graph(st, args):
+    """The step captured once in a HIP graph and replayed; every replay checked against eager."""
+    import torch
+
+    from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs
+
+    case, ins, outs, cfg, spec = st["case"], st["ins"], st["outs"], st["cfg"], st["spec"]
+    B, T = case.parent.shape
+    with SpecVerify(**cfg) as sv:
+        gouts = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                sv.run(ins, gouts)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sv.run(ins, gouts)
+        torch.cuda.synchronize()
+        equal = True
+        for _ in range(3):
+            for v in gouts.values():
+                v.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            equal &= all(bool(torch.equal(gouts[k], outs[k])) for k in outs)
+        clock_ramp(g.replay)
+        gms = time_back_to_back(g.replay, args.steps, args.warmup, st["stream"])
+        del g
+    return {"ms_per_step": gms, "value": B * T / (gms * 1e-3), "replays_equal_eager": bool(equal)}
+
+
+def time_commit(st, args):
+    """KV commit of the step's accepted paths: events around the call; kv_len restored each time."""
+    import numpy as np
+    import torch
+
+    from tree_attention_verification_verify_amd import SpecVerify
+
+    case, ins, outs, cfg, spec, stream = st["case"], st["ins"], st["outs"], st["cfg"], st["spec"], st["stream"]
+    B, T = case.parent.shape
+    with SpecVerify(**cfg) as sv:
+        sv.run(ins, outs, stream)
+        kl0 = ins["kv_len"].clone()
+        kl = kl0.clone()
+        total_ms, reps = 0.0, max(args.steps // 4, 10)
+        for rep in range(reps + 3):
+            kl.copy_(kl0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sv.commit(ins["k_cache"], ins["v_cache"], kl, outs["path"], outs["accept_len"], outs["final_node"],
+                      stream)
+            e1.record(stream)
+            e1.synchronize()
+            if rep >= 3:
+                total_ms += e0.elapsed_time(e1)
+        path_np = outs["path"].cpu().numpy()
+        acc_np = outs["accept_len"].cpu().numpy()
+    moved = sum(int((path_np[b, 1:acc_np[b] + 1] != np.arange(1, acc_np[b] + 1)).sum()) for b in range(B))
+    elem = 2 if spec.dtype == "bf16" else 4
+    nbytes = moved * spec.hkv * spec.head_dim * elem * 2 * 2     # K and V, read and write
+    us = total_ms * 1e3 / reps
+    # the caches were modified in place: restore them
+    ins["k_cache"].copy_(st["up"](case.k_cache, spec.dtype))
+    ins["v_cache"].copy_(st["up"](case.v_cache, spec.dtype))
+    return {"us_per_call": us, "rows_moved": moved, "bytes_moved": nbytes,
+            "GBps": nbytes / (us * 1e-6) / 1e9 if us > 0 else None}
+
+
+def time_other_rule(st, args):
+    """The other tree rule (sampling) on the same inputs: step time and accepted tokens."""
+    from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs
+
+    case, ins, cfg, spec, stream = st["case"], st["ins"], st["cfg"], st["spec"], st["stream"]
+    B, T = case.parent.shape
+    ocfg = dict(cfg, lossless_tree=not cfg.get("lossless_tree", False))
+    oouts = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
+    with SpecVerify(**ocfg) as sv:
+        plan = sv.describe(B, T)
+        orun = sv.prepare(ins, oouts, stream)
+        clock_ramp(orun)
+        ms = time_back_to_back(orun, args.steps, args.warmup, stream)
+    acc = oouts["accept_len"].cpu().numpy()
+    return {"rule": "lossless sibling walk" if ocfg["lossless_tree"] else "independent per-node test",
+            "plan": plan, "value": B * T / (ms * 1e-3), "ms_per_step": ms,
+            "accepted_tokens_per_step": int(acc.sum() + B)}
+
+
+def time_paged(st, args):
+    """The step with the caches read through a block table (pages scattered in a shuffled pool)."""
+    import torch
+
+    import synth
+    from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs, paged_kv
+
+    case, ins, outs, cfg, spec, stream, up = (st[k] for k in ("case", "ins", "outs", "cfg", "spec", "stream", "up"))
+    B, T = case.parent.shape
+    _, pg = synth.page_case(case, args.paged_block_size, seed=(1,))
+    pool_k, pool_v, table = up(pg.k_pool, spec.dtype), up(pg.v_pool, spec.dtype), up(pg.block_table)
+    pk = paged_kv(pool_k, pool_v, table)
+    pins = {k: v for k, v in ins.items() if k not in ("k_cache", "v_cache")}
+    pcfg = dict(cfg, kv_capacity=pg.capacity)
+    pouts = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
+    with SpecVerify(**pcfg) as sv:
+        prun = sv.prepare(pins, pouts, stream, paged=pk)
+        clock_ramp(prun)
+        ms = time_back_to_back(prun, args.steps, args.warmup, stream)
+    same = all(bool(torch.equal(pouts[k], outs[k])) for k in outs)
+    return {"block_size": args.paged_block_size, "pages": int(pg.num_blocks), "value": B * T / (ms * 1e-3),
+            "ms_per_step": ms, "outputs_equal_dense": same}
+
+
+def time_tree_build(spec, B, args, stream):
+    """Candidate-tree construction (spec_verify_build_tree) for the workload's tree shape:
+    per-depth top-k of B x depth logits rows (seeded N(0, 3^2)) and the template fill."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from tree_attention_verification_verify_amd import SpecVerify, binding, spec_verify_tree_template
+
+    caps, T = spec.tree[1], spec.tree[2]
+    parent_t, rank_t = spec_verify_tree_template(caps, T)
+    depth = len(caps)
+    rng = np.random.default_rng(2024)
+    lg = torch.from_numpy(rng.normal(0.0, 3.0, size=(B, depth, spec.vocab)).astype(np.float32)).cuda()
+    root = torch.zeros(B, dtype=torch.int32, device="cuda")
+    par = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    tok = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    cfg = dict(max_batch=B, max_nodes=T, num_q_heads=spec.hq, num_kv_heads=spec.hkv, head_dim=spec.head_dim,
+               kv_capacity=spec.kv_capacity, vocab=spec.vocab, dtype=spec.dtype, mode=spec.mode,
+               temperature=spec.temperature, top_p=spec.top_p)
+    lib = binding.load_library()
+    tp = (ctypes.c_int32 * T)(*parent_t)
+    tr = (ctypes.c_int32 * T)(*rank_t)
+    targs = binding.TreeArgs(lg.data_ptr(), root.data_ptr(), ctypes.cast(tp, ctypes.c_void_p),
+                             ctypes.cast(tr, ctypes.c_void_p), par.data_ptr(), tok.data_ptr(), B, T, depth)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    with SpecVerify(**cfg) as sv:
+        for _ in range(10):
+            sv.build_tree(lg, root, parent_t, rank_t, par, tok, stream)
+        torch.cuda.synchronize()
+        # prebuilt arguments: the host stays ahead of the kernels
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            lib.spec_verify_build_tree(sv.handle, ctypes.byref(targs), sh)
+        e1.record(stream)
+        e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    nbytes = B * depth * spec.vocab * 4
+    return {"caps": list(caps), "nodes": T, "rows": B * depth, "us_per_call": us, "bytes_read": nbytes,
+            "GBps": nbytes / (us * 1e-6) / 1e9}
+
+
+def cpu_baseline(case, min_seconds=10.0):
+    """The oracle, as it stands, on the first sequences of the same workload: one
+    sequence at a time until `min_seconds` of CPU work or the whole batch."""
     import oracle
 
     try:
@@ -129,28 +623,21 @@ def cpu_baseline(case, got, min_seconds=10.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    seqs, parts, dt = [], [], 0.0
-    while len(seqs) < case.parent.shape[0] and dt < min_seconds:
+    seqs, dt = 0, 0.0
+    while seqs < case.parent.shape[0] and dt < min_seconds:
         t0 = time.perf_counter()
-        parts.append(oracle.verify(case, attention=True, seqs=[len(seqs)]))
+        oracle.verify(case, attention=True, seqs=[seqs])
         dt += time.perf_counter() - t0
-        seqs.append(len(seqs))
-    ref = {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+        seqs += 1
     T = case.parent.shape[1]
-    ok = True
-    err = 0.0
-    for n, b in enumerate(seqs):
-        if not ref["seq_near"][n] and int(ref["status"][n]) == 0:
-            ok &= int(got["accept_len"][b]) == int(ref["accept_len"][n])
-            ok &= bool((got["out_tokens"][b] == ref["out_tokens"][n]).all())
-        err = max(err, float(np.abs(got["attn_out"][b].astype(np.float64) - ref["attn_out"][n]).max()))
-    ok &= err <= (2e-2 if case.spec.dtype == "bf16" else 1e-4)
-    return dict(value=len(seqs) * T / dt, unit="candidate tokens/s", cores=int(threads), kind="oracle",
+    return dict(value=seqs * T / dt, unit="candidate tokens/s", cores=int(threads), kind="oracle",
                 sample="sequences 0..%d of %d (%d nodes, prefix %d, vocab %d each): attention + vocab + "
-                       "acceptance + selection, %.1f s" % (len(seqs) - 1, case.parent.shape[0], T,
+                       "acceptance + selection, %.1f s" % (seqs - 1, case.parent.shape[0], T,
                                                            int(case.kv_len[0]), case.spec.vocab, dt),
-                seconds=dt), ok, err
+                seconds=dt, blas_threads=int(threads), host_cpu_count=os.cpu_count())
 
+
+# ------------------------------------------------------------------ counters and probes
 
 def copy_probe(nbytes, steps):
     import torch
@@ -165,52 +652,6 @@ def copy_probe(nbytes, steps):
     dt = (time.perf_counter() - t0) / steps
     print(json.dumps({"copy_probe_bytes": nbytes, "ms_per_copy": dt * 1e3,
                       "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
-
-
-def time_tree_build(spec, B, steps, stream):
-    """Candidate-tree construction (spec_verify_build_tree) for the workload's tree shape:
-    per-depth top-k of B x depth logits rows (seeded N(0, 3^2)) and the template fill."""
-    import numpy as np
-    import torch
-
-    from tree_attention_verification_verify_amd import SpecVerify, spec_verify_tree_template
-
-    caps, T = spec.tree[1], spec.tree[2]
-    parent_t, rank_t = spec_verify_tree_template(caps, T)
-    depth = len(caps)
-    rng = np.random.default_rng(2024)
-    lg = torch.from_numpy(rng.normal(0.0, 3.0, size=(B, depth, spec.vocab)).astype(np.float32)).cuda()
-    root = torch.zeros(B, dtype=torch.int32, device="cuda")
-    par = torch.empty((B, T), dtype=torch.int32, device="cuda")
-    tok = torch.empty((B, T), dtype=torch.int32, device="cuda")
-    cfg = dict(max_batch=B, max_nodes=T, num_q_heads=spec.hq, num_kv_heads=spec.hkv, head_dim=spec.head_dim,
-               kv_capacity=spec.kv_capacity, vocab=spec.vocab, dtype=spec.dtype, mode=spec.mode,
-               temperature=spec.temperature, top_p=spec.top_p)
-    import ctypes
-
-    from tree_attention_verification_verify_amd import binding
-
-    lib = binding.load_library()
-    tp = (ctypes.c_int32 * T)(*parent_t)
-    tr = (ctypes.c_int32 * T)(*rank_t)
-    targs = binding.TreeArgs(lg.data_ptr(), root.data_ptr(), ctypes.cast(tp, ctypes.c_void_p),
-                             ctypes.cast(tr, ctypes.c_void_p), par.data_ptr(), tok.data_ptr(), B, T, depth)
-    sh = ctypes.c_void_p(stream.cuda_stream)
-    with SpecVerify(**cfg) as sv:
-        for _ in range(10):
-            sv.build_tree(lg, root, parent_t, rank_t, par, tok, stream)
-        torch.cuda.synchronize()
-        # prebuilt arguments: the host stays ahead of the kernels
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            lib.spec_verify_build_tree(sv.handle, ctypes.byref(targs), sh)
-        e1.record(stream)
-        e1.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
-    nbytes = B * depth * spec.vocab * 4
-    return {"caps": list(caps), "nodes": T, "rows": B * depth, "us_per_call": us, "bytes_read": nbytes,
-            "GBps": nbytes / (us * 1e-6) / 1e9}
 
 
 def _counter_per_dispatch(csv_path, kernel_prefix, counter):
@@ -263,7 +704,7 @@ def main():
     if args.traffic_summary:
         import synth
         spec = synth.workload(args.workload, **({"mode": args.mode} if args.mode else {}))
-        traffic_summary(args.traffic_summary, "%s-%s" % (args.workload, spec.mode), stage_kernel("attention", spec))
+        traffic_summary(args.traffic_summary, "%s-%s" % (args.workload, spec.mode), args.kernel)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs the verify step on one GPU only; --gpus %d is not supported "
@@ -274,269 +715,59 @@ def main():
         copy_probe(args.copy_probe, args.steps)
         return
 
-    import numpy as np
-    import torch
-
-    import synth
-    from tree_attention_verification_verify_amd import SpecVerify, allocate_outputs, load_library
+    from tree_attention_verification_verify_amd import load_library
 
     load_library()   # fail loudly if the HIP library is missing
-    overrides = {}
-    if args.mode:
-        overrides["mode"] = args.mode
-    if args.top_p is not None:
-        overrides["top_p"] = args.top_p
-    spec = synth.workload(args.workload, **overrides)
-    t_gen = time.perf_counter()
-    case = synth.make_case(spec)
-    t_gen = time.perf_counter() - t_gen
-    dev = torch.device("cuda")
-
-    def up(a, dtype=None):
-        a = np.ascontiguousarray(a)
-        if dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    ins = dict(q=up(case.q, spec.dtype), k_cache=up(case.k_cache, spec.dtype), v_cache=up(case.v_cache, spec.dtype),
-               kv_len=up(case.kv_len), parent=up(case.parent), tokens=up(case.tokens),
-               target_logits=up(case.target_logits),
-               draft_logits=None if case.draft_logits is None else up(case.draft_logits),
-               u_accept=up(case.u_accept), u_final=up(case.u_final))
-    B, T = case.parent.shape
-    outs = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
-    cfg = dict(max_batch=B, max_nodes=T, num_q_heads=spec.hq, num_kv_heads=spec.hkv, head_dim=spec.head_dim,
-               kv_capacity=spec.kv_capacity, vocab=spec.vocab, dtype=spec.dtype, mode=spec.mode,
-               temperature=spec.temperature, top_p=spec.top_p,
-               lossless_tree=bool(args.lossless_tree and spec.mode == "sampling"))
-    stream = torch.cuda.current_stream()
-    work = algorithmic_work(case)
-
-    # Steps with HIP events around every kernel: per-kernel durations.  Run
-    # first, so that they also bring the GPU out of its idle clocks before the
-    # value is timed.
-    with SpecVerify(timing=True, **cfg) as sv:
-        for _ in range(args.warmup):
-            sv.run(ins, outs, stream)
-        torch.cuda.synchronize()
-        sv.timing_read()                     # discard warm-up records
-        t2 = time.perf_counter()
-        for _ in range(args.steps):
-            sv.run(ins, outs, stream)
-        torch.cuda.synchronize()
-        ms_with_events = (time.perf_counter() - t2) * 1e3 / args.steps
-        stage_ms, nruns = sv.timing_read()
-
-    # timed steps (the value): back-to-back runs, nothing else on the stream
-    with SpecVerify(timing=False, **cfg) as sv:
-        for _ in range(args.warmup):
-            sv.run(ins, outs, stream)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            sv.run(ins, outs, stream)
-        torch.cuda.synchronize()
-        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # the same step captured once in a HIP graph (its three launches) and
-    # replayed: every replay is checked against the eager outputs above, with
-    # the outputs cleared in between
-    graph = None
-    with SpecVerify(timing=False, **cfg) as sv:
-        gouts = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for _ in range(3):
-                sv.run(ins, gouts)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            sv.run(ins, gouts)
-        torch.cuda.synchronize()
-        equal = True
-        for _ in range(3):
-            for v in gouts.values():
-                v.zero_()
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            equal &= all(bool(torch.equal(gouts[k], outs[k])) for k in outs)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t5 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
-        torch.cuda.synchronize()
-        gms = (time.perf_counter() - t5) * 1e3 / args.steps
-        graph = {"ms_per_step": gms, "value": B * T / (gms * 1e-3), "replays_equal_eager": bool(equal)}
-        del g
-
-    per_launch = {k: v / max(nruns, 1) for k, v in stage_ms.items()}
-
-    # KV commit of the accepted paths (spec_verify_commit) on this step's outputs: events
-    # around the call alone; kv_len is restored before each call
-    commit = None
-    with SpecVerify(timing=False, **cfg) as sv:
-        sv.run(ins, outs, stream)
-        kl0 = ins["kv_len"].clone()
-        kl = kl0.clone()
-        total_ms, reps = 0.0, max(args.steps // 4, 10)
-        for rep in range(reps + 3):
-            kl.copy_(kl0)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            sv.commit(ins["k_cache"], ins["v_cache"], kl, outs["path"], outs["accept_len"], outs["final_node"],
-                      stream)
-            e1.record(stream)
-            e1.synchronize()
-            if rep >= 3:
-                total_ms += e0.elapsed_time(e1)
-        path_np = outs["path"].cpu().numpy()
-        acc_np = outs["accept_len"].cpu().numpy()
-        moved = sum(int((path_np[b, 1:acc_np[b] + 1] != np.arange(1, acc_np[b] + 1)).sum()) for b in range(B))
-        elem = 2 if spec.dtype == "bf16" else 4
-        nbytes = moved * spec.hkv * spec.head_dim * elem * 2 * 2     # K and V, read and write
-        us = total_ms * 1e3 / reps
-        commit = {"us_per_call": us, "rows_moved": moved, "bytes_moved": nbytes,
-                  "GBps": nbytes / (us * 1e-6) / 1e9 if us > 0 else None}
-    # the caches were modified in place: restore them for any later use of `ins`
-    ins["k_cache"].copy_(up(case.k_cache, spec.dtype))
-    ins["v_cache"].copy_(up(case.v_cache, spec.dtype))
-
-    # the other tree rule on the same inputs (sampling): its step time and finishing stage
-    other = None
-    if spec.mode == "sampling":
-        ocfg = dict(cfg, lossless_tree=not cfg["lossless_tree"])
-        oouts = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
-        with SpecVerify(timing=True, **ocfg) as sv:
-            for _ in range(args.warmup):
-                sv.run(ins, oouts, stream)
-            torch.cuda.synchronize()
-            sv.timing_read()
-            for _ in range(args.steps):
-                sv.run(ins, oouts, stream)
-            torch.cuda.synchronize()
-            oms, on = sv.timing_read()
-        with SpecVerify(timing=False, **ocfg) as sv:
-            for _ in range(args.warmup):
-                sv.run(ins, oouts, stream)
-            torch.cuda.synchronize()
-            t3 = time.perf_counter()
-            for _ in range(args.steps):
-                sv.run(ins, oouts, stream)
-            torch.cuda.synchronize()
-            oms_step = (time.perf_counter() - t3) * 1e3 / args.steps
-        ores = {k: v.cpu().numpy() for k, v in oouts.items() if k in ("accept_len",)}
-        other = {"rule": "lossless sibling walk" if ocfg["lossless_tree"] else "independent per-node test",
-                 "value": B * T / (oms_step * 1e-3), "ms_per_step": oms_step,
-                 "stage_ms_per_launch": {k: v / max(on, 1) for k, v in oms.items()},
-                 "accepted_tokens_per_step": int(ores["accept_len"].sum() + B)}
-    torch.cuda.synchronize()
-    got = {k: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy() for k, v in outs.items()}
-
-    # the same step with the caches read through a block table: pages of the
-    # given size scattered over a pool in random order (spec_verify_run_paged)
-    paged = None
-    if args.paged_block_size:
-        from tree_attention_verification_verify_amd import paged_kv
-
-        _, pg = synth.page_case(case, args.paged_block_size, seed=(1,))
-        pool_k, pool_v, table = up(pg.k_pool, spec.dtype), up(pg.v_pool, spec.dtype), up(pg.block_table)
-        pk = paged_kv(pool_k, pool_v, table)
-        pins = {k: v for k, v in ins.items() if k not in ("k_cache", "v_cache")}
-        pcfg = dict(cfg, kv_capacity=max(cfg["kv_capacity"], pg.capacity))
-        pouts = allocate_outputs(B, T, spec.hq, spec.head_dim, spec.dtype)
-        with SpecVerify(timing=True, **pcfg) as sv:
-            for _ in range(args.warmup):
-                sv.run_paged(pins, pk, pouts, stream)
-            torch.cuda.synchronize()
-            sv.timing_read()
-            for _ in range(args.steps):
-                sv.run_paged(pins, pk, pouts, stream)
-            torch.cuda.synchronize()
-            pms, pn = sv.timing_read()
-        with SpecVerify(timing=False, **pcfg) as sv:
-            for _ in range(args.warmup):
-                sv.run_paged(pins, pk, pouts, stream)
-            torch.cuda.synchronize()
-            t4 = time.perf_counter()
-            for _ in range(args.steps):
-                sv.run_paged(pins, pk, pouts, stream)
-            torch.cuda.synchronize()
-            pms_step = (time.perf_counter() - t4) * 1e3 / args.steps
-        same = all(bool(torch.equal(pouts[k], outs[k])) for k in outs)
-        paged = {"block_size": args.paged_block_size, "pages": int(pg.num_blocks),
-                 "value": B * T / (pms_step * 1e-3), "ms_per_step": pms_step,
-                 "stage_ms_per_launch": {k: v / max(pn, 1) for k, v in pms.items()},
-                 "outputs_equal_dense": same}
-        del pool_k, pool_v, table
-
-    workload = "%s-%s" % (args.workload, spec.mode)
-    # dominant kernel by measured time
-    dominant = max(("attention", "vocab"), key=lambda k: per_launch[k])
-    if dominant == "attention":
-        ai = work["attention_flops"] / work["attention_bytes"]
-        t = per_launch["attention"] * 1e-3
-        if ai > RIDGE and spec.dtype == "bf16":
-            achieved = work["attention_flops"] / t / 1e12
-            roof = dict(bound="mfma", achieved=achieved, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=achieved / MFMA_BF16_PEAK_TFLOPS)
-        else:
-            achieved = work["attention_bytes"] / t / 1e9
-            roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
-                        frac=achieved / HBM_PEAK_GBPS)
-    else:
-        achieved = work["vocab_bytes"] / (per_launch["vocab"] * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS)
-    roof["kernel"] = stage_kernel(dominant, spec)
-    roof["ms_per_launch"] = per_launch[dominant]
-    roof["traffic"] = measured_traffic(roof["kernel"], workload)
-
-    step_bytes = work["attention_bytes"] + work["vocab_bytes"]
-    attn_t = per_launch["attention"] * 1e-3
-    hbm = dict(step_GBps=step_bytes / (ms_per_step * 1e-3) / 1e9,
-               step_frac=step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-               attention_GBps=work["attention_bytes"] / attn_t / 1e9,
-               attention_TFLOPs=work["attention_flops"] / attn_t / 1e12,
-               vocab_GBps=work["vocab_bytes"] / (per_launch["vocab"] * 1e-3) / 1e9,
-               vocab_frac=work["vocab_bytes"] / (per_launch["vocab"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-               algorithmic_bytes_per_step=step_bytes, attention_flops_per_step=work["attention_flops"])
-
+    head, st = measure(args.workload, args.mode, args, headline=True)
+    if args.profile:
+        print(json.dumps(head))
+        return
+    spec, case, B, T = st["spec"], st["case"], st["case"].parent.shape[0], st["case"].parent.shape[1]
     result = {
         "metric": "verified candidate tokens/sec + achieved HBM GB/s vs peak (verify step)",
-        "value": B * T / (ms_per_step * 1e-3),
+        "value": head["value"],
         "unit": "candidate tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": spec.dtype, "data": "synthetic",
         "config": {"workload": "%s tree verify" % args.workload, "mode": spec.mode, "batch": B, "nodes": T,
                    "q_heads": spec.hq, "kv_heads": spec.hkv, "head_dim": spec.head_dim,
                    "prefix": int(case.kv_len.max()), "vocab": spec.vocab, "temperature": spec.temperature,
                    "top_p": spec.top_p},
-        "roofline": roof,
-        "hbm": hbm,
-        "stage_ms_per_launch": per_launch,
-        "ms_per_step_with_event_records": ms_with_events,
-        "accepted_tokens_per_step": int(got["accept_len"].sum() + B),
-        "tree_rule": "lossless sibling walk" if cfg["lossless_tree"] else "independent per-node test",
+        "roofline": head["roofline"],
+        "hbm": head["hbm"],
+        "warm": head["warm"], "cold": head["cold"], "clock_ramp_steps": head["clock_ramp_steps"],
+        "stage_ms_per_launch_with_events": head["stage_ms_per_launch_with_events"],
+        "acceptance": head["acceptance"],
+        "parity": head["parity"],
+        "plan": head["plan"],
+        "tree_rule": head["tree_rule"],
     }
-    if other is not None:
-        result["other_tree_rule"] = other
-    result["hip_graph"] = graph
-    result["kv_commit"] = commit
+    result["hip_graph"] = time_graph(st, args)
+    result["kv_commit"] = time_commit(st, args)
+    if spec.mode == "sampling":
+        result["other_tree_rule"] = time_other_rule(st, args)
     if spec.tree[0] == "medusa":
-        result["tree_build"] = time_tree_build(spec, B, args.steps, stream)
-    if paged is not None:
-        result["paged_kv"] = paged
+        result["tree_build"] = time_tree_build(spec, B, args, st["stream"])
+    if args.paged_block_size:
+        result["paged_kv"] = time_paged(st, args)
     if not args.no_cpu_baseline:
-        base, ok, err = cpu_baseline(case, got)
-        result["cpu_baseline"] = base
-        result["parity_sample"] = {"ok": bool(ok), "attn_max_abs_err": err}
-    result["input_generation_s"] = t_gen
+        result["cpu_baseline"] = cpu_baseline(case)
+    result["input_generation_s"] = head["input_generation_s"]
+    del st
+    if not args.no_subrecords:
+        import torch
+
+        subs = []
+        for name, mode in SUBRECORDS:
+            if name == args.workload and (mode or None) == (args.mode or None):
+                continue
+            rec, sst = measure(name, mode, args)
+            del sst
+            torch.cuda.empty_cache()
+            subs.append(rec)
+        result["configs"] = subs
     print(json.dumps(result))
 
 

@@ -342,6 +342,17 @@ int spec_verify_destroy(spec_verify_handle* h);
  * the boundary: every failure is a return code plus this message. */
 const char* spec_verify_last_error(void);
 
+/* Host only (no kernel is launched): the plan a run on this handle with
+ * `batch` sequences of `nodes` nodes would follow, as a JSON object written
+ * into buf (host memory, NUL-terminated): the names of the kernels it
+ * launches ("" for a part that is skipped), the attention's waves per
+ * workgroup, row blocks, prefix splits and keys per split, whether the
+ * finishing launch selects and/or merges splits.  For tools that report
+ * per-kernel figures (the pages ask for the latency of each round:
+ * "投机解码的五条路线", section "怎么选,以及怎么算收益").  Errors: INVALID_ARG
+ * (NULL argument, batch or nodes out of range, buffer too small). */
+int spec_verify_describe(spec_verify_handle* h, int32_t batch, int32_t nodes, char* buf, int32_t buf_len);
+
 /* Per-round latency of the verify step, by stage (the pages ask for the
  * latency of each round next to the accept lengths: "投机解码的五条路线",
  * section "怎么选,以及怎么算收益").

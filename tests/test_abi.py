@@ -92,6 +92,7 @@ def test_null_arguments():
     assert lib.spec_verify_commit_paged(None, None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
     assert lib.spec_verify_build_tree(None, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
     assert lib.spec_verify_tree_template(None, 1, 1, None, None) == binding.SPEC_VERIFY_ERR_INVALID_ARG
+    assert lib.spec_verify_describe(None, 1, 1, None, 0) == binding.SPEC_VERIFY_ERR_INVALID_ARG
     ms = (ctypes.c_float * 4)()
     n = ctypes.c_int32()
     assert lib.spec_verify_timing_read(None, ms, ctypes.byref(n)) == binding.SPEC_VERIFY_ERR_INVALID_ARG

@@ -38,7 +38,8 @@ STAGES = ("attention", "vocab", "finish")
 
 EXPORTED = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
             "spec_verify_timing_read", "spec_verify_commit", "spec_verify_run_paged", "spec_verify_commit_paged",
-            "spec_verify_build_tree", "spec_verify_tree_template", "spec_verify_run_noalloc")
+            "spec_verify_build_tree", "spec_verify_tree_template", "spec_verify_run_noalloc",
+            "spec_verify_describe")
 
 
 class SpecVerifyError(RuntimeError):
@@ -98,6 +99,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise FileNotFoundError("%s is missing: build it with __graft_entry__.build()" % path)
+    # PyTorch brings its own HIP runtime (same soname as /opt/rocm's).  Loaded
+    # first, it is the one the library binds to: one runtime per process, the
+    # one that owns the tensors passed in.  (A second runtime initialised in the
+    # same process finds no device.)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     lib.spec_verify_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_void_p)]
     lib.spec_verify_create.restype = ctypes.c_int
@@ -124,6 +133,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_commit_paged.restype = ctypes.c_int
     lib.spec_verify_build_tree.argtypes = [ctypes.c_void_p, ctypes.POINTER(TreeArgs), ctypes.c_void_p]
     lib.spec_verify_build_tree.restype = ctypes.c_int
+    lib.spec_verify_describe.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_char_p,
+                                         ctypes.c_int32]
+    lib.spec_verify_describe.restype = ctypes.c_int
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.spec_verify_tree_template.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, i32p, i32p]
     lib.spec_verify_tree_template.restype = ctypes.c_int
@@ -175,10 +187,16 @@ def _ptr(t) -> Optional[int]:
 # or a wrong shape would make it read or write the wrong memory.  These checks
 # run before any call into the library; they use only tensor metadata.
 
-def _torch_dtype(name):
-    import torch
+_DTYPES = None
 
-    return {"bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32, "u8": torch.uint8}[name]
+
+def _torch_dtype(name):
+    global _DTYPES
+    if _DTYPES is None:
+        import torch
+
+        _DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32, "u8": torch.uint8}
+    return _DTYPES[name]
 
 
 def _check_tensor(name: str, t, dtype: str, shape, optional: bool = False, seen: Optional[list] = None) -> None:
@@ -402,6 +420,15 @@ def spec_verify_build_tree(handle, cand_logits, root_token, tree_parent, tree_ra
     _check(load_library().spec_verify_build_tree(handle, ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
 
 
+def spec_verify_describe(handle, batch: int, nodes: int) -> Dict:
+    """The plan (kernel names, splits) of a run on this handle, from the library itself."""
+    import json
+
+    buf = ctypes.create_string_buffer(1024)
+    _check(load_library().spec_verify_describe(handle, batch, nodes, buf, len(buf)))
+    return json.loads(buf.value.decode())
+
+
 def spec_verify_timing_read(handle):
     """Summed per-stage kernel milliseconds over the runs since the last read, and the run count."""
     ms = (ctypes.c_float * SPEC_VERIFY_NUM_STAGES)()
@@ -436,6 +463,36 @@ def allocate_outputs(batch: int, nodes: int, num_q_heads: int, head_dim: int, dt
     return out
 
 
+class PreparedRun:
+    """One run's arguments checked and marshalled once; each call is a single
+    library call with the prebuilt structs (for loops that repeat a run on the
+    same tensors: the tensors are kept alive by this object and must not be
+    replaced or resized while it is used)."""
+
+    def __init__(self, sv: "SpecVerify", inputs: Dict, outputs: Dict, stream=None, paged: Optional[PagedKV] = None):
+        if paged is None:
+            check_run_args(sv.cfg, inputs, outputs)
+        else:
+            check_run_args(sv.cfg, inputs, outputs, paged=True)
+            _check_paged(sv.cfg, paged)
+        lib = load_library()
+        self._keep = (sv, dict(inputs), dict(outputs), paged)
+        self._i, self._o = _inputs(inputs), _outputs(outputs)
+        s = ctypes.c_void_p(_stream_handle(stream))
+        if paged is None:
+            args = (sv.handle, ctypes.byref(self._i), ctypes.byref(self._o), s)
+            self._fn = lib.spec_verify_run
+        else:
+            args = (sv.handle, ctypes.byref(self._i), ctypes.byref(paged), ctypes.byref(self._o), s)
+            self._fn = lib.spec_verify_run_paged
+        self._args = args
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != SPEC_VERIFY_OK:
+            _check(rc)
+
+
 class SpecVerify:
     """Handle owner: create on construction, destroy on close()."""
 
@@ -450,8 +507,15 @@ class SpecVerify:
     def run_paged(self, inputs: Dict, paged: PagedKV, outputs: Dict, stream=None) -> None:
         spec_verify_run_paged(self.handle, inputs, paged, outputs, stream, config=self.cfg)
 
+    def prepare(self, inputs: Dict, outputs: Dict, stream=None, paged: Optional[PagedKV] = None) -> PreparedRun:
+        """A callable that repeats run (or run_paged) on these tensors with no per-call marshalling."""
+        return PreparedRun(self, inputs, outputs, stream, paged)
+
     def timing_read(self):
         return spec_verify_timing_read(self.handle)
+
+    def describe(self, batch: int, nodes: int) -> Dict:
+        return spec_verify_describe(self.handle, batch, nodes)
 
     def commit(self, k_cache, v_cache, kv_len, path, accept_len, final_node, stream=None) -> None:
         spec_verify_commit(self.handle, k_cache, v_cache, kv_len, path, accept_len, final_node, stream,

@@ -135,6 +135,7 @@ hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
 bool valu_tiled_supported(bool bf16, int D, int R);
 hipError_t launch_attention_valu_tiled(const AttnParams& p, bool bf16, hipStream_t s);
 hipError_t launch_row_stats(const StatsParams& p, hipStream_t s);
+const char* row_stats_kernel_name(const StatsParams& p);   // the kernel launch_row_stats takes
 // probs[B,T,V] = effective target distribution of every row (after launch_row_stats).
 hipError_t launch_write_probs(const StatsParams& p, float* probs, hipStream_t s);
 // The step's last launch: selection (decisions, path, final draw) and, when
@@ -143,6 +144,7 @@ hipError_t launch_finish(const SelectParams& sp, const AttnParams& ap, bool sele
                          hipStream_t s);
 // Lossless sibling walk (sampling mode, SPEC_VERIFY_FLAG_LOSSLESS_TREE): one workgroup per sequence.
 hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s);
+const char* lossless_walk_kernel_name(const SelectParams& p);   // the kernel launch_lossless_walk takes
 // Workgroups of the walk across workgroups one CU holds at once (its register,
 // LDS and wave use, from the runtime's occupancy calculation).
 hipError_t walk_coop_blocks_per_cu(int* blocks);

@@ -1072,6 +1072,11 @@ hipError_t walk_coop_blocks_per_cu(int* blocks) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, lossless_walk_coop_kernel, CT, 0);
 }
 
+const char* lossless_walk_kernel_name(const SelectParams& p) {
+    if (p.walk_coop && p.V > kWalkSlice) return "lossless_walk_coop_kernel";
+    return p.V <= CHUNK ? "lossless_walk_resident_kernel" : "lossless_walk_kernel";
+}
+
 hipError_t launch_lossless_walk(const SelectParams& p, hipStream_t s) {
     if (p.walk_coop && p.V > kWalkSlice)
         hipLaunchKernelGGL(lossless_walk_coop_kernel, dim3(p.B * p.walk_k), dim3(CT), 0, s, p);

@@ -813,6 +813,41 @@ int spec_verify_tree_template(const int32_t* caps, int32_t ncaps, int32_t nodes,
     return SPEC_VERIFY_OK;
 }
 
+int spec_verify_describe(spec_verify_handle* h, int32_t batch, int32_t nodes, char* buf, int32_t buf_len) {
+    g_err.clear();
+    if (!h || !buf || buf_len < 1) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "NULL argument or empty buffer");
+    const spec_verify_config& c = h->cfg;
+    if (batch < 1 || batch > c.max_batch) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "batch out of range");
+    if (nodes < 1 || nodes > c.max_nodes) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "nodes out of range");
+    const bool sampling = c.mode == SPEC_VERIFY_SAMPLING;
+    const bool do_attn = !(c.flags & SPEC_VERIFY_FLAG_SKIP_ATTENTION);
+    const bool do_vocab = !(c.flags & SPEC_VERIFY_FLAG_SKIP_VOCAB);
+    const bool walk = do_vocab && sampling && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE);
+    const AttnPlan plan = plan_attention(c, batch, nodes, h->ws.part_rows_cap);
+    sv::StatsParams tp{};
+    tp.V = c.vocab;
+    tp.sampling = sampling ? 1 : 0;
+    tp.top_p = sampling ? c.top_p : 1.f;
+    sv::SelectParams sp{};
+    sp.V = c.vocab;
+    sp.walk_coop = ((long)batch * h->ws.walk_k <= h->ws.walk_cap) ? 1 : 0;
+    const char* attn = !do_attn ? "" : plan.mfma ? "attn_mfma_kernel" : plan.tiled ? "attn_valu_tiled_kernel"
+                                                                                   : "attn_valu_kernel";
+    const bool merge = do_attn && plan.nsplit > 1;
+    const bool select = do_vocab && !walk;
+    const int n = std::snprintf(
+        buf, (size_t)buf_len,
+        "{\"attention\": \"%s\", \"waves\": %d, \"rowblocks\": %d, \"nsplit\": %d, \"chunk\": %d, "
+        "\"vocab\": \"%s\", \"probs\": \"%s\", \"finish\": \"%s\", \"select\": %d, \"merge\": %d, "
+        "\"walk\": \"%s\"}",
+        attn, do_attn ? plan.waves : 0, do_attn ? plan.rowblocks : 0, do_attn ? plan.nsplit : 0,
+        do_attn ? plan.chunk : 0, do_vocab ? sv::row_stats_kernel_name(tp) : "",
+        (c.flags & SPEC_VERIFY_FLAG_WRITE_PROBS) ? "write_probs_kernel" : "", (select || merge) ? "finish_kernel" : "",
+        select ? 1 : 0, merge ? 1 : 0, walk ? sv::lossless_walk_kernel_name(sp) : "");
+    if (n < 0 || n >= buf_len) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "buffer too small");
+    return SPEC_VERIFY_OK;
+}
+
 int spec_verify_timing_read(spec_verify_handle* h, float* stage_ms, int32_t* runs) {
     g_err.clear();
     if (!h || !stage_ms || !runs) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "NULL argument");

@@ -608,17 +608,35 @@ __global__ __launch_bounds__(ST) void write_probs_kernel(StatsParams P, float* p
 
 }  // namespace
 
+namespace {
+// Which row-statistics kernel a launch takes: with top-p (sampling mode) the
+// cut needs the row on chip (up to rows::CHUNK ids) or streamed; otherwise
+// one streaming read.
+enum StatsKind { kStatsTopp, kStatsToppChunked, kStatsStream };
+StatsKind stats_kind(const StatsParams& p) {
+    if (p.sampling && p.top_p < 1.f) return p.V <= rows::CHUNK ? kStatsTopp : kStatsToppChunked;
+    return kStatsStream;
+}
+}  // namespace
+
+const char* row_stats_kernel_name(const StatsParams& p) {
+    switch (stats_kind(p)) {
+    case kStatsTopp: return "row_stats_topp_kernel";
+    case kStatsToppChunked: return "row_stats_topp_chunked_kernel";
+    default: return "row_stats_stream_kernel";
+    }
+}
+
 hipError_t launch_row_stats(const StatsParams& p, hipStream_t s) {
     const int nrows = p.sampling ? 2 * p.T : p.T;
     dim3 grid((unsigned)(p.B * nrows));
-    if (p.sampling && p.top_p < 1.f && p.V <= rows::CHUNK)
-        hipLaunchKernelGGL(row_stats_topp_kernel, grid, dim3(rows::NT), 0, s, p);
-    else if (p.sampling && p.top_p < 1.f)
-        hipLaunchKernelGGL(row_stats_topp_chunked_kernel, grid, dim3(rows::NT), 0, s, p);
-    else if (p.sampling)
-        hipLaunchKernelGGL(row_stats_stream_kernel<true>, grid, dim3(ST), 0, s, p);
-    else
-        hipLaunchKernelGGL(row_stats_stream_kernel<false>, grid, dim3(ST), 0, s, p);
+    switch (stats_kind(p)) {
+    case kStatsTopp: hipLaunchKernelGGL(row_stats_topp_kernel, grid, dim3(rows::NT), 0, s, p); break;
+    case kStatsToppChunked: hipLaunchKernelGGL(row_stats_topp_chunked_kernel, grid, dim3(rows::NT), 0, s, p); break;
+    default:
+        if (p.sampling) hipLaunchKernelGGL(row_stats_stream_kernel<true>, grid, dim3(ST), 0, s, p);
+        else hipLaunchKernelGGL(row_stats_stream_kernel<false>, grid, dim3(ST), 0, s, p);
+    }
     return hipGetLastError();
 }
 
