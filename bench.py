@@ -79,6 +79,16 @@ def parse():
                     help="write profiles/traffic_<kernel>_<workload>.json from rocprofv3 --pmc counter CSVs "
                          "(kernel: --kernel)")
     ap.add_argument("--kernel", default="attn_mfma_kernel", help="kernel of --traffic-summary")
+    ap.add_argument("--ramp-seconds", type=float, default=0.2,
+                    help="untimed steps before each timed part (0 for counter collection)")
+    ap.add_argument("--trace-summary", nargs=4, default=None,
+                    metavar=("KERNEL_TRACE_CSV", "OUT_MD", "TITLE", "COMMAND"),
+                    help="write a markdown summary of a rocprofv3 --kernel-trace csv: duration per "
+                         "(kernel, grid) with the command that made it")
+    ap.add_argument("--counter-summary", nargs=4, default=None,
+                    metavar=("COUNTER_CSV", "OUT_MD", "TITLE", "COMMAND"),
+                    help="write a markdown summary of a rocprofv3 --pmc csv (mean per (kernel, grid)), with "
+                         "clock and MFMA-pipe share derived from the same dispatches")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="instead of the verify step, run a plain device copy of this many bytes "
                          "(--steps times): the reference kernel for scaling HBM counters")
@@ -261,11 +271,15 @@ def parity_check(case, got):
             "attn_rows_checked": len(nodes) * spec.hq, "attn_max_abs_err": err, "attn_tol": ATTN_TOL[spec.dtype]}
 
 
-def clock_ramp(run, seconds=0.2):
+RAMP_SECONDS = 0.2
+
+
+def clock_ramp(run, seconds=None):
     """Steps for `seconds` of wall time (untimed): brings the GPU out of its idle
     clocks after host-side work (the parity check) before anything is timed."""
     import torch
 
+    seconds = RAMP_SECONDS if seconds is None else seconds
     n = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
@@ -699,8 +713,97 @@ def traffic_summary(paths, workload, kname):
     print(json.dumps(rec))
 
 
+def _short(name):
+    name = name.replace("void ", "").replace("sv::(anonymous namespace)::", "")
+    return name if len(name) <= 90 else name[:87] + "..."
+
+
+def _trace_rows(path):
+    """(kernel, grid threads) -> list of durations in us, from a rocprofv3 kernel-trace csv."""
+    import csv
+
+    groups = {}
+    for r in csv.DictReader(open(path)):
+        grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+        key = (_short(r["Kernel_Name"]), grid)
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return groups
+
+
+def trace_summary(csv_path, out_md, title, command):
+    groups = _trace_rows(csv_path)
+    total = sum(sum(v) for v in groups.values())
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    lines = ["# Kernel trace: %s" % title, "",
+             "Command (on the MI355X, from the repository root, with `TMPDIR=/tmp`):", "", "```", command, "```", "",
+             "Per (kernel, grid size in threads), from the per-dispatch records of `run_kernel_trace.csv`",
+             "(durations in microseconds; written by `python3 bench.py --trace-summary`):", "",
+             "| kernel | grid | calls | median us | mean us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (name, grid), d in rows[:16]:
+        lines.append("| `%s` | %d | %d | %.2f | %.2f | %.2f | %.2f | %.1f |" % (
+            name, grid, len(d), statistics.median(d), sum(d) / len(d), min(d), max(d), 100.0 * sum(d) / total))
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("wrote", out_md)
+
+
+def counter_summary(csv_path, out_md, title, command, n_xcd=8, n_simd=1024):
+    """Mean counters per (kernel, grid) of a rocprofv3 --pmc csv.  Derived, from the same
+    dispatches: clock = GRBM_GUI_ACTIVE / XCDs / dispatch duration (the counter sums the XCDs;
+    the duration is the dispatch's own, under counter collection); MFMA pipe share =
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs); VALU per MFMA."""
+    import csv
+
+    vals, durs = {}, {}
+    for r in csv.DictReader(open(csv_path)):
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+        vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        durs.setdefault(key, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    lines = ["# Counters: %s" % title, "", "Command (on the MI355X, from the repository root, with `TMPDIR=/tmp`):",
+             "", "```", command, "```", "",
+             "Mean per dispatch, per (kernel, grid size in threads); written by `python3 bench.py --counter-summary`.",
+             "Derived from the same dispatches (durations under counter collection): MFMA rate = SQ_INSTS_MFMA x "
+             "32768 / duration; for dispatches of 100 us or more, clock = GRBM_GUI_ACTIVE / %d XCDs / duration "
+             "and MFMA pipe share = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d x %d SIMDs); VALU per "
+             "MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA." % (n_xcd, n_xcd, n_simd), ""]
+    order = sorted(vals.items(), key=lambda kv: -sum(durs[kv[0]].values()))
+    for (name, grid), cs in order[:4]:
+        d = list(durs[(name, grid)].values())
+        lines += ["## `%s`, grid %d" % (name, grid), "", "| counter | mean per dispatch | dispatches |", "|---|---|---|"]
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        for c in sorted(cs):
+            lines.append("| %s | %.6g | %d |" % (c, mean[c], len(cs[c])))
+        dur = sum(d) / len(d)
+        lines.append("| duration (us) | %.2f | %d |" % (dur, len(d)))
+        if mean.get("SQ_INSTS_MFMA", 0) > 0:
+            # every MFMA of these kernels is v_mfma_f32_32x32x16_bf16: 32768 flops per wave instruction
+            lines.append("| MFMA rate (TFLOP/s, 32768 flops per instruction) | %.1f | |"
+                         % (mean["SQ_INSTS_MFMA"] * 32768 / (dur * 1e-6) / 1e12))
+        if "GRBM_GUI_ACTIVE" in mean and dur >= 100.0:
+            # the GRBM window holds the collection's setup around the dispatch: an upper
+            # bound on the clock (and a lower bound on the pipe share), close for long kernels
+            cyc = mean["GRBM_GUI_ACTIVE"] / n_xcd
+            lines.append("| clock (GHz, upper bound) | %.3f | |" % (cyc / (dur * 1e3)))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                lines.append("| MFMA pipe share (lower bound) | %.3f | |"
+                             % (mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * n_simd)))
+        if mean.get("SQ_INSTS_MFMA", 0) > 0 and "SQ_INSTS_VALU" in mean:
+            lines.append("| VALU per MFMA | %.2f | |" % (mean["SQ_INSTS_VALU"] / mean["SQ_INSTS_MFMA"]))
+        lines.append("")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("wrote", out_md)
+
+
 def main():
+    global RAMP_SECONDS
     args = parse()
+    RAMP_SECONDS = args.ramp_seconds
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(*args.counter_summary)
+        return
     if args.traffic_summary:
         import synth
         spec = synth.workload(args.workload, **({"mode": args.mode} if args.mode else {}))
