@@ -59,8 +59,6 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
 
 // ---------------------------------------------------------------- MFMA path
 
-constexpr float kLazyMax = 8.f;   // log2 headroom of the lazily raised softmax reference
-
 // H halves of WAVES waves each: with H = 2 the halves take the two halves of
 // the split's tiles and merge their (O, m, l) through LDS at the end, so a
 // workgroup of 8 waves covers what two 4-wave workgroups and a merge pass
@@ -293,13 +291,15 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
         for (int f = 0; f < 16 * NSUB; f += 2) mx = fmax3(mx, s[f / 16][f % 16], s[f / 16][f % 16 + 1]);
         return fmaxf(mx, __shfl_xor(mx, 32, kWave));
     };
-    // Online softmax in the log2 domain.  The exponent reference m_run is
-    // raised lazily, only when a score of the tile exceeds it by more than
-    // 2^kLazyMax, so most tiles need no rescale of O and weights stay below
-    // 2^kLazyMax.
+    // Online softmax in the log2 domain.  The exponent reference m_run is set
+    // from the first tile's maximum and raised only when a tile's weights
+    // would grow too large (see the step), so no per-tile maximum is taken:
+    // weights exp2(s*c - m_run) of a lane stay below 2^64 in sum (exact enough
+    // as bf16 products with fp32 sums), and a weight that underflows to 0 lies
+    // below 2^-126 of the largest one seen.
     auto raise_reference = [&](float mx) {
         const float mt = mx * P.c;
-        if (__any(mt > m_run + kLazyMax)) {
+        if (__any(mt > m_run)) {
             const float m_new = fmaxf(m_run, mt);
             const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
@@ -317,37 +317,50 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
     // in k_lds[(t/KT)&1] and V(t) in v_lds[(t/KT)&1]; a buffer is refilled
     // only after the barrier that follows its last read, and the loop is
     // unrolled by two so that every LDS access names its buffer statically.
-    // Step t, after masking tile t and raising the reference if needed:
+    // The weights of a tile are taken in two halves (sub-tile 0: keys 0..31,
+    // sub-tile 1: keys 32..63), so that every MFMA of both phases has its
+    // share of exp2 beside it (one at D = 128, two at D = 64).  Step t:
     //   phase A: the QK^T products of tile t+1, each with the K read two
     //            products ahead, a share of the block loads of K(t+2) and
-    //            V(t+1), and the weights of EPS scores of tile t (exp2, bf16
-    //            pack, row sum over the packed weights by dot2);
-    //   phase B: the PV products of tile t, each with the V read two products
-    //            ahead and a share of the maximum of tile t+1.
+    //            V(t+1), and its share of tile t's sub-tile 1 weights (exp2;
+    //            for each pair the bf16 pack and the row sum by dot2);
+    //   check:   a lane whose weights of tile t sum to 2^64 or more (scores far
+    //            above the reference), or that has no reference yet, makes the
+    //            wave take tile t's maximum, raise the reference and weigh the
+    //            tile again (rare: once per row block in practice);
+    //   phase B: masking of tile t+1 if it reaches the tree slots or the split
+    //            end, then the PV products of tile t (sub-tile 0's weights
+    //            first), each with its two transposed V reads two products
+    //            ahead and its share of tile t+1's sub-tile 0 weights.
     // Scheduling fences keep this order, so the matrix cores and the vector
     // ALU work side by side within the wave.  Products of a tile past the
     // split read stale or zero data and are never used.
     constexpr int PF = 2;                        // operand reads in flight
-    constexpr int EPS = 16 * NSUB / NQK;         // scores weighted per QK^T product
-    constexpr int MX0 = NPV / 4;                 // first PV slot that takes max work
-    constexpr int NMX = NPV / 2;                 // PV slots that take max work
-    constexpr int EPM = 16 * NSUB / NMX;         // scores per max slot
-    static_assert(EPS % 2 == 0 && EPM % 2 == 0, "pairs");
+    constexpr int WA = 16 / NQK, WB = 16 / NPV;  // weights beside each product of phase A / phase B
+    static_assert(WA * NQK == 16 && WB * NPV == 16, "16 weights per sub-tile spread over each phase");
+    // weight f (0..31) of a tile: exp2, and for odd f the bf16 pair and its row sum
+    auto weigh_one = [&](const floatx16_t (&s)[NSUB], float (&w)[2], bf16x2_t (&wp)[8 * NSUB], float (&ps)[2], int f) {
+        w[f & 1] = __builtin_amdgcn_exp2f(fmaf(s[f / 16][f % 16], P.c, neg_m));
+        if (f & 1) {
+            wp[f / 2] = __builtin_convertvector((floatx2_t){w[0], w[1]}, bf16x2_t);
+            ps[(f / 2) & 1] = __builtin_amdgcn_fdot2_f32_bf16(wp[f / 2], ones2, ps[(f / 2) & 1], false);
+        }
+    };
+    auto weigh_all = [&](const floatx16_t (&s)[NSUB], bf16x2_t (&wp)[8 * NSUB], float (&ps)[2]) {
+        float w[2];
+        ps[0] = ps[1] = 0.f;
+#pragma unroll
+        for (int f = 0; f < 16 * NSUB; ++f) weigh_one(s, w, wp, ps, f);
+    };
     auto step = [&](int t, const uint8_t* k_next, const uint8_t* v_cur, uint8_t* k_fill, uint8_t* v_fill,
-                    floatx16_t (&s_cur)[NSUB], floatx16_t (&s_next)[NSUB], float& mx_cur, float& mx_next,
-                    int pg_cur, int& pg_next) {
+                    floatx16_t (&s_cur)[NSUB], floatx16_t (&s_next)[NSUB], bf16x2_t (&wp_cur)[8 * NSUB],
+                    bf16x2_t (&wp_next)[8 * NSUB], float (&ps_cur)[2], float (&ps_next)[2], int pg_cur, int& pg_next) {
         int pages[LOADS];   // wave-uniform page entries of this step's block loads
 #pragma unroll
         for (int l = 0; l < LOADS; ++l) pages[l] = PAGED ? __builtin_amdgcn_readlane(pg_cur, l) : -1;
         if constexpr (PAGED) pg_next = load_pages(t + 3 * KT, t + 2 * KT);
-        if (t + KT > L || t + KT > k1) {
-            mask_tile(t, s_cur);
-            mx_cur = tile_max(s_cur);
-        }
-        raise_reference(mx_cur);
         bf16x8_t ka[NQK];
-        bf16x2_t wp[8 * NSUB];
-        float ps[2] = {0.f, 0.f};
+        float w[2];
 #pragma unroll
         for (int i = 0; i < PF; ++i) ka[i] = read_k(k_next, i);
 #pragma unroll
@@ -359,41 +372,38 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
             s_next[i % NSUB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qb[i / NSUB],
                                                                        i < NSUB ? zero16 : s_next[i % NSUB], 0, 0, 0);
 #pragma unroll
-            for (int f = EPS * i; f < EPS * (i + 1); f += 2) {
-                const float w0 = __builtin_amdgcn_exp2f(fmaf(s_cur[f / 16][f % 16], P.c, neg_m));
-                const float w1 = __builtin_amdgcn_exp2f(fmaf(s_cur[f / 16][f % 16 + 1], P.c, neg_m));
-                wp[f / 2] = __builtin_convertvector((floatx2_t){w0, w1}, bf16x2_t);
-                ps[(f / 2) & 1] = __builtin_amdgcn_fdot2_f32_bf16(wp[f / 2], ones2, ps[(f / 2) & 1], false);
-            }
+            for (int f = 16 + WA * i; f < 16 + WA * (i + 1); ++f) weigh_one(s_cur, w, wp_cur, ps_cur, f);
             __builtin_amdgcn_sched_barrier(0);
         }
-        l_run += ps[0] + ps[1];
+        if (__any(!(ps_cur[0] + ps_cur[1] < 0x1p64f) || m_run == -INFINITY)) {
+            raise_reference(tile_max(s_cur));
+            weigh_all(s_cur, wp_cur, ps_cur);
+        }
+        l_run += ps_cur[0] + ps_cur[1];
+        if (t + 2 * KT > L || t + 2 * KT > k1) mask_tile(t + KT, s_next);
+        ps_next[0] = ps_next[1] = 0.f;
         bf16x8_t va[NPV];
 #pragma unroll
         for (int i = 0; i < PF; ++i) va[i] = read_v(v_cur, i);
-        float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             if (i + PF < NPV) va[i + PF] = read_v(v_cur, i + PF);
             const int j = i / DT;   // 16-key step: pairs 4j .. 4j+3
-            const bf16x8_t pbj = {wp[4 * j][0], wp[4 * j][1], wp[4 * j + 1][0], wp[4 * j + 1][1],
-                                  wp[4 * j + 2][0], wp[4 * j + 2][1], wp[4 * j + 3][0], wp[4 * j + 3][1]};
+            const bf16x8_t pbj = {wp_cur[4 * j][0], wp_cur[4 * j][1], wp_cur[4 * j + 1][0], wp_cur[4 * j + 1][1],
+                                  wp_cur[4 * j + 2][0], wp_cur[4 * j + 2][1], wp_cur[4 * j + 3][0],
+                                  wp_cur[4 * j + 3][1]};
             o[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pbj, o[i % DT], 0, 0, 0);
-            if (i >= MX0 && i < MX0 + NMX) {
 #pragma unroll
-                for (int f = EPM * (i - MX0); f < EPM * (i - MX0 + 1); f += 2)
-                    mx = fmax3(mx, s_next[f / 16][f % 16], s_next[f / 16][f % 16 + 1]);
-                asm volatile("" : "+v"(mx));   // keeps this share of the maximum in its slot
-            }
+            for (int f = WB * i; f < WB * (i + 1); ++f) weigh_one(s_next, w, wp_next, ps_next, f);
             __builtin_amdgcn_sched_barrier(0);
         }
-        mx_next = fmaxf(mx, __shfl_xor(mx, 32, kWave));
         __builtin_amdgcn_s_waitcnt(0);    // K(t+2) and V(t+1) have landed
         __syncthreads();
     };
 
     floatx16_t sa[NSUB], sb[NSUB];
-    float mxa, mxb;
+    bf16x2_t wa[8 * NSUB], wb[8 * NSUB];
+    float psa[2] = {0.f, 0.f}, psb[2] = {0.f, 0.f};
     int pga = -1, pgb = -1;
     if constexpr (PAGED) {
         const int p0 = load_pages(k0, k0), p1 = load_pages(k0 + KT, k0 + KT);
@@ -415,14 +425,22 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
     for (int i = 0; i < NQK; ++i)
         sa[i % NSUB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_k(k_lds0, i), qb[i / NSUB],
                                                                i < NSUB ? zero16 : sa[i % NSUB], 0, 0, 0);
-    mxa = tile_max(sa);
+    // the reference starts at the first tile's maximum (after its masking);
+    // sub-tile 0 of the first tile is weighed here, the rest in the first step
+    if (k0 + KT > L || k0 + KT > k1) mask_tile(k0, sa);
+    raise_reference(tile_max(sa));
+    {
+        float w[2];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) weigh_one(sa, w, wa, psa, f);
+    }
     __builtin_amdgcn_s_waitcnt(0);       // every wave is done with K(k0) before it is refilled
     __syncthreads();
     for (int st = 0; st < nsteps; st += 2) {
         const int t = k0 + st * KT;
-        step(t, k_lds1, v_lds0, k_lds0, v_lds1, sa, sb, mxa, mxb, pga, pgb);
+        step(t, k_lds1, v_lds0, k_lds0, v_lds1, sa, sb, wa, wb, psa, psb, pga, pgb);
         if (st + 1 >= nsteps) break;
-        step(t + KT, k_lds0, v_lds1, k_lds1, v_lds0, sb, sa, mxb, mxa, pgb, pga);
+        step(t + KT, k_lds0, v_lds1, k_lds1, v_lds0, sb, sa, wb, wa, psb, psa, pgb, pga);
     }
 
     float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
