@@ -40,7 +40,9 @@ __device__ __forceinline__ int lane_() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_() { return threadIdx.x >> 6; }
 
 // element index of (slot j, component e) for this thread in chunk cb
-__device__ __forceinline__ int elem_index(int cb, int j, int e) { return cb + 4 * (tid_() + NT * j) + e; }
+// (TPB threads per workgroup)
+template <int TPB = NT>
+__device__ __forceinline__ int elem_index(int cb, int j, int e) { return cb + 4 * (tid_() + TPB * j) + e; }
 
 __device__ __forceinline__ float f4get(const float4& v, int e) {
     return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
@@ -119,7 +121,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tail_rsrc(uint64_t a, int V, i
 // reads past the row return 0 (mask_chunk replaces them): a chunk past the
 // end may be loaded too.  There is no branch between the loads: all of them
 // are in flight before the first is used.
-template <int N = VPT4>
+template <int N = VPT4, int TPB = NT>
 __device__ __forceinline__ void issue_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[N]) {
     const uint64_t a = uniform_addr(row);
     const int c0 = __builtin_amdgcn_readfirstlane(cb);
@@ -127,11 +129,11 @@ __device__ __forceinline__ void issue_chunk(const float* row, int V, int cb, boo
     if (aligned && (V & 3) == 0) {
 #pragma unroll
         for (int j = 0; j < N; ++j)
-            x[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(tail_rsrc(a, V, c0 + 4 * NT * j), vo, 0, 0));
+            x[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(tail_rsrc(a, V, c0 + 4 * TPB * j), vo, 0, 0));
     } else {
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-            const __amdgpu_buffer_rsrc_t rs = tail_rsrc(a, V, c0 + 4 * NT * j);
+            const __amdgpu_buffer_rsrc_t rs = tail_rsrc(a, V, c0 + 4 * TPB * j);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 f4set(x[j], e, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 4 * e, 0, 0)));
@@ -140,20 +142,21 @@ __device__ __forceinline__ void issue_chunk(const float* row, int V, int cb, boo
 }
 
 // Entries of the block at cb past V become -inf (nothing to do for a full block).
-template <int N = VPT4>
+template <int N = VPT4, int TPB = NT>
 __device__ __forceinline__ void mask_chunk(int V, int cb, float4 (&x)[N]) {
-    if (cb + NT * N * 4 <= V) return;
+    if (cb + TPB * N * 4 <= V) return;
 #pragma unroll
     for (int j = 0; j < N; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (elem_index(cb, j, e) >= V) f4set(x[j], e, -INFINITY);
+            if (elem_index<TPB>(cb, j, e) >= V) f4set(x[j], e, -INFINITY);
 }
 
-// Load chunk cb of a row: out-of-range entries become -inf.
-__device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[VPT4]) {
-    issue_chunk(row, V, cb, aligned, x);
-    mask_chunk(V, cb, x);
+// Load chunk cb of a row (N float4 per thread, TPB threads): out-of-range entries become -inf.
+template <int N = VPT4, int TPB = NT>
+__device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool aligned, float4 (&x)[N]) {
+    issue_chunk<N, TPB>(row, V, cb, aligned, x);
+    mask_chunk<N, TPB>(V, cb, x);
 }
 
 // f(x, cb) for every block of N float4 per thread (4 N NT ids at cb) of a row

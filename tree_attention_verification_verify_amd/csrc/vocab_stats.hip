@@ -251,7 +251,7 @@ __device__ __forceinline__ void topp_accumulate_list(const uint32_t* list, uint3
 // to its list after the n already there (positions by ballot); returns how
 // many there are now (the list holds them when that is at most kListCap).
 // The same in every lane.
-template <int N = rows::VPT4>
+template <int N = rows::VPT4, int CAP = kListCap>
 __device__ __forceinline__ uint32_t topp_compact(const float4 (&e)[N], uint32_t b1, uint32_t* list, uint32_t n = 0) {
     using namespace rows;
 #pragma unroll
@@ -264,7 +264,7 @@ __device__ __forceinline__ uint32_t topp_compact(const float4 (&e)[N], uint32_t 
             if (m) {
                 const uint32_t pos = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-                if (pos < (uint32_t)kListCap) list[pos] = bits;
+                if (pos < (uint32_t)CAP) list[pos] = bits;
             }
             n += (uint32_t)__popcll(mask);
         }
@@ -272,42 +272,61 @@ __device__ __forceinline__ uint32_t topp_compact(const float4 (&e)[N], uint32_t 
 }
 
 // The crossing bucket lands in sm.sel_*[L].  Returns need (level 0: the one
-// it computed).
-template <int L>
+// it computed).  TPB threads: each takes 1024 / TPB consecutive buckets in
+// descending order (thread order = descending bucket).
+template <int L, int TPB = rows::NT>
 __device__ __forceinline__ double topp_scan(double need, float top_p, ToppSmem& sm) {
     using namespace rows;
     constexpr int HC = L == 0 ? HK : 1;
+    constexpr int BPT = 1024 / TPB, NWB = TPB / kWave;
+    static_assert(BPT * TPB == 1024 && NWB <= TNW, "buckets per thread");
     unsigned long long* h = L == 0 ? sm.h1 : (L == 1 ? sm.h2 : sm.h3);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     __syncthreads();
-    const int bk = 1023 - tid;   // thread order = descending bucket
+    const int bk0 = 1023 - BPT * tid;   // this thread's largest bucket
+    unsigned long long xs[BPT];
     unsigned long long x = 0;
 #pragma unroll
-    for (int c = 0; c < HC; ++c) x += h[bk * HC + c];
+    for (int q = 0; q < BPT; ++q) {
+        xs[q] = 0;
+#pragma unroll
+        for (int c = 0; c < HC; ++c) xs[q] += h[(bk0 - q) * HC + c];
+        x += xs[q];
+    }
     unsigned long long incl = wave_scan_u64(x);
     if (lane == kWave - 1) sm.wt[L][wave] = incl;
     __syncthreads();
-    // lanes 0..TNW-1 scan the wave totals; this wave's offset and the total
+    // lanes 0..NWB-1 scan the wave totals; this wave's offset and the total
     // are then read from single lanes
-    const unsigned long long wsc = wave_scan_u64(lane < TNW ? sm.wt[L][lane] : 0ull);
+    const unsigned long long wsc = wave_scan_u64(lane < NWB ? sm.wt[L][lane] : 0ull);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const unsigned long long total = readlane_u64(wsc, TNW - 1);
+    const unsigned long long total = readlane_u64(wsc, NWB - 1);
     incl += wv > 0 ? readlane_u64(wsc, wv - 1) : 0ull;
     const unsigned long long excl = incl - x;
     if (L == 0) need = (double)top_p * (double)total;
-    // (double)excl and (double)incl tile (0, (double)total] without gaps, so a
-    // crossing exists exactly when need lies in that range, and is unique
+    // the integer bounds, as doubles, tile (0, (double)total] without gaps, so
+    // a crossing exists exactly when need lies in that range, and is unique
     const bool exists = 0.0 < need && need <= (double)total;
-    if (exists ? ((double)excl < need && need <= (double)incl) : tid == NT - 1) {
-        sm.sel_bucket[L] = bk;
-        sm.sel_above[L] = excl;
-        sm.sel_mass[L] = x;
+    unsigned long long lo = excl;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+        const unsigned long long hi = lo + xs[q];
+        if (exists ? ((double)lo < need && need <= (double)hi) : (tid == TPB - 1 && q == BPT - 1)) {
+            sm.sel_bucket[L] = bk0 - q;
+            sm.sel_above[L] = lo;
+            sm.sel_mass[L] = xs[q];
+        }
+        lo = hi;
     }
     __syncthreads();
     return need;
 }
 
-__global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P) {
+// TPB threads per row, N4 = CHUNK / (4 TPB) float4 per thread.  (256
+// threads, two rows per CU, measured slower at V = 32000: 39 against 34 us
+// for 352 rows; each row's passes then take three times as long.)
+template <int TPB>
+__global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
     using namespace rows;
     __shared__ ToppSmem sm;
     const int nrows = 2 * P.T;
@@ -318,25 +337,27 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
     const float ilog = P.ilog;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const bool aligned = (((uintptr_t)row) & 15) == 0;
-    float4 e[VPT4];
-    load_chunk(row, V, 0, aligned, e);
+    constexpr int N4 = CHUNK / (4 * TPB), NWB = TPB / kWave;
+    float4 e[N4];
+    load_chunk<N4, TPB>(row, V, 0, aligned, e);
     // cleared histograms are ordered before their atomics by the next barrier
-#pragma unroll
-    for (int k = 0; k < HK; ++k) sm.h1[k * NT + tid] = 0ull;
-    sm.h2[tid] = 0ull;
-    sm.h3[tid] = 0ull;
+    for (int k = tid; k < 1024 * HK; k += TPB) sm.h1[k] = 0ull;
+    for (int k = tid; k < 1024; k += TPB) {
+        sm.h2[k] = 0ull;
+        sm.h3[k] = 0ull;
+    }
 
     // largest logit and its smallest id (the largest logit is zmax): the
     // thread's maximum, then the first of its positions (in id order) holding it
     float bv = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < VPT4; ++j) bv = fmaxf(fmaxf(bv, fmaxf(e[j].x, e[j].y)), fmaxf(e[j].z, e[j].w));
+    for (int j = 0; j < N4; ++j) bv = fmaxf(fmaxf(bv, fmaxf(e[j].x, e[j].y)), fmaxf(e[j].z, e[j].w));
     int bi = INT_MAX;
 #pragma unroll
-    for (int j = VPT4 - 1; j >= 0; --j)
+    for (int j = N4 - 1; j >= 0; --j)
 #pragma unroll
         for (int c = 3; c >= 0; --c) {
-            const int idx = elem_index(0, j, c);
+            const int idx = elem_index<TPB>(0, j, c);
             bi = (f4get(e[j], c) == bv && idx < V) ? idx : bi;
         }
 #pragma unroll
@@ -346,30 +367,33 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
     float M = sm.bv[0];
     int best = sm.bi[0];
 #pragma unroll
-    for (int w = 1; w < TNW; ++w) argmax_step(M, best, sm.bv[w], sm.bi[w]);
+    for (int w = 1; w < NWB; ++w) argmax_step(M, best, sm.bv[w], sm.bi[w]);
 #pragma unroll
-    for (int j = 0; j < VPT4; ++j)
+    for (int j = 0; j < N4; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c) f4set(e[j], c, unnorm(f4get(e[j], c), M, ilog));
 
     // the cut
-    topp_accumulate<0>(e, 0u, sm);
-    const double need = topp_scan<0>(0.0, P.top_p, sm);
+    topp_accumulate<0, N4>(e, 0u, sm);
+    const double need = topp_scan<0, TPB>(0.0, P.top_p, sm);
     const uint32_t b1 = (uint32_t)sm.sel_bucket[0];
     const unsigned long long a1 = sm.sel_above[0];
     // levels 2 and 3 only see bucket b1: each wave lists its elements there
     // once (writes and reads of a wave's own list need no barrier) and reads
     // the list, or its registers when the list is too short for them
-    const uint32_t nlist = topp_compact(e, b1, sm.list[wave]);
-    const bool listed = nlist <= (uint32_t)kListCap;
-    if (listed) topp_accumulate_list<1>(sm.list[wave], nlist, b1, sm);
-    else topp_accumulate<1>(e, b1, sm);
-    topp_scan<1>(need - (double)a1, P.top_p, sm);
+    // the list space of TNW waves shared by the NWB waves of this row
+    constexpr int CAP = TNW * kListCap / NWB;
+    uint32_t* const mylist = &sm.list[0][0] + wave * CAP;
+    const uint32_t nlist = topp_compact<N4, CAP>(e, b1, mylist);
+    const bool listed = nlist <= (uint32_t)CAP;
+    if (listed) topp_accumulate_list<1>(mylist, nlist, b1, sm);
+    else topp_accumulate<1, N4>(e, b1, sm);
+    topp_scan<1, TPB>(need - (double)a1, P.top_p, sm);
     const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
     const unsigned long long a2 = sm.sel_above[1];
-    if (listed) topp_accumulate_list<2>(sm.list[wave], nlist, (b1 << 10) | b2, sm);
-    else topp_accumulate<2>(e, (b1 << 10) | b2, sm);
-    topp_scan<2>(need - (double)a1 - (double)a2, P.top_p, sm);
+    if (listed) topp_accumulate_list<2>(mylist, nlist, (b1 << 10) | b2, sm);
+    else topp_accumulate<2, N4>(e, (b1 << 10) | b2, sm);
+    topp_scan<2, TPB>(need - (double)a1 - (double)a2, P.top_p, sm);
     Nucleus nu;
     nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
     nu.cutoff = INT_MAX;
@@ -391,10 +415,10 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
                 const int mid = lo + (hi - lo) / 2;
                 unsigned long long cnt = 0;
 #pragma unroll
-                for (int j = 0; j < VPT4; ++j)
+                for (int j = 0; j < N4; ++j)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        const int idx = elem_index(0, j, c);
+                        const int idx = elem_index<TPB>(0, j, c);
                         if (idx < V && idx <= mid && __float_as_uint(f4get(e[j], c)) == nu.thr) ++cnt;
                     }
                 cnt = wave_sum_u64(cnt);
@@ -402,7 +426,7 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_kernel(StatsParams P)
                 __syncthreads();
                 unsigned long long tot = 0;
 #pragma unroll
-                for (int w = 0; w < TNW; ++w) tot += sm.cnt[par][w];
+                for (int w = 0; w < NWB; ++w) tot += sm.cnt[par][w];
                 par ^= 1;
                 if (tot >= (unsigned long long)k) hi = mid; else lo = mid + 1;
             }
@@ -609,6 +633,7 @@ __global__ __launch_bounds__(ST) void write_probs_kernel(StatsParams P, float* p
 }  // namespace
 
 namespace {
+constexpr int kToppThreads = 1024;  // threads per row of the on-chip top-p kernel
 // Which row-statistics kernel a launch takes: with top-p (sampling mode) the
 // cut needs the row on chip (up to rows::CHUNK ids) or streamed; otherwise
 // one streaming read.
@@ -631,7 +656,7 @@ hipError_t launch_row_stats(const StatsParams& p, hipStream_t s) {
     const int nrows = p.sampling ? 2 * p.T : p.T;
     dim3 grid((unsigned)(p.B * nrows));
     switch (stats_kind(p)) {
-    case kStatsTopp: hipLaunchKernelGGL(row_stats_topp_kernel, grid, dim3(rows::NT), 0, s, p); break;
+    case kStatsTopp: hipLaunchKernelGGL(row_stats_topp_kernel<kToppThreads>, grid, dim3(kToppThreads), 0, s, p); break;
     case kStatsToppChunked: hipLaunchKernelGGL(row_stats_topp_chunked_kernel, grid, dim3(rows::NT), 0, s, p); break;
     default:
         if (p.sampling) hipLaunchKernelGGL(row_stats_stream_kernel<true>, grid, dim3(ST), 0, s, p);
