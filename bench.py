@@ -789,6 +789,23 @@ def counter_summary(csv_path, out_md, title, command, n_xcd=8, n_simd=1024):
                              % (mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * n_simd)))
         if mean.get("SQ_INSTS_MFMA", 0) > 0 and "SQ_INSTS_VALU" in mean:
             lines.append("| VALU per MFMA | %.2f | |" % (mean["SQ_INSTS_VALU"] / mean["SQ_INSTS_MFMA"]))
+        if mean.get("SQ_WAVE_CYCLES", 0) > 0:
+            # all three count quad-cycles of resident waves, summed over the waves
+            for c, what in (("SQ_WAIT_ANY", "waiting for anything"),
+                            ("SQ_WAIT_INST_ANY", "waiting for an instruction to issue"),
+                            ("SQ_WAIT_INST_LDS", "waiting for an LDS instruction to issue")):
+                if c in mean:
+                    lines.append("| share of wave cycles %s (%s / SQ_WAVE_CYCLES) | %.3f | |"
+                                 % (what, c, mean[c] / mean["SQ_WAVE_CYCLES"]))
+        if "GRBM_GUI_ACTIVE" in mean and dur >= 100.0:
+            cyc = mean["GRBM_GUI_ACTIVE"] / n_xcd
+            if "SQ_INSTS_LDS_LOAD_BANDWIDTH" in mean:   # counts 64-byte units loaded from LDS
+                lines.append("| LDS bytes loaded per CU-cycle (SQ_INSTS_LDS_LOAD_BANDWIDTH x 64 / cycles / %d CUs) "
+                             "| %.1f | |" % (n_simd // 4, mean["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64 / cyc / (n_simd // 4)))
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in mean:
+                lines.append("| share of SIMD cycles with a VALU issue beside a busy MFMA pipe "
+                             "(SQ_VALU_MFMA_COEXEC_CYCLES / cycles / %d SIMDs) | %.3f | |"
+                             % (n_simd, mean["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cyc * n_simd)))
         lines.append("")
     open(out_md, "w").write("\n".join(lines) + "\n")
     print("wrote", out_md)

@@ -60,6 +60,7 @@ def _check(logits, root, caps, nodes, label):
     (3, (2, 2), 7, 1000, 0.5),                   # the printed two-head top-2 tree
     (2, (40,), 33, 5000, 1.0),                   # 32 entries of one list
     (4, (3, 3, 3, 3), 64, 777, 0.0),
+    (4, (10, 4, 2, 1, 1), 64, 50257, 0.125),     # odd vocabulary: 8 slices, a ragged last one, scalar rows
 ])
 def test_tree_build_matches_oracle(B, caps, nodes, V, step):
     rng = np.random.default_rng(B * 1000 + V)
@@ -83,16 +84,40 @@ def test_tree_build_special_values_and_tiny_vocab():
     _check(logits, root, (4, 3, 2), 40, "tree-special")
 
 
+def _wave_share(n, aligned, waves):
+    """Ids (relative to a slice start) that the first `waves` waves of a
+    1024-thread workgroup read: thread t takes float4 columns t, t + 1024, ...
+    of a 16-byte aligned slice (then the < 4 tail ids one each), or ids t,
+    t + 1024, ... of an unaligned one; wave w is threads 64w .. 64w + 63."""
+    x = np.arange(n)
+    if aligned:
+        v4 = n // 4
+        thread = np.where(x < 4 * v4, (x // 4) % 1024, (x - 4 * v4) % 1024)
+    else:
+        thread = x % 1024
+    return thread // 64 < waves
+
+
 def test_tree_build_crowded_row_takes_the_exact_path():
-    # the 4000 largest logits all sit in the first wave's share of the row
-    # (float4 columns 0..63 of each 1024-column stride), so far more entries
-    # pass the first pass's bound than the short list holds
+    # Rows split into 8 slices (50257 ids: spans of 6284, the last one 6269).
+    # In the first and the last slice of each row, every id that the first 4
+    # of the 16 waves read gets +100: over 1500 entries of the slice then pass
+    # the first pass's bound (the smallest of the 16 wave maxima), three times
+    # what the short list holds, so both slices take the exact fallback, on
+    # the 16-byte aligned row 0 and on the unaligned rows alike.
     rng = np.random.default_rng(13)
-    B, V = 2, 32000
+    B, V, G, CAP = 2, 50257, 8, 512
+    span = ((V + G - 1) // G + 3) & ~3
     logits = rng.normal(size=(B, 2, V)).astype(np.float32)
-    cols = np.arange(V)
-    crowd = ((cols // 4) % 1024) < 64
-    logits[:, :, crowd] += 100.0
+    for b in range(B):
+        for d in range(2):
+            aligned = ((b * 2 + d) * V) % 4 == 0          # float offset of the row start
+            for sl in (0, G - 1):
+                lo = sl * span
+                n = min(V - lo, span)
+                crowd = _wave_share(n, aligned, 4)
+                assert crowd.sum() > 3 * CAP
+                logits[b, d, lo:lo + n][crowd] += 100.0
     _check(logits, np.array([1, 2]), (16, 16), 60, "tree-crowded")
 
 
