@@ -339,22 +339,26 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
     constexpr int WA = 16 / NQK, WB = 16 / NPV;  // weights beside each product of phase A / phase B
     static_assert(WA * NQK == 16 && WB * NPV == 16, "16 weights per sub-tile spread over each phase");
     // weight f (0..31) of a tile: exp2, and for odd f the bf16 pair and its row sum
-    auto weigh_one = [&](const floatx16_t (&s)[NSUB], float (&w)[2], bf16x2_t (&wp)[8 * NSUB], float (&ps)[2], int f) {
+    // Weight pair q of a tile sits in 32-bit word q % 4 of wp[q / 4], so the
+    // four pairs of a 16-key step are the PV operand as they stand (built
+    // from separate pairs, the compiler shifted and permuted them into place).
+    auto weigh_one = [&](const floatx16_t (&s)[NSUB], float (&w)[2], u32x4 (&wp)[2 * NSUB], float (&ps)[2], int f) {
         w[f & 1] = __builtin_amdgcn_exp2f(fmaf(s[f / 16][f % 16], P.c, neg_m));
         if (f & 1) {
-            wp[f / 2] = __builtin_convertvector((floatx2_t){w[0], w[1]}, bf16x2_t);
-            ps[(f / 2) & 1] = __builtin_amdgcn_fdot2_f32_bf16(wp[f / 2], ones2, ps[(f / 2) & 1], false);
+            const bf16x2_t pair = __builtin_convertvector((floatx2_t){w[0], w[1]}, bf16x2_t);
+            wp[f / 8][(f / 2) % 4] = __builtin_bit_cast(uint32_t, pair);
+            ps[(f / 2) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, ps[(f / 2) & 1], false);
         }
     };
-    auto weigh_all = [&](const floatx16_t (&s)[NSUB], bf16x2_t (&wp)[8 * NSUB], float (&ps)[2]) {
+    auto weigh_all = [&](const floatx16_t (&s)[NSUB], u32x4 (&wp)[2 * NSUB], float (&ps)[2]) {
         float w[2];
         ps[0] = ps[1] = 0.f;
 #pragma unroll
         for (int f = 0; f < 16 * NSUB; ++f) weigh_one(s, w, wp, ps, f);
     };
     auto step = [&](int t, const uint8_t* k_next, const uint8_t* v_cur, uint8_t* k_fill, uint8_t* v_fill,
-                    floatx16_t (&s_cur)[NSUB], floatx16_t (&s_next)[NSUB], bf16x2_t (&wp_cur)[8 * NSUB],
-                    bf16x2_t (&wp_next)[8 * NSUB], float (&ps_cur)[2], float (&ps_next)[2], int pg_cur, int& pg_next) {
+                    floatx16_t (&s_cur)[NSUB], floatx16_t (&s_next)[NSUB], u32x4 (&wp_cur)[2 * NSUB],
+                    u32x4 (&wp_next)[2 * NSUB], float (&ps_cur)[2], float (&ps_next)[2], int pg_cur, int& pg_next) {
         int pages[LOADS];   // wave-uniform page entries of this step's block loads
 #pragma unroll
         for (int l = 0; l < LOADS; ++l) pages[l] = PAGED ? __builtin_amdgcn_readlane(pg_cur, l) : -1;
@@ -388,10 +392,7 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             if (i + PF < NPV) va[i + PF] = read_v(v_cur, i + PF);
-            const int j = i / DT;   // 16-key step: pairs 4j .. 4j+3
-            const bf16x8_t pbj = {wp_cur[4 * j][0], wp_cur[4 * j][1], wp_cur[4 * j + 1][0], wp_cur[4 * j + 1][1],
-                                  wp_cur[4 * j + 2][0], wp_cur[4 * j + 2][1], wp_cur[4 * j + 3][0],
-                                  wp_cur[4 * j + 3][1]};
+            const bf16x8_t pbj = __builtin_bit_cast(bf16x8_t, wp_cur[i / DT]);   // 16-key step i / DT
             o[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pbj, o[i % DT], 0, 0, 0);
 #pragma unroll
             for (int f = WB * i; f < WB * (i + 1); ++f) weigh_one(s_next, w, wp_next, ps_next, f);
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
     };
 
     floatx16_t sa[NSUB], sb[NSUB];
-    bf16x2_t wa[8 * NSUB], wb[8 * NSUB];
+    u32x4 wa[2 * NSUB], wb[2 * NSUB];
     float psa[2] = {0.f, 0.f}, psb[2] = {0.f, 0.f};
     int pga = -1, pgb = -1;
     if constexpr (PAGED) {
