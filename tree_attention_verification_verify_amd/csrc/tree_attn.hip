@@ -398,6 +398,11 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
             for (int f = WB * i; f < WB * (i + 1); ++f) weigh_one(s_next, w, wp_next, ps_next, f);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // The next tile's sub-tile 0 weights are used here, on every path: without
+        // this use the compiler sinks them past the loop's exit test between the
+        // two unrolled steps, and the first step's PV products then run with no
+        // weights beside them while the second step's QK products get twice as many.
+        asm volatile("" ::"v"(wp_next[0]), "v"(wp_next[1]), "v"(ps_next[0]), "v"(ps_next[1]));
         __builtin_amdgcn_s_waitcnt(0);    // K(t+2) and V(t+1) have landed
         __syncthreads();
     };
