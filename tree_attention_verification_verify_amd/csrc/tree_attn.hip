@@ -272,7 +272,11 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
 
     // Scores: accumulator element e of lane (qcol, half) in sub-tile sub holds
     // key sub*32 + 16*(e>>3) + 8*half + (e&7).  Masking is needed only for
-    // tiles that reach the tree slots or the end of the split.
+    // tiles that reach the tree slots or the end of the split.  Each score is
+    // replaced in its own register (a select written as an instruction whose
+    // output is tied to its input): written as a plain select, the masked
+    // branch produced the scores in new registers and the unmasked path of
+    // every step copied all 32 of them to match.
     auto mask_tile = [&](int t, floatx16_t (&s)[NSUB]) {
 #pragma unroll
         for (int sub = 0; sub < NSUB; ++sub)
@@ -282,7 +286,10 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
                 const unsigned rel = (unsigned)(key - L);
                 const bool tree_vis = (anc_row >> (rel & 63u)) & 1ull;
                 const bool vis = (key < k1) && ((key < L) | tree_vis);
-                s[sub][e] = vis ? s[sub][e] : -INFINITY;
+                const unsigned long long hide = __ballot(!vis);   // lanes whose key is hidden
+                float x = s[sub][e];
+                asm volatile("v_cndmask_b32_e64 %0, %0, %1, %2" : "+v"(x) : "v"(-INFINITY), "s"(hide));
+                s[sub][e] = x;
             }
     };
     auto tile_max = [&](const floatx16_t (&s)[NSUB]) {
