@@ -234,8 +234,13 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
                 (void*)(((uint64_t)hi << 32) | lo), 0, bytes, kRsrcFlags);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (in_page + lane / CH) * (D * 2) + c * 16, 0, 0, 0);
         } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16,
-                                                     ((isk ? tk : tv) + row) * (D * 2) + c * 16, 0, 0, 0);
+            // a resource based at the tile and ending at key k1 (wave-uniform,
+            // built in scalar registers), so the lane offset is the same at
+            // every step and loads past the split still read zeros
+            const int key = isk ? tk : tv;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)((isk ? kbase : vbase) + (size_t)key * D), 0, max(k1 - key, 0) * (D * 2), kRsrcFlags);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, row * (D * 2) + c * 16, 0, 0, 0);
         }
     };
 
