@@ -220,7 +220,7 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
             const int in_page = key0 & ((1 << P.pt.bs_log2) - 1);
             if (pool_small && page >= 0 && key0 + ROWS_PER_BLOCK <= k1) {   // wave-uniform
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16, (in_page + lane / CH) * (D * 2) + c * 16,
-                                                         (uint32_t)page * (uint32_t)page_bytes, 0, 0);
+                                                         (uint32_t)page * (uint32_t)page_bytes, 0, kStreamPolicy);
                 return;
             }
             const int room = min(max(k1 - (key0 - in_page), 0), 1 << P.pt.bs_log2);
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
             const int bytes = __builtin_amdgcn_readfirstlane(page >= 0 ? room * D * 2 : 0);
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(((uint64_t)hi << 32) | lo), 0, bytes, kRsrcFlags);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (in_page + lane / CH) * (D * 2) + c * 16, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (in_page + lane / CH) * (D * 2) + c * 16, 0, 0, kStreamPolicy);
         } else {
             // a resource based at the tile and ending at key k1 (wave-uniform,
             // built in scalar registers), so the lane offset is the same at
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
             const int key = isk ? tk : tv;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)((isk ? kbase : vbase) + (size_t)key * D), 0, max(k1 - key, 0) * (D * 2), kRsrcFlags);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, row * (D * 2) + c * 16, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, row * (D * 2) + c * 16, 0, 0, kStreamPolicy);
         }
     };
 

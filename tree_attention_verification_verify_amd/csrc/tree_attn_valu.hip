@@ -130,7 +130,7 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
             const int in_page = key0 & ((1 << P.pt.bs_log2) - 1);
             if (pool_small && page >= 0 && key0 + RPB <= k1) {   // wave-uniform
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16, (in_page + lane / CH) * ROWB + c * 16,
-                                                         (uint32_t)page * (uint32_t)page_bytes, 0, 0);
+                                                         (uint32_t)page * (uint32_t)page_bytes, 0, kStreamPolicy);
                 return;
             }
             const int room = min(max(k1 - (key0 - in_page), 0), 1 << P.pt.bs_log2);
@@ -141,9 +141,9 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
             const int bytes = __builtin_amdgcn_readfirstlane(page >= 0 ? room * ROWB : 0);
             const __amdgpu_buffer_rsrc_t rs =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, bytes, kRsrcFlags);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (in_page + lane / CH) * ROWB + c * 16, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (in_page + lane / CH) * ROWB + c * 16, 0, 0, kStreamPolicy);
         } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16, (t + row) * ROWB + c * 16, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16, (t + row) * ROWB + c * 16, 0, 0, kStreamPolicy);
         }
     };
 

@@ -101,7 +101,8 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float4 v = __builtin_bit_cast(
-                float4, __builtin_amdgcn_raw_buffer_load_b128(rows::tail_rsrc(row_a, V, 4 * (base4 + u * ST)), 16 * tid, 0, 0));
+                float4, __builtin_amdgcn_raw_buffer_load_b128(rows::tail_rsrc(row_a, V, 4 * (base4 + u * ST)), 16 * tid, 0,
+                                                               kStreamPolicy));
             x[4 * u] = v.x; x[4 * u + 1] = v.y; x[4 * u + 2] = v.z; x[4 * u + 3] = v.w;
         }
     };
