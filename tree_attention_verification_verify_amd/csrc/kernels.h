@@ -34,6 +34,7 @@ struct AttnParams {
     int nsplit;
     int chunk;          // keys per split (multiple of 64)
     int groups_per_xcd; // XCD-aware block mapping (mfma path with rowblocks > 1)
+    int stream;         // K/V tiles loaded with the non-temporal policy (see plan_attention)
     float c;            // softmax_scale * log2(e)
     PageTable pt;       // paged caches: k, v are the pools; Lcap = pt.width << pt.bs_log2
 };

@@ -58,7 +58,18 @@ struct AttnPlan {
     int nsplit = 1;
     int chunk = 0;
     size_t part_rows = 0;   // pairs * nsplit * Rpad
+    bool stream = false;    // K/V tiles loaded with the non-temporal policy
 };
+
+// K/V tiles stream with the non-temporal cache policy when no other workgroup
+// reads them (one row block) and the call's caches are too large to stay in
+// the last-level cache anyway (more than a quarter of its 256 MiB, taking the
+// capacity as the bound).  Smaller caches keep the default policy, so calls
+// that follow each other over the same cache find it there (measured at the
+// llama7b Medusa shape, 35 MB of K/V: 29.9 us per step non-temporal, 27.9
+// with the default policy; at the long-context shape, 2.1 GB: 471 us with the
+// default policy, 426 us non-temporal).
+constexpr size_t kStreamMinBytes = size_t(64) << 20;
 
 // max_part_rows: the split partials must fit this many rows (fewer splits
 // otherwise; one split needs none).
@@ -77,6 +88,9 @@ AttnPlan plan_attention(const spec_verify_config& c, int B, int T, size_t max_pa
     }
     p.rowblocks = (R + p.rows_per_block - 1) / p.rows_per_block;
     p.Rpad = p.rowblocks * p.rows_per_block;
+    const size_t elem = c.dtype == SPEC_VERIFY_BF16 ? 2 : 4;
+    const size_t kv_bytes = 2 * (size_t)B * c.num_kv_heads * (size_t)c.kv_capacity * c.head_dim * elem;
+    p.stream = p.rowblocks == 1 && kv_bytes > kStreamMinBytes;
     const long pairs = (long)B * c.num_kv_heads;
     const long base_waves = pairs * p.rowblocks * p.waves * (p.mfma ? sv::kMfmaHalves : 1);
     long want = (kTargetWaves + base_waves - 1) / base_waves;
@@ -431,6 +445,7 @@ int run_impl(const spec_verify_config& c, const Workspace& ws, const TimingRing*
     ap.R = ap.g * T;
     ap.Rpad = plan.Rpad;
     ap.rowblocks = plan.rowblocks;
+    ap.stream = plan.stream ? 1 : 0;
     ap.nsplit = plan.nsplit;
     ap.chunk = plan.chunk;
     const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt((float)D);
@@ -841,11 +856,11 @@ int spec_verify_describe(spec_verify_handle* h, int32_t batch, int32_t nodes, ch
     const bool select = do_vocab && !walk;
     const int n = std::snprintf(
         buf, (size_t)buf_len,
-        "{\"attention\": \"%s\", \"waves\": %d, \"rowblocks\": %d, \"nsplit\": %d, \"chunk\": %d, "
+        "{\"attention\": \"%s\", \"waves\": %d, \"rowblocks\": %d, \"nsplit\": %d, \"chunk\": %d, \"stream\": %d, "
         "\"vocab\": \"%s\", \"probs\": \"%s\", \"finish\": \"%s\", \"select\": %d, \"merge\": %d, "
         "\"walk\": \"%s\"}",
         attn, do_attn ? plan.waves : 0, do_attn ? plan.rowblocks : 0, do_attn ? plan.nsplit : 0,
-        do_attn ? plan.chunk : 0, do_vocab ? sv::row_stats_kernel_name(tp) : "",
+        do_attn ? plan.chunk : 0, do_attn && plan.stream ? 1 : 0, do_vocab ? sv::row_stats_kernel_name(tp) : "",
         (c.flags & SPEC_VERIFY_FLAG_WRITE_PROBS) ? "write_probs_kernel" : "", (select || merge) ? "finish_kernel" : "",
         select ? 1 : 0, merge ? 1 : 0, walk ? sv::lossless_walk_kernel_name(sp) : "");
     if (n < 0 || n >= buf_len) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "buffer too small");

@@ -65,10 +65,10 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
 // would.  Both halves run the same number of steps (barriers are shared); a
 // half with one tile fewer runs its last step on a tile past its range,
 // whose loads read zeros and whose keys are all masked.
-// STREAM: K/V tiles are read by every row block of a (sequence, KV head,
-// split).  With one row block nothing reads a tile twice and the tiles stream
-// with the non-temporal policy; with several, the default policy keeps them in
-// L2 for the other blocks (at the 70B GQA tree shape, four row blocks,
+// STREAM: K/V tiles loaded with the non-temporal policy (chosen by the host:
+// one row block, large caches).  Tiles are read by every row block of a
+// (sequence, KV head, split); with several row blocks the default policy keeps
+// them in L2 for the others (at the 70B GQA tree shape, four row blocks,
 // non-temporal tile loads fetched 320 MB instead of 288 MB and took 1.7% longer).
 template <int D, int WAVES, bool PAGED, int H, bool STREAM>
 __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams P) {   // 2 waves per SIMD
@@ -764,7 +764,7 @@ void launch_mfma_waves_s(const AttnParams& p, int waves, dim3 grid, hipStream_t 
 
 template <int D, bool PAGED>
 void launch_mfma_waves(const AttnParams& p, int waves, dim3 grid, hipStream_t s) {
-    if (p.rowblocks == 1) launch_mfma_waves_s<D, PAGED, true>(p, waves, grid, s);
+    if (p.stream) launch_mfma_waves_s<D, PAGED, true>(p, waves, grid, s);
     else launch_mfma_waves_s<D, PAGED, false>(p, waves, grid, s);
 }
 

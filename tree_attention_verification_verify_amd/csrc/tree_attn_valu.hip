@@ -33,7 +33,7 @@ constexpr int VKT = 64;          // keys per tile
 constexpr int VKW = VKT / VW;    // keys per wave per tile
 constexpr float kLazyRef = 8.f;  // log2 headroom of the lazily raised reference
 
-template <bool BF16, int D, int MAXR, bool PAGED>
+template <bool BF16, int D, int MAXR, bool PAGED, bool STREAM>   // STREAM: non-temporal K/V tile loads
 __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams P) {
     constexpr int EB = BF16 ? 2 : 4;
     constexpr int ROWB = D * EB;              // bytes per K/V row
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
             const int in_page = key0 & ((1 << P.pt.bs_log2) - 1);
             if (pool_small && page >= 0 && key0 + RPB <= k1) {   // wave-uniform
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16, (in_page + lane / CH) * ROWB + c * 16,
-                                                         (uint32_t)page * (uint32_t)page_bytes, 0, kStreamPolicy);
+                                                         (uint32_t)page * (uint32_t)page_bytes, 0, STREAM ? kStreamPolicy : 0);
                 return;
             }
             const int room = min(max(k1 - (key0 - in_page), 0), 1 << P.pt.bs_log2);
@@ -141,9 +141,11 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
             const int bytes = __builtin_amdgcn_readfirstlane(page >= 0 ? room * ROWB : 0);
             const __amdgpu_buffer_rsrc_t rs =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, bytes, kRsrcFlags);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (in_page + lane / CH) * ROWB + c * 16, 0, 0, kStreamPolicy);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (in_page + lane / CH) * ROWB + c * 16, 0, 0,
+                                                     STREAM ? kStreamPolicy : 0);
         } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16, (t + row) * ROWB + c * 16, 0, 0, kStreamPolicy);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, dst, 16, (t + row) * ROWB + c * 16, 0, 0,
+                                                     STREAM ? kStreamPolicy : 0);
         }
     };
 
@@ -348,20 +350,25 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
     }
 }
 
-template <bool BF16, int D, bool PAGED>
+template <bool BF16, int D, bool PAGED, bool STREAM>
 void launch_tiled_rows(const AttnParams& p, int maxr, dim3 grid, hipStream_t s) {
     switch (maxr) {
-        case 2: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 2, PAGED>), grid, dim3(VW * 64), 0, s, p); break;
-        case 4: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 4, PAGED>), grid, dim3(VW * 64), 0, s, p); break;
-        case 6: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 6, PAGED>), grid, dim3(VW * 64), 0, s, p); break;
-        default: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 8, PAGED>), grid, dim3(VW * 64), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 2, PAGED, STREAM>), grid, dim3(VW * 64), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 4, PAGED, STREAM>), grid, dim3(VW * 64), 0, s, p); break;
+        case 6: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 6, PAGED, STREAM>), grid, dim3(VW * 64), 0, s, p); break;
+        default: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 8, PAGED, STREAM>), grid, dim3(VW * 64), 0, s, p); break;
     }
 }
 
 template <bool BF16, int D>
 void launch_tiled(const AttnParams& p, int maxr, dim3 grid, hipStream_t s) {
-    if (p.pt.table) launch_tiled_rows<BF16, D, true>(p, maxr, grid, s);
-    else launch_tiled_rows<BF16, D, false>(p, maxr, grid, s);
+    if (p.pt.table) {
+        if (p.stream) launch_tiled_rows<BF16, D, true, true>(p, maxr, grid, s);
+        else launch_tiled_rows<BF16, D, true, false>(p, maxr, grid, s);
+    } else {
+        if (p.stream) launch_tiled_rows<BF16, D, false, true>(p, maxr, grid, s);
+        else launch_tiled_rows<BF16, D, false, false>(p, maxr, grid, s);
+    }
 }
 
 }  // namespace
