@@ -14,10 +14,9 @@
 // max grows), merged in a fixed order.  With top-p the cut needs every
 // probability relative to the final max: a row of up to 32768 logits is held
 // in the registers of a 1024-thread workgroup and cut by a 3-level radix
-// select on the fp32 bit patterns with integer mass histograms (ten barriers
-// in all unless tied probabilities straddle the cut); a longer row is
-// streamed once per step of the same cut.  The nucleus normaliser is its
-// exact integer mass.
+// select on the fp32 bit patterns with exact integer masses (significand sums
+// per bucket, see the kernel); a longer row is streamed once per step of the
+// same cut with fixed-point masses.
 
 #include "row_block.h"
 
@@ -169,15 +168,15 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-p rows.  The row stays in registers; the cut is a 3-level radix select
-// (10 bits per level, from the top) on the fp32 patterns of the unnormalised
-// probabilities, with exact integer mass histograms.  Each level costs three
-// barriers: histogram; scan of the buckets in descending order inside each
-// wave; wave offsets read by every thread (integer sums, so any order gives
-// the same result) and the crossing bucket published.  The first level sees
-// every logit, so its histogram has HK copies (lane & (HK - 1)), interleaved
-// per bucket so the copies of one bucket sit in different banks: a wave's
-// 64 atomics then collide HK times less on the crowded buckets.
+// Top-p cut of the streamed rows (V > 32768): a 3-level radix select (10 bits
+// per level, from the top) on the fp32 patterns of the unnormalised
+// probabilities, with fixed-point (2^-40) mass histograms.  Each level costs
+// three barriers: histogram; scan of the buckets in descending order inside
+// each wave; wave offsets read by every thread (integer sums, so any order
+// gives the same result) and the crossing bucket published.  The first level
+// sees every logit, so its histogram has HK copies (lane & (HK - 1)),
+// interleaved per bucket so the copies of one bucket sit in different banks:
+// a wave's 64 atomics then collide HK times less on the crowded buckets.
 constexpr int HK = 4;
 constexpr int TNW = rows::NW;
 constexpr int kListCap = 256;   // per-wave list of the elements in the first level's crossing bucket
@@ -323,13 +322,165 @@ __device__ __forceinline__ double topp_scan(double need, float top_p, ToppSmem& 
     return need;
 }
 
-// TPB threads per row, N4 = CHUNK / (4 TPB) float4 per thread.  (256
-// threads, two rows per CU, measured slower at V = 32000: 39 against 34 us
-// for 352 rows; each row's passes then take three times as long.)
+// ---------------------------------------------------------------------------
+// Top-p rows held on chip (V <= 32768): exact significand sums.
+//
+// A kept-mass candidate e (an unnormalised probability: normal, at most 1)
+// with exponent field E and 24-bit significand s equals s * 2^(E - 150), and
+// every element of a level-1 bucket (pattern bits 29..20: seven exponent
+// bits and three significand bits) shares E.  Level 1 therefore adds, per
+// bucket, the u64 value (1 << 48) + pattern: the top bits count the elements
+// n and the low 48 bits hold the sum of patterns (below 2^46), from which the
+// significand sum is sum - n * ((E - 1) << 23), exact.  The scan converts each
+// bucket to units of 2^-48 (exact for E >= 102; a bucket of e < 2^-25 is
+// rounded to the nearest unit, an error below 2^-49 of the largest
+// probability, and the row total stays below 2^63).  Levels 2 and 3 lie
+// inside the crossing bucket and stay in significand units; the nucleus
+// normaliser is assembled from the two parts in fp64.
+//
+// Only candidates (e >= 2^-12) enter the level-1 histogram: the others are
+// summed per thread (fp32 within a float4, fp64 across them: a fixed order
+// of additions, then fixed-order wave and block sums), and the cut lies among
+// the candidates whenever top_p times the row total is at most their mass.
+// At the batch-32 chain shape this leaves about 5% of the logits for the LDS
+// atomics.  A row whose cut lies lower (a flat distribution, or top_p close
+// to 1) adds the others to the histogram too and scans again, with the row
+// total taken from the histogram alone.
+constexpr int kMassUnitsLog2 = 48;                  // level-1 scan units: 2^-48
+constexpr int kExactExp = 150 - kMassUnitsLog2;     // smallest exponent field converted exactly
+constexpr uint32_t kCandBits = 115u << 23;          // 2^-12: smallest candidate
+
+__device__ __forceinline__ uint32_t significand(uint32_t bits) { return (bits & 0x7FFFFFu) | 0x800000u; }
+constexpr unsigned long long kCountOne = 1ull << 48;   // one element in a level-1 bucket entry
+constexpr int kTopBucket = 1016;                        // level-1 bucket of 1.0 (exponent 127)
+
+// Significand sum of level-1 bucket k from its entry (count << 48) + sum of patterns.
+__device__ __forceinline__ unsigned long long bucket_significands(unsigned long long entry, int k) {
+    const unsigned long long n = entry >> 48, pat = entry & (kCountOne - 1);
+    return pat - n * ((unsigned long long)((k >> 3) - 1) << 23);
+}
+
+// Level-1 bucket k (exponent field k >> 3) with significand sum h, in 2^-48 units.
+__device__ __forceinline__ unsigned long long bucket_units(unsigned long long h, int k) {
+    const int sh = (k >> 3) - kExactExp;
+    if (sh >= 0) return h << sh;
+    if (sh < -40) return 0ull;   // h < 2^40: rounds to 0
+    return (h + (1ull << (-sh - 1))) >> -sh;
+}
+
+// Maximum of three floats by v_max3_f32 (quiet NaNs are ignored; the
+// operands need no quieting first, unlike fmaxf on values loaded from memory).
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Wave maximum / minimum in every lane, by DPP row shifts and broadcasts
+// (lanes without a source keep their own value), then lane 63.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+#define SV_MAXSTEP(CTRL, ROWS) v = max3_f32(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp( \
+        __builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, false)), v)
+    SV_MAXSTEP(0x111, 0xf); SV_MAXSTEP(0x112, 0xf); SV_MAXSTEP(0x114, 0xf); SV_MAXSTEP(0x118, 0xf);
+    SV_MAXSTEP(0x142, 0xa); SV_MAXSTEP(0x143, 0xc);
+#undef SV_MAXSTEP
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+}
+__device__ __forceinline__ int wave_min_dpp(int v) {
+#define SV_MINSTEP(CTRL, ROWS) v = min(v, __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false))
+    SV_MINSTEP(0x111, 0xf); SV_MINSTEP(0x112, 0xf); SV_MINSTEP(0x114, 0xf); SV_MINSTEP(0x118, 0xf);
+    SV_MINSTEP(0x142, 0xa); SV_MINSTEP(0x143, 0xc);
+#undef SV_MINSTEP
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+struct NucleusSmem {
+    unsigned long long h1[1024 * HK];   // level 1: copy c of bucket k at k * HK + c
+    unsigned long long h2[1024];
+    unsigned long long h3[1024];
+    unsigned long long wt[4][TNW];
+    double wtail[TNW];                  // per wave: fp64 mass of the elements below the candidates
+    unsigned long long sel_above[4];
+    unsigned long long sel_mass[4];
+    int sel_bucket[4];
+    int sel_found[4];
+    double needv[4];
+    float wmax[TNW];
+    int wbest[TNW];
+    unsigned long long cnt[2][TNW];
+    uint32_t list[TNW * kListCap];      // per wave: patterns of its elements in the level-1 crossing bucket
+};
+
+// Crossing bucket of one level (selection slot S): the bucket where the mass
+// counted from the largest bucket down first reaches need; without one (need
+// outside (0, total]) bucket 0, with sel_found[S] = 0.  units(k) is bucket
+// k's mass.  With TOTAL the level sets need to top_p times (its total +
+// extra()), extra() being mass outside the buckets in the same units
+// (evaluated after the first barrier).  Returns need, the same in every
+// thread.  The first kScanThreads threads scan, 1024 / kScanThreads buckets
+// each (with all 1024 threads, one bucket each: the scan is a chain of
+// dependent steps, and one bucket per thread measured 26.4 against 28.0 us at
+// four buckets per thread on one wave per SIMD).
+constexpr int kScanThreads = 1024;
+template <int S, bool TOTAL, int TPB, class U, class X>
+__device__ __forceinline__ double nucleus_scan(double need, float top_p, NucleusSmem& sm, U&& units, X&& extra) {
+    constexpr int SCT = TPB < kScanThreads ? TPB : kScanThreads;
+    constexpr int BPT = 1024 / SCT, NWS = SCT / kWave;
+    static_assert(BPT * SCT == 1024 && NWS <= TNW, "buckets per thread");
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const bool scanner = tid < SCT;
+    const int bk0 = 1023 - BPT * tid;   // this thread's largest bucket
+    unsigned long long xs[BPT];
+    unsigned long long x = 0, incl = 0;
+    __syncthreads();
+    if (scanner) {
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+            xs[q] = units(bk0 - q);
+            x += xs[q];
+        }
+        incl = wave_scan_u64(x);
+        if (lane == kWave - 1) sm.wt[S][wave] = incl;
+    }
+    __syncthreads();
+    if (scanner) {
+        const unsigned long long wsc = wave_scan_u64(lane < NWS ? sm.wt[S][lane] : 0ull);
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const unsigned long long total = readlane_u64(wsc, NWS - 1);
+        incl += wv > 0 ? readlane_u64(wsc, wv - 1) : 0ull;
+        const unsigned long long excl = incl - x;
+        if (TOTAL) {
+            need = (double)top_p * ((double)total + extra());
+            if (tid == 0) sm.needv[S] = need;
+        }
+        const bool exists = 0.0 < need && need <= (double)total;
+        // the integer bounds, as doubles, tile (0, total] without gaps: one
+        // thread's range holds need, and one of its buckets
+        const bool mine = exists ? ((double)excl < need && need <= (double)incl) : tid == SCT - 1;
+        if (mine) {
+            unsigned long long lo = excl;
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) {
+                const unsigned long long hi = lo + xs[q];
+                if (exists ? ((double)lo < need && need <= (double)hi) : q == BPT - 1) {
+                    sm.sel_bucket[S] = bk0 - q;
+                    sm.sel_above[S] = lo;
+                    sm.sel_mass[S] = xs[q];
+                    sm.sel_found[S] = exists ? 1 : 0;
+                }
+                lo = hi;
+            }
+        }
+    }
+    __syncthreads();
+    return TOTAL ? sm.needv[S] : need;
+}
+
+// TPB threads per row, N4 = CHUNK / (4 TPB) float4 per thread.
 template <int TPB>
 __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
     using namespace rows;
-    __shared__ ToppSmem sm;
+    __shared__ NucleusSmem sm;
     const int nrows = 2 * P.T;
     const int b = blockIdx.x / nrows, r = blockIdx.x - b * nrows;
     const float* row = row_ptr(P, b, r);
@@ -340,72 +491,180 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
     const bool aligned = (((uintptr_t)row) & 15) == 0;
     constexpr int N4 = CHUNK / (4 * TPB), NWB = TPB / kWave;
     float4 e[N4];
-    load_chunk<N4, TPB>(row, V, 0, aligned, e);
+    issue_chunk<N4, TPB>(row, V, 0, aligned, e);
     // cleared histograms are ordered before their atomics by the next barrier
     for (int k = tid; k < 1024 * HK; k += TPB) sm.h1[k] = 0ull;
     for (int k = tid; k < 1024; k += TPB) {
         sm.h2[k] = 0ull;
         sm.h3[k] = 0ull;
     }
+    // entries past the row end (read as 0) become -inf; only slots that
+    // reach V need the test
+#pragma unroll
+    for (int j = 0; j < N4; ++j)
+        if (4 * TPB * (j + 1) > V)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (elem_index<TPB>(0, j, c) >= V) f4set(e[j], c, -INFINITY);
 
-    // largest logit and its smallest id (the largest logit is zmax): the
-    // thread's maximum, then the first of its positions (in id order) holding it
+    // largest logit: thread maximum (two logits per max3), wave, block
     float bv = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < N4; ++j) bv = fmaxf(fmaxf(bv, fmaxf(e[j].x, e[j].y)), fmaxf(e[j].z, e[j].w));
-    int bi = INT_MAX;
-#pragma unroll
-    for (int j = N4 - 1; j >= 0; --j)
-#pragma unroll
-        for (int c = 3; c >= 0; --c) {
-            const int idx = elem_index<TPB>(0, j, c);
-            bi = (f4get(e[j], c) == bv && idx < V) ? idx : bi;
-        }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) argmax_step(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
-    if (lane == 0) { sm.bv[wave] = bv; sm.bi[wave] = bi; }
+    for (int k = 0; k < 4 * N4; k += 2) bv = max3_f32(bv, f4get(e[k / 4], k % 4), f4get(e[k / 4], k % 4 + 1));
+    const float wm = wave_max_dpp(bv);
+    if (lane == 0) sm.wmax[wave] = wm;
     __syncthreads();
-    float M = sm.bv[0];
-    int best = sm.bi[0];
+    float M = sm.wmax[0];
 #pragma unroll
-    for (int w = 1; w < NWB; ++w) argmax_step(M, best, sm.bv[w], sm.bi[w]);
+    for (int w = 1; w < NWB; ++w) M = fmaxf(M, sm.wmax[w]);
+    // its smallest id: only threads holding M look for their first position
+    int bi = INT_MAX;
+    if (bv == M) {
+#pragma unroll
+        for (int j = N4 - 1; j >= 0; --j)
+#pragma unroll
+            for (int c = 3; c >= 0; --c) {
+                const int idx = elem_index<TPB>(0, j, c);
+                bi = (f4get(e[j], c) == M && idx < V) ? idx : bi;
+            }
+    }
+    bi = wave_min_dpp(bi);
+    if (lane == 0) sm.wbest[wave] = bi;   // read after the next barrier
+
+    // unnormalised probabilities; candidates into level 1 ((count, pattern
+    // sum) per bucket, HK copies by lane), the others into an fp64 sum
+    uint8_t* const h1c = (uint8_t*)sm.h1 + 8 * (lane & (HK - 1));
+    auto add_h1 = [&](uint32_t bits) {
+        atomicAdd((unsigned long long*)(h1c + ((bits >> 15) & (1023u * 8 * HK))), kCountOne + bits);
+    };
+    {
+        // the others' sum: fp32 within each float4 (four terms below 2^-12,
+        // relative error below 2^-22), fp64 across them, in a fixed order
+        double tail = 0.0;
+#pragma unroll
+        for (int j = 0; j < N4; ++j) {
+            float t4[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float v = unnorm(f4get(e[j], c), M, ilog);
+                f4set(e[j], c, v);
+                const uint32_t bits = __float_as_uint(v);
+                const bool cand = bits >= kCandBits;
+                t4[c] = cand ? 0.f : v;
+                if (cand) add_h1(bits);
+            }
+            tail += (double)((t4[0] + t4[1]) + (t4[2] + t4[3]));
+            // added where it is made (left to itself the compiler makes every
+            // term first and holds them all)
+            asm volatile("" : "+v"(tail));
+        }
+        const double wtl = wave_sum_d(tail);
+        if (lane == 0) sm.wtail[wave] = wtl;   // read after the scan's first barrier
+    }
+    // buckets of exponent 0 (zeros, subnormals) and above the bucket of 1.0
+    // (non-numbers) carry no mass
+    auto h1_significands = [&](int k) -> unsigned long long {
+        if (k < 8 || k > kTopBucket) return 0ull;
+        unsigned long long s = 0;
+#pragma unroll
+        for (int c = 0; c < HK; ++c) s += sm.h1[k * HK + c];
+        return bucket_significands(s, k);
+    };
+    auto h1_units = [&](int k) { return bucket_units(h1_significands(k), k); };
+    double need = nucleus_scan<0, true, TPB>(0.0, P.top_p, sm, h1_units, [&]() {
+        double t = 0.0;
+#pragma unroll
+        for (int w = 0; w < NWB; ++w) t += sm.wtail[w];
+        return ldexp(t, kMassUnitsLog2);
+    });
+    int s1 = 0;   // selection slot of level 1
+    if (!sm.sel_found[0]) {
+        // the cut lies below the candidates: the others join the histogram
+#pragma unroll
+        for (int j = 0; j < N4; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t bits = __float_as_uint(f4get(e[j], c));
+                if (bits < kCandBits) add_h1(bits);
+            }
+        need = nucleus_scan<3, true, TPB>(0.0, P.top_p, sm, h1_units, []() { return 0.0; });
+        s1 = 3;
+    }
+    const uint32_t b1 = (uint32_t)sm.sel_bucket[s1];
+    const unsigned long long a1 = sm.sel_above[s1];
+    const int E1 = (int)(b1 >> 3);
+    const unsigned long long h_b1 = h1_significands((int)b1);   // the crossing bucket's significand sum
+    // what is left to reach, in significand units of bucket b1 (the level-1
+    // conversion of a bucket below 2^-25 rounded: clamp to the bucket's sum)
+    double need1 = 0.0;
+    if (need > 0.0 && h_b1 > 0) need1 = fmin(ldexp(need - (double)a1, kExactExp - E1), (double)h_b1);
+
+    // levels 2 and 3 only see bucket b1: each wave lists its elements there
+    // (writes and reads of a wave's own list need no barrier) and reads the
+    // list, or its registers when the list is too short for them.  A bucket
+    // that carries mass has an exponent field of 1..127 and lies at or below
+    // bucket 1016, so matching its pattern bits implies carrying mass.
+    constexpr int CAP = TNW * kListCap / NWB;
+    uint32_t* const mylist = sm.list + wave * CAP;
+    const uint32_t b1m = h_b1 > 0 ? b1 : 0xFFFFFFFFu;
+    uint32_t nlist = 0;
 #pragma unroll
     for (int j = 0; j < N4; ++j)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) f4set(e[j], c, unnorm(f4get(e[j], c), M, ilog));
-
-    // the cut
-    topp_accumulate<0, N4>(e, 0u, sm);
-    const double need = topp_scan<0, TPB>(0.0, P.top_p, sm);
-    const uint32_t b1 = (uint32_t)sm.sel_bucket[0];
-    const unsigned long long a1 = sm.sel_above[0];
-    // levels 2 and 3 only see bucket b1: each wave lists its elements there
-    // once (writes and reads of a wave's own list need no barrier) and reads
-    // the list, or its registers when the list is too short for them
-    // the list space of TNW waves shared by the NWB waves of this row
-    constexpr int CAP = TNW * kListCap / NWB;
-    uint32_t* const mylist = &sm.list[0][0] + wave * CAP;
-    const uint32_t nlist = topp_compact<N4, CAP>(e, b1, mylist);
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t bits = __float_as_uint(f4get(e[j], c));
+            const bool m = (bits >> 20) == b1m;
+            const unsigned long long mask = __ballot(m);
+            if (m) {
+                const uint32_t pos = nlist + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                if (pos < (uint32_t)CAP) mylist[pos] = bits;
+            }
+            nlist += (uint32_t)__popcll(mask);
+        }
     const bool listed = nlist <= (uint32_t)CAP;
-    if (listed) topp_accumulate_list<1>(mylist, nlist, b1, sm);
-    else topp_accumulate<1, N4>(e, b1, sm);
-    topp_scan<1, TPB>(need - (double)a1, P.top_p, sm);
+    // prefix of the elements a level counts: pattern >> pshift == prefix
+    // (made opaque to the compiler, so that the register pass does not keep
+    // the listing's 64 comparison masks alive to reuse them)
+    auto accumulate = [&](unsigned long long* h, int shift, int pshift, uint32_t prefix) {
+        prefix = (uint32_t)__builtin_amdgcn_readfirstlane((int)prefix);
+        asm volatile("" : "+s"(prefix));
+        if (listed) {
+            for (uint32_t i = (uint32_t)lane; i < nlist; i += kWave) {
+                const uint32_t bits = mylist[i];
+                if ((bits >> pshift) == prefix) atomicAdd(&h[(bits >> shift) & 1023], (unsigned long long)significand(bits));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < N4; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t bits = __float_as_uint(f4get(e[j], c));
+                    if ((bits >> pshift) == prefix)
+                        atomicAdd(&h[(bits >> shift) & 1023], (unsigned long long)significand(bits));
+                }
+        }
+    };
+    auto none = []() { return 0.0; };
+    accumulate(sm.h2, 10, 20, b1m);
+    nucleus_scan<1, false, TPB>(need1, P.top_p, sm, [&](int k) { return sm.h2[k]; }, none);
     const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
     const unsigned long long a2 = sm.sel_above[1];
-    if (listed) topp_accumulate_list<2>(mylist, nlist, (b1 << 10) | b2, sm);
-    else topp_accumulate<2, N4>(e, (b1 << 10) | b2, sm);
-    topp_scan<2, TPB>(need - (double)a1 - (double)a2, P.top_p, sm);
+    double need2 = 0.0;
+    if (need1 > 0.0) need2 = fmin(need1 - (double)a2, (double)sm.sel_mass[1]);
+    accumulate(sm.h3, 0, 10, h_b1 > 0 ? ((b1 << 10) | b2) : 0xFFFFFFFFu);
+    nucleus_scan<2, false, TPB>(need2, P.top_p, sm, [&](int k) { return sm.h3[k]; }, none);
     Nucleus nu;
     nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
     nu.cutoff = INT_MAX;
-    // masses above thr, and of the elements at thr (all of the last bucket:
-    // (number of ties) * (mass of one))
-    const unsigned long long above = a1 + a2 + sm.sel_above[2];
+    // significand-unit masses above thr inside b1, and of the elements at thr
+    // (all of the last bucket: (number of ties) * (significand of one))
+    const unsigned long long a3 = sm.sel_above[2];
     unsigned long long kept = sm.sel_mass[2];
-    const unsigned long long tie_mass = fixmass(__uint_as_float(nu.thr));
-    if (tie_mass > 0) {
+    const unsigned long long tie_mass = h_b1 > 0 ? significand(nu.thr) : 0ull;
+    if (tie_mass > 0 && kept > 0) {
         const unsigned long long ties = kept / tie_mass;
-        long long k = (long long)ceil((need - (double)above) / (double)tie_mass);
+        long long k = (long long)ceil((need2 - (double)a3) / (double)tie_mass);
         if (k < 1) k = 1;
         if (ties > 1 && (unsigned long long)k < ties) {
             // ties straddle the cut: the smallest cutoff c with #ties(id < c) >= k,
@@ -436,15 +695,17 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
         }
     }
     if (tid == 0) {
-        // normaliser of the nucleus from its exact fixed-point mass: each
-        // element is rounded by at most 2^-41 and the sum holds the top
-        // element (e = 1), so the relative error is at most V * 2^-41
+        int best = sm.wbest[0];
+#pragma unroll
+        for (int w = 1; w < NWB; ++w) best = min(best, sm.wbest[w]);
+        // normaliser of the nucleus: the buckets above b1 (2^-48 units) and
+        // the kept part of b1 (significand units, 2^(E1 - 150) each)
         RowStat st;
         st.zmax = M;
         st.argmax = best;
         st.thr = nu.thr;
         st.cutoff = nu.cutoff;
-        st.Z = (double)(above + kept) * (1.0 / (double)kFix);
+        st.Z = ldexp((double)a1, -kMassUnitsLog2) + ldexp((double)(a2 + a3 + kept), E1 - 150);
         P.stats[(size_t)b * nrows + r] = st;
     }
 }
