@@ -128,15 +128,21 @@ struct TreeParams {
     int32_t* arrive;            // [B][levels] finished slices per row (zero between calls)
 };
 
-// Returns hipSuccess or the launch error.
-hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s);
+// Returns hipSuccess or the launch error.  fused != nullptr (only where
+// attention_fuses_stats allows it): the same launch also runs the streaming
+// row statistics of *fused, one extra 256-thread workgroup per row, beside
+// the attention workgroups (for grids that leave CUs idle).
+hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s, const StatsParams* fused = nullptr);
 hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
 // VALU attention with 4 waves sharing double-buffered tiles: R <= 8 rows per KV
 // head, K/V rows of 128 or 256 bytes (valu_tiled_supported); Rpad = rows per block.
 bool valu_tiled_supported(bool bf16, int D, int R);
-hipError_t launch_attention_valu_tiled(const AttnParams& p, bool bf16, hipStream_t s);
+hipError_t launch_attention_valu_tiled(const AttnParams& p, bool bf16, hipStream_t s, const StatsParams* fused = nullptr);
 hipError_t launch_row_stats(const StatsParams& p, hipStream_t s);
 const char* row_stats_kernel_name(const StatsParams& p);   // the kernel launch_row_stats takes
+// Whether launch_row_stats takes the streaming kernel (no top-p cut), the one
+// an attention launch can carry.
+bool row_stats_streams(const StatsParams& p);
 // probs[B,T,V] = effective target distribution of every row (after launch_row_stats).
 hipError_t launch_write_probs(const StatsParams& p, float* probs, hipStream_t s);
 // The step's last launch: selection (decisions, path, final draw) and, when

@@ -4,7 +4,10 @@
 //   tree attention (MFMA or VALU kernel) -> split merge (when split)
 //   row statistics of every target / draft logits row (one read)
 //   selection (ratios, decisions, longest accepted path, final draw at v*)
-// The attention and the vocabulary work read disjoint inputs.
+// The attention and the vocabulary work read disjoint inputs: when the
+// attention grid leaves at least half of the CUs idle (one sequence, few KV
+// heads) and the rows need no top-p cut, the attention launch also carries the
+// row statistics in workgroups of their own, so both run at once.
 
 #include <hip/hip_runtime.h>
 
@@ -202,7 +205,26 @@ struct Workspace {
     int walk_k = 0;
     int walk_cap = 0;                 // largest B * walk_k launched across workgroups (all resident at once)
     int walk_spin = 0;                // polls of a walk wait before it gives up
+    int cus = 0;                      // compute units of the device (0: never fuse the row statistics)
 };
+
+// Workgroups of the attention launch of a plan.
+long attention_blocks(const AttnPlan& p, int B, int Hkv) {
+    const long groups = (long)B * Hkv * p.nsplit;
+    if (p.mfma) return p.rowblocks == 1 ? groups : ((groups + 7) / 8) * 8 * p.rowblocks;
+    return p.tiled ? groups : groups * p.rowblocks;
+}
+
+// Whether the attention launch carries the row statistics: 256-thread
+// attention workgroups (the statistics' size), dense caches, no top-p cut, no
+// per-stage timing, and an attention grid that leaves at least half of the
+// CUs idle (at the llama7b Medusa shape 128 workgroups on 256 CUs).
+bool fuse_row_stats(const Workspace& ws, const AttnPlan& p, int B, int Hkv, const sv::StatsParams& tp, bool paged,
+                    bool timing) {
+    const int threads = p.mfma ? p.waves * 64 * sv::kMfmaHalves : (p.tiled ? sv::kStatsThreads : 64);
+    return threads == sv::kStatsThreads && !paged && !timing && ws.cus > 0 && sv::row_stats_streams(tp) &&
+           2 * attention_blocks(p, B, Hkv) <= ws.cus;
+}
 
 struct spec_verify_handle {
     spec_verify_config cfg;
@@ -242,6 +264,11 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_handle** out) 
         return hip_fail(e, "hipGetDevice");
     }
     h->ws.part_rows_cap = cap;
+    e = hipDeviceGetAttribute(&h->ws.cus, hipDeviceAttributeMultiprocessorCount, h->device);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e, "hipDeviceGetAttribute");
+    }
     if (cap > 0) {
         e = hipMalloc((void**)&h->ws.part_o, cap * c.head_dim * sizeof(float));
         if (e == hipSuccess) e = hipMalloc((void**)&h->ws.part_ml, cap * sizeof(float2));
@@ -451,15 +478,6 @@ int run_impl(const spec_verify_config& c, const Workspace& ws, const TimingRing*
     const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt((float)D);
     ap.c = scale * kLog2e;
 
-    hipError_t e = hipSuccess;
-    if (do_attn) {
-        e = plan.mfma    ? sv::launch_attention_mfma(ap, plan.waves, s)
-            : plan.tiled ? sv::launch_attention_valu_tiled(ap, bf16, s)
-                         : sv::launch_attention_valu(ap, bf16, s);
-        if (e != hipSuccess) return hip_fail(e, "attention launch");
-    }
-    if (int rc = mark(SPEC_VERIFY_STAGE_ATTENTION)) return rc;
-
     sv::StatsParams tp{};
     tp.target = in->target_logits;
     tp.draft = in->draft_logits;
@@ -470,8 +488,20 @@ int run_impl(const spec_verify_config& c, const Workspace& ws, const TimingRing*
     tp.sampling = sampling ? 1 : 0;
     tp.ilog = sampling ? kLog2e / c.temperature : kLog2e;
     tp.top_p = sampling ? c.top_p : 1.f;
+    const bool fused = do_attn && do_vocab && fuse_row_stats(ws, plan, B, c.num_kv_heads, tp, paged != nullptr, timing != nullptr);
+
+    hipError_t e = hipSuccess;
+    if (do_attn) {
+        const sv::StatsParams* fp = fused ? &tp : nullptr;
+        e = plan.mfma    ? sv::launch_attention_mfma(ap, plan.waves, s, fp)
+            : plan.tiled ? sv::launch_attention_valu_tiled(ap, bf16, s, fp)
+                         : sv::launch_attention_valu(ap, bf16, s);
+        if (e != hipSuccess) return hip_fail(e, "attention launch");
+    }
+    if (int rc = mark(SPEC_VERIFY_STAGE_ATTENTION)) return rc;
+
     if (do_vocab) {
-        e = sv::launch_row_stats(tp, s);
+        if (!fused) e = sv::launch_row_stats(tp, s);
         if (e != hipSuccess) return hip_fail(e, "row statistics launch");
         if (do_probs) {
             e = sv::launch_write_probs(tp, out->probs, s);
@@ -698,6 +728,8 @@ int spec_verify_run_noalloc(const spec_verify_config* cfg, const spec_verify_inp
     unsigned char* base = nullptr;
     if (int rc = scratch_for_device(dev, (hipStream_t)stream, &base)) return rc;
     carve_scratch(c, in->batch, in->nodes, base, &ws);
+    e = hipDeviceGetAttribute(&ws.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     return run_impl(c, ws, nullptr, in, nullptr, out, stream);
 }
 
@@ -858,11 +890,12 @@ int spec_verify_describe(spec_verify_handle* h, int32_t batch, int32_t nodes, ch
         buf, (size_t)buf_len,
         "{\"attention\": \"%s\", \"waves\": %d, \"rowblocks\": %d, \"nsplit\": %d, \"chunk\": %d, \"stream\": %d, "
         "\"vocab\": \"%s\", \"probs\": \"%s\", \"finish\": \"%s\", \"select\": %d, \"merge\": %d, "
-        "\"walk\": \"%s\"}",
+        "\"walk\": \"%s\", \"vocab_in_attention_launch\": %d}",
         attn, do_attn ? plan.waves : 0, do_attn ? plan.rowblocks : 0, do_attn ? plan.nsplit : 0,
         do_attn ? plan.chunk : 0, do_attn && plan.stream ? 1 : 0, do_vocab ? sv::row_stats_kernel_name(tp) : "",
         (c.flags & SPEC_VERIFY_FLAG_WRITE_PROBS) ? "write_probs_kernel" : "", (select || merge) ? "finish_kernel" : "",
-        select ? 1 : 0, merge ? 1 : 0, walk ? sv::lossless_walk_kernel_name(sp) : "");
+        select ? 1 : 0, merge ? 1 : 0, walk ? sv::lossless_walk_kernel_name(sp) : "",
+        (do_attn && do_vocab && fuse_row_stats(h->ws, plan, batch, c.num_kv_heads, tp, false, h->timing)) ? 1 : 0);
     if (n < 0 || n >= buf_len) return fail(SPEC_VERIFY_ERR_INVALID_ARG, "buffer too small");
     return SPEC_VERIFY_OK;
 }

@@ -28,6 +28,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "stats_stream.h"
 
 namespace sv {
 namespace {
@@ -70,8 +71,18 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
 // (sequence, KV head, split); with several row blocks the default policy keeps
 // them in L2 for the others (at the 70B GQA tree shape, four row blocks,
 // non-temporal tile loads fetched 320 MB instead of 288 MB and took 1.7% longer).
-template <int D, int WAVES, bool PAGED, int H, bool STREAM>
-__global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams P) {   // 2 waves per SIMD
+// FUSE: workgroups from attn_blocks on compute the streaming row statistics
+// of S instead (one per logits row; 256-thread workgroups only).
+template <int D, int WAVES, bool PAGED, int H, bool STREAM, bool FUSE = false>
+__global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams P, StatsParams S, int attn_blocks) {   // 2 waves per SIMD
+    if constexpr (FUSE) {
+        static_assert(WAVES * 64 * H == kStatsThreads, "row statistics workgroups of 256 threads");
+        if ((int)blockIdx.x >= attn_blocks) {
+            if (S.sampling) row_stats_stream_block<true>(S, (int)blockIdx.x - attn_blocks);
+            else row_stats_stream_block<false>(S, (int)blockIdx.x - attn_blocks);
+            return;
+        }
+    }
     constexpr int NSUB = 2;                 // 32-key sub-tiles per tile
     constexpr int KT = 32 * NSUB;           // keys per tile
     constexpr int CH = D / 8;               // 16-byte chunks per K/V row
@@ -755,17 +766,26 @@ hipError_t launch_valu_rows(const AttnParams& p, int maxr, dim3 grid, hipStream_
 }
 
 template <int D, bool PAGED, bool STREAM>
-void launch_mfma_waves_s(const AttnParams& p, int waves, dim3 grid, hipStream_t s) {
+void launch_mfma_waves_s(const AttnParams& p, int waves, dim3 grid, hipStream_t s, const StatsParams* fused, int blocks) {
     constexpr int H = kMfmaHalves;
-    if (waves == 4) hipLaunchKernelGGL((attn_mfma_kernel<D, 4, PAGED, H, STREAM>), grid, dim3(256 * H), 0, s, p);
-    else if (waves == 2) hipLaunchKernelGGL((attn_mfma_kernel<D, 2, PAGED, H, STREAM>), grid, dim3(128 * H), 0, s, p);
-    else hipLaunchKernelGGL((attn_mfma_kernel<D, 1, PAGED, H, STREAM>), grid, dim3(64 * H), 0, s, p);
+    const StatsParams S = fused ? *fused : StatsParams{};
+    if (fused && waves * 64 * H == kStatsThreads) {
+        const int nrows = S.sampling ? 2 * S.T : S.T;
+        hipLaunchKernelGGL((attn_mfma_kernel<D, kStatsThreads / (64 * H), PAGED, H, STREAM, true>),
+                           dim3(blocks + S.B * nrows), dim3(kStatsThreads), 0, s, p, S, blocks);
+    } else if (waves == 4) {
+        hipLaunchKernelGGL((attn_mfma_kernel<D, 4, PAGED, H, STREAM>), grid, dim3(256 * H), 0, s, p, S, blocks);
+    } else if (waves == 2) {
+        hipLaunchKernelGGL((attn_mfma_kernel<D, 2, PAGED, H, STREAM>), grid, dim3(128 * H), 0, s, p, S, blocks);
+    } else {
+        hipLaunchKernelGGL((attn_mfma_kernel<D, 1, PAGED, H, STREAM>), grid, dim3(64 * H), 0, s, p, S, blocks);
+    }
 }
 
 template <int D, bool PAGED>
-void launch_mfma_waves(const AttnParams& p, int waves, dim3 grid, hipStream_t s) {
-    if (p.stream) launch_mfma_waves_s<D, PAGED, true>(p, waves, grid, s);
-    else launch_mfma_waves_s<D, PAGED, false>(p, waves, grid, s);
+void launch_mfma_waves(const AttnParams& p, int waves, dim3 grid, hipStream_t s, const StatsParams* fused) {
+    if (p.stream) launch_mfma_waves_s<D, PAGED, true>(p, waves, grid, s, fused, (int)grid.x);
+    else launch_mfma_waves_s<D, PAGED, false>(p, waves, grid, s, fused, (int)grid.x);
 }
 
 }  // namespace
@@ -779,18 +799,18 @@ int valu_rows_for(int R) {
     return kValuRows;
 }
 
-hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s) {
+hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s, const StatsParams* fused) {
     const int groups = p.B * p.Hkv * p.nsplit;
     int blocks;
     if (p.rowblocks == 1) blocks = groups;
     else blocks = ((groups + 7) / 8) * 8 * p.rowblocks;
     dim3 grid(blocks);
-    if (p.pt.table) {
-        if (p.D == 128) launch_mfma_waves<128, true>(p, waves, grid, s);
-        else launch_mfma_waves<64, true>(p, waves, grid, s);
+    if (p.pt.table) {   // paged caches: no fused row statistics
+        if (p.D == 128) launch_mfma_waves<128, true>(p, waves, grid, s, nullptr);
+        else launch_mfma_waves<64, true>(p, waves, grid, s, nullptr);
     } else {
-        if (p.D == 128) launch_mfma_waves<128, false>(p, waves, grid, s);
-        else launch_mfma_waves<64, false>(p, waves, grid, s);
+        if (p.D == 128) launch_mfma_waves<128, false>(p, waves, grid, s, fused);
+        else launch_mfma_waves<64, false>(p, waves, grid, s, fused);
     }
     return hipGetLastError();
 }

@@ -22,6 +22,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "stats_stream.h"
 
 namespace sv {
 namespace {
@@ -33,8 +34,18 @@ constexpr int VKT = 64;          // keys per tile
 constexpr int VKW = VKT / VW;    // keys per wave per tile
 constexpr float kLazyRef = 8.f;  // log2 headroom of the lazily raised reference
 
-template <bool BF16, int D, int MAXR, bool PAGED, bool STREAM>   // STREAM: non-temporal K/V tile loads
-__global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams P) {
+// STREAM: non-temporal K/V tile loads.  FUSE: workgroups from attn_blocks on
+// compute the streaming row statistics of S instead (one per logits row).
+template <bool BF16, int D, int MAXR, bool PAGED, bool STREAM, bool FUSE = false>
+__global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams P, StatsParams S, int attn_blocks) {
+    if constexpr (FUSE) {
+        static_assert(VW * 64 == kStatsThreads, "row statistics workgroups of 256 threads");
+        if ((int)blockIdx.x >= attn_blocks) {
+            if (S.sampling) row_stats_stream_block<true>(S, (int)blockIdx.x - attn_blocks);
+            else row_stats_stream_block<false>(S, (int)blockIdx.x - attn_blocks);
+            return;
+        }
+    }
     constexpr int EB = BF16 ? 2 : 4;
     constexpr int ROWB = D * EB;              // bytes per K/V row
     static_assert(ROWB == 128 || ROWB == 256, "K/V rows of 128 or 256 bytes");
@@ -350,24 +361,32 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
     }
 }
 
-template <bool BF16, int D, bool PAGED, bool STREAM>
-void launch_tiled_rows(const AttnParams& p, int maxr, dim3 grid, hipStream_t s) {
+template <bool BF16, int D, bool PAGED, bool STREAM, bool FUSE>
+void launch_tiled_rows_f(const AttnParams& p, int maxr, dim3 grid, hipStream_t s, const StatsParams& S) {
+    const int blocks = (int)grid.x;
+    const dim3 g(blocks + (FUSE ? S.B * (S.sampling ? 2 * S.T : S.T) : 0));
     switch (maxr) {
-        case 2: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 2, PAGED, STREAM>), grid, dim3(VW * 64), 0, s, p); break;
-        case 4: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 4, PAGED, STREAM>), grid, dim3(VW * 64), 0, s, p); break;
-        case 6: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 6, PAGED, STREAM>), grid, dim3(VW * 64), 0, s, p); break;
-        default: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 8, PAGED, STREAM>), grid, dim3(VW * 64), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 2, PAGED, STREAM, FUSE>), g, dim3(VW * 64), 0, s, p, S, blocks); break;
+        case 4: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 4, PAGED, STREAM, FUSE>), g, dim3(VW * 64), 0, s, p, S, blocks); break;
+        case 6: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 6, PAGED, STREAM, FUSE>), g, dim3(VW * 64), 0, s, p, S, blocks); break;
+        default: hipLaunchKernelGGL((attn_valu_tiled_kernel<BF16, D, 8, PAGED, STREAM, FUSE>), g, dim3(VW * 64), 0, s, p, S, blocks); break;
     }
 }
 
+template <bool BF16, int D, bool PAGED, bool STREAM>
+void launch_tiled_rows(const AttnParams& p, int maxr, dim3 grid, hipStream_t s, const StatsParams* fused) {
+    if (fused) launch_tiled_rows_f<BF16, D, PAGED, STREAM, true>(p, maxr, grid, s, *fused);
+    else launch_tiled_rows_f<BF16, D, PAGED, STREAM, false>(p, maxr, grid, s, StatsParams{});
+}
+
 template <bool BF16, int D>
-void launch_tiled(const AttnParams& p, int maxr, dim3 grid, hipStream_t s) {
-    if (p.pt.table) {
-        if (p.stream) launch_tiled_rows<BF16, D, true, true>(p, maxr, grid, s);
-        else launch_tiled_rows<BF16, D, true, false>(p, maxr, grid, s);
+void launch_tiled(const AttnParams& p, int maxr, dim3 grid, hipStream_t s, const StatsParams* fused) {
+    if (p.pt.table) {   // paged caches: no fused row statistics
+        if (p.stream) launch_tiled_rows<BF16, D, true, true>(p, maxr, grid, s, nullptr);
+        else launch_tiled_rows<BF16, D, true, false>(p, maxr, grid, s, nullptr);
     } else {
-        if (p.stream) launch_tiled_rows<BF16, D, false, true>(p, maxr, grid, s);
-        else launch_tiled_rows<BF16, D, false, false>(p, maxr, grid, s);
+        if (p.stream) launch_tiled_rows<BF16, D, false, true>(p, maxr, grid, s, fused);
+        else launch_tiled_rows<BF16, D, false, false>(p, maxr, grid, s, fused);
     }
 }
 
@@ -378,14 +397,14 @@ bool valu_tiled_supported(bool bf16, int D, int R) {
     return R <= 8 && (rowb == 128 || rowb == 256);
 }
 
-hipError_t launch_attention_valu_tiled(const AttnParams& p, bool bf16, hipStream_t s) {
+hipError_t launch_attention_valu_tiled(const AttnParams& p, bool bf16, hipStream_t s, const StatsParams* fused) {
     const dim3 grid(p.B * p.Hkv * p.nsplit);
     const int maxr = p.Rpad;
     if (bf16) {
-        if (p.D == 128) launch_tiled<true, 128>(p, maxr, grid, s);
-        else launch_tiled<true, 64>(p, maxr, grid, s);
+        if (p.D == 128) launch_tiled<true, 128>(p, maxr, grid, s, fused);
+        else launch_tiled<true, 64>(p, maxr, grid, s, fused);
     } else {
-        launch_tiled<false, 64>(p, maxr, grid, s);   // fp32 rows of 256 bytes
+        launch_tiled<false, 64>(p, maxr, grid, s, fused);   // fp32 rows of 256 bytes
     }
     return hipGetLastError();
 }
