@@ -16,6 +16,9 @@ namespace sv {
 template <int D>
 constexpr int combine_rows_per_block() { return 256 / (D / 8); }
 
+// Up to this many splits a thread loads all of its partials at once.
+constexpr int kCombineMaxSplits = 8;
+
 // Merge block `blk` run by 256 threads, t = 0..255 this thread's index among them.
 template <bool BF16, int D>
 __device__ __forceinline__ void combine_block(const AttnParams& P, long blk, int t) {
@@ -30,22 +33,53 @@ __device__ __forceinline__ void combine_block(const AttnParams& P, long blk, int
     const int b = pair / P.Hkv, kvh = pair - b * P.Hkv;
     const int node = r / P.g, head = kvh * P.g + (r - node * P.g);
 
-    float mmax = -INFINITY;
-    for (int s = 0; s < P.nsplit; ++s) {
-        const float2 ml = P.part_ml[((size_t)pair * P.nsplit + s) * P.Rpad + r];
-        if (ml.y > 0.f) mmax = fmaxf(mmax, ml.x);
-    }
     float lsum = 0.f;
     floatx4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < P.nsplit; ++s) {
-        const size_t prow = ((size_t)pair * P.nsplit + s) * P.Rpad + r;
-        const float2 ml = P.part_ml[prow];
-        if (!(ml.y > 0.f)) continue;
-        const float w = exp2f(ml.x - mmax);
-        lsum += ml.y * w;
-        const floatx4_t* src = (const floatx4_t*)(P.part_o + prow * D + d0);
-        a0 += w * src[0];
-        a1 += w * src[1];
+    if (P.nsplit <= kCombineMaxSplits) {
+        // every split's (m, l) and columns loaded before any is used: one
+        // round trip to memory instead of one per split
+        float2 ml[kCombineMaxSplits];
+        floatx4_t o0[kCombineMaxSplits], o1[kCombineMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kCombineMaxSplits; ++s) {
+            if (s < P.nsplit) {
+                const size_t prow = ((size_t)pair * P.nsplit + s) * P.Rpad + r;
+                ml[s] = P.part_ml[prow];
+                const floatx4_t* src = (const floatx4_t*)(P.part_o + prow * D + d0);
+                o0[s] = src[0];
+                o1[s] = src[1];
+            }
+        }
+        float mmax = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < kCombineMaxSplits; ++s)
+            if (s < P.nsplit && ml[s].y > 0.f) mmax = fmaxf(mmax, ml[s].x);
+#pragma unroll
+        for (int s = 0; s < kCombineMaxSplits; ++s) {
+            // a split that saw no key holds no columns: skipped, not weighted by 0
+            if (s < P.nsplit && ml[s].y > 0.f) {
+                const float w = exp2f(ml[s].x - mmax);
+                lsum += ml[s].y * w;
+                a0 += w * o0[s];
+                a1 += w * o1[s];
+            }
+        }
+    } else {
+        float mmax = -INFINITY;
+        for (int s = 0; s < P.nsplit; ++s) {
+            const float2 ml = P.part_ml[((size_t)pair * P.nsplit + s) * P.Rpad + r];
+            if (ml.y > 0.f) mmax = fmaxf(mmax, ml.x);
+        }
+        for (int s = 0; s < P.nsplit; ++s) {
+            const size_t prow = ((size_t)pair * P.nsplit + s) * P.Rpad + r;
+            const float2 ml = P.part_ml[prow];
+            if (!(ml.y > 0.f)) continue;
+            const float w = exp2f(ml.x - mmax);
+            lsum += ml.y * w;
+            const floatx4_t* src = (const floatx4_t*)(P.part_o + prow * D + d0);
+            a0 += w * src[0];
+            a1 += w * src[1];
+        }
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     a0 *= inv;

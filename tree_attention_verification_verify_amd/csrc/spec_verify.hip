@@ -49,6 +49,9 @@ constexpr int kTargetWaves = 2048;   // two waves per SIMD on 256 CUs
 // against 30.2 us for 7 (the merge of the partials costs more than the extra
 // workgroups save).
 constexpr int kMinSplitKeys = 512;
+// The vector-ALU kernels' workgroups are small and latency-bound: one 64-key
+// tile per split already pays (the tiny fp32 chain, 133 slots on 4 heads).
+constexpr int kMinSplitKeysValu = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnPlan {
@@ -98,7 +101,7 @@ AttnPlan plan_attention(const spec_verify_config& c, int B, int T, size_t max_pa
     const long base_waves = pairs * p.rowblocks * p.waves * (p.mfma ? sv::kMfmaHalves : 1);
     long want = (kTargetWaves + base_waves - 1) / base_waves;
     const long keys = c.kv_capacity;
-    const long max_split = std::max(1L, keys / kMinSplitKeys);
+    const long max_split = std::max(1L, keys / (p.mfma ? kMinSplitKeys : kMinSplitKeysValu));
     long ns = std::max(1L, std::min(want, max_split));
     for (;;) {
         long chunk = (keys + ns - 1) / ns;
@@ -217,13 +220,14 @@ long attention_blocks(const AttnPlan& p, int B, int Hkv) {
 
 // Whether the attention launch carries the row statistics: 256-thread
 // attention workgroups (the statistics' size), dense caches, no top-p cut, no
-// per-stage timing, and an attention grid that leaves at least half of the
-// CUs idle (at the llama7b Medusa shape 128 workgroups on 256 CUs).
+// per-stage timing, and room on the CUs for both grids at once (at the
+// llama7b Medusa shape 128 attention and 64 statistics workgroups on 256 CUs).
 bool fuse_row_stats(const Workspace& ws, const AttnPlan& p, int B, int Hkv, const sv::StatsParams& tp, bool paged,
                     bool timing) {
     const int threads = p.mfma ? p.waves * 64 * sv::kMfmaHalves : (p.tiled ? sv::kStatsThreads : 64);
+    const long stats_blocks = (long)B * (tp.sampling ? 2 * tp.T : tp.T);
     return threads == sv::kStatsThreads && !paged && !timing && ws.cus > 0 && sv::row_stats_streams(tp) &&
-           2 * attention_blocks(p, B, Hkv) <= ws.cus;
+           attention_blocks(p, B, Hkv) + stats_blocks <= ws.cus;
 }
 
 struct spec_verify_handle {
@@ -876,6 +880,8 @@ int spec_verify_describe(spec_verify_handle* h, int32_t batch, int32_t nodes, ch
     const bool walk = do_vocab && sampling && (c.flags & SPEC_VERIFY_FLAG_LOSSLESS_TREE);
     const AttnPlan plan = plan_attention(c, batch, nodes, h->ws.part_rows_cap);
     sv::StatsParams tp{};
+    tp.B = batch;
+    tp.T = nodes;
     tp.V = c.vocab;
     tp.sampling = sampling ? 1 : 0;
     tp.top_p = sampling ? c.top_p : 1.f;
