@@ -190,39 +190,41 @@ __device__ __forceinline__ double topp_scan(double need, float top_p, ToppSmem& 
 // Top-p rows held on chip (V <= 32768): exact significand sums.
 //
 // A kept-mass candidate e (an unnormalised probability: normal, at most 1)
-// with exponent field E and 24-bit significand s equals s * 2^(E - 150), and
-// every element of a level-1 bucket (pattern bits 29..20: seven exponent
-// bits and three significand bits) shares E.  Level 1 therefore adds, per
-// bucket, the u64 value (1 << 48) + pattern: the top bits count the elements
-// n and the low 48 bits hold the sum of patterns (below 2^46), from which the
-// significand sum is sum - n * ((E - 1) << 23), exact.  The scan converts each
-// bucket to units of 2^-48 (exact for E >= 102; a bucket of e < 2^-25 is
-// rounded to the nearest unit, an error below 2^-49 of the largest
-// probability, and the row total stays below 2^63).  Levels 2 and 3 lie
-// inside the crossing bucket and stay in significand units; the nucleus
-// normaliser is assembled from the two parts in fp64.
+// with exponent field E and 24-bit significand s equals s * 2^(E - 150).  The
+// radix buckets keep the pattern's top bits, so every element of a bucket
+// shares the bits above it: a bucket's significand sum follows exactly from
+// its element count n and the sum of its patterns modulo 2^32, as long as
+// the bits below the bucket's prefix add up to less than 2^32.  Every LDS
+// atomic is therefore a 32-bit add (count, pattern), and the probabilities
+// stay in their registers (no 64-bit operand pairs): with at most 64 VGPRs a
+// CU holds two rows at once, so one row's loads overlap another's cut and
+// 352 rows of 32000 logits run in one wave of workgroups.
 //
-// Only candidates (e >= 2^-12) enter the level-1 histogram: the others are
-// summed per thread (fp32 within a float4, fp64 across them: a fixed order
-// of additions, then fixed-order wave and block sums), and the cut lies among
-// the candidates whenever top_p times the row total is at most their mass.
-// At the batch-32 chain shape this leaves about 5% of the logits for the LDS
-// atomics.  A row whose cut lies lower (a flat distribution, or top_p close
-// to 1) adds the others to the histogram too and scans again, with the row
-// total taken from the histogram alone.
+// Level 1 buckets are pattern bits 29..20 (seven exponent bits, three
+// significand bits), in windows of 13 exponents (104 buckets, 8 copies by
+// lane & 7 so that each copy holds at most V/8 = 4096 elements and its
+// low-20-bit sum stays below 2^32).  Window 0 holds the candidates, e >=
+// 2^-12; the others are summed per thread (fp32 within a float4, fp64 across
+// them, in a fixed order) and the cut lies among the candidates whenever
+// top_p times the row total is at most their mass.  At the batch-32 chain
+// shape that leaves about 5% of the logits for the atomics.  A row whose cut
+// lies lower (a flat distribution, or top_p close to 1) takes the next
+// windows down, one register pass each, until one holds the crossing.  Each
+// level-1 bucket is converted to units of 2^-48 (exact for E >= 102; a bucket
+// of e < 2^-25 is rounded to the nearest unit, below 2^-49 of the largest
+// probability; the row total stays below 2^63).  Levels 2 and 3 lie inside
+// the crossing bucket and count significand units; the nucleus normaliser is
+// assembled from the two parts in fp64.
 constexpr int kMassUnitsLog2 = 48;                  // level-1 scan units: 2^-48
 constexpr int kExactExp = 150 - kMassUnitsLog2;     // smallest exponent field converted exactly
 constexpr uint32_t kCandBits = 115u << 23;          // 2^-12: smallest candidate
+constexpr int kWinExps = 13;                        // exponents per level-1 window
+constexpr int kWinBuckets = 8 * kWinExps;           // 104
+constexpr int kH1Copies = 8;
+constexpr int kTopBucket = 1016;                    // level-1 bucket of 1.0 (exponent 127)
+constexpr int kNListCap = 128;                      // per-wave list of the crossing bucket's elements
 
 __device__ __forceinline__ uint32_t significand(uint32_t bits) { return (bits & 0x7FFFFFu) | 0x800000u; }
-constexpr unsigned long long kCountOne = 1ull << 48;   // one element in a level-1 bucket entry
-constexpr int kTopBucket = 1016;                        // level-1 bucket of 1.0 (exponent 127)
-
-// Significand sum of level-1 bucket k from its entry (count << 48) + sum of patterns.
-__device__ __forceinline__ unsigned long long bucket_significands(unsigned long long entry, int k) {
-    const unsigned long long n = entry >> 48, pat = entry & (kCountOne - 1);
-    return pat - n * ((unsigned long long)((k >> 3) - 1) << 23);
-}
 
 // Level-1 bucket k (exponent field k >> 3) with significand sum h, in 2^-48 units.
 __device__ __forceinline__ unsigned long long bucket_units(unsigned long long h, int k) {
@@ -259,50 +261,42 @@ __device__ __forceinline__ int wave_min_dpp(int v) {
 }
 
 struct NucleusSmem {
-    unsigned long long h1[1024 * HK];   // level 1: copy c of bucket k at k * HK + c
-    unsigned long long h2[1024];
-    unsigned long long h3[1024];
+    uint32_t h1[kWinBuckets][kH1Copies][2];   // level 1, one window: (count, pattern sum mod 2^32)
+    uint32_t h2[1024][2];                     // level 2: (count, pattern sum mod 2^32)
+    uint32_t h3[1024];                        // level 3: counts
     unsigned long long wt[4][TNW];
-    double wtail[TNW];                  // per wave: fp64 mass of the elements below the candidates
+    double wtail[TNW];                        // per wave: fp64 mass of the elements below the candidates
     unsigned long long sel_above[4];
     unsigned long long sel_mass[4];
     int sel_bucket[4];
     int sel_found[4];
-    double needv[4];
+    double needv;
+    unsigned long long win_total;
     float wmax[TNW];
     int wbest[TNW];
     unsigned long long cnt[2][TNW];
-    uint32_t list[TNW * kListCap];      // per wave: patterns of its elements in the level-1 crossing bucket
+    uint32_t list[TNW * kNListCap];           // per wave: patterns of its elements in the level-1 crossing bucket
 };
 
-// Crossing bucket of one level (selection slot S): the bucket where the mass
-// counted from the largest bucket down first reaches need; without one (need
-// outside (0, total]) bucket 0, with sel_found[S] = 0.  units(k) is bucket
-// k's mass.  With TOTAL the level sets need to top_p times (its total +
-// extra()), extra() being mass outside the buckets in the same units
-// (evaluated after the first barrier).  Returns need, the same in every
-// thread.  The first kScanThreads threads scan, 1024 / kScanThreads buckets
-// each (with all 1024 threads, one bucket each: the scan is a chain of
-// dependent steps, and one bucket per thread measured 26.4 against 28.0 us at
-// four buckets per thread on one wave per SIMD).
-constexpr int kScanThreads = 1024;
-template <int S, bool TOTAL, int TPB, class U, class X>
-__device__ __forceinline__ double nucleus_scan(double need, float top_p, NucleusSmem& sm, U&& units, X&& extra) {
-    constexpr int SCT = TPB < kScanThreads ? TPB : kScanThreads;
-    constexpr int BPT = 1024 / SCT, NWS = SCT / kWave;
-    static_assert(BPT * SCT == 1024 && NWS <= TNW, "buckets per thread");
+// Crossing bucket of one level (selection slot S) among NB buckets, bucket
+// j = 0 the largest: the bucket where the mass counted from the top, starting
+// at `above`, first reaches need; without one (need outside (above, above +
+// total]) sel_found[S] = 0 and bucket NB - 1.  units(j) is bucket j's mass.
+// With TOTAL need becomes top_p times (total + extra()), extra() being mass
+// outside the buckets in the same units (evaluated after the first barrier);
+// the total lands in win_total.  Threads 0..NB-1 hold one bucket each.
+// Returns need, the same in every thread.
+template <int S, int NB, bool TOTAL, int TPB, class U, class X>
+__device__ __forceinline__ double nucleus_scan(double need, unsigned long long above, float top_p, NucleusSmem& sm,
+                                               U&& units, X&& extra) {
+    constexpr int NWS = (NB + kWave - 1) / kWave;
+    static_assert(NB <= TPB && NWS <= TNW, "one bucket per thread");
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    const bool scanner = tid < SCT;
-    const int bk0 = 1023 - BPT * tid;   // this thread's largest bucket
-    unsigned long long xs[BPT];
+    const bool scanner = tid < NWS * kWave;
     unsigned long long x = 0, incl = 0;
     __syncthreads();
     if (scanner) {
-#pragma unroll
-        for (int q = 0; q < BPT; ++q) {
-            xs[q] = units(bk0 - q);
-            x += xs[q];
-        }
+        x = tid < NB ? units(tid) : 0ull;
         incl = wave_scan_u64(x);
         if (lane == kWave - 1) sm.wt[S][wave] = incl;
     }
@@ -311,33 +305,29 @@ __device__ __forceinline__ double nucleus_scan(double need, float top_p, Nucleus
         const unsigned long long wsc = wave_scan_u64(lane < NWS ? sm.wt[S][lane] : 0ull);
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         const unsigned long long total = readlane_u64(wsc, NWS - 1);
-        incl += wv > 0 ? readlane_u64(wsc, wv - 1) : 0ull;
+        incl += (wv > 0 ? readlane_u64(wsc, wv - 1) : 0ull) + above;
         const unsigned long long excl = incl - x;
         if (TOTAL) {
             need = (double)top_p * ((double)total + extra());
-            if (tid == 0) sm.needv[S] = need;
-        }
-        const bool exists = 0.0 < need && need <= (double)total;
-        // the integer bounds, as doubles, tile (0, total] without gaps: one
-        // thread's range holds need, and one of its buckets
-        const bool mine = exists ? ((double)excl < need && need <= (double)incl) : tid == SCT - 1;
-        if (mine) {
-            unsigned long long lo = excl;
-#pragma unroll
-            for (int q = 0; q < BPT; ++q) {
-                const unsigned long long hi = lo + xs[q];
-                if (exists ? ((double)lo < need && need <= (double)hi) : q == BPT - 1) {
-                    sm.sel_bucket[S] = bk0 - q;
-                    sm.sel_above[S] = lo;
-                    sm.sel_mass[S] = xs[q];
-                    sm.sel_found[S] = exists ? 1 : 0;
-                }
-                lo = hi;
+            if (tid == 0) {
+                sm.needv = need;
+                sm.win_total = total;
             }
         }
+        // the integer bounds, as doubles, tile (above, above + total] without
+        // gaps: at most one bucket holds need
+        const bool exists = (double)above < need && need <= (double)(above + total);
+        if (exists ? ((double)excl < need && need <= (double)incl) : tid == NB - 1) {
+            sm.sel_bucket[S] = tid;
+            sm.sel_above[S] = excl;
+            sm.sel_mass[S] = x;
+            sm.sel_found[S] = exists ? 1 : 0;
+            if (!TOTAL && tid == NB - 1) sm.win_total = total;
+        }
+        if (!TOTAL && tid == 0) sm.win_total = total;
     }
     __syncthreads();
-    return TOTAL ? sm.needv[S] : need;
+    return TOTAL ? sm.needv : need;
 }
 
 // TPB threads per row, N4 = CHUNK / (4 TPB) float4 per thread.
@@ -354,13 +344,18 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const bool aligned = (((uintptr_t)row) & 15) == 0;
     constexpr int N4 = CHUNK / (4 * TPB), NWB = TPB / kWave;
+    static_assert(N4 * 4 * TPB <= 8 * 4096, "each level-1 copy holds at most 4096 elements");
     float4 e[N4];
     issue_chunk<N4, TPB>(row, V, 0, aligned, e);
+    auto clear_h1 = [&]() {
+        for (int k = tid; k < kWinBuckets * kH1Copies * 2; k += TPB) (&sm.h1[0][0][0])[k] = 0u;
+    };
     // cleared histograms are ordered before their atomics by the next barrier
-    for (int k = tid; k < 1024 * HK; k += TPB) sm.h1[k] = 0ull;
+    clear_h1();
     for (int k = tid; k < 1024; k += TPB) {
-        sm.h2[k] = 0ull;
-        sm.h3[k] = 0ull;
+        sm.h2[k][0] = 0u;
+        sm.h2[k][1] = 0u;
+        sm.h3[k] = 0u;
     }
     // entries past the row end (read as 0) become -inf; only slots that
     // reach V need the test
@@ -395,15 +390,12 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
     bi = wave_min_dpp(bi);
     if (lane == 0) sm.wbest[wave] = bi;   // read after the next barrier
 
-    // unnormalised probabilities; candidates into level 1 ((count, pattern
-    // sum) per bucket, HK copies by lane), the others into an fp64 sum
-    uint8_t* const h1c = (uint8_t*)sm.h1 + 8 * (lane & (HK - 1));
-    auto add_h1 = [&](uint32_t bits) {
-        atomicAdd((unsigned long long*)(h1c + ((bits >> 15) & (1023u * 8 * HK))), kCountOne + bits);
-    };
+    // unnormalised probabilities; candidates into level-1 window 0 (anything
+    // at or above 2^-12, non-numbers in its last bucket, which carries no
+    // mass), the others into an fp64 sum
+    uint32_t* const h1c = &sm.h1[0][lane & (kH1Copies - 1)][0];
+    const uint32_t one = 1u;
     {
-        // the others' sum: fp32 within each float4 (four terms below 2^-12,
-        // relative error below 2^-22), fp64 across them, in a fixed order
         double tail = 0.0;
 #pragma unroll
         for (int j = 0; j < N4; ++j) {
@@ -415,7 +407,11 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
                 const uint32_t bits = __float_as_uint(v);
                 const bool cand = bits >= kCandBits;
                 t4[c] = cand ? 0.f : v;
-                if (cand) add_h1(bits);
+                if (cand) {
+                    const uint32_t i = min((bits >> 20) - (uint32_t)(8 * (127 - kWinExps + 1)), (uint32_t)kWinBuckets - 1);
+                    atomicAdd(h1c + i * (kH1Copies * 2), one);
+                    atomicAdd(h1c + i * (kH1Copies * 2) + 1, bits);
+                }
             }
             tail += (double)((t4[0] + t4[1]) + (t4[2] + t4[3]));
             // added where it is made (left to itself the compiler makes every
@@ -425,52 +421,88 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
         const double wtl = wave_sum_d(tail);
         if (lane == 0) sm.wtail[wave] = wtl;   // read after the scan's first barrier
     }
-    // buckets of exponent 0 (zeros, subnormals) and above the bucket of 1.0
-    // (non-numbers) carry no mass
-    auto h1_significands = [&](int k) -> unsigned long long {
-        if (k < 8 || k > kTopBucket) return 0ull;
-        unsigned long long s = 0;
+    // the probabilities, opaque to the compiler from here on: values it
+    // derived from them above (bucket indices) are not kept alive for reuse
 #pragma unroll
-        for (int c = 0; c < HK; ++c) s += sm.h1[k * HK + c];
-        return bucket_significands(s, k);
+    for (int j = 0; j < N4; ++j) asm volatile("" : "+v"(e[j].x), "+v"(e[j].y), "+v"(e[j].z), "+v"(e[j].w));
+    // significand sum of window bucket i (level-1 bucket k_lo + i): each
+    // copy's low 20 bits from its count and pattern sum
+    int k_lo = 8 * (127 - kWinExps + 1);   // the window's smallest bucket
+    int nb = kWinBuckets;                  // and its bucket count
+    auto win_significands = [&](int i) -> unsigned long long {
+        const int k = k_lo + i;
+        if (k < 8 || k > kTopBucket) return 0ull;   // zeros and subnormals; non-numbers
+        unsigned long long n = 0, low = 0;
+        const uint32_t pre = (uint32_t)k << 20;
+#pragma unroll
+        for (int c = 0; c < kH1Copies; ++c) {
+            const uint32_t nc = sm.h1[i][c][0];
+            n += nc;
+            low += (uint32_t)(sm.h1[i][c][1] - nc * pre);   // below 2^32: at most 4096 elements per copy
+        }
+        return low + n * (0x800000ull | ((unsigned long long)(k & 7) << 20));
     };
-    auto h1_units = [&](int k) { return bucket_units(h1_significands(k), k); };
-    double need = nucleus_scan<0, true, TPB>(0.0, P.top_p, sm, h1_units, [&]() {
+    // scan index t = nb - 1 - i: the largest bucket first
+    auto win_units = [&](int t) -> unsigned long long {
+        const int i = nb - 1 - t;
+        return i >= 0 ? bucket_units(win_significands(i), k_lo + i) : 0ull;
+    };
+    const double need = nucleus_scan<0, kWinBuckets, true, TPB>(0.0, 0ull, P.top_p, sm, win_units, [&]() {
         double t = 0.0;
 #pragma unroll
         for (int w = 0; w < NWB; ++w) t += sm.wtail[w];
         return ldexp(t, kMassUnitsLog2);
     });
-    int s1 = 0;   // selection slot of level 1
-    if (!sm.sel_found[0]) {
-        // the cut lies below the candidates: the others join the histogram
+    unsigned long long above = 0ull;   // mass of the windows above the current one (2^-48 units)
+    int found = sm.sel_found[0];
+    // the cut lies below the candidates: windows further down, one register
+    // pass each, until one holds the crossing
+    for (int E_hi = 127 - kWinExps; !found && need > 0.0 && E_hi >= 1; E_hi -= kWinExps) {
+        above += sm.win_total;
+        const int E_lo = max(1, E_hi - kWinExps + 1);
+        k_lo = 8 * E_lo;
+        nb = 8 * (E_hi - E_lo + 1);
+        __syncthreads();   // every thread has read the previous window
+        clear_h1();
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < N4; ++j)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const uint32_t bits = __float_as_uint(f4get(e[j], c));
-                if (bits < kCandBits) add_h1(bits);
+                const uint32_t i = (bits >> 20) - (uint32_t)k_lo;
+                if (i < (uint32_t)nb) {
+                    atomicAdd(h1c + i * (kH1Copies * 2), one);
+                    atomicAdd(h1c + i * (kH1Copies * 2) + 1, bits);
+                }
             }
-        need = nucleus_scan<3, true, TPB>(0.0, P.top_p, sm, h1_units, []() { return 0.0; });
-        s1 = 3;
+        nucleus_scan<0, kWinBuckets, false, TPB>(need, above, P.top_p, sm, win_units, []() { return 0.0; });
+        found = sm.sel_found[0];
     }
-    const uint32_t b1 = (uint32_t)sm.sel_bucket[s1];
-    const unsigned long long a1 = sm.sel_above[s1];
-    const int E1 = (int)(b1 >> 3);
-    const unsigned long long h_b1 = h1_significands((int)b1);   // the crossing bucket's significand sum
+    // b1: the crossing level-1 bucket; a1: the mass above it (2^-48 units);
+    // without a crossing every nonzero mass is kept
+    int b1 = 0;
+    unsigned long long a1 = above + sm.win_total, h_b1 = 0ull;
+    if (found) {
+        const int i = nb - 1 - sm.sel_bucket[0];
+        b1 = k_lo + i;
+        a1 = sm.sel_above[0];
+        h_b1 = win_significands(i);
+    }
+    const int E1 = b1 >> 3;
     // what is left to reach, in significand units of bucket b1 (the level-1
     // conversion of a bucket below 2^-25 rounded: clamp to the bucket's sum)
     double need1 = 0.0;
-    if (need > 0.0 && h_b1 > 0) need1 = fmin(ldexp(need - (double)a1, kExactExp - E1), (double)h_b1);
+    if (found && need > 0.0) need1 = fmin(ldexp(need - (double)a1, kExactExp - E1), (double)h_b1);
 
     // levels 2 and 3 only see bucket b1: each wave lists its elements there
     // (writes and reads of a wave's own list need no barrier) and reads the
     // list, or its registers when the list is too short for them.  A bucket
     // that carries mass has an exponent field of 1..127 and lies at or below
     // bucket 1016, so matching its pattern bits implies carrying mass.
-    constexpr int CAP = TNW * kListCap / NWB;
+    constexpr int CAP = TNW * kNListCap / NWB;
     uint32_t* const mylist = sm.list + wave * CAP;
-    const uint32_t b1m = h_b1 > 0 ? b1 : 0xFFFFFFFFu;
+    const uint32_t b1m = found ? (uint32_t)b1 : 0xFFFFFFFFu;
     uint32_t nlist = 0;
 #pragma unroll
     for (int j = 0; j < N4; ++j)
@@ -487,16 +519,16 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
             nlist += (uint32_t)__popcll(mask);
         }
     const bool listed = nlist <= (uint32_t)CAP;
-    // prefix of the elements a level counts: pattern >> pshift == prefix
-    // (made opaque to the compiler, so that the register pass does not keep
-    // the listing's 64 comparison masks alive to reuse them)
-    auto accumulate = [&](unsigned long long* h, int shift, int pshift, uint32_t prefix) {
+    // elements whose pattern >> pshift equals prefix go through f (the prefix
+    // made opaque to the compiler, so that the register pass does not keep
+    // the listing's comparison masks alive to reuse them)
+    auto each_in = [&](int pshift, uint32_t prefix, auto&& f) {
         prefix = (uint32_t)__builtin_amdgcn_readfirstlane((int)prefix);
         asm volatile("" : "+s"(prefix));
         if (listed) {
             for (uint32_t i = (uint32_t)lane; i < nlist; i += kWave) {
                 const uint32_t bits = mylist[i];
-                if ((bits >> pshift) == prefix) atomicAdd(&h[(bits >> shift) & 1023], (unsigned long long)significand(bits));
+                if ((bits >> pshift) == prefix) f(bits);
             }
         } else {
 #pragma unroll
@@ -504,28 +536,43 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const uint32_t bits = __float_as_uint(f4get(e[j], c));
-                    if ((bits >> pshift) == prefix)
-                        atomicAdd(&h[(bits >> shift) & 1023], (unsigned long long)significand(bits));
+                    if ((bits >> pshift) == prefix) f(bits);
                 }
         }
     };
-    auto none = []() { return 0.0; };
-    accumulate(sm.h2, 10, 20, b1m);
-    nucleus_scan<1, false, TPB>(need1, P.top_p, sm, [&](int k) { return sm.h2[k]; }, none);
-    const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
+    // level 2: (count, pattern sum) of pattern bits 19..10; each bucket's low
+    // 10 bits add up to below 2^25
+    each_in(20, b1m, [&](uint32_t bits) {
+        const uint32_t k2 = (bits >> 10) & 1023u;
+        atomicAdd(&sm.h2[k2][0], one);
+        atomicAdd(&sm.h2[k2][1], bits);
+    });
+    nucleus_scan<1, 1024, false, TPB>(need1, 0ull, P.top_p, sm, [&](int t) -> unsigned long long {
+        const uint32_t k2 = 1023u - (uint32_t)t;
+        const uint32_t n = sm.h2[k2][0];
+        const uint32_t pre = (((uint32_t)b1 << 10) | k2) << 10;
+        return (unsigned long long)(uint32_t)(sm.h2[k2][1] - n * pre) +
+               (unsigned long long)n * (0x800000ull | (pre & 0x7FFFFFu));
+    }, []() { return 0.0; });
+    const uint32_t b2 = 1023u - (uint32_t)sm.sel_bucket[1];
     const unsigned long long a2 = sm.sel_above[1];
     double need2 = 0.0;
     if (need1 > 0.0) need2 = fmin(need1 - (double)a2, (double)sm.sel_mass[1]);
-    accumulate(sm.h3, 0, 10, h_b1 > 0 ? ((b1 << 10) | b2) : 0xFFFFFFFFu);
-    nucleus_scan<2, false, TPB>(need2, P.top_p, sm, [&](int k) { return sm.h3[k]; }, none);
+    // level 3: counts of the exact patterns
+    const uint32_t p3 = found ? (((uint32_t)b1 << 10) | b2) : 0xFFFFFFFFu;
+    each_in(10, p3, [&](uint32_t bits) { atomicAdd(&sm.h3[bits & 1023u], one); });
+    nucleus_scan<2, 1024, false, TPB>(need2, 0ull, P.top_p, sm, [&](int t) -> unsigned long long {
+        const uint32_t k3 = 1023u - (uint32_t)t;
+        return (unsigned long long)sm.h3[k3] * significand((((uint32_t)b1 << 10 | b2) << 10) | k3);
+    }, []() { return 0.0; });
     Nucleus nu;
-    nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
+    nu.thr = found ? ((((uint32_t)b1 << 10 | b2) << 10) | (1023u - (uint32_t)sm.sel_bucket[2])) : 0u;
     nu.cutoff = INT_MAX;
     // significand-unit masses above thr inside b1, and of the elements at thr
     // (all of the last bucket: (number of ties) * (significand of one))
     const unsigned long long a3 = sm.sel_above[2];
-    unsigned long long kept = sm.sel_mass[2];
-    const unsigned long long tie_mass = h_b1 > 0 ? significand(nu.thr) : 0ull;
+    unsigned long long kept = found ? sm.sel_mass[2] : 0ull;
+    const unsigned long long tie_mass = found ? significand(nu.thr) : 0ull;
     if (tie_mass > 0 && kept > 0) {
         const unsigned long long ties = kept / tie_mass;
         long long k = (long long)ceil((need2 - (double)a3) / (double)tie_mass);
@@ -564,12 +611,13 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
         for (int w = 1; w < NWB; ++w) best = min(best, sm.wbest[w]);
         // normaliser of the nucleus: the buckets above b1 (2^-48 units) and
         // the kept part of b1 (significand units, 2^(E1 - 150) each)
+        const unsigned long long in_b1 = found ? a2 + a3 + kept : 0ull;
         RowStat st;
         st.zmax = M;
         st.argmax = best;
         st.thr = nu.thr;
         st.cutoff = nu.cutoff;
-        st.Z = ldexp((double)a1, -kMassUnitsLog2) + ldexp((double)(a2 + a3 + kept), E1 - 150);
+        st.Z = ldexp((double)a1, -kMassUnitsLog2) + ldexp((double)in_b1, E1 - 150);
         P.stats[(size_t)b * nrows + r] = st;
     }
 }
