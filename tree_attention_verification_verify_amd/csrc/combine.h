@@ -19,6 +19,37 @@ constexpr int combine_rows_per_block() { return 256 / (D / 8); }
 // Up to this many splits a thread loads all of its partials at once.
 constexpr int kCombineMaxSplits = 8;
 
+// Merge of NS splits of one row slice: every split's (m, l) and columns are
+// loaded before any is used (one round trip to memory instead of one per
+// split); a split that saw no key holds no columns and is skipped.
+template <int NS, int D>
+__device__ __forceinline__ void combine_fixed(const AttnParams& P, int pair, int r, int d0, float& lsum, floatx4_t& a0,
+                                              floatx4_t& a1) {
+    float2 ml[NS];
+    floatx4_t o0[NS], o1[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const size_t prow = ((size_t)pair * NS + s) * P.Rpad + r;
+        ml[s] = P.part_ml[prow];
+        const floatx4_t* src = (const floatx4_t*)(P.part_o + prow * D + d0);
+        o0[s] = src[0];
+        o1[s] = src[1];
+    }
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (ml[s].y > 0.f) mmax = fmaxf(mmax, ml[s].x);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if (ml[s].y > 0.f) {
+            const float w = exp2f(ml[s].x - mmax);
+            lsum += ml[s].y * w;
+            a0 += w * o0[s];
+            a1 += w * o1[s];
+        }
+    }
+}
+
 // Merge block `blk` run by 256 threads, t = 0..255 this thread's index among them.
 template <bool BF16, int D>
 __device__ __forceinline__ void combine_block(const AttnParams& P, long blk, int t) {
@@ -36,33 +67,15 @@ __device__ __forceinline__ void combine_block(const AttnParams& P, long blk, int
     float lsum = 0.f;
     floatx4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
     if (P.nsplit <= kCombineMaxSplits) {
-        // every split's (m, l) and columns loaded before any is used: one
-        // round trip to memory instead of one per split
-        float2 ml[kCombineMaxSplits];
-        floatx4_t o0[kCombineMaxSplits], o1[kCombineMaxSplits];
-#pragma unroll
-        for (int s = 0; s < kCombineMaxSplits; ++s) {
-            if (s < P.nsplit) {
-                const size_t prow = ((size_t)pair * P.nsplit + s) * P.Rpad + r;
-                ml[s] = P.part_ml[prow];
-                const floatx4_t* src = (const floatx4_t*)(P.part_o + prow * D + d0);
-                o0[s] = src[0];
-                o1[s] = src[1];
-            }
-        }
-        float mmax = -INFINITY;
-#pragma unroll
-        for (int s = 0; s < kCombineMaxSplits; ++s)
-            if (s < P.nsplit && ml[s].y > 0.f) mmax = fmaxf(mmax, ml[s].x);
-#pragma unroll
-        for (int s = 0; s < kCombineMaxSplits; ++s) {
-            // a split that saw no key holds no columns: skipped, not weighted by 0
-            if (s < P.nsplit && ml[s].y > 0.f) {
-                const float w = exp2f(ml[s].x - mmax);
-                lsum += ml[s].y * w;
-                a0 += w * o0[s];
-                a1 += w * o1[s];
-            }
+        switch (P.nsplit) {
+            case 1: combine_fixed<1, D>(P, pair, r, d0, lsum, a0, a1); break;
+            case 2: combine_fixed<2, D>(P, pair, r, d0, lsum, a0, a1); break;
+            case 3: combine_fixed<3, D>(P, pair, r, d0, lsum, a0, a1); break;
+            case 4: combine_fixed<4, D>(P, pair, r, d0, lsum, a0, a1); break;
+            case 5: combine_fixed<5, D>(P, pair, r, d0, lsum, a0, a1); break;
+            case 6: combine_fixed<6, D>(P, pair, r, d0, lsum, a0, a1); break;
+            case 7: combine_fixed<7, D>(P, pair, r, d0, lsum, a0, a1); break;
+            default: combine_fixed<8, D>(P, pair, r, d0, lsum, a0, a1); break;
         }
     } else {
         float mmax = -INFINITY;
