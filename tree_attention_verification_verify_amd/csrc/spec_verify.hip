@@ -45,10 +45,11 @@ constexpr int kTimingRing = 1024;
 constexpr int kEventsPerRun = SPEC_VERIFY_NUM_STAGES + 1;
 constexpr int kTargetWaves = 2048;   // two waves per SIMD on 256 CUs
 // Each prefix split takes at least this many keys: at the llama7b-medusa-greedy
-// shape (2112 slots, 32 KV heads, one sequence) 4 splits take 27.7 us per step
-// against 30.2 us for 7 (the merge of the partials costs more than the extra
-// workgroups save).
-constexpr int kMinSplitKeys = 512;
+// shape (2112 slots, 32 KV heads, one sequence) 6 splits (192 attention
+// workgroups, with the 64 row-statistics workgroups beside them on 256 CUs)
+// take 19.7 us per step against 20.2 us for 4 or 5; 7 would leave no room
+// for the statistics.
+constexpr int kMinSplitKeys = 352;
 // The vector-ALU kernels' workgroups are small and latency-bound: one 64-key
 // tile per split already pays (the tiny fp32 chain, 133 slots on 4 heads).
 constexpr int kMinSplitKeysValu = 64;
