@@ -55,7 +55,9 @@ extern "C" {
 #define SPEC_VERIFY_SAMPLING 1
 
 /* config.flags: record HIP events around each kernel of every run (see
- * spec_verify_timing_read).  Costs a few event records per run. */
+ * spec_verify_timing_read).  Costs a few event records per run, and keeps
+ * the three stages in launches of their own (no row statistics inside the
+ * attention launch), so each stage's time can be read. */
 #define SPEC_VERIFY_FLAG_TIMING 1u
 /* config.flags, sampling mode only: lossless multi-candidate tree sampling.
  * Instead of testing every node independently against its parent's p and
@@ -347,7 +349,10 @@ const char* spec_verify_last_error(void);
  * into buf (host memory, NUL-terminated): the names of the kernels it
  * launches ("" for a part that is skipped), the attention's waves per
  * workgroup, row blocks, prefix splits and keys per split, whether the
- * finishing launch selects and/or merges splits.  For tools that report
+ * finishing launch selects and/or merges splits, and whether the row
+ * statistics run inside the attention launch ("vocab_in_attention_launch":
+ * small attention grids that leave room on the CUs, dense caches, no top-p
+ * cut, handles without SPEC_VERIFY_FLAG_TIMING).  For tools that report
  * per-kernel figures (the pages ask for the latency of each round:
  * "投机解码的五条路线", section "怎么选,以及怎么算收益").  Errors: INVALID_ARG
  * (NULL argument, batch or nodes out of range, buffer too small). */
