@@ -142,29 +142,33 @@ def test_top_p_cut_inside_a_group_of_tied_probabilities(vocab):
     assert int(got["node_accept"][:, 1:].sum()) > 0
 
 
-def test_top_p_cut_below_the_candidate_probabilities():
-    # one logit at 10 and 2999 near 1.34 (e about 2^-12.6 of the top one):
-    # the 90% nucleus ends among the small ones, below the 2^-12 the on-chip
-    # kernel histograms first, so it takes its next exponent window down
-    spec = synth.workload("chain-batch32-topp", batch=4, prefix_len=80, ragged=None, vocab=3000, top_p=0.9,
-                          temperature=1.0, seed=(4, 3000))
+@pytest.mark.parametrize("vocab,seed", [(3000, 3001), (40000, 40000)])
+def test_top_p_cut_below_the_candidate_probabilities(vocab, seed):
+    # one logit at 10, 3000 near 1.34 (e about 2^-12.6 of the top one), the
+    # rest at -10.8 (about 2^-30): the 90% nucleus ends among the 3000, below
+    # the 2^-12 that the top-p kernels histogram first, so they take their next
+    # exponent window down (on chip at 3000 ids, streamed at 40000)
+    spec = synth.workload("chain-batch32-topp", batch=4, prefix_len=80, ragged=None, vocab=vocab, top_p=0.9,
+                          temperature=1.0, seed=(4, seed))
     case = synth.make_case(spec)
-    rng = np.random.default_rng(3000)
+    rng = np.random.default_rng(seed)
     B, T = case.batch, case.nodes
+    small = rng.choice(vocab, size=3000, replace=False)
     for logits, noise in ((case.target_logits, 0.0), (case.draft_logits, 0.3)):
-        base = rng.normal(1.336, 0.15, size=logits.shape).astype(np.float32)
-        logits[:] = base + (rng.normal(0, noise, size=logits.shape).astype(np.float32) if noise else 0)
-    top = rng.integers(0, 3000, size=(B, T))
+        logits[:] = -10.8
+        base = rng.normal(1.336, 0.15, size=(B, T, small.size)).astype(np.float32)
+        logits[:, :, small] = base + (rng.normal(0, noise, size=base.shape).astype(np.float32) if noise else 0)
+    top = rng.integers(0, vocab, size=(B, T))
     for b in range(B):
         for t in range(T):
             case.target_logits[b, t, top[b, t]] = 10.0
             case.draft_logits[b, t, top[b, t]] = 10.0
-    case.tokens[:, 1:] = rng.integers(0, 3000, size=(B, T - 1))
+    case.tokens[:, 1:] = rng.choice(small, size=(B, T - 1))
     z = case.target_logits[0, 0].astype(np.float64)
     e = np.sort(np.exp(z - z.max()))[::-1]
     cut = int(np.searchsorted(np.cumsum(e / e.sum()), 0.9))
     assert e[cut] < 2.0 ** -12      # the cut lies below the first window
-    got, ref, _ = check(case, "topp-below-candidates")
+    got, ref, _ = check(case, "topp-below-candidates-V%d" % vocab)
     assert int(got["node_accept"][:, 1:].sum()) > 0
 
 

@@ -21,7 +21,6 @@ constexpr int VPT4 = 8;                     // float4 per thread per chunk
 constexpr int CHUNK = NT * VPT4 * 4;
 static_assert(CHUNK == kVocabChunk, "chunk size");
 constexpr int MAX_CHUNKS = 128;
-constexpr float kFix = 1099511627776.0f;    // 2^40: fixed-point scale of top-p masses
 
 struct Smem {
     double d[NW];
@@ -212,7 +211,6 @@ __device__ __forceinline__ bool in_nucleus(float e, int idx, const Nucleus& nu) 
 // membership test can be skipped.
 __device__ __forceinline__ bool keeps_all(const Nucleus& nu) { return nu.thr == 0u && nu.cutoff == INT_MAX; }
 
-__device__ __forceinline__ unsigned long long fixmass(float e) { return (unsigned long long)__float2ull_rn(e * kFix); }
 
 // Totals of the weights of every slot j (token ids cb + 4*(t + NT*j) + e over
 // all threads t), all slots in one reduction: stored in sm.slot_tot[j]; the

@@ -15,8 +15,8 @@
 // probability relative to the final max: a row of up to 32768 logits is held
 // in the registers of a 1024-thread workgroup and cut by a 3-level radix
 // select on the fp32 bit patterns with exact integer masses (significand sums
-// per bucket, see the kernel); a longer row is streamed once per step of the
-// same cut with fixed-point masses.
+// per bucket, see the kernel); a longer row is streamed twice, its candidates
+// for the cut listed on chip.
 
 #include "row_block.h"
 #include "stats_stream.h"
@@ -31,159 +31,12 @@ __global__ __launch_bounds__(ST) void row_stats_stream_kernel(StatsParams P) {
     row_stats_stream_block<WITH_Z>(P, blockIdx.x);
 }
 
-// ---------------------------------------------------------------------------
-// Top-p cut of the streamed rows (V > 32768): a 3-level radix select (10 bits
-// per level, from the top) on the fp32 patterns of the unnormalised
-// probabilities, with fixed-point (2^-40) mass histograms.  Each level costs
-// three barriers: histogram; scan of the buckets in descending order inside
-// each wave; wave offsets read by every thread (integer sums, so any order
-// gives the same result) and the crossing bucket published.  The first level
-// sees every logit, so its histogram has HK copies (lane & (HK - 1)),
-// interleaved per bucket so the copies of one bucket sit in different banks:
-// a wave's 64 atomics then collide HK times less on the crowded buckets.
-constexpr int HK = 4;
 constexpr int TNW = rows::NW;
-constexpr int kListCap = 256;   // per-wave list of the elements in the first level's crossing bucket
-constexpr uint32_t kZeroMassBits = 0x2B000000u;   // 2^-41: rounds to mass 0 (ties to even)
-constexpr uint32_t kOneBits = 0x3F800000u;        // 1.0
-
-struct ToppSmem {
-    unsigned long long h1[1024 * HK];   // level 1: copy c of bucket k at k * HK + c
-    unsigned long long h2[1024];
-    unsigned long long h3[1024];
-    unsigned long long wt[3][TNW];      // per level: wave totals of the bucket scan
-    unsigned long long sel_above[3];    // per level: mass of the larger buckets
-    unsigned long long sel_mass[3];     // per level: mass of the crossing bucket
-    int sel_bucket[3];
-    float bv[TNW];
-    int bi[TNW];
-    unsigned long long cnt[2][TNW];
-    uint32_t list[TNW][kListCap];       // per wave: patterns of its elements in the first-level bucket
-};
 
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
     return ((unsigned long long)hi << 32) | lo;
-}
-
-// One level of the cut, in two parts.  Accumulate: elements whose pattern
-// above bit PSHIFT equals `prefix` add their mass to bucket
-// (bits >> SHIFT) & 1023 (no barrier: a row may take several chunks).  Scan:
-// the crossing is the bucket where the mass counted from the largest bucket
-// down first reaches need (for level 0 need is top_p times the row total,
-// which only the scan knows); without a crossing (need outside (0, total])
-// bucket 0.
-template <int L, int N = rows::VPT4>
-__device__ __forceinline__ void topp_accumulate(const float4 (&e)[N], uint32_t prefix, ToppSmem& sm) {
-    using namespace rows;
-    constexpr int SHIFT = 20 - 10 * L;
-    constexpr int PSHIFT = L == 0 ? 31 : 30 - 10 * L;
-    constexpr int HC = L == 0 ? HK : 1;
-    unsigned long long* h = L == 0 ? sm.h1 : (L == 1 ? sm.h2 : sm.h3);
-    const int copy = L == 0 ? (lane_() & (HK - 1)) : 0;
-    // only masses in (0, 2^40] count: entries past the row end (e = 0),
-    // probabilities at or below 2^-41 (zero in fixed point) and non-numbers
-    // add nothing
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float v = f4get(e[j], c);
-            const uint32_t bits = __float_as_uint(v);
-            if (bits > kZeroMassBits && bits <= kOneBits && (bits >> PSHIFT) == prefix)
-                atomicAdd(&h[((bits >> SHIFT) & 1023) * HC + copy], fixmass(v));
-        }
-}
-
-// Levels 1 and 2 from a wave's list instead of its registers (the same
-// elements: the list holds every one of the wave's nonzero masses in the
-// first level's crossing bucket); lanes take entries in turn.
-template <int L>
-__device__ __forceinline__ void topp_accumulate_list(const uint32_t* list, uint32_t n, uint32_t prefix, ToppSmem& sm) {
-    constexpr int SHIFT = 20 - 10 * L;
-    constexpr int PSHIFT = 30 - 10 * L;
-    static_assert(L == 1 || L == 2, "list levels");
-    unsigned long long* h = L == 1 ? sm.h2 : sm.h3;
-    for (uint32_t i = (uint32_t)rows::lane_(); i < n; i += kWave) {
-        const uint32_t bits = list[i];
-        if ((bits >> PSHIFT) == prefix) atomicAdd(&h[(bits >> SHIFT) & 1023], rows::fixmass(__uint_as_float(bits)));
-    }
-}
-
-// The wave's elements with a nonzero mass in first-level bucket b1, appended
-// to its list after the n already there (positions by ballot); returns how
-// many there are now (the list holds them when that is at most kListCap).
-// The same in every lane.
-template <int N = rows::VPT4, int CAP = kListCap>
-__device__ __forceinline__ uint32_t topp_compact(const float4 (&e)[N], uint32_t b1, uint32_t* list, uint32_t n = 0) {
-    using namespace rows;
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t bits = __float_as_uint(f4get(e[j], c));
-            const bool m = bits > kZeroMassBits && bits <= kOneBits && (bits >> 20) == b1;
-            const unsigned long long mask = __ballot(m);
-            if (m) {
-                const uint32_t pos = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-                if (pos < (uint32_t)CAP) list[pos] = bits;
-            }
-            n += (uint32_t)__popcll(mask);
-        }
-    return n;
-}
-
-// The crossing bucket lands in sm.sel_*[L].  Returns need (level 0: the one
-// it computed).  TPB threads: each takes 1024 / TPB consecutive buckets in
-// descending order (thread order = descending bucket).
-template <int L, int TPB = rows::NT>
-__device__ __forceinline__ double topp_scan(double need, float top_p, ToppSmem& sm) {
-    using namespace rows;
-    constexpr int HC = L == 0 ? HK : 1;
-    constexpr int BPT = 1024 / TPB, NWB = TPB / kWave;
-    static_assert(BPT * TPB == 1024 && NWB <= TNW, "buckets per thread");
-    unsigned long long* h = L == 0 ? sm.h1 : (L == 1 ? sm.h2 : sm.h3);
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    __syncthreads();
-    const int bk0 = 1023 - BPT * tid;   // this thread's largest bucket
-    unsigned long long xs[BPT];
-    unsigned long long x = 0;
-#pragma unroll
-    for (int q = 0; q < BPT; ++q) {
-        xs[q] = 0;
-#pragma unroll
-        for (int c = 0; c < HC; ++c) xs[q] += h[(bk0 - q) * HC + c];
-        x += xs[q];
-    }
-    unsigned long long incl = wave_scan_u64(x);
-    if (lane == kWave - 1) sm.wt[L][wave] = incl;
-    __syncthreads();
-    // lanes 0..NWB-1 scan the wave totals; this wave's offset and the total
-    // are then read from single lanes
-    const unsigned long long wsc = wave_scan_u64(lane < NWB ? sm.wt[L][lane] : 0ull);
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const unsigned long long total = readlane_u64(wsc, NWB - 1);
-    incl += wv > 0 ? readlane_u64(wsc, wv - 1) : 0ull;
-    const unsigned long long excl = incl - x;
-    if (L == 0) need = (double)top_p * (double)total;
-    // the integer bounds, as doubles, tile (0, (double)total] without gaps, so
-    // a crossing exists exactly when need lies in that range, and is unique
-    const bool exists = 0.0 < need && need <= (double)total;
-    unsigned long long lo = excl;
-#pragma unroll
-    for (int q = 0; q < BPT; ++q) {
-        const unsigned long long hi = lo + xs[q];
-        if (exists ? ((double)lo < need && need <= (double)hi) : (tid == TPB - 1 && q == BPT - 1)) {
-            sm.sel_bucket[L] = bk0 - q;
-            sm.sel_above[L] = lo;
-            sm.sel_mass[L] = xs[q];
-        }
-        lo = hi;
-    }
-    __syncthreads();
-    return need;
 }
 
 // ---------------------------------------------------------------------------
@@ -277,6 +130,32 @@ struct NucleusSmem {
     unsigned long long cnt[2][TNW];
     uint32_t list[TNW * kNListCap];           // per wave: patterns of its elements in the level-1 crossing bucket
 };
+
+// Significand sum of bucket i of the level-1 window whose smallest bucket is
+// k_lo: each copy's low 20 bits from its count and pattern sum (below 2^32:
+// at most 4096 elements per copy).  Buckets of exponent 0 (zeros,
+// subnormals) and above the bucket of 1.0 (non-numbers) carry no mass.
+__device__ __forceinline__ unsigned long long win_significands(const NucleusSmem& sm, int k_lo, int i) {
+    const int k = k_lo + i;
+    if (k < 8 || k > kTopBucket) return 0ull;
+    unsigned long long n = 0, low = 0;
+    const uint32_t pre = (uint32_t)k << 20;
+#pragma unroll
+    for (int c = 0; c < kH1Copies; ++c) {
+        const uint32_t nc = sm.h1[i][c][0];
+        n += nc;
+        low += (uint32_t)(sm.h1[i][c][1] - nc * pre);
+    }
+    return low + n * (0x800000ull | ((unsigned long long)(k & 7) << 20));
+}
+
+// Significand sum of level-2 bucket k2 inside level-1 bucket b1: each
+// element's low 10 bits from the count and pattern sum (below 2^25).
+__device__ __forceinline__ unsigned long long level2_significands(const NucleusSmem& sm, uint32_t b1, uint32_t k2) {
+    const uint32_t n = sm.h2[k2][0];
+    const uint32_t pre = ((b1 << 10) | k2) << 10;
+    return (unsigned long long)(uint32_t)(sm.h2[k2][1] - n * pre) + (unsigned long long)n * (0x800000ull | (pre & 0x7FFFFFu));
+}
 
 // Crossing bucket of one level (selection slot S) among NB buckets, bucket
 // j = 0 the largest: the bucket where the mass counted from the top, starting
@@ -429,19 +308,7 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
     // copy's low 20 bits from its count and pattern sum
     int k_lo = 8 * (127 - kWinExps + 1);   // the window's smallest bucket
     int nb = kWinBuckets;                  // and its bucket count
-    auto win_significands = [&](int i) -> unsigned long long {
-        const int k = k_lo + i;
-        if (k < 8 || k > kTopBucket) return 0ull;   // zeros and subnormals; non-numbers
-        unsigned long long n = 0, low = 0;
-        const uint32_t pre = (uint32_t)k << 20;
-#pragma unroll
-        for (int c = 0; c < kH1Copies; ++c) {
-            const uint32_t nc = sm.h1[i][c][0];
-            n += nc;
-            low += (uint32_t)(sm.h1[i][c][1] - nc * pre);   // below 2^32: at most 4096 elements per copy
-        }
-        return low + n * (0x800000ull | ((unsigned long long)(k & 7) << 20));
-    };
+    auto win_significands = [&](int i) { return sv::win_significands(sm, k_lo, i); };
     // scan index t = nb - 1 - i: the largest bucket first
     auto win_units = [&](int t) -> unsigned long long {
         const int i = nb - 1 - t;
@@ -547,12 +414,8 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
         atomicAdd(&sm.h2[k2][0], one);
         atomicAdd(&sm.h2[k2][1], bits);
     });
-    nucleus_scan<1, 1024, false, TPB>(need1, 0ull, P.top_p, sm, [&](int t) -> unsigned long long {
-        const uint32_t k2 = 1023u - (uint32_t)t;
-        const uint32_t n = sm.h2[k2][0];
-        const uint32_t pre = (((uint32_t)b1 << 10) | k2) << 10;
-        return (unsigned long long)(uint32_t)(sm.h2[k2][1] - n * pre) +
-               (unsigned long long)n * (0x800000ull | (pre & 0x7FFFFFu));
+    nucleus_scan<1, 1024, false, TPB>(need1, 0ull, P.top_p, sm, [&](int t) {
+        return level2_significands(sm, (uint32_t)b1, 1023u - (uint32_t)t);
     }, []() { return 0.0; });
     const uint32_t b2 = 1023u - (uint32_t)sm.sel_bucket[1];
     const unsigned long long a2 = sm.sel_above[1];
@@ -622,16 +485,24 @@ __global__ __launch_bounds__(TPB) void row_stats_topp_kernel(StatsParams P) {
     }
 }
 
-// Top-p rows longer than one register chunk (V > 32768).  The same cut, with
-// the row streamed chunk by chunk (each next chunk's loads in flight): one
-// pass for the maximum and its first position, one each for radix levels 1
-// and 2 (level 3 reads the entries of level 1's crossing bucket that the
-// level-2 pass listed, unless a wave's list overflowed), and, only when tied
-// probabilities straddle the cut, one pass counting the ties per chunk and a
-// bisection inside the chunk that holds the k-th tie.
+// Top-p rows longer than one register chunk (V > 32768): the same cut (the
+// same units, windows and levels as the on-chip kernel) with the row
+// streamed, each next block's loads in flight.  Pass 1: the maximum and its
+// first position.  Pass 2: the unnormalised probabilities; candidates (e >=
+// 2^-12) into level-1 window 0 and into a list in LDS (up to kCandListCap
+// entries), the others into the fp64 tail sum.  Levels 2 and 3 then read the
+// list, so a row is streamed twice.  Rarer cases stream again: a cut below
+// the candidates (one pass per lower window, then levels 2 and 3 from the
+// stream), a list that overflowed (levels 2 and 3 from the stream), and tied
+// probabilities straddling the cut (one pass counting the ties per 32768-id
+// chunk, then a bisection inside the chunk that holds the k-th tie).
+constexpr int kCandListCap = 8192;
+
 __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsParams P) {
     using namespace rows;
-    __shared__ ToppSmem sm;
+    __shared__ NucleusSmem sm;
+    __shared__ uint32_t clist[kCandListCap];   // patterns of the candidates (pass 2)
+    __shared__ uint32_t cn;
     __shared__ int chunk_ties[MAX_CHUNKS];
     const int nrows = 2 * P.T;
     const int b = blockIdx.x / nrows, r = blockIdx.x - b * nrows;
@@ -642,92 +513,198 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const bool aligned = (((uintptr_t)row) & 15) == 0;
     constexpr int HB = VPT4 / 2;   // float4 per thread per streamed block (two blocks in flight)
+    constexpr int TPB = NT, NWB = TPB / kWave;
+    auto clear_h1 = [&]() {
+        for (int k = tid; k < kWinBuckets * kH1Copies * 2; k += TPB) (&sm.h1[0][0][0])[k] = 0u;
+    };
     // cleared histograms and counts are ordered before their atomics by the next barrier
-#pragma unroll
-    for (int k = 0; k < HK; ++k) sm.h1[k * NT + tid] = 0ull;
-    sm.h2[tid] = 0ull;
-    sm.h3[tid] = 0ull;
+    clear_h1();
+    for (int k = tid; k < 1024; k += TPB) {
+        sm.h2[k][0] = 0u;
+        sm.h2[k][1] = 0u;
+        sm.h3[k] = 0u;
+    }
     if (tid < MAX_CHUNKS) chunk_ties[tid] = 0;
+    if (tid == 0) cn = 0u;
 
-    // largest logit and its smallest id: per chunk the thread's maximum and
-    // the first of its positions holding it; chunks come in id order
+    // pass 1: the largest logit and its smallest id: per block the thread's
+    // maximum and the first of its positions holding it; blocks come in id order
     float bv = -INFINITY;
     int bi = INT_MAX;
     for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int cb) {
         float m = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < HB; ++j) m = fmaxf(fmaxf(m, fmaxf(x[j].x, x[j].y)), fmaxf(x[j].z, x[j].w));
-        int loc = INT_MAX;
+        for (int k = 0; k < 4 * HB; k += 2) m = max3_f32(m, f4get(x[k / 4], k % 4), f4get(x[k / 4], k % 4 + 1));
+        if (m > bv) {   // the first position holding m has the smallest id of this block
+            int loc = INT_MAX;
 #pragma unroll
-        for (int j = HB - 1; j >= 0; --j)
+            for (int j = HB - 1; j >= 0; --j)
 #pragma unroll
-            for (int c = 3; c >= 0; --c) {
-                const int idx = elem_index(cb, j, c);
-                loc = (f4get(x[j], c) == m && idx < V) ? idx : loc;
-            }
-        if (m > bv || (m == bv && loc < bi)) { bv = m; bi = loc; }
+                for (int c = 3; c >= 0; --c) {
+                    const int idx = elem_index(cb, j, c);
+                    loc = (f4get(x[j], c) == m && idx < V) ? idx : loc;
+                }
+            bv = m;
+            bi = loc;
+        }
     });
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) argmax_step(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
-    if (lane == 0) { sm.bv[wave] = bv; sm.bi[wave] = bi; }
+    if (lane == 0) { sm.wmax[wave] = bv; sm.wbest[wave] = bi; }
     __syncthreads();
-    float M = sm.bv[0];
-    int best = sm.bi[0];
+    float M = sm.wmax[0];
+    int best = sm.wbest[0];
 #pragma unroll
-    for (int w = 1; w < TNW; ++w) argmax_step(M, best, sm.bv[w], sm.bi[w]);
-    auto to_e = [&](auto& x) {
-        constexpr int n = (int)(sizeof(x) / sizeof(float4));
-#pragma unroll
-        for (int j = 0; j < n; ++j)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) f4set(x[j], c, unnorm(f4get(x[j], c), M, ilog));
-    };
+    for (int w = 1; w < NWB; ++w) argmax_step(M, best, sm.wmax[w], sm.wbest[w]);
 
-    // the cut: one streamed pass per level
-    for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) { to_e(x); topp_accumulate<0, HB>(x, 0u, sm); });
-    const double need = topp_scan<0>(0.0, P.top_p, sm);
-    const uint32_t b1 = (uint32_t)sm.sel_bucket[0];
-    const unsigned long long a1 = sm.sel_above[0];
-    // the level-2 pass also lists each wave's elements in bucket b1; level 3
-    // then reads the list, and only a wave whose list overflowed streams its
-    // part of the row once more
-    uint32_t nlist = 0;
-    for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) {
-        to_e(x);
-        topp_accumulate<1, HB>(x, b1, sm);
-        nlist = topp_compact<HB>(x, b1, sm.list[wave], nlist);
+    // pass 2: candidates into level-1 window 0 and the list, the others into
+    // the tail sum
+    uint32_t* const h1c = &sm.h1[0][lane & (kH1Copies - 1)][0];
+    const uint32_t one = 1u;
+    {
+        double tail = 0.0;
+        for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) {
+#pragma unroll
+            for (int j = 0; j < HB; ++j) {
+                float t4[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float v = unnorm(f4get(x[j], c), M, ilog);
+                    const uint32_t bits = __float_as_uint(v);
+                    const bool cand = bits >= kCandBits;
+                    t4[c] = cand ? 0.f : v;
+                    const unsigned long long mask = __ballot(cand);
+                    if (cand) {
+                        const uint32_t i = min((bits >> 20) - (uint32_t)(8 * (127 - kWinExps + 1)), (uint32_t)kWinBuckets - 1);
+                        atomicAdd(h1c + i * (kH1Copies * 2), one);
+                        atomicAdd(h1c + i * (kH1Copies * 2) + 1, bits);
+                    }
+                    if (mask) {   // the wave's candidates of this slot go to the list together
+                        uint32_t at = 0;
+                        if (lane == 0) at = atomicAdd(&cn, (uint32_t)__popcll(mask));
+                        at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at);
+                        const uint32_t pos = at + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                        if (cand && pos < (uint32_t)kCandListCap) clist[pos] = bits;
+                    }
+                }
+                tail += (double)((t4[0] + t4[1]) + (t4[2] + t4[3]));
+            }
+        });
+        const double wtl = wave_sum_d(tail);
+        if (lane == 0) sm.wtail[wave] = wtl;   // read after the scan's first barrier
+    }
+    int k_lo = 8 * (127 - kWinExps + 1);
+    int nb = kWinBuckets;
+    auto win_units = [&](int t) -> unsigned long long {
+        const int i = nb - 1 - t;
+        return i >= 0 ? bucket_units(win_significands(sm, k_lo, i), k_lo + i) : 0ull;
+    };
+    const double need = nucleus_scan<0, kWinBuckets, true, TPB>(0.0, 0ull, P.top_p, sm, win_units, [&]() {
+        double t = 0.0;
+#pragma unroll
+        for (int w = 0; w < NWB; ++w) t += sm.wtail[w];
+        return ldexp(t, kMassUnitsLog2);
     });
-    topp_scan<1>(need - (double)a1, P.top_p, sm);
-    const uint32_t b2 = (uint32_t)sm.sel_bucket[1];
+    unsigned long long above = 0ull;
+    int found = sm.sel_found[0];
+    const bool in_list = found && cn <= (uint32_t)kCandListCap;   // the crossing bucket's elements are listed
+    for (int E_hi = 127 - kWinExps; !found && need > 0.0 && E_hi >= 1; E_hi -= kWinExps) {
+        above += sm.win_total;
+        const int E_lo = max(1, E_hi - kWinExps + 1);
+        k_lo = 8 * E_lo;
+        nb = 8 * (E_hi - E_lo + 1);
+        __syncthreads();   // every thread has read the previous window
+        clear_h1();
+        __syncthreads();
+        for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) {
+#pragma unroll
+            for (int j = 0; j < HB; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t bits = __float_as_uint(unnorm(f4get(x[j], c), M, ilog));
+                    const uint32_t i = (bits >> 20) - (uint32_t)k_lo;
+                    if (i < (uint32_t)nb) {
+                        atomicAdd(h1c + i * (kH1Copies * 2), one);
+                        atomicAdd(h1c + i * (kH1Copies * 2) + 1, bits);
+                    }
+                }
+        });
+        nucleus_scan<0, kWinBuckets, false, TPB>(need, above, P.top_p, sm, win_units, []() { return 0.0; });
+        found = sm.sel_found[0];
+    }
+    int b1 = 0;
+    unsigned long long a1 = above + sm.win_total, h_b1 = 0ull;
+    if (found) {
+        const int i = nb - 1 - sm.sel_bucket[0];
+        b1 = k_lo + i;
+        a1 = sm.sel_above[0];
+        h_b1 = win_significands(sm, k_lo, i);
+    }
+    const int E1 = b1 >> 3;
+    double need1 = 0.0;
+    if (found && need > 0.0) need1 = fmin(ldexp(need - (double)a1, kExactExp - E1), (double)h_b1);
+    const uint32_t b1m = found ? (uint32_t)b1 : 0xFFFFFFFFu;
+    // elements whose pattern >> pshift equals prefix go through f: from the
+    // list when it holds the crossing bucket, else from the stream
+    auto each_in = [&](int pshift, uint32_t prefix, auto&& f) {
+        if (in_list) {
+            const uint32_t n = cn;
+            for (uint32_t i = (uint32_t)tid; i < n; i += TPB) {
+                const uint32_t bits = clist[i];
+                if ((bits >> pshift) == prefix) f(bits);
+            }
+        } else {
+            for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) {
+#pragma unroll
+                for (int j = 0; j < HB; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t bits = __float_as_uint(unnorm(f4get(x[j], c), M, ilog));
+                        if ((bits >> pshift) == prefix) f(bits);
+                    }
+            });
+        }
+    };
+    each_in(20, b1m, [&](uint32_t bits) {
+        const uint32_t k2 = (bits >> 10) & 1023u;
+        atomicAdd(&sm.h2[k2][0], one);
+        atomicAdd(&sm.h2[k2][1], bits);
+    });
+    nucleus_scan<1, 1024, false, TPB>(need1, 0ull, P.top_p, sm, [&](int t) {
+        return level2_significands(sm, (uint32_t)b1, 1023u - (uint32_t)t);
+    }, []() { return 0.0; });
+    const uint32_t b2 = 1023u - (uint32_t)sm.sel_bucket[1];
     const unsigned long long a2 = sm.sel_above[1];
-    const uint32_t p2 = (b1 << 10) | b2;
-    if (nlist <= (uint32_t)kListCap)
-        topp_accumulate_list<2>(sm.list[wave], nlist, p2, sm);
-    else
-        for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int) { to_e(x); topp_accumulate<2, HB>(x, p2, sm); });
-    topp_scan<2>(need - (double)a1 - (double)a2, P.top_p, sm);
+    double need2 = 0.0;
+    if (need1 > 0.0) need2 = fmin(need1 - (double)a2, (double)sm.sel_mass[1]);
+    const uint32_t p3 = found ? (((uint32_t)b1 << 10) | b2) : 0xFFFFFFFFu;
+    each_in(10, p3, [&](uint32_t bits) { atomicAdd(&sm.h3[bits & 1023u], one); });
+    nucleus_scan<2, 1024, false, TPB>(need2, 0ull, P.top_p, sm, [&](int t) -> unsigned long long {
+        const uint32_t k3 = 1023u - (uint32_t)t;
+        return (unsigned long long)sm.h3[k3] * significand((((uint32_t)b1 << 10 | b2) << 10) | k3);
+    }, []() { return 0.0; });
     Nucleus nu;
-    nu.thr = (b1 << 20) | (b2 << 10) | (uint32_t)sm.sel_bucket[2];
+    nu.thr = found ? ((((uint32_t)b1 << 10 | b2) << 10) | (1023u - (uint32_t)sm.sel_bucket[2])) : 0u;
     nu.cutoff = INT_MAX;
-    const unsigned long long above = a1 + a2 + sm.sel_above[2];
-    unsigned long long kept = sm.sel_mass[2];
-    const unsigned long long tie_mass = fixmass(__uint_as_float(nu.thr));
-    if (tie_mass > 0) {
+    const unsigned long long a3 = sm.sel_above[2];
+    unsigned long long kept = found ? sm.sel_mass[2] : 0ull;
+    const unsigned long long tie_mass = found ? significand(nu.thr) : 0ull;
+    if (tie_mass > 0 && kept > 0) {
         const unsigned long long ties = kept / tie_mass;
-        long long k = (long long)ceil((need - (double)above) / (double)tie_mass);
+        long long k = (long long)ceil((need2 - (double)a3) / (double)tie_mass);
         if (k < 1) k = 1;
         if (ties > 1 && (unsigned long long)k < ties) {
             // ties straddle the cut: ties per chunk, then the smallest cutoff c
             // with #ties(id < c) >= k by bisection inside the chunk holding
             // the k-th tie (block counts, alternating buffers)
             for_each_chunk<HB>(row, V, aligned, [&](float4 (&x)[HB], int cb) {
-                to_e(x);
                 unsigned long long cnt = 0;
 #pragma unroll
                 for (int j = 0; j < HB; ++j)
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        if (elem_index(cb, j, c) < V && __float_as_uint(f4get(x[j], c)) == nu.thr) ++cnt;
+                        if (elem_index(cb, j, c) < V && __float_as_uint(unnorm(f4get(x[j], c), M, ilog)) == nu.thr) ++cnt;
                 cnt = wave_sum_u64(cnt);
                 if (lane == 0) atomicAdd(&chunk_ties[cb / CHUNK], (int)cnt);
             });
@@ -742,7 +719,10 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
             const int cb = cstar * CHUNK;
             float4 e[VPT4];
             load_chunk(row, V, cb, aligned, e);
-            to_e(e);
+#pragma unroll
+            for (int j = 0; j < VPT4; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) f4set(e[j], c, unnorm(f4get(e[j], c), M, ilog));
             int lo = cb, hi = min(V, cb + CHUNK) - 1, par = 0;
             while (lo < hi) {
                 const int mid = lo + (hi - lo) / 2;
@@ -759,7 +739,7 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
                 __syncthreads();
                 unsigned long long tot = (unsigned long long)before;
 #pragma unroll
-                for (int w = 0; w < TNW; ++w) tot += sm.cnt[par][w];
+                for (int w = 0; w < NWB; ++w) tot += sm.cnt[par][w];
                 par ^= 1;
                 if (tot >= (unsigned long long)k) hi = mid; else lo = mid + 1;
             }
@@ -768,12 +748,13 @@ __global__ __launch_bounds__(rows::NT) void row_stats_topp_chunked_kernel(StatsP
         }
     }
     if (tid == 0) {
+        const unsigned long long in_b1 = found ? a2 + a3 + kept : 0ull;
         RowStat st;
         st.zmax = M;
         st.argmax = best;
         st.thr = nu.thr;
         st.cutoff = nu.cutoff;
-        st.Z = (double)(above + kept) * (1.0 / (double)kFix);
+        st.Z = ldexp((double)a1, -kMassUnitsLog2) + ldexp((double)in_b1, E1 - 150);
         P.stats[(size_t)b * nrows + r] = st;
     }
 }
