@@ -49,6 +49,8 @@ def _run(case, label, **flags):
     ("chain-batch32-topp", dict(batch=3, prefix_len=200, ragged=None, seed=(21, 2))),     # top-p 0.9, tau 0.8
     ("longctx-bigvocab", dict(batch=2, prefix_len=64, seed=(21, 3))),                      # V = 128256, tau 0.7
     ("longctx-bigvocab", dict(batch=2, prefix_len=64, top_p=0.8, seed=(21, 4))),           # streamed top-p cut
+    ("tiny-chain-f32", dict(batch=2, seed=(21, 5))),                     # statistics in the attention launch
+    ("llama7b-medusa-greedy", dict(mode="sampling", prefix_len=300, seed=(21, 6))),        # the same, MFMA
 ])
 def test_write_probs_rows_match_the_oracle(name, kw):
     case = synth.make_case(synth.workload(name, **kw))
@@ -87,6 +89,37 @@ def test_skip_flags_leave_the_other_half_bit_identical(name, kw):
     ref = oracle.verify(case)
     assert not ref["seq_near"].any()
     np.testing.assert_array_equal(full["out_tokens"], ref["out_tokens"])
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny-chain-f32", dict(batch=2, seed=(24, 1))),                              # tiled VALU attention
+    ("llama7b-medusa-greedy", dict(prefix_len=900, seed=(24, 2))),                # MFMA, prefix splits
+    ("llama7b-medusa-greedy", dict(mode="sampling", prefix_len=300, seed=(24, 3))),
+])
+def test_row_statistics_inside_the_attention_launch(name, kw):
+    """Small attention grids carry the row statistics in the same launch; a
+    timing handle keeps them apart.  Both give the same outputs bit for bit."""
+    import json
+    import torch
+    from tree_attention_verification_verify_amd import SpecVerify
+
+    case = synth.make_case(synth.workload(name, **kw))
+    cfg = handle_config(case.spec, kv_capacity=case.k_cache.shape[2])
+    with torch.cuda.device(0):
+        with SpecVerify(**cfg) as sv:
+            plan = sv.describe(case.batch, case.nodes)
+        with SpecVerify(**dict(cfg, timing=True)) as sv:
+            tplan = sv.describe(case.batch, case.nodes)
+    plan = plan if isinstance(plan, dict) else json.loads(plan)
+    tplan = tplan if isinstance(tplan, dict) else json.loads(tplan)
+    assert plan["vocab_in_attention_launch"] == 1 and tplan["vocab_in_attention_launch"] == 0, (plan, tplan)
+    fused = run_gpu(case, "fused-" + name)[0]
+    apart = _run(case, "apart-" + name, timing=True)
+    for k in DECISIONS + ("attn_out",):
+        np.testing.assert_array_equal(fused[k], apart[k], err_msg=k)
+    ref = oracle.verify(case, attention=False)
+    assert not ref["seq_near"].any()
+    np.testing.assert_array_equal(fused["out_tokens"], ref["out_tokens"])
 
 
 def test_lossless_walk_gives_up_without_hanging():
