@@ -44,7 +44,7 @@ RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop/byte
 KERNEL_SOURCES = {"attn_mfma_kernel": "tree_attn.hip", "attn_valu_kernel": "tree_attn.hip",
                   "attn_valu_tiled_kernel": "tree_attn_valu.hip",
                   "row_stats_stream_kernel": "vocab_stats.hip", "row_stats_topp_kernel": "vocab_stats.hip",
-                  "row_stats_topp_chunked_kernel": "vocab_stats.hip", "finish_kernel": "select_final.hip"}
+                  "finish_kernel": "select_final.hip"}
 HEADLINE = ("70b-gqa-medusa", None)
 SUBRECORDS = [("tiny-chain-f32", None), ("llama7b-medusa-greedy", None), ("chain-batch32-topp", None),
               ("70b-gqa-medusa", "greedy"), ("longctx-bigvocab", None)]

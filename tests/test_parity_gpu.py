@@ -119,26 +119,29 @@ def test_largest_vocabulary():
     check(synth.make_case(spec), "max-vocab", max_near=1)
 
 
-@pytest.mark.parametrize("vocab", [3000, 70000])
-def test_top_p_cut_inside_a_group_of_tied_probabilities(vocab):
-    # one large logit and a group of equal ones spread over the row: with
-    # top_p = 0.5 the cut falls inside the group, so only its first k members
-    # by token id are kept (the kernel's tie cutoff; at 70000 ids the group
-    # spans three chunks and the cutoff is found in the chunk holding the
-    # k-th member)
-    spec = synth.workload("chain-batch32-topp", batch=3, prefix_len=100, ragged=None, vocab=vocab, top_p=0.5,
-                          temperature=1.0, seed=(4, vocab))
+@pytest.mark.parametrize("vocab,group,top_p", [(3000, 1000, 0.5), (70000, 23333, 0.5), (3000, 10, 0.965)])
+def test_top_p_cut_inside_a_group_of_tied_probabilities(vocab, group, top_p):
+    # one large logit and a group of equal ones spread over the row: the cut
+    # falls inside the group, so only its first k members by token id are
+    # kept (the kernel's tie cutoff; at 70000 ids the group spans three chunks
+    # and the cutoff is found in the chunk holding the k-th member; a group of
+    # 10 is few enough for the crossing bucket to be ranked by one wave)
+    spec = synth.workload("chain-batch32-topp", batch=3, prefix_len=100, ragged=None, vocab=vocab, top_p=top_p,
+                          temperature=1.0, seed=(4, vocab if group >= 1000 else vocab + group))
     case = synth.make_case(spec)
-    rng = np.random.default_rng(vocab)
+    rng = np.random.default_rng(vocab if group >= 1000 else vocab + group)
     B, T = case.batch, case.nodes
-    group = rng.choice(vocab, size=vocab // 3, replace=False)
-    for top, logits in ((group[0], case.target_logits), (group[1], case.draft_logits)):
+    members = rng.choice(vocab, size=group, replace=False)
+    for top, logits in ((members[0], case.target_logits), (members[1], case.draft_logits)):
         logits[:] = -20.0
-        logits[:, :, group] = 0.0
+        logits[:, :, members] = 0.0
         logits[:, :, top] = 5.0      # p and q differ only in their top token
+    e_tie = np.exp(-5.0)
+    k = int(np.ceil((top_p * (1.0 + (group - 1) * e_tie) - 1.0) / e_tie))
+    assert 1 < k < group - 1        # the cut lies inside the group
     # drafted tokens: members of the group on both sides of the cutoff
-    case.tokens[:, 1:] = rng.choice(group[2:], size=(B, T - 1))
-    got, ref, _ = check(case, "topp-ties-V%d" % vocab)
+    case.tokens[:, 1:] = rng.choice(members[2:], size=(B, T - 1))
+    got, ref, _ = check(case, "topp-ties-V%d-G%d" % (vocab, group))
     assert int(got["node_accept"][:, 1:].sum()) > 0
 
 
@@ -169,6 +172,39 @@ def test_top_p_cut_below_the_candidate_probabilities(vocab, seed):
     cut = int(np.searchsorted(np.cumsum(e / e.sum()), 0.9))
     assert e[cut] < 2.0 ** -12      # the cut lies below the first window
     got, ref, _ = check(case, "topp-below-candidates-V%d" % vocab)
+    assert int(got["node_accept"][:, 1:].sum()) > 0
+
+
+@pytest.mark.parametrize("layout,seed", [("flat", 7101), ("one-wave", 7102)])
+def test_top_p_candidate_list_overflow(layout, seed):
+    # rows whose candidates for the cut (e >= 2^-12 of the largest) do not fit
+    # a wave's list segment of 1024 entries, so level 1 and levels 2 and 3
+    # read the row again: 300 ids near logit 0 hold the nucleus, and ids near
+    # -7 (e about 2^-11) are candidates outside it: every other id of the row,
+    # or the ids that one wave of a 512-thread row workgroup holds (thread t
+    # holds ids 4 (t + 512 j) + c, so wave 0 the ids with ((id >> 2) & 511) < 64)
+    vocab = 32000
+    spec = synth.workload("chain-batch32-topp", batch=3, prefix_len=90, ragged=None, vocab=vocab, top_p=0.9,
+                          temperature=1.0, seed=(4, seed))
+    case = synth.make_case(spec)
+    rng = np.random.default_rng(seed)
+    B, T = case.batch, case.nodes
+    ids = np.arange(vocab)
+    top = rng.choice(vocab, size=300, replace=False)
+    mid = np.setdiff1d(ids if layout == "flat" else ids[((ids >> 2) & 511) < 64], top)
+    for logits, noise in ((case.target_logits, 0.0), (case.draft_logits, 0.2)):
+        logits[:] = -20.0
+        for sel, centre in ((top, 0.0), (mid, -7.0)):
+            base = rng.normal(centre, 0.3, size=(B, T, sel.size)).astype(np.float32)
+            logits[:, :, sel] = base + (rng.normal(0, noise, size=base.shape).astype(np.float32) if noise else 0)
+    case.tokens[:, 1:] = rng.choice(top, size=(B, T - 1))
+    z = case.target_logits[0, 0].astype(np.float64)
+    e = np.exp(z - z.max())
+    in_wave0 = ((ids >> 2) & 511) < 64
+    assert int((e[in_wave0] >= 2.0 ** -12).sum()) > 1024
+    if layout == "flat":
+        assert int((e >= 2.0 ** -12).sum()) > 8192
+    got, ref, _ = check(case, "topp-list-overflow-%s" % layout)
     assert int(got["node_accept"][:, 1:].sum()) > 0
 
 

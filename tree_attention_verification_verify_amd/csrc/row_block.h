@@ -1,6 +1,7 @@
-// Block-wide helpers for the 1024-thread row kernels (wave64, gfx950):
-// deterministic reductions and scans, register-resident logits chunks, the
-// top-p membership test and the inverse-CDF search.  Internal to the library.
+// Block-wide helpers for the row kernels (wave64, gfx950; 1024 threads unless
+// a helper takes the workgroup size): deterministic reductions and scans,
+// register-resident logits chunks, the top-p membership test and the
+// inverse-CDF search.  Internal to the library.
 //
 // Element layout of a chunk: thread t holds float4 slots j = 0..VPT4-1 at
 // token ids cb + 4*(t + NT*j) + e, so (j, t, e) order is token-id order and
@@ -158,22 +159,22 @@ __device__ __forceinline__ void load_chunk(const float* row, int V, int cb, bool
     mask_chunk<N, TPB>(V, cb, x);
 }
 
-// f(x, cb) for every block of N float4 per thread (4 N NT ids at cb) of a row
-// in order, each next block's loads in flight while f runs (loaded
+// f(x, cb) for every block of N float4 per thread (4 N TPB ids at cb) of a
+// row in order, each next block's loads in flight while f runs (loaded
 // unconditionally: a conditional load would make the compiler's later waits
 // count as if it had not been issued).
-template <int N = VPT4, class F>
+template <int N = VPT4, int TPB = NT, class F>
 __device__ __forceinline__ void for_each_chunk(const float* row, int V, bool aligned, F&& f) {
-    constexpr int STEP = 4 * NT * N;
+    constexpr int STEP = 4 * TPB * N;
     float4 xa[N], xb[N];
-    issue_chunk<N>(row, V, 0, aligned, xa);
+    issue_chunk<N, TPB>(row, V, 0, aligned, xa);
     for (int cb = 0; cb < V; cb += 2 * STEP) {
-        issue_chunk<N>(row, V, cb + STEP, aligned, xb);
-        mask_chunk<N>(V, cb, xa);
+        issue_chunk<N, TPB>(row, V, cb + STEP, aligned, xb);
+        mask_chunk<N, TPB>(V, cb, xa);
         f(xa, cb);
         if (cb + STEP >= V) break;
-        issue_chunk<N>(row, V, cb + 2 * STEP, aligned, xa);
-        mask_chunk<N>(V, cb + STEP, xb);
+        issue_chunk<N, TPB>(row, V, cb + 2 * STEP, aligned, xa);
+        mask_chunk<N, TPB>(V, cb + STEP, xb);
         f(xb, cb + STEP);
     }
 }
