@@ -119,13 +119,15 @@ def test_largest_vocabulary():
     check(synth.make_case(spec), "max-vocab", max_near=1)
 
 
-@pytest.mark.parametrize("vocab,group,top_p", [(3000, 1000, 0.5), (70000, 23333, 0.5), (3000, 10, 0.965)])
+@pytest.mark.parametrize("vocab,group,top_p", [(3000, 1000, 0.5), (70000, 23333, 0.5), (3000, 10, 0.965),
+                                               (40000, 10, 0.965)])
 def test_top_p_cut_inside_a_group_of_tied_probabilities(vocab, group, top_p):
     # one large logit and a group of equal ones spread over the row: the cut
     # falls inside the group, so only its first k members by token id are
     # kept (the kernel's tie cutoff; at 70000 ids the group spans three chunks
     # and the cutoff is found in the chunk holding the k-th member; a group of
-    # 10 is few enough for the crossing bucket to be ranked by one wave)
+    # 10 is few enough for the crossing bucket to be ranked without the radix
+    # levels, on chip at 3000 ids and streamed over two chunks at 40000)
     spec = synth.workload("chain-batch32-topp", batch=3, prefix_len=100, ragged=None, vocab=vocab, top_p=top_p,
                           temperature=1.0, seed=(4, vocab if group >= 1000 else vocab + group))
     case = synth.make_case(spec)
