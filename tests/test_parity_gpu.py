@@ -177,6 +177,16 @@ def test_top_p_cut_below_the_candidate_probabilities(vocab, seed):
     assert int(got["node_accept"][:, 1:].sum()) > 0
 
 
+@pytest.mark.parametrize("vocab,seed", [(16, 1601), (100, 1001), (777, 7771)])
+def test_top_p_small_vocabularies(vocab, seed):
+    # rows far shorter than one register slot of the top-p workgroup (2048
+    # ids): most threads hold only masked entries, and a vocabulary of 777 is
+    # not a multiple of 4 (single-float loads)
+    spec = synth.workload("chain-batch32-topp", batch=4, prefix_len=64, ragged=None, vocab=vocab, seed=(4, seed))
+    got, ref, _ = check(synth.make_case(spec), "topp-small-V%d" % vocab)
+    assert int(got["node_accept"][:, 1:].sum()) > 0
+
+
 @pytest.mark.parametrize("layout,seed", [("flat", 7101), ("one-wave", 7102)])
 def test_top_p_candidate_list_overflow(layout, seed):
     # rows whose candidates for the cut (e >= 2^-12 of the largest) do not fit
