@@ -824,7 +824,10 @@ def main():
     if args.traffic_summary:
         import synth
         spec = synth.workload(args.workload, **({"mode": args.mode} if args.mode else {}))
-        traffic_summary(args.traffic_summary, "%s-%s" % (args.workload, spec.mode), args.kernel)
+        label = "%s-%s" % (args.workload, spec.mode)
+        if args.top_p is not None:   # a top-p setting other than the workload's own
+            label = "%s-topp%g-%s" % (args.workload, args.top_p, spec.mode)
+        traffic_summary(args.traffic_summary, label, args.kernel)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs the verify step on one GPU only; --gpus %d is not supported "
