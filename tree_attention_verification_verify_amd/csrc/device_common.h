@@ -106,6 +106,26 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 // HBM-bound), the row statistics at the 70B GQA tree shape 11% faster.
 constexpr int kStreamPolicy = 2;
 
+// Sequence handled by the workgroups of rank r when a grid is ordered by
+// decreasing kv_len (ties by index), so that the longest prefixes start
+// first and the shortest fill the tail: with more workgroups than fit on the
+// GPU at once, a long prefix started last would otherwise run on alone.  One
+// wave ranks up to 64 sequences (each lane one, the others' lengths
+// broadcast in turn); larger batches keep the index order.  Every wave that
+// calls it gets the same answer.
+__device__ __forceinline__ int seq_by_length(const int* kv_len, int B, int r) {
+    if (B <= 1 || B > kWave) return r;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane < B ? kv_len[lane] : 0;
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+        const int lj = __builtin_amdgcn_readlane(li, j);
+        rank += (lj > li || (lj == li && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long m = __ballot(lane < B && rank == r);
+    return m ? __builtin_ctzll(m) : r;
+}
+
 // Arrival count of a group of G workgroups at a per-group counter: true for
 // the G-th arrival.  The increment wraps to 0 in the same atomic (an old
 // value >= G-1 becomes 0), so no reset store follows and the counter stays in

@@ -67,9 +67,13 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int group = blockIdx.x;
-    const int pair = group / P.nsplit, split = group - pair * P.nsplit;
-    const int b = pair / P.Hkv, kvh = pair - b * P.Hkv;
+    // workgroups in order of decreasing prefix length (longest first); group
+    // is the (sequence, KV head, split) slot of the partial results
+    const int pair0 = blockIdx.x / P.nsplit, split = blockIdx.x - pair0 * P.nsplit;
+    const int rank = pair0 / P.Hkv, kvh = pair0 - rank * P.Hkv;
+    const int b = seq_by_length(P.kv_len, P.B, rank);
+    const int pair = b * P.Hkv + kvh;
+    const int group = pair * P.nsplit + split;
     const int T = P.T, g = P.g, R = P.R;
     const int L = P.kv_len[b];
     bool kv_ok = (L >= 0) && (L <= P.Lcap - T);
