@@ -56,16 +56,17 @@ __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v,
 // segment, no atomics) and sums the others per thread (fp32 within a float4,
 // fp64 across them, in a fixed order).  The cut lies among the candidates
 // whenever top_p times the row total is at most their mass; at the batch-32
-// chain shape the list holds about 5% of a row, and levels 1 to 3 read it
-// instead of the row.  A row whose cut lies lower (a flat distribution, or
-// top_p close to 1) takes the next windows down, one pass over the row each,
-// until one holds the crossing; a wave whose segment overflowed (a flat row)
-// sends the levels to the row as well.  Each level-1 bucket is converted to
-// units of 2^-48 (exact for E >= 102; a bucket of e < 2^-25 is rounded to the
-// nearest unit, below 2^-49 of the largest probability; the row total stays
-// below 2^63).  Levels 2 and 3 lie inside the crossing bucket and count
-// significand units; the nucleus normaliser is assembled from the two parts
-// in fp64.
+// chain shape the list holds about 5% of a row, and level 1 and the search
+// inside the crossing bucket (a ranking of its elements when at most 64,
+// else levels 2 and 3) read it instead of the row.  A row whose cut lies
+// lower (a flat distribution, or top_p close to 1) takes the next windows
+// down, one pass over the row each, until one holds the crossing; a wave
+// whose segment overflowed (a flat row) sends the levels to the row as well.
+// Each level-1 bucket is converted to units of 2^-48 (exact for E >= 102; a
+// bucket of e < 2^-25 is rounded to the nearest unit, below 2^-49 of the
+// largest probability; the row total stays below 2^63).  Inside the crossing
+// bucket masses are counted in significand units; the nucleus normaliser is
+// assembled from the two parts in fp64.
 //
 // A row of up to rows::CHUNK logits is loaded into registers once (its
 // maximum, then its probabilities, from the same registers); a longer row is
@@ -83,7 +84,7 @@ constexpr int kH1Copies = 8;
 constexpr int kTopBucket = 1016;                    // level-1 bucket of 1.0 (exponent 127)
 constexpr int kCandListCap = 8192;                  // listed candidates per row
 constexpr int kToppThreads = 512;                   // threads per top-p row
-constexpr int kFewB1 = kWave;                       // crossing buckets ranked by one wave
+constexpr int kFewB1 = kWave;                       // largest crossing bucket ranked without levels 2 and 3 (a lane per element)
 
 __device__ __forceinline__ uint32_t significand(uint32_t bits) { return (bits & 0x7FFFFFu) | 0x800000u; }
 
@@ -231,7 +232,8 @@ __device__ __forceinline__ double nucleus_scan(double need, unsigned long long a
 // levels 2 and 3 from the row), an overflowed list (level 1 and levels 2 and
 // 3 from the row), and tied probabilities straddling the cut (a pass counting
 // the ties per chunk of rows::CHUNK ids when the row has several, then a
-// bisection on the token id inside the chunk holding the k-th tie).
+// bisection on the token id inside the chunk holding the k-th tie).  The
+// launch bounds ask for two workgroups per CU.
 template <int TPB, bool RESIDENT>
 __global__ __launch_bounds__(TPB, 2 * TPB / (4 * kWave)) void row_stats_topp_kernel(StatsParams P) {
     using namespace rows;
