@@ -95,10 +95,13 @@ def test_skip_flags_leave_the_other_half_bit_identical(name, kw):
     ("tiny-chain-f32", dict(batch=2, seed=(24, 1))),                              # tiled VALU attention
     ("llama7b-medusa-greedy", dict(prefix_len=900, seed=(24, 2))),                # MFMA, prefix splits
     ("llama7b-medusa-greedy", dict(mode="sampling", prefix_len=300, seed=(24, 3))),
+    ("70b-gqa-medusa", dict(mode="greedy", prefix_len=256, seed=(24, 5))),        # two rows per workgroup after
+    ("70b-gqa-medusa", dict(mode="greedy", prefix_len=1000, seed=(24, 4))),       # the attention grid
 ])
 def test_row_statistics_inside_the_attention_launch(name, kw):
-    """Small attention grids carry the row statistics in the same launch; a
-    timing handle keeps them apart.  Both give the same outputs bit for bit."""
+    """The attention launch carries the row statistics (beside a small
+    attention grid, or after one that fills the GPU); a timing handle keeps
+    them apart.  Both give the same outputs bit for bit."""
     import json
     import torch
     from tree_attention_verification_verify_amd import SpecVerify

@@ -219,16 +219,29 @@ long attention_blocks(const AttnPlan& p, int B, int Hkv) {
     return p.tiled ? groups : groups * p.rowblocks;
 }
 
-// Whether the attention launch carries the row statistics: 256-thread
-// attention workgroups (the statistics' size), dense caches, no top-p cut, no
-// per-stage timing, and room on the CUs for both grids at once (at the
-// llama7b Medusa shape 128 attention and 64 statistics workgroups on 256 CUs).
+// Whether the attention launch carries the row statistics (dense caches, no
+// top-p cut, no per-stage timing):
+//  * 256-thread attention workgroups (the statistics' size) with room on the
+//    CUs for both grids at once: the statistics run beside the attention (at
+//    the llama7b Medusa shape 128 attention and 64 statistics workgroups on
+//    256 CUs);
+//  * 512-thread MFMA workgroups that fill every CU, with rows of at most
+//    rows::CHUNK logits and one workgroup of two rows per CU at most:
+//    these follow the attention in the same launch and start on each CU as
+//    its attention workgroup ends, with no launch boundary between the two
+//    (the 70B GQA tree shape in greedy mode: 0.1542 -> 0.1526 ms per step).
+//    A second round would hold one such workgroup per CU (the attention's
+//    LDS), half the statistics kernel's loads in flight: in sampling mode
+//    (1016 rows) that cost what the boundary saved.
+constexpr bool kFuseAfterAttention = true;
 bool fuse_row_stats(const Workspace& ws, const AttnPlan& p, int B, int Hkv, const sv::StatsParams& tp, bool paged,
                     bool timing) {
     const int threads = p.mfma ? p.waves * 64 * sv::kMfmaHalves : (p.tiled ? sv::kStatsThreads : 64);
     const long stats_blocks = (long)B * (tp.sampling ? 2 * tp.T : tp.T);
-    return threads == sv::kStatsThreads && !paged && !timing && ws.cus > 0 && sv::row_stats_streams(tp) &&
-           attention_blocks(p, B, Hkv) + stats_blocks <= ws.cus;
+    if (paged || timing || ws.cus <= 0 || !sv::row_stats_streams(tp)) return false;
+    if (threads == sv::kStatsThreads) return attention_blocks(p, B, Hkv) + stats_blocks <= ws.cus;
+    return kFuseAfterAttention && p.mfma && threads == 2 * sv::kStatsThreads && tp.V <= sv::kVocabChunk &&
+           attention_blocks(p, B, Hkv) >= ws.cus && (stats_blocks + 1) / 2 <= ws.cus;
 }
 
 struct spec_verify_handle {

@@ -30,17 +30,21 @@ __device__ __forceinline__ const float* row_ptr(const StatsParams& P, int b, int
 // half-step, one fma and one exp2 (Z); the argmax is located only when a
 // batch raises the thread's best value (first batch, then rarely), by the
 // first position holding the batch maximum (positions are in id order).
+//
+// One group of kStatsThreads threads (t = 0..kStatsThreads-1 within the
+// group, sm its own) takes row blk.  An inactive group (a row that needs no
+// statistics, or none at all) reads nothing and writes nothing but passes the
+// same two barriers, so two groups can share a workgroup.
 template <bool WITH_Z>
-__device__ __forceinline__ void row_stats_stream_block(const StatsParams& P, int blk) {
+__device__ __forceinline__ void row_stats_stream_group(const StatsParams& P, int blk, int t, bool active, StatsSmem& sm) {
     constexpr int U = kStatsUnroll / 2;
-    __shared__ StatsSmem sm;
     const int nrows = P.sampling ? 2 * P.T : P.T;
     const int b = blk / nrows, r = blk - b * nrows;
-    if (r == P.T) return;   // no draft row for the root
-    const float* row = r < P.T ? P.target + ((size_t)b * P.T + r) * P.V
+    const float* row = !active ? P.target
+                     : r < P.T ? P.target + ((size_t)b * P.T + r) * P.V
                                : P.draft + ((size_t)b * P.T + (r - P.T)) * P.V;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int V = P.V;
+    const int tid = t, lane = tid & 63, wave = tid >> 6;
+    const int V = active ? P.V : 0;
     const float ilog = P.ilog;
     const bool aligned = (((uintptr_t)row) & 15) == 0;
     const int nv4 = aligned ? (V >> 2) : 0;
@@ -135,7 +139,7 @@ __device__ __forceinline__ void row_stats_stream_block(const StatsParams& P, int
         sm.bi[wave] = bi;
     }
     __syncthreads();
-    if (tid == 0) {
+    if (tid == 0 && active) {
         double Z = 0.0;
         float best = sm.bv[0];
         int besti = sm.bi[0];
@@ -149,6 +153,29 @@ __device__ __forceinline__ void row_stats_stream_block(const StatsParams& P, int
         st.Z = Z;
         P.stats[(size_t)b * nrows + r] = st;
     }
+}
+
+// Row blk by a workgroup of kStatsThreads threads (the root's draft row has
+// no statistics: the whole workgroup leaves).
+template <bool WITH_Z>
+__device__ __forceinline__ void row_stats_stream_block(const StatsParams& P, int blk) {
+    __shared__ StatsSmem sm;
+    const int nrows = P.sampling ? 2 * P.T : P.T;
+    if (blk % nrows == P.T) return;
+    row_stats_stream_group<WITH_Z>(P, blk, threadIdx.x, true, sm);
+}
+
+// Rows 2 blk2 and 2 blk2 + 1 by the two halves of a workgroup of
+// 2 kStatsThreads threads, each half with exactly the arithmetic of
+// row_stats_stream_block (so the statistics are the same bits).
+template <bool WITH_Z>
+__device__ __forceinline__ void row_stats_stream_pair(const StatsParams& P, int blk2) {
+    __shared__ StatsSmem sm2[2];
+    const int nrows = P.sampling ? 2 * P.T : P.T;
+    const int half = threadIdx.x / kStatsThreads;
+    const int blk = 2 * blk2 + half;
+    const bool active = blk < P.B * nrows && blk % nrows != P.T;
+    row_stats_stream_group<WITH_Z>(P, blk, (int)threadIdx.x - half * kStatsThreads, active, sm2[half]);
 }
 
 }  // namespace sv

@@ -72,14 +72,20 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
 // them in L2 for the others (at the 70B GQA tree shape, four row blocks,
 // non-temporal tile loads fetched 320 MB instead of 288 MB and took 1.7% longer).
 // FUSE: workgroups from attn_blocks on compute the streaming row statistics
-// of S instead (one per logits row; 256-thread workgroups only).
+// of S instead (one logits row per 256 threads: one row per 256-thread
+// workgroup, two per 512-thread workgroup).
 template <int D, int WAVES, bool PAGED, int H, bool STREAM, bool FUSE = false>
 __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams P, StatsParams S, int attn_blocks) {   // 2 waves per SIMD
     if constexpr (FUSE) {
-        static_assert(WAVES * 64 * H == kStatsThreads, "row statistics workgroups of 256 threads");
         if ((int)blockIdx.x >= attn_blocks) {
-            if (S.sampling) row_stats_stream_block<true>(S, (int)blockIdx.x - attn_blocks);
-            else row_stats_stream_block<false>(S, (int)blockIdx.x - attn_blocks);
+            if constexpr (WAVES * 64 * H == kStatsThreads) {   // one row per workgroup
+                if (S.sampling) row_stats_stream_block<true>(S, (int)blockIdx.x - attn_blocks);
+                else row_stats_stream_block<false>(S, (int)blockIdx.x - attn_blocks);
+            } else {                                           // two rows, one per half
+                static_assert(WAVES * 64 * H == 2 * kStatsThreads, "row statistics groups of 256 threads");
+                if (S.sampling) row_stats_stream_pair<true>(S, (int)blockIdx.x - attn_blocks);
+                else row_stats_stream_pair<false>(S, (int)blockIdx.x - attn_blocks);
+            }
             return;
         }
     }
@@ -769,10 +775,13 @@ template <int D, bool PAGED, bool STREAM>
 void launch_mfma_waves_s(const AttnParams& p, int waves, dim3 grid, hipStream_t s, const StatsParams* fused, int blocks) {
     constexpr int H = kMfmaHalves;
     const StatsParams S = fused ? *fused : StatsParams{};
+    const int nrows = S.sampling ? 2 * S.T : S.T;
     if (fused && waves * 64 * H == kStatsThreads) {
-        const int nrows = S.sampling ? 2 * S.T : S.T;
         hipLaunchKernelGGL((attn_mfma_kernel<D, kStatsThreads / (64 * H), PAGED, H, STREAM, true>),
                            dim3(blocks + S.B * nrows), dim3(kStatsThreads), 0, s, p, S, blocks);
+    } else if (fused && waves * 64 * H == 2 * kStatsThreads) {
+        hipLaunchKernelGGL((attn_mfma_kernel<D, 2 * kStatsThreads / (64 * H), PAGED, H, STREAM, true>),
+                           dim3(blocks + (S.B * nrows + 1) / 2), dim3(2 * kStatsThreads), 0, s, p, S, blocks);
     } else if (waves == 4) {
         hipLaunchKernelGGL((attn_mfma_kernel<D, 4, PAGED, H, STREAM>), grid, dim3(256 * H), 0, s, p, S, blocks);
     } else if (waves == 2) {
