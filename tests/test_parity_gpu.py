@@ -177,13 +177,14 @@ def test_top_p_cut_below_the_candidate_probabilities(vocab, seed):
     assert int(got["node_accept"][:, 1:].sum()) > 0
 
 
-@pytest.mark.parametrize("vocab,seed", [(16, 1601), (100, 1001), (777, 7771)])
-def test_top_p_small_vocabularies(vocab, seed):
+@pytest.mark.parametrize("vocab,seed", [(16, 1601), (100, 1001), (777, 7771), (32768, 3276), (32769, 3277)])
+def test_top_p_vocabulary_sizes(vocab, seed):
     # rows far shorter than one register slot of the top-p workgroup (2048
     # ids): most threads hold only masked entries, and a vocabulary of 777 is
-    # not a multiple of 4 (single-float loads)
+    # not a multiple of 4 (single-float loads); 32768 ids is the longest row
+    # held in registers, 32769 the shortest streamed one (a last block of one id)
     spec = synth.workload("chain-batch32-topp", batch=4, prefix_len=64, ragged=None, vocab=vocab, seed=(4, seed))
-    got, ref, _ = check(synth.make_case(spec), "topp-small-V%d" % vocab)
+    got, ref, _ = check(synth.make_case(spec), "topp-V%d" % vocab)
     assert int(got["node_accept"][:, 1:].sum()) > 0
 
 
