@@ -351,8 +351,9 @@ const char* spec_verify_last_error(void);
  * workgroup, row blocks, prefix splits and keys per split, whether the
  * finishing launch selects and/or merges splits, and whether the row
  * statistics run inside the attention launch ("vocab_in_attention_launch":
- * small attention grids that leave room on the CUs, dense caches, no top-p
- * cut, handles without SPEC_VERIFY_FLAG_TIMING).  For tools that report
+ * beside a small attention grid that leaves room on the CUs, or after one
+ * that fills them when one round of two-row workgroups follows; dense
+ * caches, no top-p cut, handles without SPEC_VERIFY_FLAG_TIMING).  For tools that report
  * per-kernel figures (the pages ask for the latency of each round:
  * "投机解码的五条路线", section "怎么选,以及怎么算收益").  Errors: INVALID_ARG
  * (NULL argument, batch or nodes out of range, buffer too small). */
