@@ -128,10 +128,11 @@ struct TreeParams {
     int32_t* arrive;            // [B][levels] finished slices per row (zero between calls)
 };
 
-// Returns hipSuccess or the launch error.  fused != nullptr (only where
-// attention_fuses_stats allows it): the same launch also runs the streaming
-// row statistics of *fused, one extra 256-thread workgroup per row, beside
-// the attention workgroups (for grids that leave CUs idle).
+// Returns hipSuccess or the launch error.  fused != nullptr (only where the
+// planner allows it): the same launch also runs the streaming row statistics
+// of *fused in workgroups of its own after the attention workgroups: one row
+// per 256-thread workgroup (beside a grid that leaves CUs idle), or two rows
+// per 512-thread workgroup (after a grid that fills the GPU).
 hipError_t launch_attention_mfma(const AttnParams& p, int waves, hipStream_t s, const StatsParams* fused = nullptr);
 hipError_t launch_attention_valu(const AttnParams& p, bool bf16, hipStream_t s);
 // VALU attention with 4 waves sharing double-buffered tiles: R <= 8 rows per KV

@@ -233,14 +233,13 @@ long attention_blocks(const AttnPlan& p, int B, int Hkv) {
 //    A second round would hold one such workgroup per CU (the attention's
 //    LDS), half the statistics kernel's loads in flight: in sampling mode
 //    (1016 rows) that cost what the boundary saved.
-constexpr bool kFuseAfterAttention = true;
 bool fuse_row_stats(const Workspace& ws, const AttnPlan& p, int B, int Hkv, const sv::StatsParams& tp, bool paged,
                     bool timing) {
     const int threads = p.mfma ? p.waves * 64 * sv::kMfmaHalves : (p.tiled ? sv::kStatsThreads : 64);
     const long stats_blocks = (long)B * (tp.sampling ? 2 * tp.T : tp.T);
     if (paged || timing || ws.cus <= 0 || !sv::row_stats_streams(tp)) return false;
     if (threads == sv::kStatsThreads) return attention_blocks(p, B, Hkv) + stats_blocks <= ws.cus;
-    return kFuseAfterAttention && p.mfma && threads == 2 * sv::kStatsThreads && tp.V <= sv::kVocabChunk &&
+    return p.mfma && threads == 2 * sv::kStatsThreads && tp.V <= sv::kVocabChunk &&
            attention_blocks(p, B, Hkv) >= ws.cus && (stats_blocks + 1) / 2 <= ws.cus;
 }
 
