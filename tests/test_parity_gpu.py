@@ -276,6 +276,27 @@ def test_dense_mfma_eight_prefix_splits_every_row():
     check(synth.make_case(spec), "gqa-medusa-B1-L4096-8splits")
 
 
+def test_ragged_batch_longest_first_with_prefix_splits():
+    # prefixes of 2472, 1514 and 2592 slots: the attention grid takes the
+    # sequences longest first, so the third sequence's workgroups come first
+    # and the partial results of every prefix split must still land in its
+    # own (sequence, KV head, split) slots for the merge
+    import json
+    import torch
+    from tree_attention_verification_verify_amd import SpecVerify
+
+    spec = synth.workload("70b-gqa-medusa", batch=3, ragged=(900, 3000), seed=(3, 3001))
+    case = synth.make_case(spec)
+    cfg = handle_config(case.spec, kv_capacity=case.k_cache.shape[2])
+    with torch.cuda.device(0):
+        with SpecVerify(**cfg) as sv:
+            plan = sv.describe(case.batch, case.nodes)
+    plan = plan if isinstance(plan, dict) else json.loads(plan)
+    assert plan["attention"] == "attn_mfma_kernel" and plan["nsplit"] > 1, plan
+    assert int(np.argmax(case.kv_len)) != 0
+    check(case, "gqa-medusa-ragged-B3")
+
+
 def test_split_boundary_inside_the_tree_slots():
     # capacity 4608 -> 8 splits of 576 slots; L = 4000 puts the split (and tile)
     # boundary at slot 4032 between tree nodes 31 and 32, so the tree's keys

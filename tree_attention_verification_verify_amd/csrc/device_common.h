@@ -111,10 +111,11 @@ constexpr int kStreamPolicy = 2;
 // first and the shortest fill the tail: with more workgroups than fit on the
 // GPU at once, a long prefix started last would otherwise run on alone.  One
 // wave ranks up to 64 sequences (each lane one, the others' lengths
-// broadcast in turn); larger batches keep the index order.  Every wave that
-// calls it gets the same answer.
-__device__ __forceinline__ int seq_by_length(const int* kv_len, int B, int r) {
-    if (B <= 1 || B > kWave) return r;
+// broadcast in turn); larger batches keep the index order.  Returns the
+// sequence and its kv_len (one load either way); every wave that calls it
+// gets the same answer.
+__device__ __forceinline__ int2 seq_by_length(const int* kv_len, int B, int r) {
+    if (B <= 1 || B > kWave) return make_int2(r, kv_len[r]);
     const int lane = threadIdx.x & (kWave - 1);
     const int li = lane < B ? kv_len[lane] : 0;
     int rank = 0;
@@ -123,7 +124,8 @@ __device__ __forceinline__ int seq_by_length(const int* kv_len, int B, int r) {
         rank += (lj > li || (lj == li && j < lane)) ? 1 : 0;
     }
     const unsigned long long m = __ballot(lane < B && rank == r);
-    return m ? __builtin_ctzll(m) : r;
+    const int b = m ? __builtin_ctzll(m) : r;
+    return make_int2(b, __builtin_amdgcn_readlane(li, b));
 }
 
 // Arrival count of a group of G workgroups at a per-group counter: true for

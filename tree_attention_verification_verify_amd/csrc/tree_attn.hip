@@ -122,10 +122,15 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
         group = (local / P.rowblocks) * 8 + xcd;
     }
     if (group >= P.B * P.Hkv * P.nsplit) return;
-    const int pair = group / P.nsplit, split = group - pair * P.nsplit;
-    const int b = pair / P.Hkv, kvh = pair - b * P.Hkv;
+    // workgroups in order of decreasing prefix length (longest first); group
+    // becomes the (sequence, KV head, split) slot of the partial results
+    const int pair0 = group / P.nsplit, split = group - pair0 * P.nsplit;
+    const int rank = pair0 / P.Hkv, kvh = pair0 - rank * P.Hkv;
+    const int2 bl = seq_by_length(P.kv_len, P.B, rank);
+    const int b = bl.x, L = bl.y;
+    const int pair = b * P.Hkv + kvh;
+    group = pair * P.nsplit + split;
     const int T = P.T, g = P.g;
-    const int L = P.kv_len[b];
     bool kv_ok = (L >= 0) && (L <= P.Lcap - T);
     const int N = L + T;
     if constexpr (PAGED) {   // every table entry of the used slots must name a page of the pool

@@ -71,11 +71,11 @@ __global__ __launch_bounds__(VW * 64, 2) void attn_valu_tiled_kernel(AttnParams 
     // is the (sequence, KV head, split) slot of the partial results
     const int pair0 = blockIdx.x / P.nsplit, split = blockIdx.x - pair0 * P.nsplit;
     const int rank = pair0 / P.Hkv, kvh = pair0 - rank * P.Hkv;
-    const int b = seq_by_length(P.kv_len, P.B, rank);
+    const int2 bl = seq_by_length(P.kv_len, P.B, rank);
+    const int b = bl.x, L = bl.y;
     const int pair = b * P.Hkv + kvh;
     const int group = pair * P.nsplit + split;
     const int T = P.T, g = P.g, R = P.R;
-    const int L = P.kv_len[b];
     bool kv_ok = (L >= 0) && (L <= P.Lcap - T);
     const int N = L + T;
     if constexpr (PAGED) {
