@@ -188,6 +188,21 @@ def test_top_p_vocabulary_sizes(vocab, seed):
     assert int(got["node_accept"][:, 1:].sum()) > 0
 
 
+@pytest.mark.parametrize("vocab", [32000, 40000])
+@pytest.mark.parametrize("setting", ["top_p=0.05", "temperature=0.05"])
+def test_top_p_narrow_nuclei(vocab, setting):
+    # a nucleus of a few tokens: top_p 0.05 (the cut in the largest
+    # probabilities), or temperature 0.05 (most probabilities underflow and
+    # the largest holds nearly all the mass); in registers at 32000 ids,
+    # streamed at 40000
+    key, val = setting.split("=")
+    seed = (4, (500 if key == "top_p" else 600) + vocab % 7)
+    spec = synth.workload("chain-batch32-topp", batch=3, prefix_len=64, ragged=None, vocab=vocab, seed=seed,
+                          **{key: float(val)})
+    got, ref, _ = check(synth.make_case(spec), "topp-narrow-%s-V%d" % (setting, vocab))
+    assert int(got["node_accept"][:, 1:].sum()) > 0
+
+
 @pytest.mark.parametrize("layout,seed", [("flat", 7101), ("one-wave", 7102)])
 def test_top_p_candidate_list_overflow(layout, seed):
     # rows whose candidates for the cut (e >= 2^-12 of the largest) do not fit
