@@ -270,8 +270,11 @@ __global__ __launch_bounds__(TPB, 2 * TPB / (4 * kWave)) void row_stats_topp_ker
     // the probabilities of one float4: candidates into this wave's list
     // segment (a slot's candidates together, positions from the ballot), the
     // others into the thread's fp64 tail sum.  While the segment has room for
-    // four more full slots the positions need no bounds test.
-    uint32_t* const seg = clist + wave * SEG;
+    // five more full slots every lane stores without a branch: a lane without
+    // a candidate writes past the slot's last listed entry (a position that
+    // a later candidate, stored after it, overwrites, or that is never read),
+    // so the logits of a float4 do not wait on each other's control flow.
+    uint32_t* const seg = clist + __builtin_amdgcn_readfirstlane(wave) * SEG;
     uint32_t nseg = 0;   // the same in every lane of the wave
     double tail = 0.0;
     auto take4 = [&](const float (&v)[4]) {
@@ -283,15 +286,20 @@ __global__ __launch_bounds__(TPB, 2 * TPB / (4 * kWave)) void row_stats_topp_ker
                 const bool cand = bits >= kCandBits;
                 t4[c] = cand ? 0.f : v[c];
                 const unsigned long long mask = __ballot(cand);
-                if (cand) {
-                    const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, nseg));
-                    if (!checked || pos < (uint32_t)SEG) seg[pos] = bits;
+                // position among this slot's candidates; the slot's entries
+                // start at the (wave-uniform) end of the list
+                const uint32_t own = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                const uint32_t cnt = (uint32_t)__popcll(mask);
+                if (!checked) {
+                    (seg + nseg)[cand ? own : cnt + (uint32_t)lane] = bits;
+                } else if (cand && nseg + own < (uint32_t)SEG) {
+                    seg[nseg + own] = bits;
                 }
-                nseg += (uint32_t)__popcll(mask);
+                nseg += cnt;
             }
         };
-        if (nseg + 4u * kWave <= (uint32_t)SEG) list(false);
+        if (nseg + 5u * kWave <= (uint32_t)SEG) list(false);
         else list(true);
         tail += (double)((t4[0] + t4[1]) + (t4[2] + t4[3]));
         // added where it is made (left to itself the compiler makes every
