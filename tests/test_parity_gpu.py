@@ -236,6 +236,38 @@ def test_top_p_candidate_list_overflow(layout, seed):
     assert int(got["node_accept"][:, 1:].sum()) > 0
 
 
+def test_top_p_candidate_segments_nearly_full():
+    # every wave of a 512-thread row workgroup lists 900 candidates near
+    # logit -7 (e about 2^-11) plus its share of 300 ids near 0 that hold the
+    # nucleus: its segment of 1024 entries fills past the point where the
+    # list stores stop being unconditional (704 entries) without
+    # overflowing, so both store forms write the same list
+    vocab, seed = 32000, 7103
+    spec = synth.workload("chain-batch32-topp", batch=3, prefix_len=90, ragged=None, vocab=vocab, top_p=0.9,
+                          temperature=1.0, seed=(4, seed))
+    case = synth.make_case(spec)
+    rng = np.random.default_rng(seed)
+    B, T = case.batch, case.nodes
+    ids = np.arange(vocab)
+    wave_of = ((ids >> 2) & 511) // 64     # thread t holds ids 4 (t + 512 j) + c
+    top = rng.choice(vocab, size=300, replace=False)
+    rest = np.setdiff1d(ids, top)
+    mid = np.concatenate([rng.choice(rest[wave_of[rest] == w], size=900, replace=False) for w in range(8)])
+    for logits, noise in ((case.target_logits, 0.0), (case.draft_logits, 0.1)):
+        logits[:] = -20.0
+        for sel, centre, sd in ((top, 0.0, 0.3), (mid, -7.0, 0.1)):
+            base = rng.normal(centre, sd, size=(B, T, sel.size)).astype(np.float32)
+            logits[:, :, sel] = base + (rng.normal(0, noise, size=base.shape).astype(np.float32) if noise else 0)
+    case.tokens[:, 1:] = rng.choice(top, size=(B, T - 1))
+    for row in (case.target_logits[0, 0], case.target_logits[B - 1, T - 1], case.draft_logits[0, 1]):
+        z = row.astype(np.float64)
+        cand = np.exp(z - z.max()) >= 2.0 ** -12
+        per_wave = np.bincount(wave_of[cand], minlength=8)
+        assert per_wave.min() > 704 and per_wave.max() <= 1024, per_wave
+    got, ref, _ = check(case, "topp-list-nearly-full")
+    assert int(got["node_accept"][:, 1:].sum()) > 0
+
+
 # ------------------------------------------------------------------ full sizes, sampled attention rows
 
 def _full(name, picks, deep_seqs=(0,), max_near=0, **kw):
