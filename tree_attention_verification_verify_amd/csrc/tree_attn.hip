@@ -318,7 +318,7 @@ __global__ __launch_bounds__(WAVES * 64 * H, 2) void attn_mfma_kernel(AttnParams
                 const int key = t + sub * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
                 const unsigned rel = (unsigned)(key - L);
                 const bool tree_vis = (anc_row >> (rel & 63u)) & 1ull;
-                const bool vis = (key < k1) && ((key < L) | tree_vis);
+                const bool vis = (key < k1) & ((key < L) | tree_vis);   // no short circuit: no branch per key
                 const unsigned long long hide = __ballot(!vis);   // lanes whose key is hidden
                 float x = s[sub][e];
                 asm volatile("v_cndmask_b32_e64 %0, %0, %1, %2" : "+v"(x) : "v"(-INFINITY), "s"(hide));
